@@ -1,0 +1,296 @@
+/*
+ * moe_gemm.h -- C ABI of the MI355X (gfx950) MoE grouped-GEMM library.
+ *
+ * The library computes one matrix product per expert over a jagged,
+ * routing-dependent number of token rows, as stated on the source pages:
+ *
+ *   [GG]  grouped_gemm PR "Support GPU-resident batch sizes": gmm(x, w,
+ *         batch_sizes, trans_b) with the batch sizes resident on the device,
+ *         its backward (gradient of out.sum()), and the review thread's
+ *         dynamic-k problems (dW) sorted by k, descending, with the outputs of
+ *         k = 0 problems zeroed.
+ *   [F8I4] FBGEMM PR "F8I4 Grouped Gemm Optimization for Sparse M": fp8
+ *         activations x int4 weights; kernel arguments cover only
+ *         min(total_M, groups) problems so empty groups cost nothing.
+ *   [FMOE] applied-ai issue "Column-major fused MoE": moe_align_block_size
+ *         (token ids sorted by expert, padded to block_m), fused_moe_kernel
+ *         (sorted_token_ids, expert_ids, top-k weights), silu_and_mul and the
+ *         top-k weighted sum.
+ *   [FP8] torchao commit "Optimize FP8 MoE backward pass: fused colwise kernel
+ *         + AMD tuning": fused rowwise absmax + saturated fp8 cast, and the
+ *         (dual) per-group colwise scales kernel with column-major output.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is caller-owned DEVICE memory.  The library never
+ *   allocates, frees or reads device memory on the host; nothing is copied
+ *   device -> host and nothing synchronizes.  Work is enqueued on `stream`
+ *   (a hipStream_t; NULL is the legacy default stream).
+ * - bf16 tensors are IEEE bfloat16 bit patterns; fp8 is OCP E4M3 ("e4m3fn",
+ *   max 448, no infinities); int4 is two's-complement nibbles.
+ * - Group sizes are device int32 [E]; group g owns the consecutive rows
+ *   [offs[g], offs[g+1]) of every token-stacked matrix, offs being the
+ *   exclusive prefix sum.  total_M is the host-known row count of those
+ *   matrices; the sizes must be >= 0 and sum to at most total_M.  Rows past
+ *   the sum belong to no group and are left untouched in outputs.  A device
+ *   violation (negative size, sum > total_M) is clamped so nothing is written
+ *   out of bounds, and sets a sticky error word in the workspace
+ *   (mg_workspace_error reads it back, synchronously; test use only).
+ * - FP8 scales are fp32 quantization MULTIPLIERS: value = code / scale.
+ * - Return value: MG_OK, or a negative status after which nothing has been
+ *   enqueued; mg_last_error() then describes the problem (thread-local).
+ *   Host-side checks: null pointers, sizes out of range, unsupported
+ *   alignment, E > 1024, workspace too small.
+ * - All calls are legal inside hipStreamBeginCapture / hipStreamEndCapture.
+ */
+#ifndef MOE_GEMM_H
+#define MOE_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* mg_stream_t; /* hipStream_t */
+
+enum {
+  MG_OK = 0,
+  MG_EINVAL = -1,        /* invalid argument */
+  MG_EUNSUPPORTED = -2,  /* valid but unsupported shape/alignment */
+  MG_EWORKSPACE = -3,    /* workspace missing or too small */
+  MG_EHIP = -4           /* a HIP launch failed */
+};
+
+/* Largest number of experts/groups (one workgroup scans the sizes; [GG]
+ * description: a single thread block, hence at most 1024 experts). */
+#define MG_MAX_EXPERTS 1024
+
+/* ------------------------------------------------------------------------ */
+/* Workspace                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace that every grouped-GEMM call with these E and
+ * total_M needs (offsets, tile work lists, error word).  Depends on host
+ * values only.  The workspace may be reused by consecutive calls on one
+ * stream; calls that overlap in time need distinct workspaces. */
+size_t mg_workspace_bytes(int32_t E, int64_t total_M);
+
+/* Reads the sticky device error word of a workspace (hipMemcpy, blocking):
+ * 0 = none, 1 = negative group size, 2 = sizes sum past total_M. */
+int32_t mg_workspace_error(const void* ws);
+
+/* Clears the sticky error word (enqueued on stream). */
+int mg_workspace_clear(void* ws, mg_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Argument builder ([GG] review thread: a single-block scan of the batch    */
+/* sizes fills the per-problem arguments on the device; [F8I4]: only         */
+/* non-empty groups get work).                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Work-list kinds. */
+enum { MG_WL_FIXED_M = 0, MG_WL_DYNAMIC_K = 1 };
+
+/* Runs the device builder on group_sizes and writes, to caller buffers:
+ *   offs    int32 [E+1]  exclusive prefix sum (offs[E] = clamped total);
+ *   count   int32 [1]    number of entries;
+ *   entries int32 [cap][4]:
+ *     MG_WL_FIXED_M: for each non-empty group g ascending, one entry per
+ *       bm-row slice {g, first_row, rows (<= bm), 0};
+ *       cap >= total_M / bm + min(total_M, E).
+ *     MG_WL_DYNAMIC_K: all E groups ordered by size descending, ties by g
+ *       ascending, {g, offs[g], size, 0}; cap >= E.
+ * The grouped GEMMs run this same builder internally (bm = their row tile).
+ * Errors: MG_EINVAL for null pointers, E outside [1, 1024], bm < 1, cap too
+ * small for the bound above. */
+int gmm_build_worklist(int32_t kind, const int32_t* group_sizes, int32_t E,
+                       int64_t total_M, int32_t bm, int32_t* offs,
+                       int32_t* count, int32_t* entries, int64_t cap,
+                       mg_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* bf16 grouped GEMM ([GG] description: gmm(x, w, batch_sizes, trans_b)).    */
+/* ------------------------------------------------------------------------ */
+
+/* Forward: Y[r, :] = X[r, :] . W[g(r)] for every row r of group g.
+ *   x  bf16 [total_M, K] row-major
+ *   w  bf16 [E, K, N] (trans_b = 0) or [E, N, K] (trans_b = 1), contiguous
+ *   y  bf16 [total_M, N] row-major; fp32 accumulation, round-to-nearest-even
+ * K and N must be multiples of 8 (16-byte rows).  total_M = 0 is a no-op. */
+int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes,
+            int32_t E, int64_t total_M, int32_t K, int32_t N, int32_t trans_b,
+            void* y, void* ws, size_t ws_bytes, mg_stream_t stream);
+
+/* Backward of gmm_fwd for an upstream gradient dy [total_M, N]:
+ *   dx[r, :] = dy[r, :] . W[g(r)]^T          (bf16 [total_M, K]; may be NULL)
+ *   dw[g]    = X_g^T . dY_g                   (bf16, laid out like w; may be
+ *              NULL).  The contraction runs over the group's own rows (a
+ *              "dynamic-k" problem); an empty group's dw is exactly zero.
+ * At least one of dx, dw must be non-NULL. */
+int gmm_bwd(const void* dy, const void* x, const void* w,
+            const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K,
+            int32_t N, int32_t trans_b, void* dx, void* dw, void* ws,
+            size_t ws_bytes, mg_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* FP8 grouped GEMM ([FP8] commit message: rowwise-scaled fp8 operands for   */
+/* the forward and dX, per-group colwise scales for dW).  Accumulation is    */
+/* fp32 over e4m3 products; the epilogue divides by both scales and rounds   */
+/* to bf16.                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* An fp8 stacked weight: code of element (e, c, j) -- c the contraction
+ * index, j the output column -- at codes[e * expert_stride + j * ld + c]
+ * (contraction index contiguous), with scale scales[e * J + j]. */
+typedef struct mg_fp8_weight {
+  const uint8_t* codes;
+  const float* scales;
+  int64_t ld;
+  int64_t expert_stride;
+} mg_fp8_weight;
+
+/* Forward: Y[r, n] = sum_k (xq[r,k] / sx[r]) * (Wq(g,k,n) / sw[g,n]).
+ *   xq  e4m3 [total_M, K] row-major, sx fp32 [total_M] (rowwise quantizer)
+ *   w   codes of W(e,k,n) at e*expert_stride + n*ld + k, scales [E][N]
+ *       (e.g. the colwise quantizer on W viewed [E*K, N] with E equal groups
+ *       gives ld = E*K, expert_stride = K)
+ *   y   bf16 [total_M, N]
+ * K must be a multiple of 16 and N a multiple of 8; ld and expert_stride
+ * multiples of 16. */
+int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w,
+                const int32_t* group_sizes, int32_t E, int64_t total_M,
+                int32_t K, int32_t N, void* y, void* ws, size_t ws_bytes,
+                mg_stream_t stream);
+
+/* Backward with fp8 operands (either output may be NULL):
+ *   dx[r,k] = sum_n (dyq[r,n]/sdy[r]) * (Wq(g,n,k)/sw[g,k])
+ *       dyq e4m3 [total_M, N] rowwise with sdy [total_M]; w codes of W(e,k,n)
+ *       at e*expert_stride + k*ld + n (contraction n contiguous), scales
+ *       [E][K] (the rowwise quantizer on W viewed [E*K, N] gives ld = N,
+ *       expert_stride = K*N);
+ *   dw[g,k,n] = sum_{r in g} (xc[k,r]/sxc[g,k]) * (dyc[n,r]/sdyc[g,n])
+ *       xc e4m3 column-major [K][total_M] with sxc [E][K], dyc column-major
+ *       [N][total_M] with sdyc [E][N] (the dual per-group colwise quantizer);
+ *       dw bf16 [E, K, N]; empty groups give zero.
+ * total_M must be a multiple of 16 when dw is requested. */
+int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w,
+                const uint8_t* xc, const float* sxc, const uint8_t* dyc,
+                const float* sdyc, const int32_t* group_sizes, int32_t E,
+                int64_t total_M, int32_t K, int32_t N, void* dx, void* dw,
+                void* ws, size_t ws_bytes, mg_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* F8I4 grouped GEMM ([F8I4]: fp8 activations x int4 weights, sparse M).     */
+/* ------------------------------------------------------------------------ */
+
+/* Y[r,n] = (1/sx[r]) * sum_j sw[g,j,n] * sum_{k in chunk j} xq[r,k] * q(g,n,k)
+ *   xq  e4m3 [total_M, K] row-major, sx fp32 [total_M]
+ *   w4  int4 packed [E][N][K/2]; byte (e,n,i) holds k = 2i in its low
+ *       nibble and k = 2i+1 in its high nibble
+ *   sw  bf16 [E][K/128][N], one scale per 128-long chunk of K
+ *   y   bf16 [total_M, N]
+ * K must be a multiple of 128 and N a multiple of 8.  Only non-empty
+ * groups are visited. */
+int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4,
+                 const void* sw, const int32_t* group_sizes, int32_t E,
+                 int64_t total_M, int32_t K, int32_t N, void* y, void* ws,
+                 size_t ws_bytes, mg_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* FP8 quantizers ([FP8] commit message and colwise kernel).                 */
+/* Per scaled block: amax = max |x|; t = fp32(448 / max(amax, 1e-12)) (the   */
+/* division in fp64); scale s = 2^floor(log2 t) (t's mantissa cleared);      */
+/* code = e4m3_rne(clamp(x * s, -448, 448)).                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Rowwise: x bf16 [rows, cols] with row stride ld (elements, >= cols) ->
+ * q e4m3 [rows, cols] contiguous, scales fp32 [rows].  cols % 8 == 0 and
+ * ld % 8 == 0. */
+int quantize_rowwise_fp8(const void* x, int64_t rows, int32_t cols, int64_t ld,
+                         uint8_t* q, float* scales, mg_stream_t stream);
+
+/* Per-group colwise, single or dual: for each group g and column c of a
+ * (and of b, if non-NULL), one scale over the group's rows.  Codes are
+ * written column-major: qa[c * rows + r]; scales sa[g * cols_a + c].  b,
+ * qb, sb are either all NULL (single tensor) or all set (both tensors share
+ * the group sizes and row count).  Rows beyond the sizes' sum are not
+ * written.  cols % 8 == 0. */
+int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a,
+                                   const void* b, int32_t cols_b,
+                                   const int32_t* group_sizes, int32_t G,
+                                   int64_t rows, uint8_t* qa, float* sa,
+                                   uint8_t* qb, float* sb, mg_stream_t stream);
+
+/* int4 weight quantizer for gmm_fwd_f8i4: w bf16 [E, K, N] -> w4 packed
+ * [E][N][K/2] and sw bf16 [E][K/128][N]; per (e, n, 128-chunk j):
+ * s = bf16_rne(max|w| / 7), q = clamp(rne(w / s), -8, 7) (q = 0 if s = 0).
+ * K % 128 == 0, N % 8 == 0. */
+int quantize_int4_weights(const void* w, int32_t E, int32_t K, int32_t N,
+                          uint8_t* w4, void* sw, mg_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Token permutation for the token-sorted fused path ([FMOE]).               */
+/* ------------------------------------------------------------------------ */
+
+/* Capacity helpers: sorted_token_ids holds T*k + E*(block_m-1) entries;
+ * expert_ids holds ceil(that / block_m). */
+int64_t moe_sorted_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m);
+int64_t moe_block_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m);
+
+/* moe_align_block_size + gather.  For the flattened pair f = t*top_k + j
+ * with expert topk_ids[f] (int32 [T, top_k], values in [0, E)):
+ *   sorted_token_ids int32 [cap]: pairs grouped by expert ascending, f
+ *       ascending within an expert, each expert's run padded to a multiple of
+ *       block_m with the sentinel T*top_k; entries past the padded length are
+ *       the sentinel.  An expert with no pairs has no block.
+ *   expert_ids int32 [nblk]: expert of each block_m block (tail unspecified)
+ *   num_tokens_post_padded int32 [1]: padded length
+ *   inv_pos int32 [T*top_k]: position of pair f in sorted_token_ids
+ *   padded_group_sizes int32 [E]: padded run length per expert (the group
+ *       sizes for gmm_fwd over x_sorted)
+ *   x_sorted bf16 [cap, hidden] (optional, with x bf16 [T, hidden]):
+ *       row i = x[sorted_token_ids[i] / top_k], zeros for the sentinel.
+ * A pair with an out-of-range expert id is dropped: it gets no position
+ * and inv_pos = -1 (moe_unpermute skips it).  T*top_k must be <= 2^24;
+ * hidden % 8 == 0. */
+int moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
+                int32_t block_m, const void* x, int32_t hidden,
+                int32_t* sorted_token_ids, int32_t* expert_ids,
+                int32_t* num_tokens_post_padded, int32_t* inv_pos,
+                int32_t* padded_group_sizes, void* x_sorted, void* ws,
+                size_t ws_bytes, mg_stream_t stream);
+
+/* Device workspace moe_permute needs (per-chunk counts and ranks). */
+size_t moe_permute_workspace_bytes(int64_t T, int32_t top_k, int32_t E);
+
+/* Top-k weighted combine: out[t, :] = bf16( sum_{j<top_k} w[t,j] *
+ * y_sorted[inv_pos[t*top_k + j], :] ), summed in fp32 with j ascending
+ * (deterministic, no atomics).  topk_weights fp32 [T, top_k] or NULL
+ * (weights 1).  hidden % 8 == 0. */
+int moe_unpermute(const void* y_sorted, const int32_t* inv_pos,
+                  const float* topk_weights, int64_t T, int32_t top_k,
+                  int32_t hidden, void* out, mg_stream_t stream);
+
+/* act[r, i] = bf16( silu(h[r, i]) * h[r, inter + i] ), silu(x) = x/(1+e^-x),
+ * computed in fp32 from bf16 h [rows, 2*inter]; act bf16 [rows, inter].
+ * inter % 8 == 0. */
+int silu_mul(const void* h, int64_t rows, int32_t inter, void* act,
+             mg_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* mg_last_error(void);
+
+/* Library version string. */
+const char* mg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GEMM_H */

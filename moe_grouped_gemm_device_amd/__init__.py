@@ -1,0 +1,376 @@
+"""MI355X (gfx950) MoE grouped GEMM: thin Python binding over libmoegemm.so.
+
+Every function here only marshals arguments (torch tensors -> device
+pointers, the current HIP stream) and calls the C ABI declared in
+``include/moe_gemm.h``; every step of the computation runs in the library's
+HIP kernels.  PyTorch provides device memory and streams.  There is no CPU
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoegemm.so")
+
+MG_OK, MG_EINVAL, MG_EUNSUPPORTED, MG_EWORKSPACE, MG_EHIP = 0, -1, -2, -3, -4
+MG_WL_FIXED_M, MG_WL_DYNAMIC_K = 0, 1
+MAX_EXPERTS = 1024
+
+_lib = None
+
+
+class MoeGemmError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+class FP8Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("ld", ctypes.c_int64), ("expert_stride", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "mg_workspace_bytes": (_SZ, [_I32, _I64]),
+    "mg_workspace_error": (_I32, [_P]),
+    "mg_workspace_clear": (ctypes.c_int, [_P, _P]),
+    "gmm_build_worklist": (ctypes.c_int, [_I32, _P, _I32, _I64, _I32, _P, _P, _P, _I64, _P]),
+    "gmm_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "gmm_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "gmm_fwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "gmm_bwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
+                                   _P, _P, _P, _SZ, _P]),
+    "gmm_fwd_f8i4": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "quantize_rowwise_fp8": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P, _P]),
+    "quantize_colwise_per_group_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _I32, _I64, _P, _P, _P, _P, _P]),
+    "quantize_int4_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_sorted_capacity": (_I64, [_I64, _I32, _I32, _I32]),
+    "moe_block_capacity": (_I64, [_I64, _I32, _I32, _I32]),
+    "moe_permute_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_unpermute": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "silu_mul": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "mg_last_error": (ctypes.c_char_p, []),
+    "mg_version": (ctypes.c_char_p, []),
+}
+
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """Load libmoegemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "or python moe_grouped_gemm_device_amd/build.py")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _call(name, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != MG_OK:
+        raise MoeGemmError(name, rc, lib().mg_last_error().decode())
+    return rc
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def workspace_bytes(E, total_M):
+    return int(lib().mg_workspace_bytes(int(E), int(total_M)))
+
+
+def workspace(E, total_M, device="cuda"):
+    """A device workspace big enough for any grouped-GEMM call with E, total_M."""
+    return torch.empty(max(workspace_bytes(E, total_M), 256), dtype=torch.uint8, device=device)
+
+
+def workspace_error(ws):
+    return int(lib().mg_workspace_error(_ptr(ws)))
+
+
+def workspace_clear(ws, stream=None):
+    _call("mg_workspace_clear", _ptr(ws), _stream(stream))
+
+
+# --------------------------------------------------------------------------
+# argument builder
+# --------------------------------------------------------------------------
+
+def build_worklist(kind, group_sizes, total_M, bm, stream=None):
+    """Run the device builder; returns (offs int32[E+1], count int32[1], entries int32[cap,4])."""
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    E = group_sizes.numel()
+    cap = (total_M // bm + min(total_M, E)) if kind == MG_WL_FIXED_M else E
+    cap = max(cap, 1)
+    dev = group_sizes.device
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    entries = torch.empty(cap, 4, dtype=torch.int32, device=dev)
+    _call("gmm_build_worklist", int(kind), _ptr(group_sizes), E, int(total_M), int(bm), _ptr(offs),
+          _ptr(count), _ptr(entries), cap, _stream(stream))
+    return offs, count, entries
+
+
+# --------------------------------------------------------------------------
+# bf16 grouped GEMM
+# --------------------------------------------------------------------------
+
+def gmm_fwd(x, w, group_sizes, trans_b=False, out=None, ws=None, stream=None):
+    """y[r] = x[r] @ w[g(r)] (w [E,K,N], or [E,N,K] with trans_b)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w, torch.bfloat16, "w", 3)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = x.shape
+    E = w.shape[0]
+    N = w.shape[1] if trans_b else w.shape[2]
+    if (w.shape[2] if trans_b else w.shape[1]) != K or group_sizes.numel() != E:
+        raise ValueError("shape mismatch between x, w and group_sizes")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, torch.bfloat16, "out", 2)
+    ws = workspace(E, M, x.device) if ws is None else ws
+    _call("gmm_fwd", _ptr(x), _ptr(w), _ptr(group_sizes), E, M, K, N, int(bool(trans_b)), _ptr(y),
+          _ptr(ws), ws.numel(), _stream(stream))
+    return y
+
+
+def gmm_bwd(dy, x, w, group_sizes, trans_b=False, need_dx=True, need_dw=True, dx=None, dw=None, ws=None,
+            stream=None):
+    """Returns (dx, dw): dx = dy @ w[g]^T, dw[g] = x_g^T @ dy_g (laid out like w)."""
+    _need(dy, torch.bfloat16, "dy", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w, torch.bfloat16, "w", 3)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = x.shape
+    E = w.shape[0]
+    N = dy.shape[1]
+    if need_dx and dx is None:
+        dx = torch.empty(M, K, dtype=torch.bfloat16, device=x.device)
+    if need_dw and dw is None:
+        dw = torch.empty_like(w)
+    ws = workspace(E, M, x.device) if ws is None else ws
+    _call("gmm_bwd", _ptr(dy), _ptr(x), _ptr(w), _ptr(group_sizes), E, M, K, N, int(bool(trans_b)),
+          _ptr(dx if need_dx else None), _ptr(dw if need_dw else None), _ptr(ws), ws.numel(), _stream(stream))
+    return (dx if need_dx else None), (dw if need_dw else None)
+
+
+# --------------------------------------------------------------------------
+# fp8 / f8i4 grouped GEMM
+# --------------------------------------------------------------------------
+
+def _fp8w(codes, scales, ld, expert_stride):
+    return FP8Weight(codes.data_ptr(), scales.data_ptr(), int(ld), int(expert_stride))
+
+
+def gmm_fwd_fp8(xq, sx, wq, sw, w_ld, w_expert_stride, group_sizes, N, out=None, ws=None, stream=None):
+    """y[r,n] = sum_k (xq[r,k]/sx[r]) (Wq(g,k,n)/sw[g,n]); Wq(e,k,n) at e*w_expert_stride + n*w_ld + k."""
+    _need(xq, torch.uint8, "xq", 2)
+    _need(sx, torch.float32, "sx", 1)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = xq.shape
+    E = group_sizes.numel()
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=xq.device) if out is None else out
+    ws = workspace(E, M, xq.device) if ws is None else ws
+    wd = _fp8w(wq, sw, w_ld, w_expert_stride)
+    _call("gmm_fwd_fp8", _ptr(xq), _ptr(sx), ctypes.byref(wd), _ptr(group_sizes), E, M, K, int(N), _ptr(y),
+          _ptr(ws), ws.numel(), _stream(stream))
+    return y
+
+
+def gmm_bwd_fp8(group_sizes, K, N, dyq=None, sdy=None, wq=None, sw=None, w_ld=0, w_expert_stride=0,
+                xc=None, sxc=None, dyc=None, sdyc=None, need_dx=True, need_dw=True, dx=None, dw=None,
+                ws=None, stream=None):
+    """fp8 backward; see gmm_bwd_fp8 in include/moe_gemm.h for operand layouts."""
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    E = group_sizes.numel()
+    dev = group_sizes.device
+    M = dyq.shape[0] if dyq is not None else xc.shape[1]
+    if need_dx and dx is None:
+        dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    if need_dw and dw is None:
+        dw = torch.empty(E, K, N, dtype=torch.bfloat16, device=dev)
+    ws = workspace(E, M, dev) if ws is None else ws
+    wd = _fp8w(wq, sw, w_ld, w_expert_stride) if need_dx else None
+    _call("gmm_bwd_fp8", _ptr(dyq), _ptr(sdy), ctypes.byref(wd) if wd is not None else None, _ptr(xc),
+          _ptr(sxc), _ptr(dyc), _ptr(sdyc), _ptr(group_sizes), E, M, int(K), int(N),
+          _ptr(dx if need_dx else None), _ptr(dw if need_dw else None), _ptr(ws), ws.numel(), _stream(stream))
+    return (dx if need_dx else None), (dw if need_dw else None)
+
+
+def gmm_fwd_f8i4(xq, sx, w4, sw, group_sizes, out=None, ws=None, stream=None):
+    """y = (xq/sx) @ dequant(w4, sw) per group; w4 [E,N,K/2] uint8, sw bf16 [E,K/128,N]."""
+    _need(xq, torch.uint8, "xq", 2)
+    _need(sx, torch.float32, "sx", 1)
+    _need(w4, torch.uint8, "w4", 3)
+    _need(sw, torch.bfloat16, "sw", 3)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = xq.shape
+    E, N, K2 = w4.shape
+    if K2 * 2 != K or group_sizes.numel() != E:
+        raise ValueError("shape mismatch between xq, w4 and group_sizes")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=xq.device) if out is None else out
+    ws = workspace(E, M, xq.device) if ws is None else ws
+    _call("gmm_fwd_f8i4", _ptr(xq), _ptr(sx), _ptr(w4), _ptr(sw), _ptr(group_sizes), E, M, K, N, _ptr(y),
+          _ptr(ws), ws.numel(), _stream(stream))
+    return y
+
+
+# --------------------------------------------------------------------------
+# quantizers
+# --------------------------------------------------------------------------
+
+def quantize_rowwise_fp8(x, q=None, scales=None, stream=None):
+    """bf16 [R, C] -> (e4m3 codes uint8 [R, C], fp32 scales [R])."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 matrix with unit column stride")
+    R, C = x.shape
+    q = torch.empty(R, C, dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty(R, dtype=torch.float32, device=x.device) if scales is None else scales
+    _call("quantize_rowwise_fp8", _ptr(x), R, C, x.stride(0), _ptr(q), _ptr(scales), _stream(stream))
+    return q, scales
+
+
+def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None):
+    """Per-group colwise quantization of a (and b).  Returns
+    (qa [Ca, M] column-major codes, sa [G, Ca]) or, with b,
+    (qa, sa, qb, sb)."""
+    _need(a, torch.bfloat16, "a", 2)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, Ca = a.shape
+    G = group_sizes.numel()
+    qa = torch.zeros(Ca, M, dtype=torch.uint8, device=a.device)
+    sa = torch.empty(G, Ca, dtype=torch.float32, device=a.device)
+    qb = sb = None
+    Cb = 0
+    if b is not None:
+        _need(b, torch.bfloat16, "b", 2)
+        if b.shape[0] != M:
+            raise ValueError("a and b must have the same number of rows")
+        Cb = b.shape[1]
+        qb = torch.zeros(Cb, M, dtype=torch.uint8, device=a.device)
+        sb = torch.empty(G, Cb, dtype=torch.float32, device=a.device)
+    _call("quantize_colwise_per_group_fp8", _ptr(a), Ca, _ptr(b), Cb, _ptr(group_sizes), G, M, _ptr(qa),
+          _ptr(sa), _ptr(qb), _ptr(sb), _stream(stream))
+    return (qa, sa) if b is None else (qa, sa, qb, sb)
+
+
+def quantize_int4_weights(w, stream=None):
+    """bf16 [E, K, N] -> (int4 packed uint8 [E, N, K/2], bf16 scales [E, K/128, N])."""
+    _need(w, torch.bfloat16, "w", 3)
+    E, K, N = w.shape
+    w4 = torch.empty(E, N, K // 2, dtype=torch.uint8, device=w.device)
+    sw = torch.empty(E, K // 128, N, dtype=torch.bfloat16, device=w.device)
+    _call("quantize_int4_weights", _ptr(w), E, K, N, _ptr(w4), _ptr(sw), _stream(stream))
+    return w4, sw
+
+
+# --------------------------------------------------------------------------
+# token permutation for the fused path
+# --------------------------------------------------------------------------
+
+def sorted_capacity(T, k, E, block_m):
+    return int(lib().moe_sorted_capacity(int(T), int(k), int(E), int(block_m)))
+
+
+def block_capacity(T, k, E, block_m):
+    return int(lib().moe_block_capacity(int(T), int(k), int(E), int(block_m)))
+
+
+def moe_permute(topk_ids, E, block_m, x=None, ws=None, stream=None):
+    """moe_align_block_size (+ gather of x rows).  Returns a dict with
+    sorted_token_ids, expert_ids, num_tokens_post_padded, inv, padded_sizes
+    and x_sorted (or None)."""
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    cap = sorted_capacity(T, k, E, block_m)
+    nblk = block_capacity(T, k, E, block_m)
+    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(max(nblk, 1), dtype=torch.int32, device=dev)
+    ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+    inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    padded = torch.empty(E, dtype=torch.int32, device=dev)
+    hidden = 0
+    xs = None
+    if x is not None:
+        _need(x, torch.bfloat16, "x", 2)
+        hidden = x.shape[1]
+        xs = torch.empty(max(cap, 1), hidden, dtype=torch.bfloat16, device=dev)
+    need = int(lib().moe_permute_workspace_bytes(T, k, E))
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _call("moe_permute", _ptr(topk_ids), T, k, int(E), int(block_m), _ptr(x), hidden, _ptr(sorted_ids),
+          _ptr(expert_ids), _ptr(ntpp), _ptr(inv), _ptr(padded), _ptr(xs), _ptr(ws), ws.numel(),
+          _stream(stream))
+    return dict(sorted_token_ids=sorted_ids[:cap], expert_ids=expert_ids[:nblk], num_tokens_post_padded=ntpp,
+                inv=inv[:T * k], padded_sizes=padded, x_sorted=None if xs is None else xs[:cap])
+
+
+def moe_unpermute(y_sorted, inv, topk_weights, T, k, out=None, stream=None):
+    """out[t] = sum_j w[t,j] * y_sorted[inv[t*k+j]] (fp32 sum, bf16 out)."""
+    _need(y_sorted, torch.bfloat16, "y_sorted", 2)
+    _need(inv, torch.int32, "inv")
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, "topk_weights")
+    H = y_sorted.shape[1]
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=y_sorted.device) if out is None else out
+    _call("moe_unpermute", _ptr(y_sorted), _ptr(inv), _ptr(topk_weights), int(T), int(k), H, _ptr(out),
+          _stream(stream))
+    return out
+
+
+def silu_mul(h, out=None, stream=None):
+    """act = silu(h[:, :I]) * h[:, I:] in bf16."""
+    _need(h, torch.bfloat16, "h", 2)
+    R, I2 = h.shape
+    out = torch.empty(R, I2 // 2, dtype=torch.bfloat16, device=h.device) if out is None else out
+    _call("silu_mul", _ptr(h), R, I2 // 2, _ptr(out), _stream(stream))
+    return out
+
+
+def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, stream=None):
+    """Token-sorted MoE expert FFN: permute -> gmm(W1) -> SiLU*mul -> gmm(W2)
+    -> top-k weighted combine.  w1 [E, H, 2I], w2 [E, I, H] bf16."""
+    T, k = topk_ids.shape
+    E = w1.shape[0]
+    if block_m is None:
+        block_m = 16 if T * k <= 64 * E else 128
+    p = moe_permute(topk_ids, E, block_m, x=x, stream=stream)
+    xs = p["x_sorted"]
+    sizes = p["padded_sizes"]
+    ws = workspace(E, xs.shape[0], x.device)
+    h1 = gmm_fwd(xs, w1, sizes, ws=ws, stream=stream)
+    act = silu_mul(h1, stream=stream)
+    y2 = gmm_fwd(act, w2, sizes, ws=ws, stream=stream)
+    return moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream), p

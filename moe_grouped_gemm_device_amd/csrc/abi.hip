@@ -1,0 +1,578 @@
+// C ABI of the library: host-side argument checks, workspace carving and
+// kernel launches.  Nothing here reads device memory or synchronizes, except
+// mg_workspace_error, which exists for tests.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe_gemm.h"
+#include "kernels.h"
+
+using namespace mg;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MG_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MG_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+hipStream_t S(mg_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+int check_common(const int32_t* sizes, int32_t E, int64_t total_M, const void* ws, size_t ws_bytes) {
+  if (E < 1 || E > MG_MAX_EXPERTS) return fail(MG_EINVAL, "E=%d outside [1, %d]", E, MG_MAX_EXPERTS);
+  if (total_M < 0 || total_M >= kMaxRows) return fail(MG_EINVAL, "total_M=%lld outside [0, 2^31)", (long long)total_M);
+  if (sizes == nullptr) return fail(MG_EINVAL, "group_sizes is NULL");
+  if (ws == nullptr) return fail(MG_EWORKSPACE, "workspace is NULL");
+  const size_t need = (size_t)ws_layout(E, total_M).total;
+  if (ws_bytes < need) return fail(MG_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(MG_EINVAL, "workspace must be 256-byte aligned");
+  return MG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+struct Ws {
+  int32_t* err;
+  int32_t* count;
+  int32_t* offs;
+  int32_t* entries;
+  int32_t* dk;
+  int64_t cap;
+};
+
+Ws carve(void* ws, int32_t E, int64_t total_M) {
+  const WsLayout L = ws_layout(E, total_M);
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  Ws w;
+  w.err = reinterpret_cast<int32_t*>(b) + kWsErrorWord;
+  w.count = reinterpret_cast<int32_t*>(b) + kWsCountWord;
+  w.offs = reinterpret_cast<int32_t*>(b + L.offs);
+  w.entries = reinterpret_cast<int32_t*>(b + L.entries);
+  w.dk = reinterpret_cast<int32_t*>(b + L.dk_entries);
+  w.cap = L.cap;
+  return w;
+}
+
+hipError_t run_builder(const Ws& w, const int32_t* sizes, int32_t E, int64_t total_M, int bm, bool fixed,
+                       bool dynamic, hipStream_t st) {
+  BuildArgs b;
+  b.sizes = sizes;
+  b.E = E;
+  b.total_M = total_M;
+  b.bm = bm;
+  b.want_fixed = fixed;
+  b.want_dynamic = dynamic;
+  b.offs = w.offs;
+  b.count = w.count;
+  b.entries = w.entries;
+  b.dk_entries = w.dk;
+  b.err = w.err;
+  return launch_build_worklist(b, st);
+}
+
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+__global__ void set_word_kernel(int32_t* p, int32_t v) {
+  if (threadIdx.x == 0) p[0] = v;
+}
+
+GemmArgs blank_args() {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mg_last_error(void) { return g_err; }
+
+const char* mg_version(void) { return "moe-gemm-gfx950 0.1"; }
+
+size_t mg_workspace_bytes(int32_t E, int64_t total_M) {
+  if (E < 1 || E > MG_MAX_EXPERTS || total_M < 0) return 0;
+  return (size_t)ws_layout(E, total_M).total;
+}
+
+int32_t mg_workspace_error(const void* ws) {
+  if (ws == nullptr) return -1;
+  int32_t v = 0;
+  if (hipMemcpy(&v, reinterpret_cast<const int32_t*>(ws) + kWsErrorWord, sizeof v, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return -1;
+  return v;
+}
+
+int mg_workspace_clear(void* ws, mg_stream_t stream) {
+  if (ws == nullptr) return fail(MG_EINVAL, "workspace is NULL");
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, S(stream), reinterpret_cast<int32_t*>(ws), 2);
+  return hip_status(hipGetLastError(), "mg_workspace_clear");
+}
+
+int gmm_build_worklist(int32_t kind, const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t bm,
+                       int32_t* offs, int32_t* count, int32_t* entries, int64_t cap, mg_stream_t stream) {
+  if (E < 1 || E > MG_MAX_EXPERTS) return fail(MG_EINVAL, "E=%d outside [1, %d]", E, MG_MAX_EXPERTS);
+  if (total_M < 0 || total_M >= kMaxRows) return fail(MG_EINVAL, "total_M out of range");
+  if (bm < 1) return fail(MG_EINVAL, "bm must be >= 1");
+  if (!group_sizes || !offs || !count || !entries) return fail(MG_EINVAL, "NULL pointer argument");
+  if (kind != MG_WL_FIXED_M && kind != MG_WL_DYNAMIC_K) return fail(MG_EINVAL, "unknown work-list kind %d", kind);
+  const int64_t need = kind == MG_WL_FIXED_M ? fixed_m_capacity(total_M, E, bm) : E;
+  if (cap < need) return fail(MG_EINVAL, "cap %lld < %lld", (long long)cap, (long long)need);
+  BuildArgs b;
+  b.sizes = group_sizes;
+  b.E = E;
+  b.total_M = total_M;
+  b.bm = bm;
+  b.want_fixed = kind == MG_WL_FIXED_M;
+  b.want_dynamic = kind == MG_WL_DYNAMIC_K;
+  b.offs = offs;
+  b.count = count;
+  b.entries = entries;
+  b.dk_entries = entries;
+  b.err = nullptr;
+  if (kind == MG_WL_DYNAMIC_K) {
+    // the dynamic list has exactly E entries; report that count too
+    b.want_fixed = 0;
+  }
+  hipError_t e = launch_build_worklist(b, S(stream));
+  if (e == hipSuccess && kind == MG_WL_DYNAMIC_K) {
+    // count = E, written by a one-thread kernel so nothing is read back
+    hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, S(stream), count, E);
+    e = hipGetLastError();
+  }
+  return hip_status(e, "gmm_build_worklist");
+}
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+
+int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K,
+            int32_t N, int32_t trans_b, void* y, void* ws, size_t ws_bytes, mg_stream_t stream) {
+  int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
+  if (rc) return rc;
+  if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
+  if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "K and N must be multiples of 8");
+  if (total_M == 0) return ok();
+  if (!x || !w || !y) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  const Ws s = carve(ws, E, total_M);
+  const int bm = 128, bn = 128;
+  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, true, false, S(stream));
+  if (e != hipSuccess) return hip_status(e, "gmm_fwd builder");
+  GemmArgs a = blank_args();
+  a.A = x;
+  a.a_ld = K;
+  a.B = w;
+  if (trans_b) {
+    a.b_ld = K;                 // W[g, n, k]
+  } else {
+    a.b_ld = N;                 // W[g, k, n]
+  }
+  a.b_gs = (int64_t)K * N;
+  a.C = y;
+  a.c_ld = N;
+  a.c_gs = 0;
+  a.Nout = N;
+  a.Kc = K;
+  a.E = E;
+  a.total_rows = total_M;
+  a.count = s.count;
+  a.entries = s.entries;
+  GemmLaunch L;
+  L.kind = FIXED_M;
+  L.elem = EL_BF16;
+  L.a_kc = true;
+  L.b_kc = trans_b != 0;
+  L.bm = bm;
+  L.bn = bn;
+  L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(N, bn);
+  return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd");
+}
+
+int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_sizes, int32_t E,
+            int64_t total_M, int32_t K, int32_t N, int32_t trans_b, void* dx, void* dw, void* ws,
+            size_t ws_bytes, mg_stream_t stream) {
+  int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
+  if (rc) return rc;
+  if (!dx && !dw) return fail(MG_EINVAL, "dx and dw are both NULL");
+  if (total_M > 0 && (!dy || (dx && !w) || (dw && !x))) return fail(MG_EINVAL, "NULL tensor argument");
+  if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
+  if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "K and N must be multiples of 8");
+  if (!aligned16(dy) || (x && !aligned16(x)) || (w && !aligned16(w)) || (dx && !aligned16(dx)) ||
+      (dw && !aligned16(dw)))
+    return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  const Ws s = carve(ws, E, total_M);
+  const int bm = 128, bn = 128;
+  if (total_M == 0 && !dw) return ok();
+  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, dx != nullptr, dw != nullptr, S(stream));
+  if (e != hipSuccess) return hip_status(e, "gmm_bwd builder");
+  if (dx && total_M > 0) {
+    GemmArgs a = blank_args();
+    a.A = dy;
+    a.a_ld = N;
+    a.B = w;
+    a.b_ld = trans_b ? K : N;   // [E,K,N]: W[g,k,n], contraction n contiguous; [E,N,K]: k contiguous
+    a.b_gs = (int64_t)K * N;
+    a.C = dx;
+    a.c_ld = K;
+    a.Nout = K;
+    a.Kc = N;
+    a.E = E;
+    a.total_rows = total_M;
+    a.count = s.count;
+    a.entries = s.entries;
+    GemmLaunch L;
+    L.kind = FIXED_M;
+    L.elem = EL_BF16;
+    L.a_kc = true;
+    L.b_kc = trans_b == 0;
+    L.bm = bm;
+    L.bn = bn;
+    L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(K, bn);
+    e = launch_gemm(L, a, S(stream));
+    if (e != hipSuccess) return hip_status(e, "gmm_bwd dx");
+  }
+  if (dw) {
+    GemmArgs a = blank_args();
+    if (!trans_b) {   // dW[g, k, n] = sum_r X[r, k] dY[r, n]
+      a.A = x;
+      a.a_ld = K;
+      a.B = dy;
+      a.b_ld = N;
+      a.Mout = K;
+      a.Nout = N;
+      a.c_ld = N;
+    } else {          // dW[g, n, k] = sum_r dY[r, n] X[r, k]
+      a.A = dy;
+      a.a_ld = N;
+      a.B = x;
+      a.b_ld = K;
+      a.Mout = N;
+      a.Nout = K;
+      a.c_ld = K;
+    }
+    a.b_gs = 0;
+    a.C = dw;
+    a.c_gs = (int64_t)K * N;
+    a.E = E;
+    a.total_rows = total_M;
+    a.entries = s.dk;
+    GemmLaunch L;
+    L.kind = DYNAMIC_K;
+    L.elem = EL_BF16;
+    L.a_kc = false;
+    L.b_kc = false;
+    L.bm = bm;
+    L.bn = bn;
+    L.max_items = (int64_t)E * cdiv(a.Mout, bm) * cdiv(a.Nout, bn);
+    e = launch_gemm(L, a, S(stream));
+    if (e != hipSuccess) return hip_status(e, "gmm_bwd dw");
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// fp8
+// ---------------------------------------------------------------------------
+
+static int check_fp8_weight(const mg_fp8_weight* w) {
+  if (!w || !w->codes || !w->scales) return fail(MG_EINVAL, "fp8 weight descriptor incomplete");
+  if (w->ld < 1 || w->expert_stride < 0) return fail(MG_EINVAL, "fp8 weight strides invalid");
+  if (w->ld % 16 || w->expert_stride % 16 || !aligned16(w->codes))
+    return fail(MG_EUNSUPPORTED, "fp8 weight strides and base must be multiples of 16 bytes");
+  return MG_OK;
+}
+
+int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w, const int32_t* group_sizes,
+                int32_t E, int64_t total_M, int32_t K, int32_t N, void* y, void* ws, size_t ws_bytes,
+                mg_stream_t stream) {
+  int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_fp8_weight(w))) return rc;
+  if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
+  if (K % 16 || N % 8) return fail(MG_EUNSUPPORTED, "K must be a multiple of 16 and N of 8");
+  if (w->ld < K) return fail(MG_EINVAL, "weight ld < K");
+  if (total_M == 0) return ok();
+  if (!xq || !sx || !y) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(xq) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  const Ws s = carve(ws, E, total_M);
+  const int bm = 128, bn = 128;
+  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, true, false, S(stream));
+  if (e != hipSuccess) return hip_status(e, "gmm_fwd_fp8 builder");
+  GemmArgs a = blank_args();
+  a.A = xq;
+  a.a_ld = K;
+  a.B = w->codes;
+  a.b_ld = w->ld;
+  a.b_gs = w->expert_stride;
+  a.C = y;
+  a.c_ld = N;
+  a.sa = sx;
+  a.sb = w->scales;
+  a.Nout = N;
+  a.Kc = K;
+  a.E = E;
+  a.total_rows = total_M;
+  a.count = s.count;
+  a.entries = s.entries;
+  GemmLaunch L;
+  L.kind = FIXED_M;
+  L.elem = EL_FP8;
+  L.a_kc = L.b_kc = true;
+  L.bm = bm;
+  L.bn = bn;
+  L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(N, bn);
+  return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd_fp8");
+}
+
+int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, const uint8_t* xc,
+                const float* sxc, const uint8_t* dyc, const float* sdyc, const int32_t* group_sizes, int32_t E,
+                int64_t total_M, int32_t K, int32_t N, void* dx, void* dw, void* ws, size_t ws_bytes,
+                mg_stream_t stream) {
+  int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
+  if (rc) return rc;
+  if (!dx && !dw) return fail(MG_EINVAL, "dx and dw are both NULL");
+  if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
+  if (dx) {
+    if ((rc = check_fp8_weight(w))) return rc;
+    if (total_M > 0 && (!dyq || !sdy)) return fail(MG_EINVAL, "NULL dx operand");
+    if (N % 16 || K % 8) return fail(MG_EUNSUPPORTED, "dx needs N % 16 == 0 and K % 8 == 0");
+    if (w->ld < N) return fail(MG_EINVAL, "weight ld < N");
+    if (!aligned16(dyq) || !aligned16(dx)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  }
+  if (dw) {
+    if (!sxc || !sdyc || (total_M > 0 && (!xc || !dyc))) return fail(MG_EINVAL, "NULL dw operand");
+    if (total_M % 16) return fail(MG_EUNSUPPORTED, "dw needs total_M % 16 == 0");
+    if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "dw needs K and N multiples of 8");
+    if (!aligned16(xc) || !aligned16(dyc) || !aligned16(dw)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  }
+  const Ws s = carve(ws, E, total_M);
+  const int bm = 128, bn = 128;
+  if (total_M == 0 && !dw) return ok();
+  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, dx != nullptr, dw != nullptr, S(stream));
+  if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 builder");
+  if (dx && total_M > 0) {
+    GemmArgs a = blank_args();
+    a.A = dyq;
+    a.a_ld = N;
+    a.B = w->codes;
+    a.b_ld = w->ld;
+    a.b_gs = w->expert_stride;
+    a.C = dx;
+    a.c_ld = K;
+    a.sa = sdy;
+    a.sb = w->scales;
+    a.Nout = K;
+    a.Kc = N;
+    a.E = E;
+    a.total_rows = total_M;
+    a.count = s.count;
+    a.entries = s.entries;
+    GemmLaunch L;
+    L.kind = FIXED_M;
+    L.elem = EL_FP8;
+    L.a_kc = L.b_kc = true;
+    L.bm = bm;
+    L.bn = bn;
+    L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(K, bn);
+    e = launch_gemm(L, a, S(stream));
+    if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 dx");
+  }
+  if (dw) {
+    GemmArgs a = blank_args();
+    a.A = xc;
+    a.a_ld = total_M;
+    a.B = dyc;
+    a.b_ld = total_M;
+    a.b_gs = 0;
+    a.C = dw;
+    a.c_ld = N;
+    a.c_gs = (int64_t)K * N;
+    a.sa = sxc;
+    a.sb = sdyc;
+    a.Mout = K;
+    a.Nout = N;
+    a.E = E;
+    a.total_rows = total_M;
+    a.entries = s.dk;
+    GemmLaunch L;
+    L.kind = DYNAMIC_K;
+    L.elem = EL_FP8;
+    L.a_kc = L.b_kc = true;
+    L.bm = bm;
+    L.bn = bn;
+    L.max_items = (int64_t)E * cdiv(K, bm) * cdiv(N, bn);
+    e = launch_gemm(L, a, S(stream));
+    if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 dw");
+  }
+  return ok();
+}
+
+int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4, const void* sw,
+                 const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K, int32_t N, void* y, void* ws,
+                 size_t ws_bytes, mg_stream_t stream) {
+  int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
+  if (rc) return rc;
+  if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
+  if (K % 128 || N % 8) return fail(MG_EUNSUPPORTED, "K must be a multiple of 128 and N of 8");
+  if (total_M == 0) return ok();
+  if (!xq || !sx || !w4 || !sw || !y) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(xq) || !aligned16(w4)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  const Ws s = carve(ws, E, total_M);
+  const int bm = 32;
+  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, true, false, S(stream));
+  if (e != hipSuccess) return hip_status(e, "gmm_fwd_f8i4 builder");
+  GemmArgs a = blank_args();
+  a.A = xq;
+  a.a_ld = K;
+  a.B = w4;
+  a.s4 = reinterpret_cast<const uint16_t*>(sw);
+  a.sa = sx;
+  a.C = y;
+  a.c_ld = N;
+  a.Nout = N;
+  a.Kc = K;
+  a.E = E;
+  a.total_rows = total_M;
+  a.count = s.count;
+  a.entries = s.entries;
+  return hip_status(launch_f8i4(a, fixed_m_capacity(total_M, E, bm), S(stream)), "gmm_fwd_f8i4");
+}
+
+// ---------------------------------------------------------------------------
+// quantizers
+// ---------------------------------------------------------------------------
+
+int quantize_rowwise_fp8(const void* x, int64_t rows, int32_t cols, int64_t ld, uint8_t* q, float* scales,
+                         mg_stream_t stream) {
+  if (rows < 0 || cols < 1) return fail(MG_EINVAL, "rows must be >= 0 and cols >= 1");
+  if (ld < cols) return fail(MG_EINVAL, "ld < cols");
+  if (cols % 8 || ld % 8) return fail(MG_EUNSUPPORTED, "cols and ld must be multiples of 8");
+  if (rows == 0) return ok();
+  if (!x || !q || !scales) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7)) return fail(MG_EUNSUPPORTED, "x must be 16-byte and q 8-byte aligned");
+  return hip_status(launch_quant_rowwise(reinterpret_cast<const uint16_t*>(x), rows, cols, ld, q, scales, S(stream)),
+                    "quantize_rowwise_fp8");
+}
+
+int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a, const void* b, int32_t cols_b,
+                                   const int32_t* group_sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
+                                   uint8_t* qb, float* sb, mg_stream_t stream) {
+  if (G < 1 || G > 65535) return fail(MG_EINVAL, "G=%d outside [1, 65535]", G);
+  if (rows < 0) return fail(MG_EINVAL, "rows < 0");
+  if (!a || !qa || !sa || !group_sizes) return fail(MG_EINVAL, "NULL tensor argument");
+  const bool dual = b != nullptr;
+  if (dual != (qb != nullptr) || dual != (sb != nullptr)) return fail(MG_EINVAL, "b, qb, sb must be all set or all NULL");
+  if (cols_a < 1 || (dual && cols_b < 1)) return fail(MG_EINVAL, "cols must be positive");
+  if (cols_a % 8 || (dual && cols_b % 8)) return fail(MG_EUNSUPPORTED, "cols must be multiples of 8");
+  if (!aligned16(a) || (dual && !aligned16(b))) return fail(MG_EUNSUPPORTED, "inputs must be 16-byte aligned");
+  return hip_status(launch_quant_colwise(reinterpret_cast<const uint16_t*>(a), cols_a,
+                                         reinterpret_cast<const uint16_t*>(b), dual ? cols_b : 0, group_sizes, G,
+                                         rows, qa, sa, qb, sb, S(stream)),
+                    "quantize_colwise_per_group_fp8");
+}
+
+int quantize_int4_weights(const void* w, int32_t E, int32_t K, int32_t N, uint8_t* w4, void* sw,
+                          mg_stream_t stream) {
+  if (E < 1 || E > 65535 || K < 1 || N < 1) return fail(MG_EINVAL, "E, K, N out of range");
+  if (K % 128 || N % 8) return fail(MG_EUNSUPPORTED, "K % 128 == 0 and N % 8 == 0 required");
+  if (!w || !w4 || !sw) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(w4)) return fail(MG_EUNSUPPORTED, "w4 must be 16-byte aligned");
+  return hip_status(launch_quant_int4(reinterpret_cast<const uint16_t*>(w), E, K, N, w4,
+                                      reinterpret_cast<uint16_t*>(sw), S(stream)),
+                    "quantize_int4_weights");
+}
+
+// ---------------------------------------------------------------------------
+// permutation
+// ---------------------------------------------------------------------------
+
+int64_t moe_sorted_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m) {
+  if (T < 0 || top_k < 1 || E < 1 || block_m < 1) return 0;
+  return T * top_k + (int64_t)E * (block_m - 1);
+}
+
+int64_t moe_block_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m) {
+  if (T < 0 || top_k < 1 || E < 1 || block_m < 1) return 0;
+  return cdiv(moe_sorted_capacity(T, top_k, E, block_m), block_m);
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t top_k, int32_t E) {
+  if (T < 0 || top_k < 1 || E < 1 || E > MG_MAX_EXPERTS) return 0;
+  return (size_t)perm_workspace_bytes(T * top_k, E);
+}
+
+int moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t block_m, const void* x,
+                int32_t hidden, int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                int32_t* inv_pos, int32_t* padded_group_sizes, void* x_sorted, void* ws, size_t ws_bytes,
+                mg_stream_t stream) {
+  if (E < 1 || E > MG_MAX_EXPERTS) return fail(MG_EINVAL, "E=%d outside [1, %d]", E, MG_MAX_EXPERTS);
+  if (T < 0 || top_k < 1 || block_m < 1) return fail(MG_EINVAL, "T >= 0, top_k >= 1, block_m >= 1 required");
+  if (T * top_k > (1 << 24)) return fail(MG_EUNSUPPORTED, "T * top_k must be <= 2^24");
+  const int64_t cap = moe_sorted_capacity(T, top_k, E, block_m);
+  if (cap >= kMaxRows) return fail(MG_EUNSUPPORTED, "sorted capacity exceeds int32");
+  if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded || !inv_pos || !padded_group_sizes)
+    return fail(MG_EINVAL, "NULL output argument");
+  if (T > 0 && !topk_ids) return fail(MG_EINVAL, "topk_ids is NULL");
+  if ((x == nullptr) != (x_sorted == nullptr)) return fail(MG_EINVAL, "x and x_sorted must both be set or NULL");
+  if (x && (hidden < 1 || hidden % 8)) return fail(MG_EUNSUPPORTED, "hidden must be a positive multiple of 8");
+  if (x && (!aligned16(x) || !aligned16(x_sorted))) return fail(MG_EUNSUPPORTED, "x, x_sorted must be 16-byte aligned");
+  const size_t need = moe_permute_workspace_bytes(T, top_k, E);
+  if (!ws || ws_bytes < need) return fail(MG_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return hip_status(launch_moe_permute_ws(topk_ids, T, top_k, E, block_m, reinterpret_cast<const uint16_t*>(x),
+                                          hidden, sorted_token_ids, expert_ids, num_tokens_post_padded, inv_pos,
+                                          padded_group_sizes, reinterpret_cast<uint16_t*>(x_sorted), cap,
+                                          moe_block_capacity(T, top_k, E, block_m), ws, S(stream)),
+                    "moe_permute");
+}
+
+int moe_unpermute(const void* y_sorted, const int32_t* inv_pos, const float* topk_weights, int64_t T,
+                  int32_t top_k, int32_t hidden, void* out, mg_stream_t stream) {
+  if (T < 0 || top_k < 1 || hidden < 1) return fail(MG_EINVAL, "T >= 0, top_k >= 1, hidden >= 1 required");
+  if (hidden % 8) return fail(MG_EUNSUPPORTED, "hidden must be a multiple of 8");
+  if (T > 65535) {
+    // grid.y limit
+    return fail(MG_EUNSUPPORTED, "T must be <= 65535 per call");
+  }
+  if (T == 0) return ok();
+  if (!y_sorted || !inv_pos || !out) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(y_sorted) || !aligned16(out)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  return hip_status(launch_moe_unpermute(reinterpret_cast<const uint16_t*>(y_sorted), inv_pos, topk_weights, T,
+                                         top_k, hidden, reinterpret_cast<uint16_t*>(out), S(stream)),
+                    "moe_unpermute");
+}
+
+int silu_mul(const void* h, int64_t rows, int32_t inter, void* act, mg_stream_t stream) {
+  if (rows < 0 || inter < 1) return fail(MG_EINVAL, "rows >= 0 and inter >= 1 required");
+  if (inter % 8) return fail(MG_EUNSUPPORTED, "inter must be a multiple of 8");
+  if (rows == 0) return ok();
+  if (!h || !act) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(h) || !aligned16(act)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  return hip_status(launch_silu_mul(reinterpret_cast<const uint16_t*>(h), rows, inter,
+                                    reinterpret_cast<uint16_t*>(act), S(stream)),
+                    "silu_mul");
+}
+
+}  // extern "C"

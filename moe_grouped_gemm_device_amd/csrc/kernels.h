@@ -1,0 +1,111 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include "common.h"
+
+namespace mg {
+
+// ---------------------------------------------------------------------------
+// K1: argument builder
+// ---------------------------------------------------------------------------
+struct BuildArgs {
+  const int32_t* sizes;
+  int32_t E;
+  int64_t total_M;
+  int32_t bm;
+  int32_t want_fixed;
+  int32_t want_dynamic;
+  int32_t* offs;        // [E+1]
+  int32_t* count;       // [1]   (fixed-M entries)
+  int32_t* entries;     // [cap][4]
+  int32_t* dk_entries;  // [E][4]
+  int32_t* err;         // sticky error word (may be null)
+};
+hipError_t launch_build_worklist(const BuildArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// K2: grouped GEMM
+//
+// C(m, n) = sum_c A(m, c) * B_g(c, n), computed per work item.
+//   FIXED_M   (forward, dX): rows m are token rows of a work-list entry
+//             {g, row0, rows}; the contraction length Kc is fixed.
+//   DYNAMIC_K (dW): output C_g is [Mout, Nout] per group; the contraction
+//             runs over the group's token rows [offs[g], offs[g+1]).
+// Operand element addresses (in elements):
+//   A k-contiguous: A[m * a_ld + c]     A m-contiguous: A[c * a_ld + m]
+//   B k-contiguous: B[g * b_gs + n * b_ld + c]
+//   B n-contiguous: B[g * b_gs + c * b_ld + n]
+//   C: C[g * c_gs + m * c_ld + n]  (c_gs = 0 for token-stacked outputs)
+// ---------------------------------------------------------------------------
+enum Kind { FIXED_M = 0, DYNAMIC_K = 1 };
+enum Elem { EL_BF16 = 0, EL_FP8 = 1, EL_I4 = 2 };
+enum Epi { EPI_NONE = 0, EPI_ROW_COL = 1, EPI_GROUP = 2 };
+
+struct GemmArgs {
+  const void* A;
+  int64_t a_ld;
+  const void* B;
+  int64_t b_ld;
+  int64_t b_gs;
+  void* C;
+  int64_t c_ld;
+  int64_t c_gs;
+  // scales (fp8): FIXED_M: sa[row], sb[g * Nout + n]
+  //               DYNAMIC_K: sa[g * Mout + m], sb[g * Nout + n]
+  const float* sa;
+  const float* sb;
+  const uint16_t* s4;   // int4 chunk scales, bf16 [E][Kc/128][Nout]
+  int32_t Mout;         // DYNAMIC_K: output rows per group
+  int32_t Nout;
+  int32_t Kc;           // FIXED_M contraction length
+  int32_t E;
+  int64_t total_rows;
+  const int32_t* count;     // FIXED_M: number of entries (device)
+  const int32_t* entries;   // FIXED_M or DYNAMIC_K entries (device)
+};
+
+struct GemmLaunch {
+  int kind;      // Kind
+  int elem;      // Elem of A (B is the same except EL_I4)
+  bool a_kc, b_kc;
+  int bm, bn;
+  int64_t max_items;  // host upper bound on work items
+};
+
+// Row tile the fixed-M kernels use for a given problem (heuristic, static).
+int pick_bm_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout);
+int pick_bn_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout, int bm);
+
+hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_f8i4(const GemmArgs& a, int64_t cap_entries, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// K3/K4: fp8 quantizers, int4 weight quantizer
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int32_t cols,
+                                int64_t ld, uint8_t* q, float* s, hipStream_t stream);
+hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_t* b,
+                                int32_t cols_b, const int32_t* sizes, int32_t G,
+                                int64_t rows, uint8_t* qa, float* sa, uint8_t* qb,
+                                float* sb, hipStream_t stream);
+hipError_t launch_quant_int4(const uint16_t* w, int32_t E, int32_t K, int32_t N,
+                             uint8_t* w4, uint16_t* sw, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// K5-K7: permutation, activation, combine
+// ---------------------------------------------------------------------------
+int64_t perm_workspace_bytes(int64_t P, int32_t E);
+hipError_t launch_moe_permute_ws(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                                 int32_t block_m, const uint16_t* x, int32_t hidden,
+                                 int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
+                                 int32_t* inv, int32_t* padded, uint16_t* x_sorted,
+                                 int64_t cap, int64_t nblk, void* ws, hipStream_t stream);
+hipError_t launch_moe_unpermute(const uint16_t* y, const int32_t* inv, const float* w,
+                                int64_t T, int32_t k, int32_t hidden, uint16_t* out,
+                                hipStream_t stream);
+hipError_t launch_silu_mul(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* act,
+                           hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace mg

@@ -1,0 +1,273 @@
+// Token permutation for the token-sorted fused MoE path (K5), SiLU-and-mul
+// (K6) and the top-k weighted combine (K7), for gfx950.
+//
+// applied-ai issue "Column-major fused MoE": moe_align_block_size sorts the
+// flattened (token, slot) pairs by expert and pads every expert's run to a
+// multiple of block_m with the sentinel T*k (docstring and worked example);
+// fused_moe_kernel reads A row sorted_id // top_k and masks the sentinel;
+// fused_moe applies silu_and_mul between the two GEMMs and sums the top-k
+// expert outputs of every token.
+//
+// The alignment is a stable counting sort in three small kernels with no
+// device-to-host traffic:
+//   1. per chunk of pairs: stable rank of every pair among the chunk's pairs
+//      with the same expert, and the chunk's per-expert counts;
+//   2. one workgroup: per-expert totals, padded run starts, per-chunk bases,
+//      block -> expert table, padded sizes, padded length;
+//   3. scatter: position = base[chunk][expert] + rank; inverse positions.
+// The sentinel fill runs first; the gather of X rows runs last.
+#include "kernels.h"
+
+namespace mg {
+
+constexpr int PT = 256;                 // threads per permutation workgroup
+
+struct PermWs {
+  int32_t* chunk_counts;   // [nchunks][E], becomes chunk bases after pass 2
+  int32_t* rank;           // [P]
+};
+
+// Stable within-chunk ranks.  A chunk is processed in sub-chunks of 256
+// pairs; inside a wave, lanes with equal experts are matched with ballots;
+// waves take turns (in order) to advance the per-expert cursors in LDS.
+__global__ void __launch_bounds__(PT) perm_rank_kernel(const int32_t* __restrict__ ids, int64_t P, int32_t E,
+                                                      int64_t chunk, int32_t* __restrict__ chunk_counts,
+                                                      int32_t* __restrict__ rank) {
+  extern __shared__ int32_t cursor[];   // [E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += PT) cursor[e] = 0;
+  __syncthreads();
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  const int64_t c1 = c0 + chunk < P ? c0 + chunk : P;
+  for (int64_t sub = c0; sub < c1; sub += PT) {
+    const int64_t f = sub + tid;
+    int e = -1;
+    if (f < c1) {
+      e = ids[f];
+      if (e < 0 || e >= E) e = -1;
+    }
+    uint64_t active = __ballot(e >= 0);
+    int my_rank = 0, my_cnt = 0, my_leader = 0;
+    while (active) {
+      const int leader = __ffsll((unsigned long long)active) - 1;
+      const int el = __shfl(e, leader, kWave);
+      const uint64_t m = __ballot(e == el) & active;
+      if ((m >> lane) & 1) {
+        my_rank = __popcll(m & ((1ull << lane) - 1));
+        my_cnt = __popcll(m);
+        my_leader = leader;
+      }
+      active &= ~m;
+    }
+    int base = 0;
+    for (int w = 0; w < PT / kWave; ++w) {
+      if (wave == w && e >= 0 && lane == my_leader) {
+        base = cursor[e];
+        cursor[e] = base + my_cnt;
+      }
+      __syncthreads();
+    }
+    const int b = __shfl(base, my_leader, kWave);
+    if (e >= 0) rank[f] = b + my_rank;
+  }
+  for (int e = tid; e < E; e += PT) chunk_counts[(int64_t)blockIdx.x * E + e] = cursor[e];
+}
+
+// One workgroup (>= E threads, <= 1024): thread e owns expert e.
+__global__ void __launch_bounds__(1024) perm_plan_kernel(int32_t E, int32_t block_m, int64_t nchunks,
+                                                        int32_t* __restrict__ chunk_counts,
+                                                        int32_t* __restrict__ expert_ids, int64_t nblk,
+                                                        int32_t* __restrict__ ntpp,
+                                                        int32_t* __restrict__ padded) {
+  __shared__ int32_t s_start[kMaxExperts + 1];
+  __shared__ int32_t s_blk[kMaxExperts + 1];
+  const int e = threadIdx.x;
+  int64_t total = 0;
+  if (e < E)
+    for (int64_t c = 0; c < nchunks; ++c) total += chunk_counts[c * E + e];
+  const int32_t pad = (int32_t)((total + block_m - 1) / block_m * block_m);
+  if (e < E) padded[e] = pad;
+  // exclusive scan of padded sizes across experts (E <= 1024; serial in LDS
+  // by thread 0 keeps this obviously right and costs ~E adds)
+  if (e < E) s_start[e] = pad;
+  __syncthreads();
+  if (e == 0) {
+    int32_t run = 0, blk = 0;
+    for (int h = 0; h < E; ++h) {
+      const int32_t p = s_start[h];
+      s_start[h] = run;
+      s_blk[h] = blk;
+      run += p;
+      blk += p / block_m;
+    }
+    s_start[E] = run;
+    s_blk[E] = blk;
+    *ntpp = run;
+  }
+  __syncthreads();
+  if (e < E) {
+    int32_t base = s_start[e];
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int32_t cnt = chunk_counts[c * E + e];
+      chunk_counts[c * E + e] = base;
+      base += cnt;
+    }
+    for (int32_t b = s_blk[e]; b < s_blk[e + 1] && b < nblk; ++b) expert_ids[b] = e;
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+__global__ void __launch_bounds__(256) perm_scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                          int32_t E, int64_t chunk,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          const int32_t* __restrict__ rank,
+                                                          int32_t* __restrict__ sorted_ids,
+                                                          int32_t* __restrict__ inv) {
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= P) return;
+  const int e = ids[f];
+  if (e < 0 || e >= E) {
+    inv[f] = -1;
+    return;
+  }
+  const int64_t c = f / chunk;
+  const int32_t pos = chunk_base[c * E + e] + rank[f];
+  sorted_ids[pos] = (int32_t)f;
+  inv[f] = pos;
+}
+
+// x_sorted[i] = x[sorted[i] / k] (16 bytes per thread), zeros for the sentinel.
+__global__ void __launch_bounds__(256) gather_rows_kernel(const uint16_t* __restrict__ x, int64_t P, int32_t k,
+                                                         int32_t hidden, const int32_t* __restrict__ sorted_ids,
+                                                         int64_t rows, uint16_t* __restrict__ out) {
+  const int cpr = hidden >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / cpr;
+  const int ch = (int)(idx - row * cpr);
+  if (row >= rows) return;
+  const int32_t f = sorted_ids[row];
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (f >= 0 && f < P) v = *reinterpret_cast<const uint4*>(x + (int64_t)(f / k) * hidden + ch * 8);
+  *reinterpret_cast<uint4*>(out + row * hidden + ch * 8) = v;
+}
+
+static int64_t perm_chunk(int64_t P, int32_t E) {
+  // keep nchunks * E <= 2^20 so the count table stays small
+  int64_t chunk = 1024;
+  while (cdiv(P, chunk) * E > (1 << 20)) chunk *= 2;
+  return chunk;
+}
+
+int64_t perm_workspace_bytes(int64_t P, int32_t E) {
+  const int64_t chunk = perm_chunk(P, E);
+  const int64_t nchunks = cdiv(P > 0 ? P : 1, chunk);
+  return align_up(nchunks * E * 4, 256) + align_up((P > 0 ? P : 1) * 4, 256);
+}
+
+hipError_t launch_moe_permute_ws(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                                 const uint16_t* x, int32_t hidden, int32_t* sorted_ids, int32_t* expert_ids,
+                                 int32_t* ntpp, int32_t* inv, int32_t* padded, uint16_t* x_sorted,
+                                 int64_t cap, int64_t nblk, void* ws, hipStream_t stream) {
+  const int64_t P = T * k;
+  const int64_t chunk = perm_chunk(P, E);
+  const int64_t nchunks = cdiv(P > 0 ? P : 1, chunk);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws);
+  int32_t* rank = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(ws) + align_up(nchunks * E * 4, 256));
+
+  if (cap > 0) {
+    const int fill_grid = (int)(cdiv(cap, 256) < 4096 ? cdiv(cap, 256) : 4096);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_grid), dim3(256), 0, stream, sorted_ids, cap, (int32_t)P);
+  }
+  hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(PT), (size_t)E * 4, stream, ids, P, E,
+                     chunk, counts, rank);
+  int plan_threads = (int)align_up(E, kWave);
+  hipLaunchKernelGGL(perm_plan_kernel, dim3(1), dim3(plan_threads), 0, stream, E, block_m, nchunks, counts,
+                     expert_ids, nblk, ntpp, padded);
+  if (P > 0)
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)cdiv(P, 256)), dim3(256), 0, stream, ids, P, E,
+                       chunk, counts, rank, sorted_ids, inv);
+  if (x != nullptr && x_sorted != nullptr && cap > 0) {
+    const int64_t n = cap * (hidden / 8);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, x, P, k,
+                       hidden, sorted_ids, cap, x_sorted);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K7: out[t, :] = bf16(sum_j w[t,j] * y[inv[t*k+j], :]), fp32, j ascending.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) unpermute_kernel(const uint16_t* __restrict__ y,
+                                                       const int32_t* __restrict__ inv,
+                                                       const float* __restrict__ w, int64_t T, int32_t k,
+                                                       int32_t hidden, uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.y;
+  const int ch = blockIdx.x * 256 + threadIdx.x;
+  if (ch * 8 >= hidden) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const int32_t pos = inv[t * k + j];
+    if (pos < 0) continue;
+    const float wt = w ? w[t * k + j] : 1.f;
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)pos * hidden + ch * 8);
+    const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wt * bf16_to_f32(ww[i] & 0xFFFFu);
+      acc[2 * i + 1] += wt * bf16_to_f32(ww[i] >> 16);
+    }
+  }
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(out + t * hidden + ch * 8) = o;
+}
+
+hipError_t launch_moe_unpermute(const uint16_t* y, const int32_t* inv, const float* w, int64_t T, int32_t k,
+                                int32_t hidden, uint16_t* out, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(hidden / 8, 256), (unsigned)T);
+  hipLaunchKernelGGL(unpermute_kernel, grid, dim3(256), 0, stream, y, inv, w, T, k, hidden, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K6: act = bf16(silu(gate) * up), gate = first half of the row.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) silu_mul_kernel(const uint16_t* __restrict__ h, int64_t rows,
+                                                      int32_t inter, uint16_t* __restrict__ act) {
+  const int cpr = inter >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / cpr;
+  const int ch = (int)(idx - row * cpr);
+  if (row >= rows) return;
+  const uint16_t* hr = h + row * (2 * (int64_t)inter);
+  const uint4 g = *reinterpret_cast<const uint4*>(hr + ch * 8);
+  const uint4 u = *reinterpret_cast<const uint4*>(hr + inter + ch * 8);
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+  const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float g0 = bf16_to_f32(gw[i] & 0xFFFFu), g1 = bf16_to_f32(gw[i] >> 16);
+    const float u0 = bf16_to_f32(uw[i] & 0xFFFFu), u1 = bf16_to_f32(uw[i] >> 16);
+    const float a0 = g0 / (1.f + expf(-g0)) * u0;
+    const float a1 = g1 / (1.f + expf(-g1)) * u1;
+    o[i] = pack_bf16x2(a0, a1);
+  }
+  *reinterpret_cast<uint4*>(act + row * inter + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_silu_mul(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* act, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t n = rows * (inter / 8);
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, h, rows, inter, act);
+  return hipGetLastError();
+}
+
+}  // namespace mg

@@ -1,0 +1,206 @@
+"""GPU parity: device argument builder and the bf16 grouped GEMM (forward,
+dX, dynamic-K dW) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_device_amd as mg
+import oracle
+import workloads as wl
+from gpu_util import BF16_TOL, bf16_dev, bf16_host, dev, gpu, host, rel_fro, require_gpu
+
+pytestmark = gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# --------------------------------------------------------------------------
+# builder
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,total,bm,seed", [
+    (4, 37, 16, 0), (8, 1024, 128, 1), (128, 1, 32, 2), (128, 16, 32, 3), (128, 128, 32, 4),
+    (64, 5000, 128, 5), (1024, 20000, 16, 6), (1, 0, 128, 7), (7, 3, 1, 8), (300, 777, 64, 9),
+])
+def test_builder_fixed_m_bit_exact(E, total, bm, seed):
+    sizes = wl.random_group_sizes(E, total, seed, zero_frac=0.5)
+    offs, count, ent = mg.build_worklist(mg.MG_WL_FIXED_M, dev(sizes), total, bm)
+    torch.cuda.synchronize()
+    n_ref, ent_ref = oracle.worklist_fixed_m(sizes, bm)
+    np.testing.assert_array_equal(host(offs), oracle.offsets(sizes))
+    assert int(host(count)[0]) == n_ref
+    np.testing.assert_array_equal(host(ent)[:n_ref], ent_ref)
+
+
+@pytest.mark.parametrize("E,total,seed", [(8, 1024, 0), (64, 98304, 1), (1024, 3000, 2), (3, 0, 3), (128, 1, 4)])
+def test_builder_dynamic_k_bit_exact(E, total, seed):
+    sizes = wl.random_group_sizes(E, total, seed, zero_frac=0.3)
+    sizes[: E // 3] = sizes[0]   # ties
+    total = int(sizes.sum())
+    offs, count, ent = mg.build_worklist(mg.MG_WL_DYNAMIC_K, dev(sizes), total, 128)
+    torch.cuda.synchronize()
+    assert int(host(count)[0]) == E
+    np.testing.assert_array_equal(host(ent), oracle.worklist_dynamic_k(sizes))
+    np.testing.assert_array_equal(host(offs), oracle.offsets(sizes))
+
+
+def test_builder_flags_bad_sizes_without_writing_out_of_bounds():
+    E, M, K, N = 4, 64, 64, 64
+    x = torch.zeros(M, K, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(E, K, N, dtype=torch.bfloat16, device="cuda")
+    canary = torch.full((M + 64, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = canary[:M]
+    for sizes, code in [([10, -5, 20, 30], 1), ([40, 40, 0, 0], 2)]:
+        ws = mg.workspace(E, M)
+        mg.workspace_clear(ws)
+        mg.gmm_fwd(x, w, dev(np.array(sizes, np.int32)), out=y, ws=ws)
+        torch.cuda.synchronize()
+        assert mg.workspace_error(ws) == code
+        assert (canary[M:] == 7.0).all()
+    ws = mg.workspace(E, M)
+    mg.workspace_clear(ws)
+    mg.gmm_fwd(x, w, dev(np.array([10, 20, 30, 4], np.int32)), out=y, ws=ws)
+    torch.cuda.synchronize()
+    assert mg.workspace_error(ws) == 0
+
+
+# --------------------------------------------------------------------------
+# bf16 grouped GEMM
+# --------------------------------------------------------------------------
+
+def _run_all(X, W, dY, sizes, trans_b):
+    """GPU forward/dX/dW from numpy bf16 bits; returns fp64 numpy results."""
+    Wg = np.ascontiguousarray(np.transpose(W, (0, 2, 1))) if trans_b else W
+    gs = dev(sizes)
+    y = mg.gmm_fwd(bf16_dev(X), bf16_dev(Wg), gs, trans_b=trans_b)
+    dx, dw = mg.gmm_bwd(bf16_dev(dY), bf16_dev(X), bf16_dev(Wg), gs, trans_b=trans_b)
+    torch.cuda.synchronize()
+    f = lambda t: oracle.bf16_to_f64(bf16_host(t))
+    dwh = f(dw)
+    if trans_b:
+        dwh = np.transpose(dwh, (0, 2, 1))
+    return f(y), f(dx), dwh
+
+
+def test_tiny_config_forward_and_backward():
+    c = wl.tiny_bf16(seed=0)
+    dY = wl.normal_bf16((c["M"], c["N"]), 1.0, 0, wl.T_DY)
+    y, dx, dw = _run_all(c["X"], c["W"], dY, c["sizes"], False)
+    assert rel_fro(y, oracle.gmm_fwd_bf16(c["X"], c["W"], c["sizes"])) <= BF16_TOL
+    assert rel_fro(dx, oracle.gmm_dx_bf16(dY, c["W"], c["sizes"])) <= BF16_TOL
+    assert rel_fro(dw, oracle.gmm_dw_bf16(c["X"], dY, c["sizes"])) <= BF16_TOL
+    assert (dw[0] == 0).all()   # the empty group
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("E,M,K,N,seed", [
+    (5, 300, 200, 264, 0),      # ragged in every dimension, several tiles
+    (3, 513, 136, 392, 1),
+    (1, 129, 64, 128, 2),       # one group: plain GEMM
+    (17, 700, 72, 40, 3),       # many groups, some empty
+    (8, 1024, 256, 384, 4),     # balanced
+])
+def test_bf16_gmm_matches_oracle(E, M, K, N, seed, trans_b):
+    sizes = wl.random_group_sizes(E, M, seed, zero_frac=0.25) if E > 1 else np.array([M], np.int32)
+    if E == 8:
+        sizes = np.full(8, M // 8, np.int32)
+    X = wl.normal_bf16((M, K), 1.0, seed, wl.T_X)
+    W = wl.normal_bf16((E, K, N), 0.5, seed, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, seed, wl.T_DY)
+    y, dx, dw = _run_all(X, W, dY, sizes, trans_b)
+    assert rel_fro(y, oracle.gmm_fwd_bf16(X, W, sizes)) <= BF16_TOL
+    assert rel_fro(dx, oracle.gmm_dx_bf16(dY, W, sizes)) <= BF16_TOL
+    dw_ref = oracle.gmm_dw_bf16(X, dY, sizes)
+    assert rel_fro(dw, dw_ref) <= BF16_TOL
+    for g in np.flatnonzero(sizes == 0):
+        assert (dw[g] == 0).all()
+
+
+def test_rows_past_the_groups_are_untouched():
+    E, M, K, N = 4, 200, 64, 64
+    sizes = np.array([30, 0, 50, 20], np.int32)     # sum 100 < 200
+    X = wl.normal_bf16((M, K), 1.0, 0, wl.T_X)
+    W = wl.normal_bf16((E, K, N), 1.0, 0, wl.T_W)
+    y = torch.full((M, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    mg.gmm_fwd(bf16_dev(X), bf16_dev(W), dev(sizes), out=y)
+    torch.cuda.synchronize()
+    yh = oracle.bf16_to_f64(bf16_host(y))
+    assert (yh[100:] == 3.0).all()
+    assert rel_fro(yh[:100], oracle.gmm_fwd_bf16(X[:100], W, sizes)) <= BF16_TOL
+
+
+def test_zero_group_insertion_is_bitwise_invariant():
+    E, M, K, N = 5, 260, 128, 192
+    sizes = wl.random_group_sizes(E, M, 3, zero_frac=0.0)
+    X = wl.normal_bf16((M, K), 1.0, 1, wl.T_X)
+    W = wl.normal_bf16((E, K, N), 1.0, 1, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, 1, wl.T_DY)
+    base = _run_all(X, W, dY, sizes, False)
+    junk = wl.normal_bf16((K, N), 100.0, 9, wl.T_W)
+    for pos in [0, 2, 5]:
+        s2 = np.insert(sizes, pos, 0)
+        W2 = np.insert(W, pos, junk, axis=0)
+        y, dx, dw = _run_all(X, W2, dY, s2, False)
+        np.testing.assert_array_equal(y, base[0])
+        np.testing.assert_array_equal(dx, base[1])
+        np.testing.assert_array_equal(np.delete(dw, pos, axis=0), base[2])
+        assert (dw[pos] == 0).all()
+
+
+def test_deterministic_and_empty_total():
+    E, M, K, N = 6, 333, 96, 104
+    sizes = wl.random_group_sizes(E, M, 5)
+    X = wl.normal_bf16((M, K), 1.0, 5, wl.T_X)
+    W = wl.normal_bf16((E, K, N), 1.0, 5, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, 5, wl.T_DY)
+    a = _run_all(X, W, dY, sizes, False)
+    b = _run_all(X, W, dY, sizes, False)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    # total_M = 0: forward is a no-op, dW is all zeros
+    x0 = torch.empty(0, K, dtype=torch.bfloat16, device="cuda")
+    dy0 = torch.empty(0, N, dtype=torch.bfloat16, device="cuda")
+    w = bf16_dev(W)
+    gs = dev(np.zeros(E, np.int32))
+    assert mg.gmm_fwd(x0, w, gs).shape == (0, N)
+    dw = torch.full_like(w, 5.0)
+    mg.gmm_bwd(dy0, x0, w, gs, need_dx=False, dw=dw)
+    torch.cuda.synchronize()
+    assert (dw == 0).all()
+
+
+def test_balanced_config_full_size():
+    """E=8, M=1024 (128 rows each), K=4096, N=6400; X, W uniform[0,1);
+    dY = ones.  dX and dW are checked in full against closed forms the
+    oracle evaluates in fp64 (dX[r,k] = sum_n W[g,k,n]; dW[g,k,n] =
+    sum_{r in g} X[r,k] for every n); Y on sampled rows and columns."""
+    c = wl.balanced_bf16(seed=0)
+    E, M, K, N = c["E"], c["M"], c["K"], c["N"]
+    sizes = c["sizes"]
+    gs = dev(sizes)
+    x, w, dy = bf16_dev(c["X"]), bf16_dev(c["W"]), bf16_dev(c["dY"])
+    y = mg.gmm_fwd(x, w, gs)
+    dx, dw = mg.gmm_bwd(dy, x, w, gs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(M, 24, replace=False))
+    cols = np.sort(rng.choice(N, 24, replace=False))
+    # forward on samples: the oracle on the sampled rows and columns
+    sub_sizes = np.array([np.sum((rows >= 128 * g) & (rows < 128 * (g + 1))) for g in range(E)], np.int32)
+    y_ref = oracle.gmm_fwd_bf16(c["X"][rows], np.ascontiguousarray(c["W"][:, :, cols]), sub_sizes)
+    y_got = oracle.bf16_to_f64(bf16_host(y))[np.ix_(rows, cols)]
+    assert rel_fro(y_got, y_ref) <= BF16_TOL
+    # dX in full
+    Wf = oracle.bf16_to_f64(c["W"])
+    dx_ref = np.repeat(Wf.sum(axis=2), 128, axis=0)
+    del Wf
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(dx)), dx_ref) <= BF16_TOL
+    # dW: constant along n, equal to the group's column sums of X
+    dwh = oracle.bf16_to_f64(bf16_host(dw))
+    Xf = oracle.bf16_to_f64(c["X"])
+    colsum = Xf.reshape(E, 128, K).sum(axis=1)
+    assert rel_fro(dwh[:, :, 0], colsum) <= BF16_TOL
+    assert (dwh == dwh[:, :, :1]).all()

@@ -1,0 +1,114 @@
+"""GPU parity: fp8 grouped GEMM (forward, dX, dynamic-K dW with per-group
+colwise scales) and the F8I4 sparse-M grouped GEMM.  The oracle and the GPU
+get the identical quantized operands, produced by the oracle's quantizers."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_device_amd as mg
+import oracle
+import workloads as wl
+from gpu_util import FP8_TOL, bf16_dev, bf16_host, dev, gpu, rel_fro, require_gpu
+
+pytestmark = gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _f64(t):
+    return oracle.bf16_to_f64(bf16_host(t))
+
+
+def _fp8_problem(E, M, K, N, seed, zero_frac=0.25):
+    sizes = wl.random_group_sizes(E, M, seed, zero_frac=zero_frac)
+    X = wl.normal_bf16((M, K), 1.0, seed, wl.T_X)
+    dY = wl.normal_bf16((M, N), 1.0, seed, wl.T_DY)
+    W = wl.stacked_normal_bf16(E, (K, N), 0.02, seed, wl.T_W)
+    return sizes, X, dY, W
+
+
+@pytest.mark.parametrize("E,M,K,N,seed", [(4, 300, 256, 200, 0), (9, 1000, 384, 136, 1), (1, 130, 128, 128, 2),
+                                          (16, 2048, 2048, 1408, 3)])
+def test_fp8_forward(E, M, K, N, seed):
+    sizes, X, _, W = _fp8_problem(E, M, K, N, seed)
+    xq, sx = oracle.quant_rowwise(X)
+    # weights: per-(e, n) scales over K, column-major codes [N][E*K]
+    wq, sw = oracle.quant_colwise(W.reshape(E * K, N), np.full(E, K, np.int32))
+    y = mg.gmm_fwd_fp8(dev(xq), dev(sx), dev(wq), dev(sw), E * K, K, dev(sizes), N)
+    torch.cuda.synchronize()
+    ref = oracle.gmm_fwd(oracle.dequant_rowwise(xq, sx),
+                         oracle.dequant_colwise(wq, sw, np.full(E, K, np.int32)).reshape(E, K, N), sizes)
+    assert rel_fro(_f64(y), ref) <= FP8_TOL
+
+
+@pytest.mark.parametrize("E,M,K,N,seed", [(4, 304, 256, 208, 0), (9, 1008, 136, 384, 1), (16, 2048, 1408, 2048, 3)])
+def test_fp8_backward(E, M, K, N, seed):
+    sizes, X, dY, W = _fp8_problem(E, M, K, N, seed)
+    dyq, sdy = oracle.quant_rowwise(dY)
+    wq, sw = oracle.quant_rowwise(W.reshape(E * K, N))          # per (e, k) over N
+    dyc, sdyc = oracle.quant_colwise(dY, sizes)
+    xc, sxc = oracle.quant_colwise(X, sizes)
+    dx, dw = mg.gmm_bwd_fp8(dev(sizes), K, N, dyq=dev(dyq), sdy=dev(sdy), wq=dev(wq), sw=dev(sw), w_ld=N,
+                            w_expert_stride=K * N, xc=dev(xc), sxc=dev(sxc), dyc=dev(dyc), sdyc=dev(sdyc))
+    torch.cuda.synchronize()
+    Wd = oracle.dequant_rowwise(wq, sw).reshape(E, K, N)
+    dx_ref = oracle.gmm_dx(oracle.dequant_rowwise(dyq, sdy), Wd, sizes)
+    assert rel_fro(_f64(dx), dx_ref) <= FP8_TOL
+    dw_ref = oracle.gmm_dw(oracle.dequant_colwise(xc, sxc, sizes), oracle.dequant_colwise(dyc, sdyc, sizes), sizes)
+    dwh = _f64(dw)
+    assert rel_fro(dwh, dw_ref) <= FP8_TOL
+    for g in np.flatnonzero(sizes == 0):
+        assert (dwh[g] == 0).all()
+
+
+def _f8i4_case(E, total_M, K, N, seed):
+    counts = wl.uniform_expert_rows(total_M, E, seed)
+    X = wl.normal_bf16((total_M, K), 1.0, seed, wl.T_X)
+    xq, sx = oracle.quant_rowwise(X)
+    Xd = oracle.dequant_rowwise(xq, sx)
+    offs = oracle.offsets(counts)
+    w4 = torch.randint(0, 256, (E, N, K // 2), dtype=torch.uint8, device="cuda")   # never read for empty experts
+    sw = torch.randn(E, K // 128, N, device="cuda").to(torch.bfloat16)
+    ref = np.zeros((total_M, N))
+    for e in np.flatnonzero(counts):
+        We = oracle.bf16_to_f64(wl.normal_bf16((K, N), 0.02, seed, wl.T_W, int(e)))[None]
+        p, s = oracle.quant_int4(We, 128)
+        w4[e] = dev(p[0])
+        sw[e] = bf16_dev(s[0])
+        rows = slice(offs[e], offs[e + 1])
+        ref[rows] = oracle.gmm_fwd(Xd[rows], oracle.dequant_int4(p, s, 128), np.array([counts[e]]))
+    y = mg.gmm_fwd_f8i4(dev(xq), dev(sx), w4, sw, dev(counts))
+    torch.cuda.synchronize()
+    return _f64(y), ref
+
+
+@pytest.mark.parametrize("E,total_M,K,N,seed", [(8, 5, 256, 64, 0), (16, 100, 512, 136, 1), (128, 1, 5120, 8192, 2),
+                                                (128, 16, 5120, 8192, 3)])
+def test_f8i4_sparse_m(E, total_M, K, N, seed):
+    got, ref = _f8i4_case(E, total_M, K, N, seed)
+    assert rel_fro(got, ref) <= FP8_TOL
+
+
+def test_f8i4_one_token_over_128_groups_matches_single_group():
+    """The routed row gives the same result whether the expert sits among 127
+    empty ones or alone (empty groups are skipped, not looped over)."""
+    K, N = 1024, 256
+    X = wl.normal_bf16((1, K), 1.0, 0, wl.T_X)
+    xq, sx = oracle.quant_rowwise(X)
+    W = oracle.bf16_to_f64(wl.normal_bf16((1, K, N), 0.02, 0, wl.T_W))
+    p, s = oracle.quant_int4(W, 128)
+    sizes = np.zeros(128, np.int32)
+    sizes[77] = 1
+    w4 = torch.zeros(128, N, K // 2, dtype=torch.uint8, device="cuda")
+    sw = torch.zeros(128, K // 128, N, dtype=torch.bfloat16, device="cuda")
+    w4[77] = dev(p[0])
+    sw[77] = bf16_dev(s[0])
+    y128 = mg.gmm_fwd_f8i4(dev(xq), dev(sx), w4, sw, dev(sizes))
+    y1 = mg.gmm_fwd_f8i4(dev(xq), dev(sx), dev(p), bf16_dev(s), dev(np.array([1], np.int32)))
+    torch.cuda.synchronize()
+    assert torch.equal(y128, y1)
+    ref = oracle.gmm_fwd(oracle.dequant_rowwise(xq, sx), oracle.dequant_int4(p, s, 128), np.array([1]))
+    assert rel_fro(_f64(y1), ref) <= FP8_TOL

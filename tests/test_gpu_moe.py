@@ -1,0 +1,98 @@
+"""GPU parity: token permutation (align + gather), SiLU-and-mul, the top-k
+weighted combine and the token-sorted fused MoE path."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_device_amd as mg
+import oracle
+import workloads as wl
+from gpu_util import BF16_TOL, bf16_dev, bf16_host, dev, gpu, host, rel_fro, require_gpu
+
+pytestmark = gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _check_permute(ids, E, bm, x=None):
+    p = mg.moe_permute(dev(ids), E, bm, x=None if x is None else bf16_dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.moe_align(ids, E, bm)
+    n = ref["num_tokens_post_padded"]
+    assert int(host(p["num_tokens_post_padded"])[0]) == n
+    np.testing.assert_array_equal(host(p["sorted_token_ids"]), ref["sorted_token_ids"])
+    np.testing.assert_array_equal(host(p["expert_ids"])[: n // bm], ref["expert_ids"][: n // bm])
+    np.testing.assert_array_equal(host(p["inv"]), ref["inv"])
+    np.testing.assert_array_equal(host(p["padded_sizes"]), ref["padded_sizes"])
+    if x is not None:
+        np.testing.assert_array_equal(bf16_host(p["x_sorted"]),
+                                      oracle.gather_rows(x, ids.shape[1], ref["sorted_token_ids"]))
+    return p, ref
+
+
+def test_permute_worked_example():
+    with open(os.path.join(GOLDEN, "moe_align_example.json")) as f:
+        ex = json.load(f)
+    ids = np.array(ex["topk_ids_printed"], np.int32) - 1
+    p, _ = _check_permute(ids, ex["num_experts"], ex["block_size"])
+    np.testing.assert_array_equal(host(p["sorted_token_ids"])[:16], ex["expected_sorted_token_ids"])
+
+
+@pytest.mark.parametrize("T,k,E,bm,seed", [
+    (1, 2, 8, 16, 0), (64, 2, 8, 16, 1), (4096, 2, 8, 128, 2), (37, 6, 64, 16, 3), (16384, 6, 64, 128, 4),
+    (5, 1, 3, 1, 5), (3000, 4, 1024, 32, 6),
+])
+def test_permute_random(T, k, E, bm, seed):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = wl.normal_bf16((T, 64), 1.0, seed, wl.T_X) if T <= 4096 else None
+    _check_permute(ids, E, bm, x)
+
+
+def test_permute_skewed_routing():
+    ids = wl.zipf_topk_routing(2000, 64, 6, 1.1, 0)
+    _check_permute(ids, 64, 64)
+
+
+def test_silu_mul_and_unpermute():
+    rows, I = 300, 136
+    h = wl.normal_bf16((rows, 2 * I), 2.0, 0, wl.T_X)
+    act = mg.silu_mul(bf16_dev(h))
+    torch.cuda.synchronize()
+    ref = oracle.silu_mul(oracle.bf16_to_f64(h))
+    got = oracle.bf16_to_f64(bf16_host(act))
+    assert rel_fro(got, ref) <= 4e-3
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -7 + 1e-30)
+
+    T, k, E, H = 123, 2, 8, 64
+    rng = np.random.default_rng(1)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    al = oracle.moe_align(ids, E, 16)
+    y = wl.normal_bf16((al["sorted_token_ids"].size, H), 1.0, 2, wl.T_DY)
+    out = mg.moe_unpermute(bf16_dev(y), dev(al["inv"]), dev(w), T, k)
+    torch.cuda.synchronize()
+    ref = oracle.unpermute(oracle.bf16_to_f64(y), al["inv"], w, T, k)
+    got = oracle.bf16_to_f64(bf16_host(out))
+    assert rel_fro(got, ref) <= BF16_TOL
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
+
+
+@pytest.mark.parametrize("T,bm", [(1, 16), (64, 16), (200, 32)])
+def test_fused_moe_small_matches_oracle(T, bm):
+    E, k, H, I = 8, 2, 256, 128
+    ids, w = wl.softmax_topk_routing(T, E, k, 0)
+    x = wl.normal_bf16((T, H), 1.0, 0, wl.T_X)
+    w1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.05, 0, wl.T_W1)
+    w2 = wl.stacked_normal_bf16(E, (I, H), 0.05, 0, wl.T_W2)
+    out, _ = mg.fused_moe(bf16_dev(x), bf16_dev(w1), bf16_dev(w2), dev(ids), dev(w), block_m=bm)
+    torch.cuda.synchronize()
+    ref, _ = oracle.fused_moe(x, w1, w2, ids, w, bm)
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), ref) <= BF16_TOL

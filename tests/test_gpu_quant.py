@@ -1,0 +1,128 @@
+"""GPU parity: fp8 rowwise and per-group colwise (single and dual) quantizers
+and the int4 weight quantizer, bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_device_amd as mg
+import oracle
+import workloads as wl
+from gpu_util import bf16_dev, bf16_host, dev, gpu, host, require_gpu
+
+pytestmark = gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _all_finite_bf16_rows(cols):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = wl.bf16_bits_to_f32(bits)
+    bits = bits[np.isfinite(f)]
+    pad = (-bits.size) % cols
+    bits = np.concatenate([bits, np.zeros(pad, np.uint16)])
+    return bits.reshape(-1, cols)
+
+
+@pytest.mark.parametrize("cols", [128, 1024])
+def test_rowwise_every_bf16_pattern_bit_exact(cols):
+    x = _all_finite_bf16_rows(cols)
+    # shuffle within rows so each row mixes magnitudes; also a shuffled copy by rows
+    rng = np.random.default_rng(cols)
+    x = np.concatenate([x, rng.permuted(x, axis=1)], axis=0)
+    q, s = mg.quantize_rowwise_fp8(bf16_dev(x))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rowwise(x)
+    np.testing.assert_array_equal(host(s), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
+def test_rowwise_each_bf16_value_against_many_scales():
+    """Rows whose amax sets scales 2^-126 .. 2^48, each row containing a
+    spread of bf16 values below its amax: hits subnormal e4m3 codes, ties and
+    the top code for every scale."""
+    rng = np.random.default_rng(1)
+    rows = []
+    for e in range(-120, 120, 3):
+        amax = np.float32(2.0 ** e * 1.37)
+        vals = rng.uniform(-1, 1, 255).astype(np.float32) * amax
+        rows.append(np.concatenate([[amax], vals]))
+    x = wl.f32_to_bf16_bits(np.array(rows, np.float32))
+    q, s = mg.quantize_rowwise_fp8(bf16_dev(x))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rowwise(x)
+    np.testing.assert_array_equal(host(s), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("rows,cols,ld", [(1, 8, 8), (37, 200, 208), (4096, 2048, 2048), (64, 14336, 14336),
+                                          (3, 8192 + 8, 8192 + 8)])
+def test_rowwise_shapes(rows, cols, ld):
+    full = wl.normal_bf16((rows, ld), 1.0, rows, wl.T_X)
+    full[rows // 2] = 0
+    xt = bf16_dev(full)[:, :cols]
+    q, s = mg.quantize_rowwise_fp8(xt)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rowwise(np.ascontiguousarray(full[:, :cols]))
+    np.testing.assert_array_equal(host(s), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
+def _check_colwise(x, sizes, q, s):
+    q_ref, s_ref = oracle.quant_colwise(x, sizes)
+    np.testing.assert_array_equal(host(s), s_ref)
+    covered = int(sizes.sum())
+    np.testing.assert_array_equal(host(q)[:, :covered], q_ref[:, :covered])
+
+
+@pytest.mark.parametrize("M,C,G,mult,seed", [
+    (1000, 64, 5, 1, 0), (16640, 2048, 64, 16, 1), (777, 200, 9, 1, 2), (4096, 1408, 64, 1, 3),
+    (64, 8, 3, 1, 4), (3000, 520, 128, 1, 5),
+])
+def test_colwise_single_bit_exact(M, C, G, mult, seed):
+    if mult > 1:
+        sizes = wl.jagged_sizes_multiple_of(G, M, mult, seed)
+    else:
+        sizes = wl.random_group_sizes(G, M, seed, zero_frac=0.2)
+    x = wl.normal_bf16((M, C), 1.0, seed, wl.T_DY)
+    qa, sa = mg.quantize_colwise_per_group_fp8(bf16_dev(x), dev(sizes))
+    torch.cuda.synchronize()
+    _check_colwise(x, sizes, qa, sa)
+
+
+def test_colwise_dual_equals_two_singles_and_oracle():
+    M, G = 5000, 64
+    sizes = wl.random_group_sizes(G, M, 7, zero_frac=0.2)
+    a = wl.normal_bf16((M, 1408), 1.0, 7, wl.T_DY)
+    b = wl.normal_bf16((M, 2048), 1.0, 7, wl.T_X)
+    gs = dev(sizes)
+    qa, sa, qb, sb = mg.quantize_colwise_per_group_fp8(bf16_dev(a), gs, b=bf16_dev(b))
+    qa1, sa1 = mg.quantize_colwise_per_group_fp8(bf16_dev(a), gs)
+    qb1, sb1 = mg.quantize_colwise_per_group_fp8(bf16_dev(b), gs)
+    torch.cuda.synchronize()
+    for u, v in [(qa, qa1), (sa, sa1), (qb, qb1), (sb, sb1)]:
+        assert torch.equal(u, v)
+    _check_colwise(a, sizes, qa, sa)
+    _check_colwise(b, sizes, qb, sb)
+
+
+def test_colwise_rows_outside_groups_untouched():
+    M, C = 300, 64
+    sizes = np.array([50, 0, 70], np.int32)       # covers 120 rows
+    x = wl.normal_bf16((M, C), 1.0, 0, wl.T_X)
+    qa, sa = mg.quantize_colwise_per_group_fp8(bf16_dev(x), dev(sizes))   # qa starts zeroed
+    torch.cuda.synchronize()
+    assert (host(qa)[:, 120:] == 0).all()
+    _check_colwise(x, sizes, qa, sa)
+
+
+@pytest.mark.parametrize("E,K,N", [(2, 256, 64), (3, 5120, 136)])
+def test_int4_quantizer_bit_exact(E, K, N):
+    w = wl.stacked_normal_bf16(E, (K, N), 0.02, 0, wl.T_W)
+    w4, sw = mg.quantize_int4_weights(bf16_dev(w))
+    torch.cuda.synchronize()
+    p_ref, s_ref = oracle.quant_int4(oracle.bf16_to_f64(w), 128)
+    np.testing.assert_array_equal(bf16_host(sw), s_ref)
+    np.testing.assert_array_equal(host(w4), p_ref)
