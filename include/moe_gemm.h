@@ -71,10 +71,11 @@ enum {
 /* Workspace                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of device workspace that every grouped-GEMM call with these E and
- * total_M needs (offsets, tile work lists, error word).  Depends on host
- * values only.  The workspace may be reused by consecutive calls on one
- * stream; calls that overlap in time need distinct workspaces. */
+/* Bytes of device workspace that a grouped-GEMM call with these E and
+ * total_M needs (the sticky error word; the work lists themselves are built
+ * in LDS by every kernel's prologue).  Depends on host values only; the
+ * pointer must be 256-byte aligned.  Calls that overlap in time may share a
+ * workspace: they only ever set the error word. */
 size_t mg_workspace_bytes(int32_t E, int64_t total_M);
 
 /* Reads the sticky device error word of a workspace (hipMemcpy, blocking):
@@ -102,7 +103,8 @@ enum { MG_WL_FIXED_M = 0, MG_WL_DYNAMIC_K = 1 };
  *       cap >= total_M / bm + min(total_M, E).
  *     MG_WL_DYNAMIC_K: all E groups ordered by size descending, ties by g
  *       ascending, {g, offs[g], size, 0}; cap >= E.
- * The grouped GEMMs run this same builder internally (bm = their row tile).
+ * Every grouped-GEMM kernel runs this same builder in its prologue (bm =
+ * its row tile: 128, or 32 for gmm_fwd_f8i4), so a call is one launch.
  * Errors: MG_EINVAL for null pointers, E outside [1, 1024], bm < 1, cap too
  * small for the bound above. */
 int gmm_build_worklist(int32_t kind, const int32_t* group_sizes, int32_t E,

@@ -49,44 +49,7 @@ int check_common(const int32_t* sizes, int32_t E, int64_t total_M, const void* w
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-struct Ws {
-  int32_t* err;
-  int32_t* count;
-  int32_t* offs;
-  int32_t* entries;
-  int32_t* dk;
-  int64_t cap;
-};
-
-Ws carve(void* ws, int32_t E, int64_t total_M) {
-  const WsLayout L = ws_layout(E, total_M);
-  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
-  Ws w;
-  w.err = reinterpret_cast<int32_t*>(b) + kWsErrorWord;
-  w.count = reinterpret_cast<int32_t*>(b) + kWsCountWord;
-  w.offs = reinterpret_cast<int32_t*>(b + L.offs);
-  w.entries = reinterpret_cast<int32_t*>(b + L.entries);
-  w.dk = reinterpret_cast<int32_t*>(b + L.dk_entries);
-  w.cap = L.cap;
-  return w;
-}
-
-hipError_t run_builder(const Ws& w, const int32_t* sizes, int32_t E, int64_t total_M, int bm, bool fixed,
-                       bool dynamic, hipStream_t st) {
-  BuildArgs b;
-  b.sizes = sizes;
-  b.E = E;
-  b.total_M = total_M;
-  b.bm = bm;
-  b.want_fixed = fixed;
-  b.want_dynamic = dynamic;
-  b.offs = w.offs;
-  b.count = w.count;
-  b.entries = w.entries;
-  b.dk_entries = w.dk;
-  b.err = w.err;
-  return launch_build_worklist(b, st);
-}
+int32_t* err_word(void* ws) { return reinterpret_cast<int32_t*>(ws) + kWsErrorWord; }
 
 __global__ void zero_words_kernel(int32_t* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
@@ -144,23 +107,11 @@ int gmm_build_worklist(int32_t kind, const int32_t* group_sizes, int32_t E, int6
   b.E = E;
   b.total_M = total_M;
   b.bm = bm;
-  b.want_fixed = kind == MG_WL_FIXED_M;
-  b.want_dynamic = kind == MG_WL_DYNAMIC_K;
+  b.kind = kind;
   b.offs = offs;
   b.count = count;
   b.entries = entries;
-  b.dk_entries = entries;
-  b.err = nullptr;
-  if (kind == MG_WL_DYNAMIC_K) {
-    // the dynamic list has exactly E entries; report that count too
-    b.want_fixed = 0;
-  }
   hipError_t e = launch_build_worklist(b, S(stream));
-  if (e == hipSuccess && kind == MG_WL_DYNAMIC_K) {
-    // count = E, written by a one-thread kernel so nothing is read back
-    hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, S(stream), count, E);
-    e = hipGetLastError();
-  }
   return hip_status(e, "gmm_build_worklist");
 }
 
@@ -177,10 +128,7 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E,
   if (total_M == 0) return ok();
   if (!x || !w || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
-  const Ws s = carve(ws, E, total_M);
   const int bm = 128, bn = 128;
-  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, true, false, S(stream));
-  if (e != hipSuccess) return hip_status(e, "gmm_fwd builder");
   GemmArgs a = blank_args();
   a.A = x;
   a.a_ld = K;
@@ -198,8 +146,8 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E,
   a.Kc = K;
   a.E = E;
   a.total_rows = total_M;
-  a.count = s.count;
-  a.entries = s.entries;
+  a.sizes = group_sizes;
+  a.err = err_word(ws);
   GemmLaunch L;
   L.kind = FIXED_M;
   L.elem = EL_BF16;
@@ -223,11 +171,9 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
   if (!aligned16(dy) || (x && !aligned16(x)) || (w && !aligned16(w)) || (dx && !aligned16(dx)) ||
       (dw && !aligned16(dw)))
     return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
-  const Ws s = carve(ws, E, total_M);
   const int bm = 128, bn = 128;
   if (total_M == 0 && !dw) return ok();
-  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, dx != nullptr, dw != nullptr, S(stream));
-  if (e != hipSuccess) return hip_status(e, "gmm_bwd builder");
+  hipError_t e = hipSuccess;
   if (dx && total_M > 0) {
     GemmArgs a = blank_args();
     a.A = dy;
@@ -241,8 +187,8 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
     a.Kc = N;
     a.E = E;
     a.total_rows = total_M;
-    a.count = s.count;
-    a.entries = s.entries;
+    a.sizes = group_sizes;
+    a.err = err_word(ws);
     GemmLaunch L;
     L.kind = FIXED_M;
     L.elem = EL_BF16;
@@ -278,7 +224,8 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
     a.c_gs = (int64_t)K * N;
     a.E = E;
     a.total_rows = total_M;
-    a.entries = s.dk;
+    a.sizes = group_sizes;
+    a.err = err_word(ws);
     GemmLaunch L;
     L.kind = DYNAMIC_K;
     L.elem = EL_BF16;
@@ -317,10 +264,7 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w, cons
   if (total_M == 0) return ok();
   if (!xq || !sx || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(xq) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
-  const Ws s = carve(ws, E, total_M);
   const int bm = 128, bn = 128;
-  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, true, false, S(stream));
-  if (e != hipSuccess) return hip_status(e, "gmm_fwd_fp8 builder");
   GemmArgs a = blank_args();
   a.A = xq;
   a.a_ld = K;
@@ -335,8 +279,8 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w, cons
   a.Kc = K;
   a.E = E;
   a.total_rows = total_M;
-  a.count = s.count;
-  a.entries = s.entries;
+  a.sizes = group_sizes;
+  a.err = err_word(ws);
   GemmLaunch L;
   L.kind = FIXED_M;
   L.elem = EL_FP8;
@@ -368,11 +312,9 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
     if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "dw needs K and N multiples of 8");
     if (!aligned16(xc) || !aligned16(dyc) || !aligned16(dw)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
   }
-  const Ws s = carve(ws, E, total_M);
   const int bm = 128, bn = 128;
   if (total_M == 0 && !dw) return ok();
-  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, dx != nullptr, dw != nullptr, S(stream));
-  if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 builder");
+  hipError_t e = hipSuccess;
   if (dx && total_M > 0) {
     GemmArgs a = blank_args();
     a.A = dyq;
@@ -388,8 +330,8 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
     a.Kc = N;
     a.E = E;
     a.total_rows = total_M;
-    a.count = s.count;
-    a.entries = s.entries;
+    a.sizes = group_sizes;
+    a.err = err_word(ws);
     GemmLaunch L;
     L.kind = FIXED_M;
     L.elem = EL_FP8;
@@ -416,7 +358,8 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
     a.Nout = N;
     a.E = E;
     a.total_rows = total_M;
-    a.entries = s.dk;
+    a.sizes = group_sizes;
+    a.err = err_word(ws);
     GemmLaunch L;
     L.kind = DYNAMIC_K;
     L.elem = EL_FP8;
@@ -440,10 +383,7 @@ int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4, const vo
   if (total_M == 0) return ok();
   if (!xq || !sx || !w4 || !sw || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(xq) || !aligned16(w4)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
-  const Ws s = carve(ws, E, total_M);
   const int bm = 32;
-  hipError_t e = run_builder(s, group_sizes, E, total_M, bm, true, false, S(stream));
-  if (e != hipSuccess) return hip_status(e, "gmm_fwd_f8i4 builder");
   GemmArgs a = blank_args();
   a.A = xq;
   a.a_ld = K;
@@ -456,8 +396,8 @@ int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4, const vo
   a.Kc = K;
   a.E = E;
   a.total_rows = total_M;
-  a.count = s.count;
-  a.entries = s.entries;
+  a.sizes = group_sizes;
+  a.err = err_word(ws);
   return hip_status(launch_f8i4(a, fixed_m_capacity(total_M, E, bm), S(stream)), "gmm_fwd_f8i4");
 }
 

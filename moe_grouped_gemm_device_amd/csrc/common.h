@@ -32,25 +32,21 @@ __host__ __device__ inline int64_t fixed_m_capacity(int64_t total_M, int32_t E, 
   return total_M / bm + (total_M < E ? total_M : E);
 }
 
-// Workspace: header | offs int32[E+1] (padded) | count int32 (in header) |
-//            entries int32[cap][4] for bm = kMinTileM | dk entries int32[E][4]
+// Workspace: a 256-byte header holding the sticky error word.  Every work
+// list lives in LDS (each kernel rebuilds it in its prologue), so the
+// workspace does not grow with E or total_M.
 struct WsLayout {
-  int64_t offs, entries, dk_entries, total;
-  int64_t cap;
+  int64_t total;
 };
 
 __host__ __device__ inline WsLayout ws_layout(int32_t E, int64_t total_M) {
+  (void)E;
+  (void)total_M;
   WsLayout L;
-  L.offs = kWsHeader;
-  L.entries = L.offs + align_up(4 * (int64_t)(E + 1), 256);
-  L.cap = fixed_m_capacity(total_M, E, kMinTileM) + 1;
-  L.dk_entries = L.entries + align_up(16 * L.cap, 256);
-  L.total = L.dk_entries + align_up(16 * (int64_t)E, 256);
+  L.total = kWsHeader;
   return L;
 }
 
-// Index of the count word inside the header.
-constexpr int kWsCountWord = 1;
 
 // ---------------------------------------------------------------------------
 // Number-format helpers.

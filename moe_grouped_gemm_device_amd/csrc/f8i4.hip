@@ -17,6 +17,7 @@
 // The four waves of a workgroup split K; their partial tiles are summed in
 // LDS, divided by the row scale of the activations and rounded to bf16.
 #include "kernels.h"
+#include "worklist.h"
 
 namespace mg {
 
@@ -51,7 +52,7 @@ __device__ inline i32x8 i4x32_to_e4m3(const uint4& w) {
   return r;
 }
 
-constexpr int F_BM = 32;
+constexpr int F_BM = kF8I4RowTile;
 constexpr int F_BN = 32;
 constexpr int F_UNROLL = 4;   // K chunks whose weights are requested together
 
@@ -61,8 +62,12 @@ __global__ void __launch_bounds__(256) f8i4_kernel(GemmArgs a) {
   const int K = a.Kc;
   const int N = a.Nout;
   const int nchunk = K / 128;
+  extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
+  const GroupTable tab = carve_table(table_lds, a.E);
+  const int err = build_group_table(a.sizes, a.E, a.total_rows, F_BM, false, tab);
+  if (err != 0 && blockIdx.x == 0 && tid == 0 && a.err != nullptr) *a.err = err;
   const int n_tiles = (int)cdiv(N, F_BN);
-  const int64_t items = (int64_t)(*a.count) * n_tiles;
+  const int64_t items = (int64_t)tab.tstart[a.E] * n_tiles;
   const uint8_t* xq = reinterpret_cast<const uint8_t*>(a.A);
   const uint8_t* w4 = reinterpret_cast<const uint8_t*>(a.B);
 
@@ -77,7 +82,7 @@ __global__ void __launch_bounds__(256) f8i4_kernel(GemmArgs a) {
   for (int64_t w = first; w < items; w += gridDim.x) {
     const int64_t mt = w / n_tiles;
     const int nt = (int)(w - mt * n_tiles);
-    const int4 e = reinterpret_cast<const int4*>(a.entries)[mt];
+    const int4 e = fixed_m_entry(tab, a.E, F_BM, (int32_t)mt);
     const int g = e.x;
     const int64_t row0 = e.y;
     const int m_valid = e.z;
@@ -163,7 +168,7 @@ hipError_t launch_f8i4(const GemmArgs& a, int64_t cap_entries, hipStream_t strea
   if (max_items <= 0) return hipSuccess;
   const int64_t slots = (int64_t)device_cu_count() * 4;
   const int grid = (int)(max_items < slots ? max_items : slots);
-  hipLaunchKernelGGL(f8i4_kernel, dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(f8i4_kernel, dim3(grid), dim3(256), (size_t)table_lds_bytes(a.E), stream, a);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@
 // 16 contiguous bytes.  The grid is persistent (about two workgroups per CU)
 // and consecutive work items are placed on the same XCD.
 #include "kernels.h"
+#include "worklist.h"
 
 namespace mg {
 
@@ -178,9 +179,15 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
+  // prologue: the group table (offsets, tiles, dynamic-K order) in LDS
+  extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
+  const GroupTable tab = carve_table(table_lds, a.E);
+  const int err = build_group_table(a.sizes, a.E, a.total_rows, BM, KIND == DYNAMIC_K, tab);
+  if (err != 0 && blockIdx.x == 0 && tid == 0 && a.err != nullptr) *a.err = err;
+
   const int n_tiles = (int)cdiv(a.Nout, BN);
   const int m_tiles_dk = (KIND == DYNAMIC_K) ? (int)cdiv(a.Mout, BM) : 1;
-  const int64_t items = (KIND == FIXED_M) ? (int64_t)(*a.count) * n_tiles
+  const int64_t items = (KIND == FIXED_M) ? (int64_t)tab.tstart[a.E] * n_tiles
                                           : (int64_t)a.E * m_tiles_dk * n_tiles;
 
   // consecutive work items on one XCD (workgroups are dealt round-robin to
@@ -194,7 +201,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     if (KIND == FIXED_M) {
       const int64_t mt = w / n_tiles;
       nt = (int)(w - mt * n_tiles);
-      const int4 e = reinterpret_cast<const int4*>(a.entries)[mt];
+      const int4 e = fixed_m_entry(tab, a.E, BM, (int32_t)mt);
       g = e.x;
       rowbase = e.y;
       m_valid = e.z;
@@ -207,13 +214,12 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       const int64_t rem = w - gi * per;
       const int mt = (int)(rem / n_tiles);
       nt = (int)(rem - (int64_t)mt * n_tiles);
-      const int4 e = reinterpret_cast<const int4*>(a.entries)[gi];
-      g = e.x;
+      g = tab.order[gi];
       rowbase = (int64_t)mt * BM;
       m_valid = a.Mout - (int)rowbase;
-      c_lo = e.y;
-      c_hi = (int64_t)e.y + e.z;
-      c_begin = e.z > 0 ? (c_lo & ~(int64_t)15) : c_hi;
+      c_lo = tab.off[g];
+      c_hi = c_lo + tab.eff[g];
+      c_begin = tab.eff[g] > 0 ? (c_lo & ~(int64_t)15) : c_hi;
     }
     const int n0 = nt * BN;
     const int n_valid = a.Nout - n0;
@@ -389,10 +395,18 @@ int pick_bn_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout, int bm) {
 template <int BM, int BN, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
 static hipError_t launch_one(const GemmArgs& a, int64_t max_items, hipStream_t stream) {
   if (max_items <= 0) return hipSuccess;
+  auto kern = gmm_kernel<BM, BN, A_KC, B_KC, KIND, ELEM, EPI>;
+  const int dyn = table_lds_bytes(a.E);
+  static int configured = 0;   // largest dynamic LDS size already allowed
+  if (dyn > configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, table_lds_bytes(kMaxExperts));
+    if (e != hipSuccess) return e;
+    configured = table_lds_bytes(kMaxExperts);
+  }
   const int64_t slots = (int64_t)device_cu_count() * 2;
   const int grid = (int)(max_items < slots ? max_items : slots);
-  hipLaunchKernelGGL((gmm_kernel<BM, BN, A_KC, B_KC, KIND, ELEM, EPI>), dim3(grid), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), (size_t)dyn, stream, a);
   return hipGetLastError();
 }
 

@@ -13,13 +13,10 @@ struct BuildArgs {
   int32_t E;
   int64_t total_M;
   int32_t bm;
-  int32_t want_fixed;
-  int32_t want_dynamic;
+  int32_t kind;         // 0: fixed-M entries, 1: dynamic-K entries
   int32_t* offs;        // [E+1]
-  int32_t* count;       // [1]   (fixed-M entries)
+  int32_t* count;       // [1]
   int32_t* entries;     // [cap][4]
-  int32_t* dk_entries;  // [E][4]
-  int32_t* err;         // sticky error word (may be null)
 };
 hipError_t launch_build_worklist(const BuildArgs& a, hipStream_t stream);
 
@@ -59,9 +56,9 @@ struct GemmArgs {
   int32_t Nout;
   int32_t Kc;           // FIXED_M contraction length
   int32_t E;
-  int64_t total_rows;
-  const int32_t* count;     // FIXED_M: number of entries (device)
-  const int32_t* entries;   // FIXED_M or DYNAMIC_K entries (device)
+  int64_t total_rows;       // total_M: rows of the token-stacked operands
+  const int32_t* sizes;     // device group sizes [E]
+  int32_t* err;             // sticky error word (workspace header)
 };
 
 struct GemmLaunch {
@@ -77,7 +74,8 @@ int pick_bm_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout);
 int pick_bn_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout, int bm);
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream);
-hipError_t launch_f8i4(const GemmArgs& a, int64_t cap_entries, hipStream_t stream);
+hipError_t launch_f8i4(const GemmArgs& a, int64_t max_items, hipStream_t stream);
+constexpr int kF8I4RowTile = 32;
 
 // ---------------------------------------------------------------------------
 // K3/K4: fp8 quantizers, int4 weight quantizer

@@ -1,0 +1,156 @@
+// Device-side group table: the argument builder that every grouped-GEMM
+// kernel runs in its prologue, and that the standalone builder kernel writes
+// out for inspection.
+//
+// From the device-resident group sizes one 256-thread workgroup computes in
+// LDS, with no host involvement (grouped_gemm PR "Support GPU-resident batch
+// sizes": a single-block scan of the batch sizes fills the kernel arguments):
+//   off[g]     exclusive prefix sum of the clamped sizes,
+//   eff[g]     the clamped size (negative -> 0, nothing past total_M),
+//   tstart[g]  first fixed-M tile of group g (tiles of bm rows; only
+//              non-empty groups own tiles -- FBGEMM PR "F8I4 Grouped Gemm
+//              Optimization for Sparse M": min(total_M, groups) problems),
+//   order[i]   the dynamic-K order: groups by size descending, ties by index
+//              (same PR as above, review thread: kDynamicK sorts by k).
+#pragma once
+
+#include "common.h"
+
+namespace mg {
+
+constexpr int kTableThreads = 256;
+
+// LDS bytes a table for E groups needs (off, eff, tstart, order + scan scratch).
+__host__ __device__ inline int table_lds_bytes(int E) { return 4 * (4 * (E + 1)) + 2 * 8 * 8; }
+
+struct GroupTable {
+  int32_t* off;     // [E+1]
+  int32_t* eff;     // [E]
+  int32_t* tstart;  // [E+1]
+  int32_t* order;   // [E]
+  int64_t* scratch; // [16]
+};
+
+__device__ inline GroupTable carve_table(void* lds, int E) {
+  int32_t* p = reinterpret_cast<int32_t*>(lds);
+  GroupTable t;
+  t.scratch = reinterpret_cast<int64_t*>(p);
+  p += 32;
+  t.off = p;
+  t.eff = p + (E + 1);
+  t.tstart = p + 2 * (E + 1);
+  t.order = p + 3 * (E + 1);
+  return t;
+}
+
+__device__ inline int64_t wave_incl_scan64(int64_t x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int64_t t = __shfl_up(x, d, kWave);
+    if (lane >= d) x += t;
+  }
+  return x;
+}
+
+// Inclusive scan over the 256 threads of the workgroup.
+__device__ inline int64_t block_incl_scan64(int64_t x, int64_t* s_wave) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  x = wave_incl_scan64(x);
+  if (lane == kWave - 1) s_wave[wave] = x;
+  __syncthreads();
+  int64_t before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  __syncthreads();
+  return x + before;
+}
+
+// Builds the table.  Must be called by all 256 threads.  Returns (in every
+// thread) an error code: 0, 1 (a negative size) or 2 (sizes sum past
+// total_M).  want_order enables the dynamic-K ordering (O(E^2/256) work).
+__device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E, int64_t total_M, int bm,
+                                        bool want_order, GroupTable t) {
+  const int tid = threadIdx.x;
+  const int per = (E + kTableThreads - 1) / kTableThreads;   // groups per thread (<= 4)
+  const int g0 = tid * per;
+  int64_t local = 0;
+  int neg = 0;
+  int32_t raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    raw[i] = 0;
+    if (i < per && g0 + i < E) {
+      const int32_t s = sizes[g0 + i];
+      if (s < 0) neg = 1;
+      raw[i] = s > 0 ? s : 0;
+      local += raw[i];
+    }
+  }
+  const int64_t incl = block_incl_scan64(local, t.scratch);
+  const int64_t total = __shfl(incl, kWave - 1, kWave);   // wave-local; fixed below
+  (void)total;
+  int64_t run = incl - local;
+  int32_t tiles_local = 0;
+  int32_t eff_l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    eff_l[i] = 0;
+    if (i < per && g0 + i < E) {
+      const int64_t a = run < total_M ? run : total_M;
+      const int64_t b0 = run + raw[i];
+      const int64_t b = b0 < total_M ? b0 : total_M;
+      t.off[g0 + i] = (int32_t)a;
+      eff_l[i] = (int32_t)(b - a);
+      t.eff[g0 + i] = eff_l[i];
+      tiles_local += (eff_l[i] + bm - 1) / bm;
+      run = b0;
+    }
+  }
+  // grand total and error flags (last thread holding groups knows the sum)
+  const int64_t tincl = block_incl_scan64(tiles_local, t.scratch + 8);
+  int32_t tr = (int32_t)(tincl - tiles_local);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < per && g0 + i < E) {
+      t.tstart[g0 + i] = tr;
+      tr += (eff_l[i] + bm - 1) / bm;
+    }
+  }
+  const int last = (E - 1) / per;   // thread owning group E-1
+  int err = 0;
+  if (tid == last) {
+    t.off[E] = (int32_t)(incl < total_M ? incl : total_M);
+    t.tstart[E] = (int32_t)tincl;
+    if (incl > total_M) err = 2;
+  }
+  err = __syncthreads_or(err | (neg ? 4 : 0));
+  if (want_order) {
+    for (int g = tid; g < E; g += kTableThreads) {
+      const int32_t eg = t.eff[g];
+      int rank = 0;
+      for (int h = 0; h < E; ++h) {
+        const int32_t e = t.eff[h];
+        rank += (e > eg) || (e == eg && h < g);
+      }
+      t.order[rank] = g;
+    }
+    __syncthreads();
+  }
+  return (err & 4) ? 1 : (err & 2) ? 2 : 0;
+}
+
+// Fixed-M tile index -> {group, first row, rows}.
+__device__ inline int4 fixed_m_entry(const GroupTable& t, int E, int bm, int32_t tile) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {   // last group whose first tile is <= tile
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.tstart[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int32_t i = tile - t.tstart[lo];
+  const int32_t r0 = i * bm;
+  const int32_t rows = t.eff[lo] - r0 < bm ? t.eff[lo] - r0 : bm;
+  return make_int4(lo, t.off[lo] + r0, rows, 0);
+}
+
+}  // namespace mg
