@@ -88,8 +88,6 @@ __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E
     }
   }
   const int64_t incl = block_incl_scan64(local, t.scratch);
-  const int64_t total = __shfl(incl, kWave - 1, kWave);   // wave-local; fixed below
-  (void)total;
   int64_t run = incl - local;
   int32_t tiles_local = 0;
   int32_t eff_l[4];
@@ -118,13 +116,15 @@ __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E
     }
   }
   const int last = (E - 1) / per;   // thread owning group E-1
-  int err = 0;
+  int over = 0;
   if (tid == last) {
     t.off[E] = (int32_t)(incl < total_M ? incl : total_M);
     t.tstart[E] = (int32_t)tincl;
-    if (incl > total_M) err = 2;
+    over = incl > total_M;
   }
-  err = __syncthreads_or(err | (neg ? 4 : 0));
+  // predicate reductions (each returns non-zero if any thread's is)
+  const int any_neg = __syncthreads_or(neg);
+  const int any_over = __syncthreads_or(over);
   if (want_order) {
     for (int g = tid; g < E; g += kTableThreads) {
       const int32_t eg = t.eff[g];
@@ -137,7 +137,7 @@ __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E
     }
     __syncthreads();
   }
-  return (err & 4) ? 1 : (err & 2) ? 2 : 0;
+  return any_neg ? 1 : any_over ? 2 : 0;
 }
 
 // Fixed-M tile index -> {group, first row, rows}.
