@@ -49,6 +49,17 @@ int check_common(const int32_t* sizes, int32_t E, int64_t total_M, const void* w
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// The GEMM kernels address each operand tile through a buffer resource that
+// reaches at most 2 GiB from the tile origin: one expert's weight slice and
+// the token rows of one operand must stay below that.
+int check_extents(int64_t total_M, int32_t K, int32_t N, int esz) {
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  const int64_t mx = K > N ? K : N;
+  if ((int64_t)K * N * esz > lim || total_M * mx * esz > lim)
+    return fail(MG_EUNSUPPORTED, "operand larger than 2 GiB (K*N or total_M*max(K,N) bytes)");
+  return MG_OK;
+}
+
 int32_t* err_word(void* ws) { return reinterpret_cast<int32_t*>(ws) + kWsErrorWord; }
 
 __global__ void zero_words_kernel(int32_t* p, int n) {
@@ -125,6 +136,7 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E,
   if (rc) return rc;
   if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
   if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "K and N must be multiples of 8");
+  if ((rc = check_extents(total_M, K, N, 2))) return rc;
   if (total_M == 0) return ok();
   if (!x || !w || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
@@ -168,6 +180,7 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
   if (total_M > 0 && (!dy || (dx && !w) || (dw && !x))) return fail(MG_EINVAL, "NULL tensor argument");
   if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
   if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "K and N must be multiples of 8");
+  if ((rc = check_extents(total_M, K, N, 2))) return rc;
   if (!aligned16(dy) || (x && !aligned16(x)) || (w && !aligned16(w)) || (dx && !aligned16(dx)) ||
       (dw && !aligned16(dw)))
     return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
@@ -200,7 +213,10 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
     e = launch_gemm(L, a, S(stream));
     if (e != hipSuccess) return hip_status(e, "gmm_bwd dx");
   }
-  if (dw) {
+  if (dw && total_M == 0) {
+    e = launch_zero_fill(dw, (int64_t)E * K * N * 2, S(stream));
+    if (e != hipSuccess) return hip_status(e, "gmm_bwd dw zero fill");
+  } else if (dw) {
     GemmArgs a = blank_args();
     if (!trans_b) {   // dW[g, k, n] = sum_r X[r, k] dY[r, n]
       a.A = x;
@@ -261,6 +277,7 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w, cons
   if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
   if (K % 16 || N % 8) return fail(MG_EUNSUPPORTED, "K must be a multiple of 16 and N of 8");
   if (w->ld < K) return fail(MG_EINVAL, "weight ld < K");
+  if ((rc = check_extents(total_M, K, N, 1))) return rc;
   if (total_M == 0) return ok();
   if (!xq || !sx || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(xq) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
@@ -299,6 +316,7 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
   if (rc) return rc;
   if (!dx && !dw) return fail(MG_EINVAL, "dx and dw are both NULL");
   if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
+  if ((rc = check_extents(total_M, K, N, 1))) return rc;
   if (dx) {
     if ((rc = check_fp8_weight(w))) return rc;
     if (total_M > 0 && (!dyq || !sdy)) return fail(MG_EINVAL, "NULL dx operand");
@@ -342,7 +360,10 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
     e = launch_gemm(L, a, S(stream));
     if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 dx");
   }
-  if (dw) {
+  if (dw && total_M == 0) {
+    e = launch_zero_fill(dw, (int64_t)E * K * N * 2, S(stream));
+    if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 dw zero fill");
+  } else if (dw) {
     GemmArgs a = blank_args();
     a.A = xc;
     a.a_ld = total_M;

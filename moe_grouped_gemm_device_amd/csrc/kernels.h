@@ -74,6 +74,9 @@ int pick_bm_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout);
 int pick_bn_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout, int bm);
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream);
+// The GEMM kernels read every operand's tile base unconditionally, so a
+// DYNAMIC_K launch needs total_M > 0; with no rows, dW is a plain zero fill.
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t stream);
 hipError_t launch_f8i4(const GemmArgs& a, int64_t max_items, hipStream_t stream);
 constexpr int kF8I4RowTile = 32;
 

@@ -53,7 +53,7 @@ __device__ inline int64_t wave_incl_scan64(int64_t x) {
   return x;
 }
 
-// Inclusive scan over the 256 threads of the workgroup.
+// Inclusive scan over the threads of the workgroup (at most 8 waves).
 __device__ inline int64_t block_incl_scan64(int64_t x, int64_t* s_wave) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -66,7 +66,8 @@ __device__ inline int64_t block_incl_scan64(int64_t x, int64_t* s_wave) {
   return x + before;
 }
 
-// Builds the table.  Must be called by all 256 threads.  Returns (in every
+// Builds the table.  Must be called by all threads of the workgroup
+// (256 or 512; groups are owned by the first 256).  Returns (in every
 // thread) an error code: 0, 1 (a negative size) or 2 (sizes sum past
 // total_M).  want_order enables the dynamic-K ordering (O(E^2/256) work).
 __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E, int64_t total_M, int bm,
@@ -126,7 +127,7 @@ __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E
   const int any_neg = __syncthreads_or(neg);
   const int any_over = __syncthreads_or(over);
   if (want_order) {
-    for (int g = tid; g < E; g += kTableThreads) {
+    for (int g = tid; g < E; g += blockDim.x) {
       const int32_t eg = t.eff[g];
       int rank = 0;
       for (int h = 0; h < E; ++h) {
