@@ -109,8 +109,11 @@ __global__ void __launch_bounds__(256) f8i4_kernel(GemmArgs a) {
         sc[u] = 0.f;
         if (j < j1 && col_ok) {
           // k = 128 j + 64 s + 32 half .. +32  ->  bytes (128 j + 64 s + 32 half) / 2
-          wv[u][0] = *reinterpret_cast<const uint4*>(wrow + j * 64 + half * 16);
-          wv[u][1] = *reinterpret_cast<const uint4*>(wrow + j * 64 + 32 + half * 16);
+          // weights are read once: non-temporal loads
+          const i32x4 w0 = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow + j * 64 + half * 16));
+          const i32x4 w1 = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow + j * 64 + 32 + half * 16));
+          wv[u][0] = make_uint4((uint32_t)w0[0], (uint32_t)w0[1], (uint32_t)w0[2], (uint32_t)w0[3]);
+          wv[u][1] = make_uint4((uint32_t)w1[0], (uint32_t)w1[1], (uint32_t)w1[2], (uint32_t)w1[3]);
           sc[u] = bf16_to_f32(srow[(int64_t)j * N]);
         }
       }

@@ -28,7 +28,7 @@
 
 namespace mg {
 
-constexpr int kThreads = 512;   // 8 waves: 2 (M) x 4 (N)
+constexpr int kThreads = 256;   // 4 waves: 2 (M) x 2 (N), 64 x 64 each
 
 template <int ELEM> struct ElemTraits;
 template <> struct ElemTraits<EL_BF16> {
@@ -83,15 +83,44 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, nr, kBufFlags);
 }
 
+// Cache policy of a load: operands that are read exactly once (the weights
+// of the forward and dX products) are loaded non-temporal, which lets a CU
+// keep far more reads in flight than cached loads do (measured: ~7.0 vs
+// ~4.8 TB/s for a pure stream on MI355X); operands reused by other tiles keep
+// the default policy so they stay in L2.
+constexpr int kPolicyCached = 0;
+constexpr int kPolicyStream = 2;   // nt
+
+// Build-time knobs (defaults are the measured best on MI355X):
+//   MG_GEMM_NPF        k-steps of loads in flight per workgroup (even)
+//   MG_GEMM_POL_REUSED cache policy of the operand that other tiles re-read
+#ifndef MG_GEMM_NPF
+#define MG_GEMM_NPF 6
+#endif
+#ifndef MG_GEMM_POL_REUSED
+#define MG_GEMM_POL_REUSED kPolicyCached
+#endif
+
+template <int POL>
 __device__ inline uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, POL);
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// 16-byte store that does not keep the line in cache (outputs are written once).
+__device__ inline void store16_nt(void* p, const uint4& v) {
+  i32x4 x;
+  x[0] = (int)v.x;
+  x[1] = (int)v.y;
+  x[2] = (int)v.z;
+  x[3] = (int)v.w;
+  __builtin_nontemporal_store(x, reinterpret_cast<i32x4*>(p));
 }
 
 // Contraction-contiguous operand: tile of R rows x BK contraction elements,
 // element (i, c) at base + (i * ld + c) * ESZ.  Thread chunk q: row q >> 3,
 // 16-byte chunk q & 7 of the row.
-template <int R, int ELEM>
+template <int R, int ELEM, int POL>
 struct KcTile {
   using T = ElemTraits<ELEM>;
   static constexpr int N = R * 8 / kThreads;   // chunks per thread
@@ -109,7 +138,7 @@ struct KcTile {
   }
   __device__ inline void load(uint4* dst, __amdgpu_buffer_rsrc_t r) const {
 #pragma unroll
-    for (int i = 0; i < N; ++i) dst[i] = bload(r, voff[i]);
+    for (int i = 0; i < N; ++i) dst[i] = bload<POL>(r, voff[i]);
   }
   // Loads of one k-step starting at contraction index c0, keeping only
   // chunks that meet [c_lo, c_hi): lo = c_lo - c0 and hi = c_hi - c0 are
@@ -123,7 +152,7 @@ struct KcTile {
     for (int i = 0; i < N; ++i) {
       const int c = ((threadIdx.x + i * kThreads) & 7) * T::EPC;
       const bool ok = (c + T::EPC > lo) & (c < hi);
-      dst[i] = bload(r, ok ? voff[i] : kOOB);
+      dst[i] = bload<POL>(r, ok ? voff[i] : kOOB);
     }
   }
   __device__ static inline void store(uint8_t* lds, const uint4* src) {
@@ -153,66 +182,70 @@ __device__ inline uint32_t half_of(const uint4& u) {
   return (J & 1) ? (d >> 16) : (d & 0xFFFFu);
 }
 
-// Row-contiguous bf16 operand: tile of R rows x 64 contraction elements,
-// element (i, c) at base + (c * ld + i) * 2.  Each thread loads a 2
-// (contraction) x 8 (rows) block and writes it to LDS transposed, as eight
-// 4-byte (two contraction values) pieces.
-template <int R>
-struct McTile {
-  static constexpr int RB = R / 8;          // row blocks
-  static constexpr int NB = 32 * RB;        // 32 contraction blocks of 2
-  static constexpr int PER = (NB + kThreads - 1) / kThreads;
-  static constexpr int LOADS = PER * 2;
-  uint32_t voff[PER][2];
+// Row-contiguous bf16 operand (its contraction index is strided: W in
+// [K, N] layout for the forward, X and dY for dW): the tile keeps the
+// operand's natural layout in LDS -- 64 contraction rows of R values, R * 2
+// bytes per row, 16-byte chunks XOR-swizzled by 4 * (row % 4) -- and the MFMA
+// fragments are read with gfx950's transposing LDS load (ds_read_b64_tr_b16),
+// see frag_nt.  Loads and LDS writes are plain 16-byte chunks.
+template <int R, int POL>
+struct NtTile {
+  static constexpr int CPR = R / 8;                   // 16-byte chunks per row
+  static constexpr int N = 64 * CPR / kThreads;       // chunks per thread
+  static constexpr int LOADS = N;
+  static_assert(N >= 1 && CPR >= 16, "tile shape");
+  uint32_t voff[N];
 
   __device__ inline void setup(int64_t ld, int rows_valid) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int q = threadIdx.x + p * kThreads;
-      const int rb = q % RB, cb = q / RB;
-      const bool rok = (q < NB) && (rb * 8 < rows_valid);
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
-        voff[p][ii] = rok ? (uint32_t)(((cb * 2 + ii) * ld + rb * 8) * 2) : kOOB;
+    for (int i = 0; i < N; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      const int row = q / CPR, ch = q % CPR;
+      voff[i] = ch * 8 < rows_valid ? (uint32_t)((row * ld + ch * 8) * 2) : kOOB;
     }
   }
   __device__ inline void load(uint4* dst, __amdgpu_buffer_rsrc_t r) const {
 #pragma unroll
-    for (int p = 0; p < PER; ++p)
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) dst[p * 2 + ii] = bload(r, voff[p][ii]);
+    for (int i = 0; i < N; ++i) dst[i] = bload<POL>(r, voff[i]);
   }
-
-  template <int J>
-  __device__ static inline void store_row(uint8_t* lds, const uint4* v, int rb, int cb) {
-    const int row = rb * 8 + J;
-    const uint32_t d = half_of<J>(v[0]) | (half_of<J>(v[1]) << 16);
-    *reinterpret_cast<uint32_t*>(lds + lds_off(row, cb >> 2) + (cb & 3) * 4) = d;
+  __device__ static inline int lds_addr(int row, int col) {
+    return row * (R * 2) + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2;
   }
-
   __device__ static inline void store(uint8_t* lds, const uint4* src) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int q = threadIdx.x + p * kThreads;
-      if (q < NB) {
-        const int rb = q % RB, cb = q / RB;
-        const uint4* v = src + p * 2;
-        store_row<0>(lds, v, rb, cb);
-        store_row<1>(lds, v, rb, cb);
-        store_row<2>(lds, v, rb, cb);
-        store_row<3>(lds, v, rb, cb);
-        store_row<4>(lds, v, rb, cb);
-        store_row<5>(lds, v, rb, cb);
-        store_row<6>(lds, v, rb, cb);
-        store_row<7>(lds, v, rb, cb);
-      }
+    for (int i = 0; i < N; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      const int row = q / CPR, ch = q % CPR;
+      *reinterpret_cast<uint4*>(lds + lds_addr(row, ch * 8)) = src[i];
     }
   }
 };
 
-template <int R, int ELEM, bool KC> struct TileSel;
-template <int R, int ELEM> struct TileSel<R, ELEM, true> { using type = KcTile<R, ELEM>; };
-template <int R> struct TileSel<R, EL_BF16, false> { using type = McTile<R>; };
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA bf16 fragment (lane l: operand row l % 32 of the 32-block at mn0, the
+// 8 contraction values 16 * ks + 8 * (l / 32) + 0..7) from an NtTile in LDS.
+// Within each 16-lane group, lane s points at row k0 + s / 4, columns
+// c0 + 4 * (s % 4) .. +3; the transposing load hands lane t the four rows
+// k0..k0+3 of column c0 + t.  Two loads (rows k0 and k0 + 4) make the 8
+// values.
+template <int R>
+__device__ inline bf16x8 frag_nt(const uint8_t* tile, int ks, int mn0, int lane) {
+  const int G = lane >> 4, sl = lane & 15;
+  const int k0 = ks * 16 + 8 * (G >> 1) + (sl >> 2);
+  const int col = mn0 + 16 * (G & 1) + 4 * (sl & 3);
+  const int a0 = NtTile<R, 0>::lds_addr(k0, col);
+  const int a1 = a0 + 4 * R * 2;   // row k0 + 4: same swizzle
+  auto p = (__attribute__((address_space(3))) uint8_t*)tile;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + a0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + a1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int R, int ELEM, bool KC, int POL> struct TileSel;
+template <int R, int ELEM, int POL> struct TileSel<R, ELEM, true, POL> { using type = KcTile<R, ELEM, POL>; };
+template <int R, int POL> struct TileSel<R, EL_BF16, false, POL> { using type = NtTile<R, POL>; };
 
 __device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ inline int64_t uni64(int64_t v) {
@@ -290,8 +323,8 @@ template <int BM, int BN, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
 __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   using T = ElemTraits<ELEM>;
   constexpr int BK = T::BK;
-  constexpr int NPF = 4;              // positions in flight (even)
-  constexpr int WM = BM / 2, WN = BN / 4;   // wave sub-tile (2 x 4 waves)
+  constexpr int NPF = MG_GEMM_NPF;    // positions in flight (even)
+  constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile (2 x 2 waves)
   constexpr int TI = WM / 32, TJ = WN / 32;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -305,8 +338,10 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   __shared__ __attribute__((aligned(16))) StgT stg[BM * SROWT];
 
-  using ATile = typename TileSel<BM, ELEM, A_KC>::type;
-  using BTile = typename TileSel<BN, ELEM, B_KC>::type;
+  // Fixed-M bf16 products read each weight element once: stream B.
+  constexpr int POL_B = (KIND == FIXED_M && ELEM == EL_BF16) ? kPolicyStream : kPolicyCached;
+  using ATile = typename TileSel<BM, ELEM, A_KC, MG_GEMM_POL_REUSED>::type;
+  using BTile = typename TileSel<BN, ELEM, B_KC, POL_B>::type;
   constexpr int LA = ATile::LOADS, LB = BTile::LOADS;
   // K-tail chunks of contraction-contiguous operands need masking (fixed-M:
   // the last k-step when K is not a multiple of BK; fp8 dW: the k-steps at
@@ -317,7 +352,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
 
   // prologue: the group table (offsets, tiles, dynamic-K order) in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
@@ -408,13 +443,21 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
         const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-          const int row = wm * WM + i * 32 + (lane & 31);
-          af[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(row, ch));
+          if constexpr (A_KC) {
+            const int row = wm * WM + i * 32 + (lane & 31);
+            af[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(row, ch));
+          } else {
+            af[i] = frag_nt<BM>(As, ks, wm * WM + i * 32, lane);
+          }
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          const int row = wn * WN + j * 32 + (lane & 31);
-          bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(row, ch));
+          if constexpr (B_KC) {
+            const int row = wn * WN + j * 32 + (lane & 31);
+            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(row, ch));
+          } else {
+            bfr[j] = frag_nt<BN>(Bs, ks, wn * WN + j * 32, lane);
+          }
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i)
@@ -493,7 +536,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
           val.z = pack_bf16x2(hi.x * rs, hi.y * rs);
           val.w = pack_bf16x2(hi.z * rs, hi.w * rs);
         }
-        *reinterpret_cast<uint4*>(cbase + (int64_t)row * a.c_ld + ch * 8) = val;
+        store16_nt(cbase + (int64_t)row * a.c_ld + ch * 8, val);
       }
     }
   };
