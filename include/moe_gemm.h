@@ -72,17 +72,24 @@ enum {
 /* ------------------------------------------------------------------------ */
 
 /* Bytes of device workspace that a grouped-GEMM call with these E and
- * total_M needs (the sticky error word; the work lists themselves are built
- * in LDS by every kernel's prologue).  Depends on host values only; the
- * pointer must be 256-byte aligned.  Calls that overlap in time may share a
- * workspace: they only ever set the error word. */
+ * total_M needs: a 256-byte header (the sticky error word), one arrival
+ * counter per workgroup of a stream-K launch (at most 256) and two fp32
+ * partial output tiles (128 x 256) per workgroup, about 64 MiB in all.  The
+ * work lists themselves are built in LDS by every kernel's prologue.
+ * Depends on host values only; the pointer must be 256-byte aligned.
+ * A fresh workspace must be zeroed once before its first use (a
+ * zero-filled allocation, or mg_workspace_clear); the GEMM calls leave the
+ * counters at zero again when they finish.  Calls that share a workspace
+ * must not overlap in time (enqueue them on one stream): the partial tiles
+ * and counters of one call would be taken for another's. */
 size_t mg_workspace_bytes(int32_t E, int64_t total_M);
 
 /* Reads the sticky device error word of a workspace (hipMemcpy, blocking):
  * 0 = none, 1 = negative group size, 2 = sizes sum past total_M. */
 int32_t mg_workspace_error(const void* ws);
 
-/* Clears the sticky error word (enqueued on stream). */
+/* Zeroes the workspace header (error word) and the stream-K counters
+ * (enqueued on stream, by a fill kernel). */
 int mg_workspace_clear(void* ws, mg_stream_t stream);
 
 /* ------------------------------------------------------------------------ */

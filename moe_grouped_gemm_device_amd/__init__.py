@@ -113,7 +113,7 @@ def workspace_bytes(E, total_M):
 
 def workspace(E, total_M, device="cuda"):
     """A device workspace big enough for any grouped-GEMM call with E, total_M."""
-    return torch.empty(max(workspace_bytes(E, total_M), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(workspace_bytes(E, total_M), 256), dtype=torch.uint8, device=device)
 
 
 def workspace_error(ws):

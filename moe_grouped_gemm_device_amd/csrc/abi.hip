@@ -62,8 +62,16 @@ int check_extents(int64_t total_M, int32_t K, int32_t N, int esz) {
 
 int32_t* err_word(void* ws) { return reinterpret_cast<int32_t*>(ws) + kWsErrorWord; }
 
+// Workspace pointers every GEMM launch carries.
+void attach_ws(GemmArgs& a, void* ws) {
+  uint8_t* p = reinterpret_cast<uint8_t*>(ws);
+  a.err = err_word(ws);
+  a.sk_ctr = reinterpret_cast<int32_t*>(p + kWsCounters);
+  a.sk_part = reinterpret_cast<float*>(p + kWsPartials);
+}
+
 __global__ void zero_words_kernel(int32_t* p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
 __global__ void set_word_kernel(int32_t* p, int32_t v) {
@@ -100,7 +108,8 @@ int32_t mg_workspace_error(const void* ws) {
 
 int mg_workspace_clear(void* ws, mg_stream_t stream) {
   if (ws == nullptr) return fail(MG_EINVAL, "workspace is NULL");
-  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, S(stream), reinterpret_cast<int32_t*>(ws), 2);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, S(stream), reinterpret_cast<int32_t*>(ws),
+                     kWsZeroWords);
   return hip_status(hipGetLastError(), "mg_workspace_clear");
 }
 
@@ -140,7 +149,6 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E,
   if (total_M == 0) return ok();
   if (!x || !w || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
-  const int bm = 128, bn = 128;
   GemmArgs a = blank_args();
   a.A = x;
   a.a_ld = K;
@@ -159,15 +167,12 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E,
   a.E = E;
   a.total_rows = total_M;
   a.sizes = group_sizes;
-  a.err = err_word(ws);
+  attach_ws(a, ws);
   GemmLaunch L;
   L.kind = FIXED_M;
   L.elem = EL_BF16;
   L.a_kc = true;
   L.b_kc = trans_b != 0;
-  L.bm = bm;
-  L.bn = bn;
-  L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(N, bn);
   return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd");
 }
 
@@ -184,7 +189,6 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
   if (!aligned16(dy) || (x && !aligned16(x)) || (w && !aligned16(w)) || (dx && !aligned16(dx)) ||
       (dw && !aligned16(dw)))
     return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
-  const int bm = 128, bn = 128;
   if (total_M == 0 && !dw) return ok();
   hipError_t e = hipSuccess;
   if (dx && total_M > 0) {
@@ -201,15 +205,12 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
     a.E = E;
     a.total_rows = total_M;
     a.sizes = group_sizes;
-    a.err = err_word(ws);
+    attach_ws(a, ws);
     GemmLaunch L;
     L.kind = FIXED_M;
     L.elem = EL_BF16;
     L.a_kc = true;
     L.b_kc = trans_b == 0;
-    L.bm = bm;
-    L.bn = bn;
-    L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(K, bn);
     e = launch_gemm(L, a, S(stream));
     if (e != hipSuccess) return hip_status(e, "gmm_bwd dx");
   }
@@ -241,15 +242,12 @@ int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_s
     a.E = E;
     a.total_rows = total_M;
     a.sizes = group_sizes;
-    a.err = err_word(ws);
+    attach_ws(a, ws);
     GemmLaunch L;
     L.kind = DYNAMIC_K;
     L.elem = EL_BF16;
     L.a_kc = false;
     L.b_kc = false;
-    L.bm = bm;
-    L.bn = bn;
-    L.max_items = (int64_t)E * cdiv(a.Mout, bm) * cdiv(a.Nout, bn);
     e = launch_gemm(L, a, S(stream));
     if (e != hipSuccess) return hip_status(e, "gmm_bwd dw");
   }
@@ -281,7 +279,6 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w, cons
   if (total_M == 0) return ok();
   if (!xq || !sx || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(xq) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
-  const int bm = 128, bn = 128;
   GemmArgs a = blank_args();
   a.A = xq;
   a.a_ld = K;
@@ -297,14 +294,11 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w, cons
   a.E = E;
   a.total_rows = total_M;
   a.sizes = group_sizes;
-  a.err = err_word(ws);
+  attach_ws(a, ws);
   GemmLaunch L;
   L.kind = FIXED_M;
   L.elem = EL_FP8;
   L.a_kc = L.b_kc = true;
-  L.bm = bm;
-  L.bn = bn;
-  L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(N, bn);
   return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd_fp8");
 }
 
@@ -330,7 +324,6 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
     if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "dw needs K and N multiples of 8");
     if (!aligned16(xc) || !aligned16(dyc) || !aligned16(dw)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
   }
-  const int bm = 128, bn = 128;
   if (total_M == 0 && !dw) return ok();
   hipError_t e = hipSuccess;
   if (dx && total_M > 0) {
@@ -349,14 +342,11 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
     a.E = E;
     a.total_rows = total_M;
     a.sizes = group_sizes;
-    a.err = err_word(ws);
+    attach_ws(a, ws);
     GemmLaunch L;
     L.kind = FIXED_M;
     L.elem = EL_FP8;
     L.a_kc = L.b_kc = true;
-    L.bm = bm;
-    L.bn = bn;
-    L.max_items = fixed_m_capacity(total_M, E, bm) * cdiv(K, bn);
     e = launch_gemm(L, a, S(stream));
     if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 dx");
   }
@@ -380,14 +370,11 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
     a.E = E;
     a.total_rows = total_M;
     a.sizes = group_sizes;
-    a.err = err_word(ws);
+    attach_ws(a, ws);
     GemmLaunch L;
     L.kind = DYNAMIC_K;
     L.elem = EL_FP8;
     L.a_kc = L.b_kc = true;
-    L.bm = bm;
-    L.bn = bn;
-    L.max_items = (int64_t)E * cdiv(K, bm) * cdiv(N, bn);
     e = launch_gemm(L, a, S(stream));
     if (e != hipSuccess) return hip_status(e, "gmm_bwd_fp8 dw");
   }
@@ -418,7 +405,7 @@ int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4, const vo
   a.E = E;
   a.total_rows = total_M;
   a.sizes = group_sizes;
-  a.err = err_word(ws);
+  attach_ws(a, ws);
   return hip_status(launch_f8i4(a, fixed_m_capacity(total_M, E, bm), S(stream)), "gmm_fwd_f8i4");
 }
 

@@ -32,9 +32,20 @@ __host__ __device__ inline int64_t fixed_m_capacity(int64_t total_M, int32_t E, 
   return total_M / bm + (total_M < E ? total_M : E);
 }
 
-// Workspace: a 256-byte header holding the sticky error word.  Every work
-// list lives in LDS (each kernel rebuilds it in its prologue), so the
-// workspace does not grow with E or total_M.
+// Workspace layout (bytes):
+//   [0, 256)            header: the sticky error word;
+//   [256, 1280)         one int32 arrival counter per workgroup of a
+//                       stream-K launch (zero between calls: the workgroup
+//                       that consumes a counter resets it);
+//   [1280, +64 MiB)     two fp32 partial output tiles per workgroup.
+// Every work list lives in LDS (each kernel rebuilds it in its prologue), so
+// the workspace does not grow with E or total_M.
+constexpr int kSkMaxGrid = 256;                       // workgroups of a stream-K launch, at most
+constexpr int64_t kSkPartBytes = 128 * 256 * 4;       // one fp32 partial tile (fixed-M tile)
+constexpr int64_t kWsCounters = kWsHeader;
+constexpr int64_t kWsPartials = kWsHeader + 4 * kSkMaxGrid;
+constexpr int kWsZeroWords = (int)(kWsPartials / 4);  // words a fresh workspace must have zeroed
+
 struct WsLayout {
   int64_t total;
 };
@@ -43,10 +54,9 @@ __host__ __device__ inline WsLayout ws_layout(int32_t E, int64_t total_M) {
   (void)E;
   (void)total_M;
   WsLayout L;
-  L.total = kWsHeader;
+  L.total = kWsPartials + 2 * (int64_t)kSkMaxGrid * kSkPartBytes;
   return L;
 }
-
 
 // ---------------------------------------------------------------------------
 // Number-format helpers.

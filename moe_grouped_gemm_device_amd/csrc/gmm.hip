@@ -6,36 +6,60 @@
 // "dynamic-k" problem whose contraction runs over each group's own rows):
 //   FIXED_M   : C[r, :] = A[r, :] . B_g        (forward, dX)
 //   DYNAMIC_K : C_g    = A_g^T . B_g           (dW; empty group -> zeros)
-// The work list comes from the device builder, so only non-empty groups are
-// visited (FBGEMM PR "F8I4 Grouped Gemm Optimization for Sparse M").
+// The work list comes from the device group table, so only non-empty groups
+// are visited (FBGEMM PR "F8I4 Grouped Gemm Optimization for Sparse M").
 //
-// Design (CDNA4): 256 threads = 4 waves in a 2x2 arrangement, each wave owns
-// a (BM/2) x (BN/2) sub-tile built from 32x32 MFMA blocks
-// (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4 with unit
-// block scales for e4m3).  K tiles are 128 bytes per row (64 bf16 or 128 fp8),
-// staged global -> registers -> LDS with double buffering: the next tile's
-// global loads are in flight while the current LDS tile feeds the MFMAs.
-// Operands whose contraction index is strided (W in [K, N] layout, X^T and
-// dY in dW) are transposed in registers (4 x 8 bf16 blocks) on their way to
-// LDS so every MFMA fragment is one 16-byte LDS read.  The epilogue applies
-// the fp8 scales, rounds to bf16 and goes through LDS so each lane writes
-// 16 contiguous bytes.  The grid is persistent (about two workgroups per CU)
-// and consecutive work items are placed on the same XCD.
-#include <type_traits>
-
+// Design (CDNA4):
+//  * 256 threads = 4 waves in a 2 x 2 arrangement; a wave owns a
+//    (BM/2) x (BN/2) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16,
+//    or v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales for e4m3).
+//    Output tiles are 128 x 256 (a 256 x 256 dW tile would not fit its
+//    accumulators beside the rest without spills): for
+//    these skinny products a CU's vector-memory path (its L1 keeps a bounded
+//    number of line requests in flight) limits throughput before HBM does,
+//    and every re-read of the shared operand costs as much as a fresh weight
+//    byte, so wider tiles mean fewer bytes per CU.
+//  * Operand tiles move global -> LDS by the buffer unit's LDS-DMA path
+//    (buffer_load_dwordx4 ... lds, 16 bytes per lane), never through VGPRs.
+//    NS k-steps are in flight in LDS; with no register staging the large
+//    accumulator blocks fit.  Synchronisation is explicit: a vmcnt wait sized
+//    to the loads issued after the stage being consumed, then s_barrier.
+//  * Operands whose contraction index is contiguous (X rows, W as [N, K],
+//    fp8 column-major codes) use 128-byte LDS rows with 16-byte chunks
+//    XOR-swizzled by row, read by ds_read_b128; operands whose contraction
+//    index is strided (W as [K, N], X and dY for bf16 dW) keep their natural
+//    layout, chunks swizzled by 4 * (row % 4), and are read with gfx950's
+//    transposing LDS load (ds_read_b64_tr_b16).  Each DMA lane fetches the
+//    global chunk that belongs at its LDS slot, so the LDS image comes out
+//    swizzled.
+//  * The MFMAs take their operands swapped (C^T blocks), so a lane holds four
+//    consecutive output columns of one row: the epilogue writes 8-byte runs
+//    into an LDS staging area (the stage just consumed) and 16-byte
+//    coalesced non-temporal buffer stores go to HBM.
+//  * Fixed-M products are balanced stream-K style: the (tile, k-step)
+//    positions of all work items form one sequence cut into G equal ranges,
+//    one per workgroup.  A tile split between workgroups is summed in a fixed
+//    order: each piece stores its fp32 partial tile in the workspace and
+//    bumps the tile's counter; the piece that arrives last adds all pieces in
+//    workgroup order, runs the epilogue and resets the counter.  Nobody waits
+//    for anybody, so the persistent grid cannot deadlock.
+//  * dW work items are whole tiles dealt round-robin; loads run ahead across
+//    item boundaries.
+//  * Consecutive logical workgroups sit on one XCD (dispatch deals
+//    workgroups round-robin to the 8 XCDs), so neighbouring tiles share L2.
 #include "kernels.h"
 #include "worklist.h"
 
 namespace mg {
 
-constexpr int kThreads = 256;   // 4 waves: 2 (M) x 2 (N), 64 x 64 each
+constexpr int kThreads = 256;   // 4 waves: 2 (M) x 2 (N)
 
 template <int ELEM> struct ElemTraits;
 template <> struct ElemTraits<EL_BF16> {
   static constexpr int EPC = 8;    // elements per 16-byte chunk
   static constexpr int ESZ = 2;    // bytes per element
-  static constexpr int BK = 64;    // contraction elements per tile row (128 B)
-  static constexpr int KSUB = 4;   // MFMA k-steps per tile
+  static constexpr int BK = 64;    // contraction elements per k-step (128 B per row)
+  static constexpr int KSUB = 4;   // MFMA k-steps per k-step
 };
 template <> struct ElemTraits<EL_FP8> {
   static constexpr int EPC = 16;
@@ -44,180 +68,159 @@ template <> struct ElemTraits<EL_FP8> {
   static constexpr int KSUB = 2;
 };
 
-// Bytes [lo, hi) of a 4-byte word kept, the rest cleared (lo, hi relative
-// to the word; any values).
-__device__ inline uint32_t byte_range_mask(int64_t lo, int64_t hi) {
-  const int l = lo < 0 ? 0 : (lo > 4 ? 4 : (int)lo);
-  const int h = hi < 0 ? 0 : (hi > 4 ? 4 : (int)hi);
-  if (h <= l) return 0u;
-  uint32_t m = l >= 4 ? 0u : (0xFFFFFFFFu << (8 * l));
-  if (h < 4) m &= (1u << (8 * h)) - 1u;
-  return m;
-}
-
-// Keep the bytes of a 16-byte fp8 chunk starting at contraction index c whose
-// index lies in [lo, hi); clear the others.
-__device__ inline uint4 mask_fp8_chunk(uint4 x, int64_t c, int64_t lo, int64_t hi) {
-  x.x &= byte_range_mask(lo - c, hi - c);
-  x.y &= byte_range_mask(lo - c - 4, hi - c - 4);
-  x.z &= byte_range_mask(lo - c - 8, hi - c - 8);
-  x.w &= byte_range_mask(lo - c - 12, hi - c - 12);
-  return x;
-}
-
 // ---------------------------------------------------------------------------
-// Operand tiles are fetched with raw buffer loads.  For every work item and
-// operand the workgroup builds a buffer resource in SGPRs whose base is the
-// tile origin at the current k-step and whose size ends where the operand's
-// valid contraction range ends, so rows past a group's end (or past K) read
-// as zeros with no per-load arithmetic.  Each thread keeps one 32-bit offset
-// per 16-byte chunk for the whole item; a chunk outside the tile's valid rows
-// gets an offset past any buffer size.  Advancing a k-step only moves the
-// scalar base.
+// Buffer resources and LDS DMA.  For every work item and operand the
+// workgroup builds a buffer resource (in SGPRs) whose base is the tile origin
+// at the current k-step and whose size ends where the operand's valid
+// contraction range ends, so rows past a group's end read as zeros with no
+// per-load arithmetic.  A lane whose chunk lies outside the tile's valid rows
+// or columns gets an offset past any buffer size; the DMA then writes zeros.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kOOB = 0x80000000u;       // offset no buffer below 2 GiB reaches
-constexpr int kBufFlags = 0x00020000;        // raw buffer, 32-bit data format
+constexpr uint32_t kOOB = 0x80000000u;   // offset no buffer below 2 GiB reaches
+constexpr int kBufFlags = 0x00020000;    // raw buffer, 32-bit data format
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int32_t nr = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, nr, kBufFlags);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, kBufFlags);
 }
 
-// Cache policy of a load: operands that are read exactly once (the weights
-// of the forward and dX products) are loaded non-temporal, which lets a CU
-// keep far more reads in flight than cached loads do (measured: ~7.0 vs
-// ~4.8 TB/s for a pure stream on MI355X); operands reused by other tiles keep
-// the default policy so they stay in L2.
+// The same descriptor as four words, for the LDS-DMA asm below: base address
+// (48 bits, stride 0), size in bytes, raw-buffer flags.
+__device__ inline i32x4 make_rsrc_words(const void* base, int64_t bytes) {
+  const int32_t nr = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)p;
+  r[1] = (int)((uint32_t)(p >> 32) & 0xFFFFu);
+  r[2] = nr;
+  r[3] = kBufFlags;
+  return r;
+}
+
+// Cache policy: operands read exactly once (the weights of fixed-M bf16
+// products) are loaded non-temporal; measured on MI355X, a pure stream runs
+// at ~7.0 TB/s that way against ~4.8 TB/s with the default policy.  Operands
+// that other tiles re-read keep the default policy so they stay in L2.
 constexpr int kPolicyCached = 0;
 constexpr int kPolicyStream = 2;   // nt
+constexpr int kPolicyDevice = 16;  // sc1: coherent at device scope (across XCDs)
 
-// Build-time knobs (defaults are the measured best on MI355X):
-//   MG_GEMM_NPF        k-steps of loads in flight per workgroup (even)
-//   MG_GEMM_POL_REUSED cache policy of the operand that other tiles re-read
-#ifndef MG_GEMM_NPF
-#define MG_GEMM_NPF 6
-#endif
-#ifndef MG_GEMM_POL_REUSED
-#define MG_GEMM_POL_REUSED kPolicyCached
-#endif
+typedef __attribute__((address_space(3))) void lds_void_t;
 
+__device__ inline uint32_t lds_address(uint8_t* p) { return (uint32_t)(uintptr_t)(lds_void_t*)p; }
+
+// 16 bytes per lane from global memory to LDS: lane l writes lds + 16 l (lds
+// is an LDS byte address, the same in all lanes of the wave).  Written as
+// asm rather than the compiler builtin: the compiler cannot tell which LDS
+// stage a transfer targets, so with the builtin it drains every transfer in
+// flight before each LDS read, which would serialise the K pipeline.  The
+// waits that order these transfers are all explicit (wait_vm_sync).  M0,
+// which supplies the LDS address, is restored before the statement ends.
 template <int POL>
-__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, POL);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+__device__ inline void dma16(const i32x4& r, uint32_t lds, uint32_t voff) {
+  uint32_t save;
+  if constexpr (POL == kPolicyStream) {
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "v"(voff), "s"(lds), "s"(r)
+                 : "memory");
+  } else {
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "v"(voff), "s"(lds), "s"(r)
+                 : "memory");
+  }
 }
 
-// 16-byte store that does not keep the line in cache (outputs are written once).
-__device__ inline void store16_nt(void* p, const uint4& v) {
-  i32x4 x;
-  x[0] = (int)v.x;
-  x[1] = (int)v.y;
-  x[2] = (int)v.z;
-  x[3] = (int)v.w;
-  __builtin_nontemporal_store(x, reinterpret_cast<i32x4*>(p));
+// Wait until at most VM vector-memory operations of this wave are still in
+// flight and its LDS operations are done, then meet the other waves.  One asm
+// statement, so the compiler moves no memory access across it and adds no
+// full drain of the vector-memory counter (a release fence would, for the
+// LDS-DMA transfers still in flight).
+template <int VM>
+__device__ inline void wait_vm_sync() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ inline void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uni64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Contraction-contiguous operand: tile of R rows x BK contraction elements,
-// element (i, c) at base + (i * ld + c) * ESZ.  Thread chunk q: row q >> 3,
-// 16-byte chunk q & 7 of the row.
+// ---------------------------------------------------------------------------
+// Operand tiles in LDS.
+// ---------------------------------------------------------------------------
+
+// Contraction-contiguous operand: R rows x 128 bytes (BK elements); row r at
+// r * 128, its 16-byte chunk c at slot swz_chunk(r, c).  Each 1 KB block
+// (8 rows) is one DMA instruction of one wave.
 template <int R, int ELEM, int POL>
 struct KcTile {
   using T = ElemTraits<ELEM>;
-  static constexpr int N = R * 8 / kThreads;   // chunks per thread
-  static constexpr int LOADS = N;
-  static_assert(N >= 1, "tile too small");
-  uint32_t voff[N];
+  static constexpr int BYTES = R * 128;
+  static constexpr int LPT = BYTES / (1024 * 4);   // DMA instructions per thread per k-step
+  static_assert(LPT >= 1, "tile too small");
+  uint32_t voff[LPT];
 
-  __device__ inline void setup(int64_t ld, int rows_valid) {
+  __device__ static inline int row_of(int wave, int lane, int i) { return 8 * (wave * LPT + i) + (lane >> 3); }
+  // the chunk that belongs at slot lane & 7 of its row (the swizzle is an involution)
+  __device__ static inline int chunk_of(int wave, int lane, int i) { return swz_chunk(row_of(wave, lane, i), lane & 7); }
+
+  __device__ inline void setup(int wave, int lane, int64_t ld, int rows_valid) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q >> 3, ch = q & 7;
-      voff[i] = row < rows_valid ? (uint32_t)(row * ld * T::ESZ + ch * 16) : kOOB;
+    for (int i = 0; i < LPT; ++i) {
+      const int row = row_of(wave, lane, i);
+      voff[i] = row < rows_valid ? (uint32_t)(row * ld * T::ESZ + chunk_of(wave, lane, i) * 16) : kOOB;
     }
   }
-  __device__ inline void load(uint4* dst, __amdgpu_buffer_rsrc_t r) const {
+  // RANGE: keep only chunks meeting the contraction range [lo, hi) (relative
+  // to the k-step; lo and hi are workgroup-uniform).
+  template <bool RANGE>
+  __device__ inline void issue(const i32x4& r, uint32_t tile, int wave, int lane, int lo, int hi) const {
 #pragma unroll
-    for (int i = 0; i < N; ++i) dst[i] = bload<POL>(r, voff[i]);
-  }
-  // Loads of one k-step starting at contraction index c0, keeping only
-  // chunks that meet [c_lo, c_hi): lo = c_lo - c0 and hi = c_hi - c0 are
-  // workgroup-uniform, so the test is two compares against scalars.  (fp8 dW
-  // chunks that straddle a bound are trimmed to their bytes inside it when
-  // they are written to LDS, see store_masked, so no load has to complete
-  // early.)
-  template <bool BYTES>
-  __device__ inline void load_range(uint4* dst, __amdgpu_buffer_rsrc_t r, int lo, int hi) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = ((threadIdx.x + i * kThreads) & 7) * T::EPC;
-      const bool ok = (c + T::EPC > lo) & (c < hi);
-      dst[i] = bload<POL>(r, ok ? voff[i] : kOOB);
-    }
-  }
-  __device__ static inline void store(uint8_t* lds, const uint4* src) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q >> 3, ch = q & 7;
-      *reinterpret_cast<uint4*>(lds + lds_off(row, ch)) = src[i];
-    }
-  }
-  // store() keeping only the bytes whose contraction index (relative to the
-  // k-step) lies in [lo, hi).
-  __device__ static inline void store_masked(uint8_t* lds, const uint4* src, int lo, int hi) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q >> 3, ch = q & 7;
-      *reinterpret_cast<uint4*>(lds + lds_off(row, ch)) = mask_fp8_chunk(src[i], ch * T::EPC, lo, hi);
+    for (int i = 0; i < LPT; ++i) {
+      uint32_t vo = voff[i];
+      if constexpr (RANGE) {
+        const int c = chunk_of(wave, lane, i) * T::EPC;
+        vo = ((c + T::EPC > lo) & (c < hi)) ? vo : kOOB;
+      }
+      dma16<POL>(r, tile + (wave * LPT + i) * 1024, vo);
     }
   }
 };
 
-// bf16 element j (0..7) of a 16-byte chunk.
-template <int J>
-__device__ inline uint32_t half_of(const uint4& u) {
-  const uint32_t d = (J < 2) ? u.x : (J < 4) ? u.y : (J < 6) ? u.z : u.w;
-  return (J & 1) ? (d >> 16) : (d & 0xFFFFu);
-}
-
-// Row-contiguous bf16 operand (its contraction index is strided: W in
-// [K, N] layout for the forward, X and dY for dW): the tile keeps the
-// operand's natural layout in LDS -- 64 contraction rows of R values, R * 2
-// bytes per row, 16-byte chunks XOR-swizzled by 4 * (row % 4) -- and the MFMA
-// fragments are read with gfx950's transposing LDS load (ds_read_b64_tr_b16),
-// see frag_nt.  Loads and LDS writes are plain 16-byte chunks.
+// Row-contiguous bf16 operand (contraction index strided): 64 contraction
+// rows of R values in their natural layout, R * 2 bytes per row, 16-byte
+// chunk c of row r at slot c ^ (4 * (r % 4)); the MFMA fragments are read
+// with the transposing LDS load, see frag_nt.
 template <int R, int POL>
 struct NtTile {
-  static constexpr int CPR = R / 8;                   // 16-byte chunks per row
-  static constexpr int N = 64 * CPR / kThreads;       // chunks per thread
-  static constexpr int LOADS = N;
-  static_assert(N >= 1 && CPR >= 16, "tile shape");
-  uint32_t voff[N];
+  static constexpr int BYTES = 64 * R * 2;
+  static constexpr int CPR = R / 8;        // chunks per row
+  static constexpr int RPB = 64 / CPR;     // rows per 1 KB block
+  static constexpr int LPT = BYTES / (1024 * 4);
+  static_assert(CPR >= 16 && CPR <= 64 && LPT >= 1, "tile shape");
+  uint32_t voff[LPT];
 
-  __device__ inline void setup(int64_t ld, int rows_valid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q / CPR, ch = q % CPR;
-      voff[i] = ch * 8 < rows_valid ? (uint32_t)((row * ld + ch * 8) * 2) : kOOB;
-    }
-  }
-  __device__ inline void load(uint4* dst, __amdgpu_buffer_rsrc_t r) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) dst[i] = bload<POL>(r, voff[i]);
-  }
   __device__ static inline int lds_addr(int row, int col) {
     return row * (R * 2) + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2;
   }
-  __device__ static inline void store(uint8_t* lds, const uint4* src) {
+  __device__ inline void setup(int wave, int lane, int64_t ld, int cols_valid) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q / CPR, ch = q % CPR;
-      *reinterpret_cast<uint4*>(lds + lds_addr(row, ch * 8)) = src[i];
+    for (int i = 0; i < LPT; ++i) {
+      const int row = (wave * LPT + i) * RPB + lane / CPR;
+      const int ch = (lane % CPR) ^ (4 * (row & 3));
+      voff[i] = ch * 8 < cols_valid ? (uint32_t)((row * ld + ch * 8) * 2) : kOOB;
     }
+  }
+  __device__ inline void issue(const i32x4& r, uint32_t tile, int wave) const {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) dma16<POL>(r, tile + (wave * LPT + i) * 1024, voff[i]);
   }
 };
 
@@ -225,7 +228,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // MFMA bf16 fragment (lane l: operand row l % 32 of the 32-block at mn0, the
-// 8 contraction values 16 * ks + 8 * (l / 32) + 0..7) from an NtTile in LDS.
+// 8 contraction values 16 * ks + 8 * (l / 32) + 0..7) from an NtTile.
 // Within each 16-lane group, lane s points at row k0 + s / 4, columns
 // c0 + 4 * (s % 4) .. +3; the transposing load hands lane t the four rows
 // k0..k0+3 of column c0 + t.  Two loads (rows k0 and k0 + 4) make the 8
@@ -247,21 +250,35 @@ template <int R, int ELEM, bool KC, int POL> struct TileSel;
 template <int R, int ELEM, int POL> struct TileSel<R, ELEM, true, POL> { using type = KcTile<R, ELEM, POL>; };
 template <int R, int POL> struct TileSel<R, EL_BF16, false, POL> { using type = NtTile<R, POL>; };
 
-__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ inline int64_t uni64(int64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
+// Bytes [lo, hi) of a 4-byte word kept, the rest cleared (lo, hi relative to
+// the word; any values).
+__device__ inline uint32_t byte_range_mask(int lo, int hi) {
+  const int l = lo < 0 ? 0 : (lo > 4 ? 4 : lo);
+  const int h = hi < 0 ? 0 : (hi > 4 ? 4 : hi);
+  if (h <= l) return 0u;
+  uint32_t m = l >= 4 ? 0u : (0xFFFFFFFFu << (8 * l));
+  if (h < 4) m &= (1u << (8 * h)) - 1u;
+  return m;
 }
 
-// One work item: an output tile and its contraction range.
+// Keep the bytes of a 32-byte fp8 fragment whose contraction index k0 + byte
+// lies in [lo, hi).
+__device__ inline i32x8 mask_frag8(i32x8 v, int k0, int lo, int hi) {
+#pragma unroll
+  for (int d = 0; d < 8; ++d) v[d] = (int)((uint32_t)v[d] & byte_range_mask(lo - k0 - 4 * d, hi - k0 - 4 * d));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Work items.
+// ---------------------------------------------------------------------------
 struct Item {
   int g;            // group (expert)
   int64_t rowbase;  // first output row (token row for FIXED_M, row of C_g for DYNAMIC_K)
   int m_valid;      // rows of the tile that exist
   int n0, n_valid;  // first column, columns that exist
   int64_t c_lo, c_hi, c_begin;
-  int nsteps;       // K tiles (>= 1; an empty dW group runs one all-zero step)
+  int nsteps;       // k-steps (>= 1; an empty dW group runs one all-zero step)
 };
 
 template <int BM, int BN, int KIND, int ELEM, int BK>
@@ -313,48 +330,51 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
   return it;
 }
 
-// The K loop of every work item assigned to a workgroup forms one stream of
-// (item, k-step) positions.  Global loads run NPF positions ahead of the
-// MFMAs in a ring of register slots -- across item boundaries, so a short
-// dW contraction or an epilogue never drains the memory pipeline -- and pass
-// through two LDS buffers.  One workgroup per CU; the output tile is staged
-// in a separate LDS area so the epilogue does not stall the ring.
-template <int BM, int BN, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
 __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   using T = ElemTraits<ELEM>;
   constexpr int BK = T::BK;
-  constexpr int NPF = MG_GEMM_NPF;    // positions in flight (even)
   constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile (2 x 2 waves)
   constexpr int TI = WM / 32, TJ = WN / 32;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int SROW = BN + 8;   // bf16 elements per staged output row
-  static_assert(TI >= 1 && TJ >= 1, "tile too small");
-  static_assert(NPF % 2 == 0, "ring length must be even");
-  // Output staging: bf16 for plain bf16 GEMMs; fp32 when scales follow, so
-  // the only rounding is the final one to bf16.
-  using StgT = typename std::conditional<EPI == EPI_NONE, uint16_t, float>::type;
-  constexpr int SROWT = (EPI == EPI_NONE) ? SROW : BN + 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  __shared__ __attribute__((aligned(16))) StgT stg[BM * SROWT];
-
-  // Fixed-M bf16 products read each weight element once: stream B.
+  constexpr int POL_A = kPolicyCached;
   constexpr int POL_B = (KIND == FIXED_M && ELEM == EL_BF16) ? kPolicyStream : kPolicyCached;
-  using ATile = typename TileSel<BM, ELEM, A_KC, MG_GEMM_POL_REUSED>::type;
+  using ATile = typename TileSel<BM, ELEM, A_KC, POL_A>::type;
   using BTile = typename TileSel<BN, ELEM, B_KC, POL_B>::type;
-  constexpr int LA = ATile::LOADS, LB = BTile::LOADS;
-  // K-tail chunks of contraction-contiguous operands need masking (fixed-M:
-  // the last k-step when K is not a multiple of BK; fp8 dW: the k-steps at
-  // the group's two ends).  Row-contiguous bf16 operands are bounded by the
-  // buffer size alone.
+  static_assert(ATile::BYTES == A_BYTES && BTile::BYTES == B_BYTES, "tile bytes");
+  constexpr int LPS = ATile::LPT + BTile::LPT;   // DMA instructions per thread per k-step
+  // Epilogue staging in the stage just consumed: bf16 rows of EC columns,
+  // then (fp8) the reciprocal row and column scales of the tile.
+  constexpr int SC_BYTES = (EPI == EPI_NONE) ? 0 : (BM + BN) * 4;
+  constexpr int EC = (BM * (BN + 8) * 2 + SC_BYTES <= STAGE)       ? BN
+                     : (BM * (BN / 2 + 8) * 2 + SC_BYTES <= STAGE) ? BN / 2
+                     : (BM * (BN / 4 + 8) * 2 + SC_BYTES <= STAGE) ? BN / 4
+                                                                   : BN / 8;
+  constexpr int SROW = EC + 8;
+  constexpr int PASSES = BN / EC;
+  constexpr int SPP = BM * EC / 8 / kThreads;    // 16-byte stores per thread per pass
+  constexpr int NST = PASSES * SPP;              // per epilogue
+  static_assert(EC >= 32 && BM * SROW * 2 + SC_BYTES <= STAGE, "staging does not fit");
+  static_assert(SPP >= 1 && (BM * EC / 8) % kThreads == 0, "store split");
+  static_assert((NS - 2) * LPS + NST <= 63, "vmcnt range");
+  static_assert(NS >= 2, "at least double buffering");
+  static_assert(KIND == DYNAMIC_K || (int64_t)BM * BN * 4 <= kSkPartBytes, "partial tile size");
+  // fp8 dW: chunks straddling a group boundary carry bytes of the next
+  // group; they are cleared in the fragments of the boundary k-steps
   constexpr bool MASK_BYTES = (ELEM == EL_FP8) && (KIND == DYNAMIC_K);
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uni(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // prologue: the group table (offsets, tiles, dynamic-K order) in LDS
+  // prologue: the group table (offsets, tiles or dynamic-K order) in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
   const GroupTable tab = carve_table(table_lds, a.E);
   const int err = build_group_table(a.sizes, a.E, a.total_rows, BM, KIND == DYNAMIC_K, tab);
@@ -362,66 +382,105 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
 
   const int n_tiles = (int)cdiv(a.Nout, BN);
   const int m_tiles_dk = (KIND == DYNAMIC_K) ? (int)cdiv(a.Mout, BM) : 1;
-  const int64_t items = (KIND == FIXED_M) ? (int64_t)tab.tstart[a.E] * n_tiles
-                                          : (int64_t)a.E * m_tiles_dk * n_tiles;
+  const int64_t items = uni64((KIND == FIXED_M) ? (int64_t)tab.tstart[a.E] * n_tiles
+                                                : (int64_t)a.E * m_tiles_dk * n_tiles);
+  const int G = gridDim.x;
+  // logical workgroup index: consecutive indices on one XCD
+  int b = blockIdx.x;
+  if ((G & 7) == 0) b = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // consecutive work items on one XCD (workgroups are dealt round-robin to
-  // the 8 XCDs)
-  int64_t first = blockIdx.x;
-  if ((gridDim.x & 7) == 0) first = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  if (first >= items) return;
-  const int64_t G = gridDim.x;
+  // FIXED_M: this workgroup's range [p0, p1) of the L (item, k-step)
+  // positions.  Only GS = min(G, L) workgroups take part, so every range is
+  // non-empty and the pieces of a split tile are exactly the workgroups
+  // whose ranges meet it.
+  const int S = (KIND == FIXED_M) ? (int)cdiv(a.Kc, BK) : 1;
+  const int64_t L = items * S;
+  const int64_t GS = L < G ? L : G;
+  if (KIND == FIXED_M ? b >= GS : b >= items) return;
+  const int64_t p0 = (KIND == FIXED_M) ? (int64_t)b * L / GS : 0;
+  const int64_t p1 = (KIND == FIXED_M) ? (int64_t)(b + 1) * L / GS : 0;
+
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(a.B);
-
-  ATile aad;   // per-thread chunk offsets of the load cursor's item
-  BTile bad;
-  auto setup = [&](const Item& it) {
-    aad.setup(a.a_ld, it.m_valid);
-    bad.setup(a.b_ld, it.n_valid);
-  };
-
-  // Issue the loads of k-step s of item it into (da, db); (mlo, mhi) get the
-  // step's contraction range for the byte trimming of fp8 dW.
-  auto load_slot = [&](uint4* da, uint4* db, const Item& it, int s, int& mlo, int& mhi) {
-    const int64_t c0 = it.c_begin + (int64_t)s * BK;
-    const bool empty = it.c_hi <= it.c_lo;
-    __amdgpu_buffer_rsrc_t ra, rb;
-    if constexpr (A_KC) {
-      const uint8_t* base = Ab + (it.rowbase * a.a_ld + c0) * T::ESZ;
-      int64_t ext = 0x7FFFFFFF;
-      if (KIND == DYNAMIC_K) ext = empty ? 0 : (int64_t)(it.m_valid - 1) * a.a_ld + (a.total_rows - c0);
-      ra = make_rsrc(base, ext);
+  auto fetch = [&](int64_t w) { return get_item<BM, BN, KIND, ELEM, BK>(a, tab, w, n_tiles, m_tiles_dk); };
+  // k-steps of item w this workgroup runs end at (exclusive)
+  auto item_end = [&](int64_t w, const Item& it) -> int {
+    if constexpr (KIND == FIXED_M) {
+      const int64_t e = p1 - w * S;
+      return e < S ? (int)e : S;
     } else {
-      ra = make_rsrc(Ab + (c0 * a.a_ld + it.rowbase) * 2, (it.c_hi - c0) * a.a_ld * 2);
+      return it.nsteps;
+    }
+  };
+  auto next_item = [&](int64_t w) -> int64_t { return KIND == FIXED_M ? w + 1 : w + G; };
+  auto has_item = [&](int64_t w) -> bool { return KIND == FIXED_M ? w * S < p1 : w < items; };
+
+  // load cursor (NS - 1 positions ahead of the compute cursor)
+  int64_t lw = (KIND == FIXED_M) ? p0 / S : b;
+  int ls = (KIND == FIXED_M) ? (int)(p0 - lw * S) : 0;
+  Item li = fetch(lw);
+  int lend = item_end(lw, li);
+  bool ldone = false;
+  ATile at;
+  BTile bt;
+  auto setup = [&](const Item& it) {
+    at.setup(wave, lane, a.a_ld, A_KC ? it.m_valid : it.m_valid);
+    bt.setup(wave, lane, a.b_ld, it.n_valid);
+  };
+  setup(li);
+  // compute cursor
+  int64_t cw = lw;
+  int cs = ls, cend = lend;
+  Item ci = li;
+
+  // DMA of the load cursor's k-step into an LDS stage.  Past the end of the
+  // workgroup's positions the loads still issue (all out of range: no
+  // traffic) so every k-step has the same number of vector-memory
+  // instructions, which the waits count on.
+  auto issue_loads = [&](uint8_t* st) {
+    const Item& it = li;
+    const int64_t c0 = it.c_begin + (int64_t)ls * BK;
+    i32x4 ra, rb;
+    if constexpr (A_KC) {
+      int64_t ext = 0x7FFFFFFF;
+      if (KIND == DYNAMIC_K) ext = it.c_hi <= it.c_lo ? 0 : (int64_t)(it.m_valid - 1) * a.a_ld + (a.total_rows - c0);
+      ra = make_rsrc_words(Ab + (it.rowbase * a.a_ld + c0) * T::ESZ, ldone ? 0 : ext);
+    } else {
+      ra = make_rsrc_words(Ab + (c0 * a.a_ld + it.rowbase) * 2, ldone ? 0 : (it.c_hi - c0) * a.a_ld * 2);
     }
     if constexpr (B_KC) {
-      const uint8_t* base = Bb + ((int64_t)it.g * a.b_gs + (int64_t)it.n0 * a.b_ld + c0) * T::ESZ;
       int64_t ext = 0x7FFFFFFF;
-      if (KIND == DYNAMIC_K) ext = empty ? 0 : (int64_t)(it.n_valid - 1) * a.b_ld + (a.total_rows - c0);
-      rb = make_rsrc(base, ext);
+      if (KIND == DYNAMIC_K) ext = it.c_hi <= it.c_lo ? 0 : (int64_t)(it.n_valid - 1) * a.b_ld + (a.total_rows - c0);
+      rb = make_rsrc_words(Bb + ((int64_t)it.g * a.b_gs + (int64_t)it.n0 * a.b_ld + c0) * T::ESZ, ldone ? 0 : ext);
     } else {
-      rb = make_rsrc(Bb + ((int64_t)it.g * a.b_gs + c0 * a.b_ld + it.n0) * 2, (it.c_hi - c0) * a.b_ld * 2);
+      rb = make_rsrc_words(Bb + ((int64_t)it.g * a.b_gs + c0 * a.b_ld + it.n0) * 2, ldone ? 0 : (it.c_hi - c0) * a.b_ld * 2);
     }
     // contraction range relative to this k-step, clamped to int
     const int64_t lo64 = it.c_lo - c0, hi64 = it.c_hi - c0;
     const int lo = lo64 < -BK ? -BK : (lo64 > 2 * BK ? 2 * BK : (int)lo64);
     const int hi = hi64 < -BK ? -BK : (hi64 > 2 * BK ? 2 * BK : (int)hi64);
-    mlo = lo;
-    mhi = hi;
-    if constexpr (A_KC) aad.template load_range<MASK_BYTES>(da, ra, lo, hi);
-    else aad.load(da, ra);
-    if constexpr (B_KC) bad.template load_range<MASK_BYTES>(db, rb, lo, hi);
-    else bad.load(db, rb);
+    const uint32_t sa = lds_address(st);
+    if constexpr (A_KC) at.template issue<true>(ra, sa, wave, lane, lo, hi);
+    else at.issue(ra, sa, wave);
+    if constexpr (B_KC) bt.template issue<true>(rb, sa + A_BYTES, wave, lane, lo, hi);
+    else bt.issue(rb, sa + A_BYTES, wave);
   };
-  auto store_slot = [&](uint8_t* buf, const uint4* da, const uint4* db, int mlo, int mhi) {
-    if constexpr (MASK_BYTES) {
-      ATile::store_masked(buf, da, mlo, mhi);
-      BTile::store_masked(buf + A_BYTES, db, mlo, mhi);
-    } else {
-      ATile::store(buf, da);
-      BTile::store(buf + A_BYTES, db);
+  auto advance_load = [&]() {
+    if (ldone) return;
+    if (ls + 1 < lend) {
+      ++ls;
+      return;
     }
+    const int64_t nw = next_item(lw);
+    if (!has_item(nw)) {
+      ldone = true;
+      return;
+    }
+    lw = nw;
+    ls = 0;
+    li = fetch(nw);
+    lend = item_end(nw, li);
+    setup(li);
   };
 
   f32x16 acc[TI][TJ];
@@ -434,8 +493,19 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   };
 
+  // acc[i][j] holds the transposed 32 x 32 block: lane l has output row
+  // wm * WM + 32 i + l % 32 and columns wn * WN + 32 j + 8 q + 4 (l / 32) + r
+  // in element 4 q + r.
   auto compute = [&](const uint8_t* As) {
     const uint8_t* Bs = As + A_BYTES;
+    int mlo = 0, mhi = BK;
+    if constexpr (MASK_BYTES) {
+      const int64_t c0 = ci.c_begin + (int64_t)cs * BK;
+      const int64_t lo64 = ci.c_lo - c0, hi64 = ci.c_hi - c0;
+      mlo = lo64 < 0 ? 0 : (lo64 > BK ? BK : (int)lo64);
+      mhi = hi64 < 0 ? 0 : (hi64 > BK ? BK : (int)hi64);
+    }
+    const bool edge = MASK_BYTES && (mlo > 0 || mhi < BK);
 #pragma unroll
     for (int ks = 0; ks < T::KSUB; ++ks) {
       if constexpr (ELEM == EL_BF16) {
@@ -463,16 +533,18 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
         for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       } else {
         i32x8 af[TI], bfr[TJ];
         const int ch = 4 * ks + 2 * (lane >> 5);
+        const int k0 = 16 * ch;   // contraction index of the fragment's first byte
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           const int row = wm * WM + i * 32 + (lane & 31);
           const i32x4 lo = *reinterpret_cast<const i32x4*>(As + lds_off(row, ch));
           const i32x4 hi = *reinterpret_cast<const i32x4*>(As + lds_off(row, ch + 1));
           af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          if (edge) af[i] = mask_frag8(af[i], k0, mlo, mhi);
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
@@ -480,130 +552,212 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
           const i32x4 lo = *reinterpret_cast<const i32x4*>(Bs + lds_off(row, ch));
           const i32x4 hi = *reinterpret_cast<const i32x4*>(Bs + lds_off(row, ch + 1));
           bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          if (edge) bfr[j] = mask_frag8(bfr[j], k0, mlo, mhi);
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0,
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0,
                                                                          127, 0, 127);
       }
     }
   };
 
-  // epilogue: column scale, staging, row scale, bf16 rounding, coalesced store
-  auto epilogue = [&](const Item& it) {
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int col = wn * WN + j * 32 + (lane & 31);
-      float cs = 1.f;
-      if constexpr (EPI != EPI_NONE) {
-        if (col < it.n_valid) cs = 1.f / a.sb[(int64_t)it.g * a.Nout + it.n0 + col];
+  // Epilogue into the stage st just consumed: (fp8: scales), bf16 rounding,
+  // staging, 16-byte stores.  Issues exactly NST vector-memory stores per
+  // thread (lanes outside the tile store out of range).
+  auto epilogue = [&](uint8_t* st, const Item& it) {
+    uint16_t* stg = reinterpret_cast<uint16_t*>(st);
+    float* rsc = reinterpret_cast<float*>(st + BM * SROW * 2);   // [BM] 1 / row scale
+    float* csc = rsc + BM;                                        // [BN] 1 / column scale
+    lds_sync();   // every wave is done reading st
+    if constexpr (EPI != EPI_NONE) {
+      for (int idx = tid; idx < BM + BN; idx += kThreads) {
+        if (idx < BM) {
+          float v = 0.f;
+          if (idx < it.m_valid) {
+            const int64_t r = (EPI == EPI_ROW_COL) ? it.rowbase + idx : (int64_t)it.g * a.Mout + it.rowbase + idx;
+            v = 1.f / a.sa[r];
+          }
+          rsc[idx] = v;
+        } else {
+          const int c = idx - BM;
+          float v = 0.f;
+          if (c < it.n_valid) v = 1.f / a.sb[(int64_t)it.g * a.Nout + it.n0 + c];
+          csc[c] = v;
+        }
       }
+      lds_sync();
+    }
+    const __amdgpu_buffer_rsrc_t cr =
+        make_rsrc(reinterpret_cast<uint16_t*>(a.C) + (int64_t)it.g * a.c_gs + it.rowbase * a.c_ld + it.n0, 0x7FFFFFFF);
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
+    for (int e = 0; e < PASSES; ++e) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if constexpr (EPI == EPI_NONE) {
-            stg[row * SROWT + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
-          } else {
-            stg[row * SROWT + col] = acc[i][j][v] * cs;
+      for (int j = 0; j < TJ; ++j) {
+        const int cb = wn * WN + 32 * j;   // first column of block j
+        if (cb / EC == e) {
+#pragma unroll
+          for (int i = 0; i < TI; ++i) {
+            const int row = wm * WM + 32 * i + (lane & 31);
+            float rs = 1.f;
+            if constexpr (EPI != EPI_NONE) rs = rsc[row];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int col = cb + 8 * q + 4 * (lane >> 5);
+              float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+              float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+              if constexpr (EPI != EPI_NONE) {
+                const f32x4 cs4 = *reinterpret_cast<const f32x4*>(csc + col);
+                v0 = (v0 * cs4[0]) * rs;
+                v1 = (v1 * cs4[1]) * rs;
+                v2 = (v2 * cs4[2]) * rs;
+                v3 = (v3 * cs4[3]) * rs;
+              }
+              uint2 pk;
+              pk.x = pack_bf16x2(v0, v1);
+              pk.y = pack_bf16x2(v2, v3);
+              *reinterpret_cast<uint2*>(stg + row * SROW + (col - e * EC)) = pk;
+            }
           }
         }
       }
-    }
-    __syncthreads();
-    constexpr int CPR = BN / 8;                 // 16-byte output chunks per row
-    constexpr int TOTAL = BM * CPR;
-    uint16_t* cbase = reinterpret_cast<uint16_t*>(a.C) + (int64_t)it.g * a.c_gs + it.rowbase * a.c_ld + it.n0;
+      lds_sync();
 #pragma unroll
-    for (int q0 = 0; q0 < TOTAL; q0 += kThreads) {
-      const int q = q0 + tid;
-      const int row = q / CPR, ch = q % CPR;
-      if (row < it.m_valid && ch * 8 < it.n_valid) {
-        uint4 val;
-        if constexpr (EPI == EPI_NONE) {
-          val = *reinterpret_cast<const uint4*>(stg + row * SROWT + ch * 8);
-        } else {
-          float rs;
-          if constexpr (EPI == EPI_ROW_COL) rs = 1.f / a.sa[it.rowbase + row];
-          else rs = 1.f / a.sa[(int64_t)it.g * a.Mout + it.rowbase + row];
-          const float4 lo = *reinterpret_cast<const float4*>(stg + row * SROWT + ch * 8);
-          const float4 hi = *reinterpret_cast<const float4*>(stg + row * SROWT + ch * 8 + 4);
-          val.x = pack_bf16x2(lo.x * rs, lo.y * rs);
-          val.y = pack_bf16x2(lo.z * rs, lo.w * rs);
-          val.z = pack_bf16x2(hi.x * rs, hi.y * rs);
-          val.w = pack_bf16x2(hi.z * rs, hi.w * rs);
-        }
-        store16_nt(cbase + (int64_t)row * a.c_ld + ch * 8, val);
+      for (int k = 0; k < SPP; ++k) {
+        const int q = tid + k * kThreads;
+        const int row = q / (EC / 8), ch = q % (EC / 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + row * SROW + ch * 8);
+        const int col = e * EC + ch * 8;
+        const uint32_t vo = (row < it.m_valid && col < it.n_valid) ? (uint32_t)((row * a.c_ld + col) * 2) : kOOB;
+        i32x4 d;
+        d[0] = (int)v.x;
+        d[1] = (int)v.y;
+        d[2] = (int)v.z;
+        d[3] = (int)v.w;
+        __builtin_amdgcn_raw_buffer_store_b128(d, cr, (int)vo, 0, kPolicyStream);
+      }
+      if (e + 1 < PASSES) lds_sync();
+    }
+  };
+
+  // Stream-K combination of a fixed-M tile (FIXED_M only).  Returns true when
+  // acc holds the whole tile's sum afterwards and this workgroup must write it.
+  // Partial tiles are stored and loaded with device-scope coherence (sc1:
+  // written through to, and read from, the point where all XCDs agree), so
+  // no L2-wide writeback or invalidate is needed: a wait for the stores to
+  // complete orders them before the counter update, and the loads after the
+  // counter update cannot hit stale lines.  (A __threadfence() here would
+  // write back and invalidate the whole L2 of the XCD, and every later
+  // operand load on that XCD would go back to HBM.)
+  constexpr int PART_BYTES = BM * BN * 4;
+  constexpr int WAVE_BYTES = TI * TJ * 4096;   // 16 floats x 64 lanes per block
+  auto wg_of = [&](int64_t pos) -> int { return (int)(((pos + 1) * GS - 1) / L); };
+  auto part_rsrc = [&](int bb, int64_t w) {
+    const int64_t first = ((int64_t)bb * L / GS) / S;   // first item in bb's range
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sk_part) +
+                          (int64_t)(2 * bb + (first == w ? 0 : 1)) * PART_BYTES + wave * WAVE_BYTES;
+    return make_rsrc(base, WAVE_BYTES);
+  };
+  auto sk_combine = [&](const Item& it, int64_t w) -> bool {
+    const int bf = wg_of(w * S), bl = wg_of(w * S + S - 1);
+    if (bf == bl) return true;
+    {
+      const __amdgpu_buffer_rsrc_t mine = part_rsrc(b, w);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const bool ok = wm * WM + 32 * i + (lane & 31) < it.m_valid;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            i32x4 v;
+            v[0] = __float_as_int(acc[i][j][4 * q]);
+            v[1] = __float_as_int(acc[i][j][4 * q + 1]);
+            v[2] = __float_as_int(acc[i][j][4 * q + 2]);
+            v[3] = __float_as_int(acc[i][j][4 * q + 3]);
+            const uint32_t vo = ok ? (uint32_t)((((i * TJ + j) * 4 + q) * 64 + lane) * 16) : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(v, mine, (int)vo, 0, kPolicyDevice);
+          }
       }
     }
-  };
-
-  uint4 da[NPF][LA];
-  uint4 db[NPF][LB];
-  int mlo[NPF], mhi[NPF];
-
-  // load cursor (runs NPF positions ahead) and compute cursor
-  int64_t lw = first;
-  int ls = 0;
-  Item li = get_item<BM, BN, KIND, ELEM, BK>(a, tab, lw, n_tiles, m_tiles_dk);
-  int64_t cw = first;
-  int cs = 0;
-  Item ci = li;
-  setup(li);
-  // Past the end of its stream the load cursor keeps re-reading its last
-  // item's final k-step (never consumed), so loads need no branch.
-  auto advance_load = [&]() {
-    if (lw >= items) return;
-    if (ls + 1 < li.nsteps) {
-      ++ls;
-      return;
+    wait_vm_all();   // this wave's partial has reached the coherence point
+    lds_sync();
+    int32_t* flag = reinterpret_cast<int32_t*>(tab.scratch);
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(a.sk_ctr + bf, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == bl - bf;
+      if (last) __hip_atomic_store(a.sk_ctr + bf, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = last;
     }
-    if (lw + G < items) {
-      lw += G;
-      ls = 0;
-      li = get_item<BM, BN, KIND, ELEM, BK>(a, tab, lw, n_tiles, m_tiles_dk);
-      setup(li);
-    } else {
-      lw = items;   // finished: stay on the last k-step
-    }
-  };
-  auto advance_compute = [&]() {
-    if (++cs >= ci.nsteps) {
-      cs = 0;
-      cw += G;
-      if (cw < items) ci = get_item<BM, BN, KIND, ELEM, BK>(a, tab, cw, n_tiles, m_tiles_dk);
-    }
-  };
-
+    lds_sync();
+    const int last = uni(*flag);
+    if (!last) return false;
+    zero_acc();
+    for (int bb = bf; bb <= bl; ++bb) {
+      const __amdgpu_buffer_rsrc_t src = part_rsrc(bb, w);
 #pragma unroll
-  for (int u = 0; u < NPF; ++u) {
-    load_slot(da[u], db[u], li, ls, mlo[u], mhi[u]);
+      for (int i = 0; i < TI; ++i) {
+        const bool ok = wm * WM + 32 * i + (lane & 31) < it.m_valid;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t vo = ok ? (uint32_t)((((i * TJ + j) * 4 + q) * 64 + lane) * 16) : kOOB;
+            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, (int)vo, 0, kPolicyDevice);
+            acc[i][j][4 * q] += __int_as_float(v[0]);
+            acc[i][j][4 * q + 1] += __int_as_float(v[1]);
+            acc[i][j][4 * q + 2] += __int_as_float(v[2]);
+            acc[i][j][4 * q + 3] += __int_as_float(v[3]);
+          }
+      }
+    }
+    return true;
+  };
+
+  // ---- main loop ----------------------------------------------------------
+  // NS - 1 k-steps are loaded ahead; stages are used round-robin.
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) {
+    issue_loads(smem + u * STAGE);
     advance_load();
   }
+  int stage = 0;            // stage holding the compute cursor's k-step
+  int lstage = NS - 1;      // stage the next load goes to
+  bool epi_prev = false;    // the last epilogue's NST stores follow the newest loads
   zero_acc();
-  store_slot(smem, da[0], db[0], mlo[0], mhi[0]);
-  __syncthreads();
-
   for (;;) {
-#pragma unroll
-    for (int u = 0; u < NPF; ++u) {
-      load_slot(da[u], db[u], li, ls, mlo[u], mhi[u]);
+    int last_stage = stage;
+    for (; cs < cend; ++cs) {
+      // this thread's DMA for the current stage has landed (only the next
+      // NS - 2 stages' loads and the last epilogue's stores may be in
+      // flight), and every wave is past the previous k-step
+      if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
+      else wait_vm_sync<(NS - 2) * LPS>();
+      epi_prev = false;
+      issue_loads(smem + lstage * STAGE);
       advance_load();
-      compute(smem + (u & 1) * STAGE);
-      if (cs == ci.nsteps - 1) {
-        epilogue(ci);
-        zero_acc();
-      }
-      advance_compute();
-      if (cw >= items) return;
-      const int nx = (u + 1) % NPF;
-      store_slot(smem + ((u + 1) & 1) * STAGE, da[nx], db[nx], mlo[nx], mhi[nx]);
-      __syncthreads();
+      lstage = lstage + 1 == NS ? 0 : lstage + 1;
+      compute(smem + stage * STAGE);
+      last_stage = stage;
+      stage = stage + 1 == NS ? 0 : stage + 1;
     }
+    bool write = true;
+    if constexpr (KIND == FIXED_M) write = sk_combine(ci, cw);
+    if (write) {
+      epilogue(smem + last_stage * STAGE, ci);
+      epi_prev = true;
+    }
+    zero_acc();
+    const int64_t nw = next_item(cw);
+    if (!has_item(nw)) break;
+    cw = nw;
+    cs = 0;
+    ci = fetch(nw);
+    cend = item_end(nw, ci);
   }
+  wait_vm_all();   // no LDS-DMA transfer may outlive the workgroup
 }
 
 // Zero n 16-byte words (dW when there are no token rows at all: every group
@@ -638,51 +792,48 @@ int device_cu_count() {
   return cached[dev];
 }
 
-int pick_bm_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout) {
-  (void)elem; (void)total_M; (void)E; (void)Nout;
-  return 128;
-}
+int gemm_tile_m(int kind) { (void)kind; return 128; }
+int gemm_tile_n(int kind) { (void)kind; return 256; }
 
-int pick_bn_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout, int bm) {
-  (void)elem; (void)total_M; (void)E; (void)Nout; (void)bm;
-  return 128;
-}
-
-template <int BM, int BN, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
-static hipError_t launch_one(const GemmArgs& a, int64_t max_items, hipStream_t stream) {
-  if (max_items <= 0) return hipSuccess;
-  auto kern = gmm_kernel<BM, BN, A_KC, B_KC, KIND, ELEM, EPI>;
+template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
+static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
+  using T = ElemTraits<ELEM>;
+  // host bound on the work: fixed-M tiles cover at most
+  // floor(total_M / BM) + min(total_M, E) row slices
+  int64_t work;
+  if (KIND == FIXED_M) work = fixed_m_capacity(a.total_rows, a.E, BM) * cdiv(a.Nout, BN) * cdiv(a.Kc, T::BK);
+  else work = (int64_t)a.E * cdiv(a.Mout, BM) * cdiv(a.Nout, BN);
+  if (work <= 0) return hipSuccess;
+  auto kern = gmm_kernel<BM, BN, NS, A_KC, B_KC, KIND, ELEM, EPI>;
   const int dyn = table_lds_bytes(a.E);
-  static int configured = 0;   // largest dynamic LDS size already allowed
-  if (dyn > configured) {
+  static int configured = 0;   // dynamic LDS size already allowed
+  if (configured == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, table_lds_bytes(kMaxExperts));
     if (e != hipSuccess) return e;
-    configured = table_lds_bytes(kMaxExperts);
+    configured = 1;
   }
-  const int64_t slots = (int64_t)device_cu_count();
-  const int grid = (int)(max_items < slots ? max_items : slots);
+  int64_t slots = device_cu_count();
+  if (KIND == FIXED_M && slots > kSkMaxGrid) slots = kSkMaxGrid;
+  const int grid = (int)(work < slots ? work : slots);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), (size_t)dyn, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream) {
-  if (L.bm != 128 || L.bn != 128) return hipErrorInvalidValue;
   if (L.elem == EL_BF16) {
     if (L.kind == FIXED_M) {
       if (!L.a_kc) return hipErrorInvalidValue;
-      if (L.b_kc) return launch_one<128, 128, true, true, FIXED_M, EL_BF16, EPI_NONE>(a, L.max_items, stream);
-      return launch_one<128, 128, true, false, FIXED_M, EL_BF16, EPI_NONE>(a, L.max_items, stream);
+      if (L.b_kc) return launch_one<128, 256, 3, true, true, FIXED_M, EL_BF16, EPI_NONE>(a, stream);
+      return launch_one<128, 256, 3, true, false, FIXED_M, EL_BF16, EPI_NONE>(a, stream);
     }
-    if (!L.a_kc && !L.b_kc)
-      return launch_one<128, 128, false, false, DYNAMIC_K, EL_BF16, EPI_NONE>(a, L.max_items, stream);
+    if (!L.a_kc && !L.b_kc) return launch_one<128, 256, 3, false, false, DYNAMIC_K, EL_BF16, EPI_NONE>(a, stream);
     return hipErrorInvalidValue;
   }
   if (L.elem == EL_FP8) {
     if (!L.a_kc || !L.b_kc) return hipErrorInvalidValue;
-    if (L.kind == FIXED_M)
-      return launch_one<128, 128, true, true, FIXED_M, EL_FP8, EPI_ROW_COL>(a, L.max_items, stream);
-    return launch_one<128, 128, true, true, DYNAMIC_K, EL_FP8, EPI_GROUP>(a, L.max_items, stream);
+    if (L.kind == FIXED_M) return launch_one<128, 256, 3, true, true, FIXED_M, EL_FP8, EPI_ROW_COL>(a, stream);
+    return launch_one<128, 256, 3, true, true, DYNAMIC_K, EL_FP8, EPI_GROUP>(a, stream);
   }
   return hipErrorInvalidValue;
 }

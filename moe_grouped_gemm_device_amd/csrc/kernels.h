@@ -59,19 +59,21 @@ struct GemmArgs {
   int64_t total_rows;       // total_M: rows of the token-stacked operands
   const int32_t* sizes;     // device group sizes [E]
   int32_t* err;             // sticky error word (workspace header)
+  // stream-K scratch (workspace): arrival counters [kSkMaxGrid] and two fp32
+  // partial tiles per workgroup
+  int32_t* sk_ctr;
+  float* sk_part;
 };
 
 struct GemmLaunch {
   int kind;      // Kind
   int elem;      // Elem of A (B is the same except EL_I4)
   bool a_kc, b_kc;
-  int bm, bn;
-  int64_t max_items;  // host upper bound on work items
 };
 
-// Row tile the fixed-M kernels use for a given problem (heuristic, static).
-int pick_bm_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout);
-int pick_bn_fixed(int elem, int64_t total_M, int32_t E, int32_t Nout, int bm);
+// Output tile of the GEMM kernel for a launch (rows x columns).
+int gemm_tile_m(int kind);
+int gemm_tile_n(int kind);
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream);
 // The GEMM kernels read every operand's tile base unconditionally, so a

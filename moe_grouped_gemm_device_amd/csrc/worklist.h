@@ -12,6 +12,8 @@
 //              Optimization for Sparse M": min(total_M, groups) problems),
 //   order[i]   the dynamic-K order: groups by size descending, ties by index
 //              (same PR as above, review thread: kDynamicK sorts by k).
+// A fixed-M table needs tstart and a dynamic-K table needs order, never
+// both, so the two share one array (less LDS beside the GEMM's K stages).
 #pragma once
 
 #include "common.h"
@@ -20,14 +22,15 @@ namespace mg {
 
 constexpr int kTableThreads = 256;
 
-// LDS bytes a table for E groups needs (off, eff, tstart, order + scan scratch).
-__host__ __device__ inline int table_lds_bytes(int E) { return 4 * (4 * (E + 1)) + 2 * 8 * 8; }
+// LDS bytes a table for E groups needs (off, eff, tstart or order, and the
+// scan scratch).
+__host__ __device__ inline int table_lds_bytes(int E) { return 4 * (3 * (E + 1)) + 2 * 8 * 8; }
 
 struct GroupTable {
   int32_t* off;     // [E+1]
   int32_t* eff;     // [E]
-  int32_t* tstart;  // [E+1]
-  int32_t* order;   // [E]
+  int32_t* tstart;  // [E+1]  (fixed-M tables)
+  int32_t* order;   // [E]    (dynamic-K tables; same storage as tstart)
   int64_t* scratch; // [16]
 };
 
@@ -39,7 +42,7 @@ __device__ inline GroupTable carve_table(void* lds, int E) {
   t.off = p;
   t.eff = p + (E + 1);
   t.tstart = p + 2 * (E + 1);
-  t.order = p + 3 * (E + 1);
+  t.order = t.tstart;
   return t;
 }
 
@@ -69,7 +72,8 @@ __device__ inline int64_t block_incl_scan64(int64_t x, int64_t* s_wave) {
 // Builds the table.  Must be called by all threads of the workgroup
 // (256 or 512; groups are owned by the first 256).  Returns (in every
 // thread) an error code: 0, 1 (a negative size) or 2 (sizes sum past
-// total_M).  want_order enables the dynamic-K ordering (O(E^2/256) work).
+// total_M).  want_order builds the dynamic-K ordering (O(E^2/256) work)
+// instead of the fixed-M tile starts.
 __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E, int64_t total_M, int bm,
                                         bool want_order, GroupTable t) {
   const int tid = threadIdx.x;
@@ -109,18 +113,20 @@ __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E
   // grand total and error flags (last thread holding groups knows the sum)
   const int64_t tincl = block_incl_scan64(tiles_local, t.scratch + 8);
   int32_t tr = (int32_t)(tincl - tiles_local);
+  if (!want_order) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i < per && g0 + i < E) {
-      t.tstart[g0 + i] = tr;
-      tr += (eff_l[i] + bm - 1) / bm;
+    for (int i = 0; i < 4; ++i) {
+      if (i < per && g0 + i < E) {
+        t.tstart[g0 + i] = tr;
+        tr += (eff_l[i] + bm - 1) / bm;
+      }
     }
   }
   const int last = (E - 1) / per;   // thread owning group E-1
   int over = 0;
   if (tid == last) {
     t.off[E] = (int32_t)(incl < total_M ? incl : total_M);
-    t.tstart[E] = (int32_t)tincl;
+    if (!want_order) t.tstart[E] = (int32_t)tincl;
     over = incl > total_M;
   }
   // predicate reductions (each returns non-zero if any thread's is)
