@@ -145,6 +145,15 @@ __device__ inline void wait_vm_sync() {
 __device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ inline void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2_hw(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ inline int64_t uni64(int64_t v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
@@ -178,19 +187,17 @@ struct KcTile {
       voff[i] = row < rows_valid ? (uint32_t)(row * ld * T::ESZ + chunk_of(wave, lane, i) * 16) : kOOB;
     }
   }
-  // RANGE: keep only chunks meeting the contraction range [lo, hi) (relative
-  // to the k-step; lo and hi are workgroup-uniform).
-  template <bool RANGE>
-  __device__ inline void issue(const i32x4& r, uint32_t tile, int wave, int lane, int lo, int hi) const {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      uint32_t vo = voff[i];
-      if constexpr (RANGE) {
-        const int c = chunk_of(wave, lane, i) * T::EPC;
-        vo = ((c + T::EPC > lo) & (c < hi)) ? vo : kOOB;
-      }
-      dma16<POL>(r, tile + (wave * LPT + i) * 1024, vo);
+  // DMA i of this thread's k-step share; only chunks meeting the contraction
+  // range [lo, hi) (relative to the k-step; workgroup-uniform) are fetched.
+  // (edge: the k-step is cut by the range; otherwise every chunk is inside.)
+  __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int lane, int lo, int hi,
+                               bool edge) const {
+    uint32_t vo = voff[i];
+    if (edge) {
+      const int c = chunk_of(wave, lane, i) * T::EPC;
+      vo = ((c + T::EPC > lo) & (c < hi)) ? vo : kOOB;
     }
+    dma16<POL>(r, tile + (wave * LPT + i) * 1024, vo);
   }
 };
 
@@ -218,9 +225,8 @@ struct NtTile {
       voff[i] = ch * 8 < cols_valid ? (uint32_t)((row * ld + ch * 8) * 2) : kOOB;
     }
   }
-  __device__ inline void issue(const i32x4& r, uint32_t tile, int wave) const {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) dma16<POL>(r, tile + (wave * LPT + i) * 1024, voff[i]);
+  __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int, int, int, bool) const {
+    dma16<POL>(r, tile + (wave * LPT + i) * 1024, voff[i]);
   }
 };
 
@@ -279,54 +285,59 @@ struct Item {
   int n0, n_valid;  // first column, columns that exist
   int64_t c_lo, c_hi, c_begin;
   int nsteps;       // k-steps (>= 1; an empty dW group runs one all-zero step)
+  int mt;           // FIXED_M: row tile (work-list entry) of the item
 };
 
+// Work item w.  Work-item counts stay below 2^31 (the host bounds every
+// operand below 2 GiB), so the index arithmetic is 32-bit.  A fixed-M item
+// in the same row tile as `prev` reuses its group lookup.
 template <int BM, int BN, int KIND, int ELEM, int BK>
-__device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_t w, int n_tiles, int m_tiles_dk) {
+__device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_t w64, int n_tiles, int m_tiles_dk,
+                                const Item* prev) {
   Item it;
+  const uint32_t w = (uint32_t)w64;
   int nt;
   if (KIND == FIXED_M) {
-    const int64_t mt = w / n_tiles;
-    nt = (int)(w - mt * n_tiles);
-    const int4 e = fixed_m_entry(tab, a.E, BM, (int32_t)mt);
-    it.g = e.x;
-    it.rowbase = e.y;
-    it.m_valid = e.z;
-    it.c_lo = 0;
-    it.c_hi = a.Kc;
-    it.c_begin = 0;
+    const uint32_t mt = w / (uint32_t)n_tiles;
+    nt = (int)(w - mt * (uint32_t)n_tiles);
+    if (prev != nullptr && prev->mt == (int)mt) {
+      it = *prev;
+    } else {
+      const int4 e = fixed_m_entry(tab, a.E, BM, (int32_t)mt);
+      it.g = uni(e.x);
+      it.rowbase = uni(e.y);
+      it.m_valid = uni(e.z);
+      it.c_lo = 0;
+      it.c_hi = a.Kc;
+      it.c_begin = 0;
+      it.nsteps = (int)cdiv(a.Kc, BK);
+      it.mt = (int)mt;
+    }
   } else {
-    const int64_t per = (int64_t)m_tiles_dk * n_tiles;
-    const int64_t gi = w / per;
-    const int64_t rem = w - gi * per;
-    const int mt = (int)(rem / n_tiles);
-    nt = (int)(rem - (int64_t)mt * n_tiles);
-    it.g = tab.order[gi];
+    const uint32_t per = (uint32_t)m_tiles_dk * (uint32_t)n_tiles;
+    const uint32_t gi = w / per;
+    const uint32_t rem = w - gi * per;
+    const uint32_t mt = rem / (uint32_t)n_tiles;
+    nt = (int)(rem - mt * (uint32_t)n_tiles);
+    // every field is the same in all lanes (it comes from LDS reads of the
+    // group table, which the compiler cannot see are uniform); say so, so the
+    // buffer resources built from them live in SGPRs
+    it.g = uni(tab.order[gi]);
     it.rowbase = (int64_t)mt * BM;
     it.m_valid = a.Mout - (int)it.rowbase;
-    it.c_lo = tab.off[it.g];
-    it.c_hi = it.c_lo + tab.eff[it.g];
+    const int32_t off = uni(tab.off[it.g]), eff = uni(tab.eff[it.g]);
+    it.c_lo = off;
+    it.c_hi = (int64_t)off + eff;
     // fp8 operands are column-major codes read 16 rows at a time from a
     // 16-aligned row; bf16 operands are read one row at a time
     const int64_t start = (ELEM == EL_FP8) ? (it.c_lo & ~(int64_t)15) : it.c_lo;
-    it.c_begin = tab.eff[it.g] > 0 ? start : it.c_hi;
+    it.c_begin = eff > 0 ? start : it.c_hi;
+    const int64_t span = it.c_hi - it.c_begin;
+    it.nsteps = span > 0 ? (int)cdiv(span, BK) : 1;
+    it.mt = (int)mt;
   }
   it.n0 = nt * BN;
   it.n_valid = a.Nout - it.n0;
-  const int64_t span = it.c_hi - it.c_begin;
-  it.nsteps = span > 0 ? (int)cdiv(span, BK) : 1;
-  // every field is the same in all lanes (it comes from LDS reads of the
-  // group table, which the compiler cannot see are uniform); say so, so the
-  // buffer resources built from them live in SGPRs
-  it.g = uni(it.g);
-  it.rowbase = uni64(it.rowbase);
-  it.m_valid = uni(it.m_valid);
-  it.n0 = uni(it.n0);
-  it.n_valid = uni(it.n_valid);
-  it.c_lo = uni64(it.c_lo);
-  it.c_hi = uni64(it.c_hi);
-  it.c_begin = uni64(it.c_begin);
-  it.nsteps = uni(it.nsteps);
   return it;
 }
 
@@ -347,19 +358,21 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   using BTile = typename TileSel<BN, ELEM, B_KC, POL_B>::type;
   static_assert(ATile::BYTES == A_BYTES && BTile::BYTES == B_BYTES, "tile bytes");
   constexpr int LPS = ATile::LPT + BTile::LPT;   // DMA instructions per thread per k-step
-  // Epilogue staging in the stage just consumed: bf16 rows of EC columns,
+  // Epilogue staging in the stage just consumed: each wave stages its own
+  // WM x WN sub-tile, ECW columns at a time, in a private region (bf16 rows
+  // of ECW + 8 elements), so the waves need no barrier among themselves;
   // then (fp8) the reciprocal row and column scales of the tile.
   constexpr int SC_BYTES = (EPI == EPI_NONE) ? 0 : (BM + BN) * 4;
-  constexpr int EC = (BM * (BN + 8) * 2 + SC_BYTES <= STAGE)       ? BN
-                     : (BM * (BN / 2 + 8) * 2 + SC_BYTES <= STAGE) ? BN / 2
-                     : (BM * (BN / 4 + 8) * 2 + SC_BYTES <= STAGE) ? BN / 4
-                                                                   : BN / 8;
-  constexpr int SROW = EC + 8;
-  constexpr int PASSES = BN / EC;
-  constexpr int SPP = BM * EC / 8 / kThreads;    // 16-byte stores per thread per pass
+  constexpr int ECW = (4 * WM * (WN + 8) * 2 + SC_BYTES <= STAGE)     ? WN
+                      : (4 * WM * (WN / 2 + 8) * 2 + SC_BYTES <= STAGE) ? WN / 2
+                                                                        : WN / 4;
+  constexpr int SROW = ECW + 8;
+  constexpr int WREG = WM * SROW * 2;            // bytes of one wave's staging region
+  constexpr int PASSES = WN / ECW;
+  constexpr int SPP = WM * ECW / 8 / kWave;      // 16-byte stores per lane per pass
   constexpr int NST = PASSES * SPP;              // per epilogue
-  static_assert(EC >= 32 && BM * SROW * 2 + SC_BYTES <= STAGE, "staging does not fit");
-  static_assert(SPP >= 1 && (BM * EC / 8) % kThreads == 0, "store split");
+  static_assert(ECW >= 32 && ECW % 32 == 0 && 4 * WREG + SC_BYTES <= STAGE, "staging does not fit");
+  static_assert(SPP >= 1 && (WM * ECW / 8) % kWave == 0, "store split");
   static_assert((NS - 2) * LPS + NST <= 63, "vmcnt range");
   static_assert(NS >= 2, "at least double buffering");
   static_assert(KIND == DYNAMIC_K || (int64_t)BM * BN * 4 <= kSkPartBytes, "partial tile size");
@@ -402,7 +415,9 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
 
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(a.B);
-  auto fetch = [&](int64_t w) { return get_item<BM, BN, KIND, ELEM, BK>(a, tab, w, n_tiles, m_tiles_dk); };
+  auto fetch = [&](int64_t w, const Item* prev) {
+    return get_item<BM, BN, KIND, ELEM, BK>(a, tab, w, n_tiles, m_tiles_dk, prev);
+  };
   // k-steps of item w this workgroup runs end at (exclusive)
   auto item_end = [&](int64_t w, const Item& it) -> int {
     if constexpr (KIND == FIXED_M) {
@@ -418,7 +433,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   // load cursor (NS - 1 positions ahead of the compute cursor)
   int64_t lw = (KIND == FIXED_M) ? p0 / S : b;
   int ls = (KIND == FIXED_M) ? (int)(p0 - lw * S) : 0;
-  Item li = fetch(lw);
+  Item li = fetch(lw, nullptr);
   int lend = item_end(lw, li);
   bool ldone = false;
   ATile at;
@@ -433,37 +448,49 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   int cs = ls, cend = lend;
   Item ci = li;
 
-  // DMA of the load cursor's k-step into an LDS stage.  Past the end of the
-  // workgroup's positions the loads still issue (all out of range: no
-  // traffic) so every k-step has the same number of vector-memory
-  // instructions, which the waits count on.
-  auto issue_loads = [&](uint8_t* st) {
+  // DMA of the load cursor's k-step into an LDS stage: prepare_loads builds
+  // the descriptors, issue_one(q) sends the thread's q-th 16-byte transfer
+  // (q < LA: operand A, then B).  The transfers are spread over the MFMA
+  // sub-steps of the k-step being computed, so their issue overlaps MFMA
+  // execution.  Past the end of the workgroup's positions the loads still
+  // issue (all out of range: no traffic), so every k-step has the same
+  // number of vector-memory instructions, which the waits count on.
+  struct LoadCtx {
+    i32x4 ra, rb;
+    int lo, hi;
+    bool edge;
+    uint32_t st;
+  };
+  auto prepare_loads = [&](uint8_t* st) -> LoadCtx {
     const Item& it = li;
     const int64_t c0 = it.c_begin + (int64_t)ls * BK;
-    i32x4 ra, rb;
+    LoadCtx x;
     if constexpr (A_KC) {
       int64_t ext = 0x7FFFFFFF;
       if (KIND == DYNAMIC_K) ext = it.c_hi <= it.c_lo ? 0 : (int64_t)(it.m_valid - 1) * a.a_ld + (a.total_rows - c0);
-      ra = make_rsrc_words(Ab + (it.rowbase * a.a_ld + c0) * T::ESZ, ldone ? 0 : ext);
+      x.ra = make_rsrc_words(Ab + (it.rowbase * a.a_ld + c0) * T::ESZ, ldone ? 0 : ext);
     } else {
-      ra = make_rsrc_words(Ab + (c0 * a.a_ld + it.rowbase) * 2, ldone ? 0 : (it.c_hi - c0) * a.a_ld * 2);
+      x.ra = make_rsrc_words(Ab + (c0 * a.a_ld + it.rowbase) * 2, ldone ? 0 : (it.c_hi - c0) * a.a_ld * 2);
     }
     if constexpr (B_KC) {
       int64_t ext = 0x7FFFFFFF;
       if (KIND == DYNAMIC_K) ext = it.c_hi <= it.c_lo ? 0 : (int64_t)(it.n_valid - 1) * a.b_ld + (a.total_rows - c0);
-      rb = make_rsrc_words(Bb + ((int64_t)it.g * a.b_gs + (int64_t)it.n0 * a.b_ld + c0) * T::ESZ, ldone ? 0 : ext);
+      x.rb = make_rsrc_words(Bb + ((int64_t)it.g * a.b_gs + (int64_t)it.n0 * a.b_ld + c0) * T::ESZ, ldone ? 0 : ext);
     } else {
-      rb = make_rsrc_words(Bb + ((int64_t)it.g * a.b_gs + c0 * a.b_ld + it.n0) * 2, ldone ? 0 : (it.c_hi - c0) * a.b_ld * 2);
+      x.rb = make_rsrc_words(Bb + ((int64_t)it.g * a.b_gs + c0 * a.b_ld + it.n0) * 2, ldone ? 0 : (it.c_hi - c0) * a.b_ld * 2);
     }
     // contraction range relative to this k-step, clamped to int
     const int64_t lo64 = it.c_lo - c0, hi64 = it.c_hi - c0;
-    const int lo = lo64 < -BK ? -BK : (lo64 > 2 * BK ? 2 * BK : (int)lo64);
-    const int hi = hi64 < -BK ? -BK : (hi64 > 2 * BK ? 2 * BK : (int)hi64);
-    const uint32_t sa = lds_address(st);
-    if constexpr (A_KC) at.template issue<true>(ra, sa, wave, lane, lo, hi);
-    else at.issue(ra, sa, wave);
-    if constexpr (B_KC) bt.template issue<true>(rb, sa + A_BYTES, wave, lane, lo, hi);
-    else bt.issue(rb, sa + A_BYTES, wave);
+    x.lo = lo64 < -BK ? -BK : (lo64 > 2 * BK ? 2 * BK : (int)lo64);
+    x.hi = hi64 < -BK ? -BK : (hi64 > 2 * BK ? 2 * BK : (int)hi64);
+    x.edge = x.lo > 0 || x.hi < BK;
+    x.st = lds_address(st);
+    return x;
+  };
+  constexpr int LA = ATile::LPT;
+  auto issue_one = [&](const LoadCtx& x, int q) {
+    if (q < LA) at.issue(q, x.ra, x.st, wave, lane, x.lo, x.hi, x.edge);
+    else bt.issue(q - LA, x.rb, x.st + A_BYTES, wave, lane, x.lo, x.hi, x.edge);
   };
   auto advance_load = [&]() {
     if (ldone) return;
@@ -478,7 +505,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     }
     lw = nw;
     ls = 0;
-    li = fetch(nw);
+    li = fetch(nw, &li);
     lend = item_end(nw, li);
     setup(li);
   };
@@ -496,7 +523,9 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   // acc[i][j] holds the transposed 32 x 32 block: lane l has output row
   // wm * WM + 32 i + l % 32 and columns wn * WN + 32 j + 8 q + 4 (l / 32) + r
   // in element 4 q + r.
-  auto compute = [&](const uint8_t* As) {
+  constexpr int QPS = LPS / T::KSUB;   // transfers issued per MFMA sub-step
+  static_assert(LPS % T::KSUB == 0, "transfers per sub-step");
+  auto compute = [&](const uint8_t* As, const LoadCtx& lx) {
     const uint8_t* Bs = As + A_BYTES;
     int mlo = 0, mhi = BK;
     if constexpr (MASK_BYTES) {
@@ -534,6 +563,8 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int q = ks * QPS; q < (ks + 1) * QPS; ++q) issue_one(lx, q);
       } else {
         i32x8 af[TI], bfr[TJ];
         const int ch = 4 * ks + 2 * (lane >> 5);
@@ -560,17 +591,20 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
           for (int j = 0; j < TJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0,
                                                                          127, 0, 127);
+#pragma unroll
+        for (int q = ks * QPS; q < (ks + 1) * QPS; ++q) issue_one(lx, q);
       }
     }
   };
 
   // Epilogue into the stage st just consumed: (fp8: scales), bf16 rounding,
-  // staging, 16-byte stores.  Issues exactly NST vector-memory stores per
-  // thread (lanes outside the tile store out of range).
+  // per-wave staging, 16-byte stores of whole 128-byte row segments.  Issues
+  // exactly NST vector-memory stores per lane (lanes outside the tile store
+  // out of range).
   auto epilogue = [&](uint8_t* st, const Item& it) {
-    uint16_t* stg = reinterpret_cast<uint16_t*>(st);
-    float* rsc = reinterpret_cast<float*>(st + BM * SROW * 2);   // [BM] 1 / row scale
-    float* csc = rsc + BM;                                        // [BN] 1 / column scale
+    uint16_t* stg = reinterpret_cast<uint16_t*>(st + wave * WREG);
+    float* rsc = reinterpret_cast<float*>(st + 4 * WREG);   // [BM] 1 / row scale
+    float* csc = rsc + BM;                                  // [BN] 1 / column scale
     lds_sync();   // every wave is done reading st
     if constexpr (EPI != EPI_NONE) {
       for (int idx = tid; idx < BM + BN; idx += kThreads) {
@@ -592,44 +626,45 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     }
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(reinterpret_cast<uint16_t*>(a.C) + (int64_t)it.g * a.c_gs + it.rowbase * a.c_ld + it.n0, 0x7FFFFFFF);
+    const int r0 = wm * WM, c0 = wn * WN;   // the wave's sub-tile
 #pragma unroll
     for (int e = 0; e < PASSES; ++e) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const int cb = wn * WN + 32 * j;   // first column of block j
-        if (cb / EC == e) {
+        if (32 * j / ECW != e) continue;
 #pragma unroll
-          for (int i = 0; i < TI; ++i) {
-            const int row = wm * WM + 32 * i + (lane & 31);
-            float rs = 1.f;
-            if constexpr (EPI != EPI_NONE) rs = rsc[row];
+        for (int i = 0; i < TI; ++i) {
+          const int rw = 32 * i + (lane & 31);
+          float rs = 1.f;
+          if constexpr (EPI != EPI_NONE) rs = rsc[r0 + rw];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int col = cb + 8 * q + 4 * (lane >> 5);
-              float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-              float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-              if constexpr (EPI != EPI_NONE) {
-                const f32x4 cs4 = *reinterpret_cast<const f32x4*>(csc + col);
-                v0 = (v0 * cs4[0]) * rs;
-                v1 = (v1 * cs4[1]) * rs;
-                v2 = (v2 * cs4[2]) * rs;
-                v3 = (v3 * cs4[3]) * rs;
-              }
-              uint2 pk;
-              pk.x = pack_bf16x2(v0, v1);
-              pk.y = pack_bf16x2(v2, v3);
-              *reinterpret_cast<uint2*>(stg + row * SROW + (col - e * EC)) = pk;
+          for (int q = 0; q < 4; ++q) {
+            const int cw = 32 * j + 8 * q + 4 * (lane >> 5);   // column in the sub-tile
+            float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+            float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+            if constexpr (EPI != EPI_NONE) {
+              const f32x4 cs4 = *reinterpret_cast<const f32x4*>(csc + c0 + cw);
+              v0 = (v0 * cs4[0]) * rs;
+              v1 = (v1 * cs4[1]) * rs;
+              v2 = (v2 * cs4[2]) * rs;
+              v3 = (v3 * cs4[3]) * rs;
             }
+            uint2 pk;
+            pk.x = pack_bf16x2_hw(v0, v1);
+            pk.y = pack_bf16x2_hw(v2, v3);
+            *reinterpret_cast<uint2*>(stg + rw * SROW + (cw - e * ECW)) = pk;
           }
         }
       }
-      lds_sync();
+      // the wave reads back what its own lanes wrote: LDS executes a wave's
+      // accesses in order, so a wait for the writes is all it takes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int k = 0; k < SPP; ++k) {
-        const int q = tid + k * kThreads;
-        const int row = q / (EC / 8), ch = q % (EC / 8);
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + row * SROW + ch * 8);
-        const int col = e * EC + ch * 8;
+        const int q = lane + k * kWave;
+        const int rw = q / (ECW / 8), ch = q % (ECW / 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + rw * SROW + ch * 8);
+        const int row = r0 + rw, col = c0 + e * ECW + ch * 8;
         const uint32_t vo = (row < it.m_valid && col < it.n_valid) ? (uint32_t)((row * a.c_ld + col) * 2) : kOOB;
         i32x4 d;
         d[0] = (int)v.x;
@@ -638,7 +673,8 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
         d[3] = (int)v.w;
         __builtin_amdgcn_raw_buffer_store_b128(d, cr, (int)vo, 0, kPolicyStream);
       }
-      if (e + 1 < PASSES) lds_sync();
+      // the next pass overwrites the region only after these reads returned
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   };
 
@@ -660,31 +696,75 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
                           (int64_t)(2 * bb + (first == w ? 0 : 1)) * PART_BYTES + wave * WAVE_BYTES;
     return make_rsrc(base, WAVE_BYTES);
   };
-  auto sk_combine = [&](const Item& it, int64_t w) -> bool {
-    const int bf = wg_of(w * S), bl = wg_of(w * S + S - 1);
-    if (bf == bl) return true;
-    {
-      const __amdgpu_buffer_rsrc_t mine = part_rsrc(b, w);
+  auto part_io = [&](bool store, const __amdgpu_buffer_rsrc_t& r, const Item& it, bool add) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const bool ok = wm * WM + 32 * i + (lane & 31) < it.m_valid;
+    for (int i = 0; i < TI; ++i) {
+      const bool ok = wm * WM + 32 * i + (lane & 31) < it.m_valid;
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t vo = ok ? (uint32_t)((((i * TJ + j) * 4 + q) * 64 + lane) * 16) : kOOB;
+          if (store) {
             i32x4 v;
             v[0] = __float_as_int(acc[i][j][4 * q]);
             v[1] = __float_as_int(acc[i][j][4 * q + 1]);
             v[2] = __float_as_int(acc[i][j][4 * q + 2]);
             v[3] = __float_as_int(acc[i][j][4 * q + 3]);
-            const uint32_t vo = ok ? (uint32_t)((((i * TJ + j) * 4 + q) * 64 + lane) * 16) : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b128(v, mine, (int)vo, 0, kPolicyDevice);
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)vo, 0, kPolicyDevice);
+          } else {
+            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, 0, kPolicyDevice);
+            if (add) {
+              acc[i][j][4 * q] += __int_as_float(v[0]);
+              acc[i][j][4 * q + 1] += __int_as_float(v[1]);
+              acc[i][j][4 * q + 2] += __int_as_float(v[2]);
+              acc[i][j][4 * q + 3] += __int_as_float(v[3]);
+            } else {
+              acc[i][j][4 * q] = __int_as_float(v[0]);
+              acc[i][j][4 * q + 1] = __int_as_float(v[1]);
+              acc[i][j][4 * q + 2] = __int_as_float(v[2]);
+              acc[i][j][4 * q + 3] = __int_as_float(v[3]);
+            }
           }
-      }
+        }
     }
-    wait_vm_all();   // this wave's partial has reached the coherence point
-    lds_sync();
+  };
+  auto sk_combine = [&](const Item& it, int64_t w) -> bool {
+    const int bf = wg_of(w * S), bl = wg_of(w * S + S - 1);
+    if (bf == bl) return true;
     int32_t* flag = reinterpret_cast<int32_t*>(tab.scratch);
+    if (bl - bf == 1) {
+      // Two pieces (the usual split): the tile is own + other, and fp32
+      // addition is commutative, so whichever piece finishes second adds the
+      // other's partial to its registers -- the same bits either way.  A
+      // piece that finds the other already published skips storing its own.
+      const int other = b == bf ? bl : bf;
+      if (tid == 0) *flag = __hip_atomic_load(a.sk_ctr + bf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_sync();
+      if (uni(*flag) == 1) {
+        if (tid == 0) __hip_atomic_store(a.sk_ctr + bf, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        part_io(false, part_rsrc(other, w), it, true);
+        return true;
+      }
+      lds_sync();   // the peek is read by every wave before the flag is reused
+      part_io(true, part_rsrc(b, w), it, false);
+      wait_vm_all();   // this wave's partial has reached the coherence point
+      lds_sync();
+      if (tid == 0) {
+        const int last = __hip_atomic_fetch_add(a.sk_ctr + bf, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1;
+        if (last) __hip_atomic_store(a.sk_ctr + bf, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+      }
+      lds_sync();
+      if (!uni(*flag)) return false;
+      part_io(false, part_rsrc(other, w), it, true);
+      return true;
+    }
+    // Three or more pieces: every piece stores its partial; the last to
+    // arrive adds them all in workgroup order.
+    part_io(true, part_rsrc(b, w), it, false);
+    wait_vm_all();
+    lds_sync();
     if (tid == 0) {
       const int old = __hip_atomic_fetch_add(a.sk_ctr + bf, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = old == bl - bf;
@@ -692,27 +772,8 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       *flag = last;
     }
     lds_sync();
-    const int last = uni(*flag);
-    if (!last) return false;
-    zero_acc();
-    for (int bb = bf; bb <= bl; ++bb) {
-      const __amdgpu_buffer_rsrc_t src = part_rsrc(bb, w);
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const bool ok = wm * WM + 32 * i + (lane & 31) < it.m_valid;
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t vo = ok ? (uint32_t)((((i * TJ + j) * 4 + q) * 64 + lane) * 16) : kOOB;
-            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, (int)vo, 0, kPolicyDevice);
-            acc[i][j][4 * q] += __int_as_float(v[0]);
-            acc[i][j][4 * q + 1] += __int_as_float(v[1]);
-            acc[i][j][4 * q + 2] += __int_as_float(v[2]);
-            acc[i][j][4 * q + 3] += __int_as_float(v[3]);
-          }
-      }
-    }
+    if (!uni(*flag)) return false;
+    for (int bb = bf; bb <= bl; ++bb) part_io(false, part_rsrc(bb, w), it, bb != bf);
     return true;
   };
 
@@ -720,7 +781,9 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   // NS - 1 k-steps are loaded ahead; stages are used round-robin.
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u) {
-    issue_loads(smem + u * STAGE);
+    const LoadCtx lx = prepare_loads(smem + u * STAGE);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) issue_one(lx, q);
     advance_load();
   }
   int stage = 0;            // stage holding the compute cursor's k-step
@@ -736,10 +799,10 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
       else wait_vm_sync<(NS - 2) * LPS>();
       epi_prev = false;
-      issue_loads(smem + lstage * STAGE);
-      advance_load();
+      const LoadCtx lx = prepare_loads(smem + lstage * STAGE);
       lstage = lstage + 1 == NS ? 0 : lstage + 1;
-      compute(smem + stage * STAGE);
+      compute(smem + stage * STAGE, lx);   // also issues the loads of lx
+      advance_load();                      // only now: setup() replaces the tiles' offsets
       last_stage = stage;
       stage = stage + 1 == NS ? 0 : stage + 1;
     }
@@ -754,7 +817,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     if (!has_item(nw)) break;
     cw = nw;
     cs = 0;
-    ci = fetch(nw);
+    ci = fetch(nw, &ci);
     cend = item_end(nw, ci);
   }
   wait_vm_all();   // no LDS-DMA transfer may outlive the workgroup
