@@ -51,6 +51,62 @@ def algorithmic_bytes(E, M, K, N):
     return {"fwd": w + M * K * 2 + M * N * 2, "dx": w + M * N * 2 + M * K * 2, "dw": w + M * K * 2 + M * N * 2}
 
 
+KERNEL_SOURCES = ["moe_grouped_gemm_device_amd/csrc/gmm.hip", "moe_grouped_gemm_device_amd/csrc/worklist.h",
+                  "moe_grouped_gemm_device_amd/csrc/common.h", "moe_grouped_gemm_device_amd/csrc/kernels.h"]
+TRAFFIC_PROFILE = "profiles/gmm_bf16_balanced_traffic.md"
+
+
+def kernel_source_digest():
+    """SHA-256 over the sources the GEMM kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(which):
+    """HBM bytes per launch of `which` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain copy
+    of known size gives), or None when that summary was taken on other kernel
+    sources than the ones in the tree."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip().strip("`")
+        if "=" in line and line.split("=")[0].strip().replace("_", "").replace(".", "").isalnum():
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    key = f"traffic_bytes.{which}"
+    return int(vals[key]) if key in vals else None
+
+
+def traffic_probe(torch, mg):
+    """Runs each product of the step a few times and a plain copy of known
+    size, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes (no timing)."""
+    E, M, K, N = 8, 1024, 4096, 6400
+    d = balanced_inputs(torch, mg, E, M, K, N)
+    x, w, dy, sizes = d["x"], d["w"], d["dy"], d["sizes"]
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty_like(w)
+    ws = mg.workspace(E, M)
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")   # copy calibration: 256 MiB each way
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        mg.gmm_fwd(x, w, sizes, out=y, ws=ws)
+        mg.gmm_bwd(dy, x, w, sizes, need_dw=False, dx=dx, ws=ws)
+        mg.gmm_bwd(dy, x, w, sizes, need_dx=False, dw=dw, ws=ws)
+    torch.cuda.synchronize()
+    log("traffic probe done; kernel source sha256 " + kernel_source_digest())
+
+
 def run_gpu(args, torch, mg):
     E, M, K, N = 8, 1024, 4096, 6400
     log("generating inputs")
@@ -61,46 +117,51 @@ def run_gpu(args, torch, mg):
     dw = torch.empty_like(w)
     ws = mg.workspace(E, M)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        mg.gmm_fwd(x, w, sizes, out=y, ws=ws)
-        if ev is not None:
-            ev[1].record()
-        mg.gmm_bwd(dy, x, w, sizes, need_dw=False, dx=dx, ws=ws)
-        if ev is not None:
-            ev[2].record()
-        mg.gmm_bwd(dy, x, w, sizes, need_dx=False, dw=dw, ws=ws)
-        if ev is not None:
-            ev[3].record()
+    products = {
+        "fwd": lambda: mg.gmm_fwd(x, w, sizes, out=y, ws=ws),
+        "dx": lambda: mg.gmm_bwd(dy, x, w, sizes, need_dw=False, dx=dx, ws=ws),
+        "dw": lambda: mg.gmm_bwd(dy, x, w, sizes, need_dx=False, dw=dw, ws=ws),
+    }
+
+    def step():
+        for fn in products.values():
+            fn()
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The timed steps carry no per-launch events: an event marker between two
+    # kernels costs several microseconds of idle GPU on ROCm.
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per = {"fwd": [], "dx": [], "dw": []}
-    for ev in events:
-        per["fwd"].append(ev[0].elapsed_time(ev[1]))
-        per["dx"].append(ev[1].elapsed_time(ev[2]))
-        per["dw"].append(ev[2].elapsed_time(ev[3]))
-    avg_ms = {k: sum(v) / len(v) for k, v in per.items()}
+    # Per-kernel durations: HIP events around R back-to-back launches of each
+    # product (the same launches as in a step), so that only the dispatch gap
+    # between identical kernels is counted besides the kernels themselves.
+    R = max(args.steps, 5)
+    avg_ms = {}
+    for name, fn in products.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(R):
+            fn()
+        e1.record()
+        e1.synchronize()
+        avg_ms[name] = e0.elapsed_time(e1) / R
     flops_step = 3 * 2.0 * M * K * N
     ms_step = elapsed * 1e3 / args.steps
     tflops = flops_step / (ms_step * 1e-3) / 1e12
     bytes_per = algorithmic_bytes(E, M, K, N)
     dom = max(avg_ms, key=avg_ms.get)
     achieved = bytes_per[dom] / (avg_ms[dom] * 1e-3) / 1e9
-    kernel_names = {"fwd": "gmm_kernel<128,128,A k-contig,B n-contig,FIXED_M,bf16> (forward)",
-                    "dx": "gmm_kernel<128,128,A k-contig,B k-contig,FIXED_M,bf16> (dX)",
-                    "dw": "gmm_kernel<128,128,A m-contig,B n-contig,DYNAMIC_K,bf16> (dW)"}
+    kernel_names = {"fwd": "gmm_kernel<128,256,3,true,false,FIXED_M,bf16> (forward: X rows k-contiguous, W [K,N])",
+                    "dx": "gmm_kernel<128,256,3,true,true,FIXED_M,bf16> (dX: dY rows, W rows contraction-contiguous)",
+                    "dw": "gmm_kernel<128,256,3,false,false,DYNAMIC_K,bf16> (dW: X and dY row-contiguous)"}
     roofline = {
         "bound": "hbm",
         "kernel": kernel_names[dom],
@@ -108,7 +169,7 @@ def run_gpu(args, torch, mg):
         "peak": PEAK_HBM_GBS,
         "unit": "GB/s",
         "frac": round(achieved / PEAK_HBM_GBS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(dom),
         "algorithmic_bytes_per_launch": bytes_per[dom],
         "avg_launch_us": {k: round(v * 1e3, 2) for k, v in avg_ms.items()},
         "mfma_frac": {k: round(2.0 * M * K * N / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) for k, v in avg_ms.items()},
@@ -175,7 +236,8 @@ def sparse_m_latency(torch, mg, reps=50):
 
 def cpu_baseline(host):
     """The fp64 oracle (unchanged, OpenMP over output rows) running the same
-    step at full size: forward, dX and dW of the balanced workload."""
+    step at full size -- forward, dX and dW of the balanced workload --
+    repeated until about 10 s of CPU work (at most 3 steps)."""
     import oracle
     threads = min(os.cpu_count() or 1, 16)
     used = oracle.set_threads(threads)
@@ -183,14 +245,17 @@ def cpu_baseline(host):
     M, K = X.shape
     N = dY.shape[1]
     t0 = time.perf_counter()
-    oracle.gmm_fwd_bf16(X, W, s)
-    oracle.gmm_dx_bf16(dY, W, s)
-    oracle.gmm_dw_bf16(X, dY, s)
+    n = 0
+    while n < 3 and (n == 0 or time.perf_counter() - t0 < 10.0):
+        oracle.gmm_fwd_bf16(X, W, s)
+        oracle.gmm_dx_bf16(dY, W, s)
+        oracle.gmm_dw_bf16(X, dY, s)
+        n += 1
     dt = time.perf_counter() - t0
-    flops = 3 * 2.0 * M * K * N
+    flops = n * 3 * 2.0 * M * K * N
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": used, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"the whole step (fwd + dX + dW, M={M}, K={K}, N={N}, E={len(s)}) in fp64, "
+            "sample": f"{n} x the whole step (fwd + dX + dW, M={M}, K={K}, N={N}, E={len(s)}) in fp64, "
                       "including the bf16 -> fp64 decode of the operands"}
 
 
@@ -201,6 +266,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse-M latency measurement")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run each product and a known-size copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -214,6 +281,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.traffic_probe:
+        traffic_probe(torch, mg)
+        return
     r = run_gpu(args, torch, mg)
     out = {
         "metric": METRIC,
