@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "grouped-GEMM TFLOP/s & % MFMA peak; µs latency at total_M=1, 128 groups"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 def log(msg):
@@ -230,8 +231,147 @@ def sparse_m_latency(torch, mg, reps=50):
                     "ratio": round(t128 / t1, 3)}
     bytes_expert = N * K // 2 + (K // 128) * N * 2
     res["cold"]["hbm_frac"] = round(bytes_expert / (res["cold"]["us_total_M1_E128"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    # total_M = 16 and 128 routed rows on uniformly random experts (warm):
+    # weight bytes of the experts that have rows against HBM peak
+    gen = torch.Generator()
+    gen.manual_seed(1)
+    for tm in (16, 128):
+        picks = torch.randint(0, E, (tm,), generator=gen)
+        sz = torch.bincount(picks, minlength=E).to(torch.int32).cuda()
+        xm = torch.randn(tm, K, generator=g, device="cuda").to(torch.bfloat16)
+        xqm, sxm = mg.quantize_rowwise_fp8(xm)
+        ym = torch.empty(tm, N, dtype=torch.bfloat16, device="cuda")
+        wsm = mg.workspace(E, tm)
+        t = timed(lambda: mg.gmm_fwd_f8i4(xqm, sxm, w4, sw, sz, out=ym, ws=wsm), False)
+        touched = int((sz > 0).sum().item())
+        res[f"warm_total_M{tm}"] = {"us": round(t, 2), "experts_with_rows": touched,
+                                    "hbm_frac": round(touched * bytes_expert / (t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     res["workload"] = "F8I4: E=128, total_M=1 (one routed row), K=5120, N=8192; int4 per-128-K bf16 scales"
     return res
+
+
+def _timeit(torch, fn, reps=10):
+    """Average microseconds of fn over reps back-to-back launches (HIP events)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def _row(what, us, amount, unit, peak):
+    """One measured row: achieved = amount / time against the peak in unit."""
+    scale = 1e3 if unit == "GB/s" else 1e6   # bytes/us -> GB/s, flops/us -> TFLOP/s
+    achieved = amount / us / scale
+    return {"what": what, "us": round(us, 2), "achieved": round(achieved, 1), "unit": unit, "peak": peak,
+            "frac": round(achieved / peak, 4)}
+
+
+def row_measurements(torch, mg):
+    """Each hot-path step of the fp8 training layer (DeepSeek-MoE-16B share:
+    16384 tokens, 64 experts, top-6 with Zipf(1.1) loads, hidden 2048,
+    expert intermediate 1408) and of the token-sorted Mixtral-8x7B expert FFN
+    (T=4096, top-2 of 8, hidden 4096, intermediate 14336), timed on its own
+    against its roofline.  Inputs: seeded synthetic bf16 N(0,1) activations
+    and N(0,0.02) weights."""
+    import numpy as np
+    import workloads as wl
+    rows = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    # ---- fp8 layer share (configuration: DeepSeek-MoE-16B-shaped) ----------
+    T, E, k, H, I = 16384, 64, 6, 2048, 1408
+    ids = wl.zipf_topk_routing(T, E, k, 1.1, seed=0)
+    sizes_np = np.bincount(ids.ravel(), minlength=E).astype(np.int32)
+    M = T * k
+    sizes = torch.from_numpy(sizes_np).cuda()
+    X = torch.randn(M, H, generator=g, device="cuda").to(torch.bfloat16)
+    dY = torch.randn(M, I, generator=g, device="cuda").to(torch.bfloat16)
+    W = (torch.randn(E, H, I, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    ws = mg.workspace(E, M)
+    xq = torch.empty(M, H, dtype=torch.uint8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    us = _timeit(torch, lambda: mg.quantize_rowwise_fp8(X, q=xq, scales=sx))
+    rows["A5_quantize_rowwise_fp8"] = _row(f"X [{M},{H}] bf16 -> e4m3 + row scales", us,
+                                           M * H * 3 + M * 4, "GB/s", PEAK_HBM_GBS)
+    cq = (torch.zeros(I, M, dtype=torch.uint8, device="cuda"), torch.empty(E, I, dtype=torch.float32, device="cuda"),
+          torch.zeros(H, M, dtype=torch.uint8, device="cuda"), torch.empty(E, H, dtype=torch.float32, device="cuda"))
+    us = _timeit(torch, lambda: mg.quantize_colwise_per_group_fp8(dY, sizes, b=X, out=cq))
+    rows["A6_quantize_colwise_dual"] = _row(f"dY [{M},{I}] and X [{M},{H}], {E} Zipf groups -> column-major e4m3",
+                                            us, M * (I + H) * 3 + E * (I + H) * 4, "GB/s", PEAK_HBM_GBS)
+    dyc, sdyc, xc, sxc = cq
+    wq_c, sw_c = mg.quantize_colwise_per_group_fp8(W.reshape(E * H, I),
+                                                   torch.full((E,), H, dtype=torch.int32, device="cuda"))
+    y = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
+    us = _timeit(torch, lambda: mg.gmm_fwd_fp8(xq, sx, wq_c, sw_c, E * H, H, sizes, I, out=y, ws=ws))
+    rows["A7_fp8_gmm_fwd"] = _row(f"Y [{M},{I}] = Xq . Wq_g, K={H}", us, 2.0 * M * H * I, "TFLOP/s", PEAK_FP8_TFLOPS)
+    dyq = torch.empty(M, I, dtype=torch.uint8, device="cuda")
+    sdy = torch.empty(M, dtype=torch.float32, device="cuda")
+    mg.quantize_rowwise_fp8(dY, q=dyq, scales=sdy)
+    wq_r, sw_r = mg.quantize_rowwise_fp8(W.reshape(E * H, I))
+    dxo = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    us = _timeit(torch, lambda: mg.gmm_bwd_fp8(sizes, H, I, dyq=dyq, sdy=sdy, wq=wq_r, sw=sw_r, w_ld=I,
+                                               w_expert_stride=H * I, need_dw=False, dx=dxo, ws=ws))
+    rows["A7_fp8_gmm_dx"] = _row(f"dX [{M},{H}] = dYq . Wq_g^T, contraction {I}", us, 2.0 * M * H * I,
+                                 "TFLOP/s", PEAK_FP8_TFLOPS)
+    dwo = torch.empty(E, H, I, dtype=torch.bfloat16, device="cuda")
+    us = _timeit(torch, lambda: mg.gmm_bwd_fp8(sizes, H, I, xc=xc, sxc=sxc, dyc=dyc, sdyc=sdyc, need_dx=False,
+                                               dw=dwo, ws=ws))
+    rows["A7_fp8_gmm_dw"] = _row(f"dW [{E},{H},{I}] = Xq_g^T . dYq_g (dynamic K)", us, 2.0 * M * H * I,
+                                 "TFLOP/s", PEAK_FP8_TFLOPS)
+    us = _timeit(torch, lambda: mg.build_worklist(mg.MG_WL_FIXED_M, sizes, M, 128))
+    rows["A1_builder"] = {"what": f"work list for {E} groups, total_M={M}, 128-row tiles (own launch)",
+                          "us": round(us, 2)}
+    del X, dY, W, xq, dyq, cq, wq_c, wq_r, y, dxo, dwo, ws
+    torch.cuda.empty_cache()
+    # ---- token-sorted fused FFN (configuration: Mixtral-8x7B-shaped) -------
+    T, E, k, H, I = 4096, 8, 2, 4096, 14336
+    ids_np, wts_np = wl.softmax_topk_routing(T, E, k, seed=0)
+    ids = torch.from_numpy(ids_np).cuda()
+    wts = torch.from_numpy(wts_np).cuda()
+    x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+    w1 = (torch.randn(E, H, 2 * I, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(E, I, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    bm = 128
+    p = mg.moe_permute(ids, E, bm, x=x)
+    us = _timeit(torch, lambda: mg.moe_permute(ids, E, bm, x=x))
+    ntpp = int(p["num_tokens_post_padded"].item())
+    rows["A9_moe_permute"] = _row(f"align + gather of {T}x{k} routed rows, hidden {H}, block_m {bm}", us,
+                                  T * H * 2 + ntpp * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS)
+    xs, psz = p["x_sorted"], p["padded_sizes"]
+    wsf = mg.workspace(E, xs.shape[0])
+    h1 = torch.empty(xs.shape[0], 2 * I, dtype=torch.bfloat16, device="cuda")
+    us = _timeit(torch, lambda: mg.gmm_fwd(xs, w1, psz, out=h1, ws=wsf), reps=5)
+    rows["A10_gemm1"] = _row(f"H1 = X_sorted . W1_e, {ntpp} padded rows, K={H}, N={2 * I} (useful flops of {T * k} rows)",
+                             us, 2.0 * T * k * H * 2 * I, "TFLOP/s", PEAK_BF16_TFLOPS)
+    act = torch.empty(xs.shape[0], I, dtype=torch.bfloat16, device="cuda")
+    us = _timeit(torch, lambda: mg.silu_mul(h1, out=act))
+    rows["A11_silu_mul"] = _row(f"silu(H1[:, :I]) * H1[:, I:], {xs.shape[0]} rows, I={I}", us,
+                                xs.shape[0] * I * 6, "GB/s", PEAK_HBM_GBS)
+    y2 = torch.empty(xs.shape[0], H, dtype=torch.bfloat16, device="cuda")
+    us = _timeit(torch, lambda: mg.gmm_fwd(act, w2, psz, out=y2, ws=wsf), reps=5)
+    rows["A12_gemm2"] = _row(f"Y2 = act . W2_e, K={I}, N={H} (useful flops of {T * k} rows)", us,
+                             2.0 * T * k * I * H, "TFLOP/s", PEAK_BF16_TFLOPS)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    us = _timeit(torch, lambda: mg.moe_unpermute(y2, p["inv"], wts, T, k, out=out))
+    rows["A13_moe_unpermute"] = _row(f"top-{k} weighted combine of {T * k} rows, hidden {H}", us,
+                                     T * k * H * 2 + T * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS)
+    us = _timeit(torch, lambda: mg.fused_moe(x, w1, w2, ids, wts, block_m=bm, ws=wsf), reps=3)
+    rows["C3_fused_ffn_T4096"] = _row("permute -> GEMM1 -> SiLU*mul -> GEMM2 -> combine, end to end", us,
+                                      2.0 * T * k * H * 3 * I, "TFLOP/s", PEAK_BF16_TFLOPS)
+    for Tsmall in (1, 64):
+        sub_ids, sub_w = ids[:Tsmall].contiguous(), wts[:Tsmall].contiguous()
+        xsub = x[:Tsmall].contiguous()
+        us = _timeit(torch, lambda: mg.fused_moe(xsub, w1, w2, sub_ids, sub_w, ws=wsf), reps=5)
+        experts = int(torch.unique(sub_ids).numel())
+        rows[f"C3_fused_ffn_T{Tsmall}"] = _row(
+            f"end to end, {experts} experts touched: weight bytes of those experts", us,
+            experts * (H * 2 * I + I * H) * 2, "GB/s", PEAK_HBM_GBS)
+    return rows
 
 
 def cpu_baseline(host):
@@ -266,6 +406,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse-M latency measurement")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other configurations")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run each product and a known-size copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()
@@ -308,6 +449,9 @@ def main():
     if not args.no_sparse:
         log("sparse-M latency")
         out["sparse_m"] = sparse_m_latency(torch, mg)
+    if not args.no_rows:
+        log("per-step rows (fp8 layer share, fused FFN)")
+        out["rows"] = row_measurements(torch, mg)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(r["host"])

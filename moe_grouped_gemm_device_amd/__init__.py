@@ -261,16 +261,20 @@ def quantize_rowwise_fp8(x, q=None, scales=None, stream=None):
     return q, scales
 
 
-def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None):
+def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None):
     """Per-group colwise quantization of a (and b).  Returns
     (qa [Ca, M] column-major codes, sa [G, Ca]) or, with b,
-    (qa, sa, qb, sb)."""
+    (qa, sa, qb, sb).  Codes of rows past the groups are not written (fresh
+    outputs start zeroed); out=(qa, sa[, qb, sb]) reuses buffers."""
     _need(a, torch.bfloat16, "a", 2)
     _need(group_sizes, torch.int32, "group_sizes", 1)
     M, Ca = a.shape
     G = group_sizes.numel()
-    qa = torch.zeros(Ca, M, dtype=torch.uint8, device=a.device)
-    sa = torch.empty(G, Ca, dtype=torch.float32, device=a.device)
+    if out is not None:
+        qa, sa = out[0], out[1]
+    else:
+        qa = torch.zeros(Ca, M, dtype=torch.uint8, device=a.device)
+        sa = torch.empty(G, Ca, dtype=torch.float32, device=a.device)
     qb = sb = None
     Cb = 0
     if b is not None:
@@ -278,8 +282,11 @@ def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None):
         if b.shape[0] != M:
             raise ValueError("a and b must have the same number of rows")
         Cb = b.shape[1]
-        qb = torch.zeros(Cb, M, dtype=torch.uint8, device=a.device)
-        sb = torch.empty(G, Cb, dtype=torch.float32, device=a.device)
+        if out is not None:
+            qb, sb = out[2], out[3]
+        else:
+            qb = torch.zeros(Cb, M, dtype=torch.uint8, device=a.device)
+            sb = torch.empty(G, Cb, dtype=torch.float32, device=a.device)
     _call("quantize_colwise_per_group_fp8", _ptr(a), Ca, _ptr(b), Cb, _ptr(group_sizes), G, M, _ptr(qa),
           _ptr(sa), _ptr(qb), _ptr(sb), _stream(stream))
     return (qa, sa) if b is None else (qa, sa, qb, sb)
@@ -359,7 +366,7 @@ def silu_mul(h, out=None, stream=None):
     return out
 
 
-def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, stream=None):
+def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, ws=None, stream=None):
     """Token-sorted MoE expert FFN: permute -> gmm(W1) -> SiLU*mul -> gmm(W2)
     -> top-k weighted combine.  w1 [E, H, 2I], w2 [E, I, H] bf16."""
     T, k = topk_ids.shape
@@ -369,7 +376,7 @@ def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, stream=None):
     p = moe_permute(topk_ids, E, block_m, x=x, stream=stream)
     xs = p["x_sorted"]
     sizes = p["padded_sizes"]
-    ws = workspace(E, xs.shape[0], x.device)
+    ws = workspace(E, xs.shape[0], x.device) if ws is None else ws
     h1 = gmm_fwd(xs, w1, sizes, ws=ws, stream=stream)
     act = silu_mul(h1, stream=stream)
     y2 = gmm_fwd(act, w2, sizes, ws=ws, stream=stream)
