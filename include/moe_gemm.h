@@ -225,7 +225,10 @@ int quantize_rowwise_fp8(const void* x, int64_t rows, int32_t cols, int64_t ld,
  * written column-major: qa[c * rows + r]; scales sa[g * cols_a + c].  b,
  * qb, sb are either all NULL (single tensor) or all set (both tensors share
  * the group sizes and row count).  Rows beyond the sizes' sum are not
- * written.  cols % 8 == 0. */
+ * written.  cols % 8 == 0; 1 <= G <= MG_MAX_EXPERTS; rows < 2^31.  Enqueues
+ * four kernels (zero the scales, column amax per 256-row chunk of a group,
+ * cast, amax -> scale); sa and sb hold amax bits between them, so they must
+ * not be read before the call's work has completed on the stream. */
 int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a,
                                    const void* b, int32_t cols_b,
                                    const int32_t* group_sizes, int32_t G,

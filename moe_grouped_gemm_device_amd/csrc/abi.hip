@@ -428,8 +428,8 @@ int quantize_rowwise_fp8(const void* x, int64_t rows, int32_t cols, int64_t ld, 
 int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a, const void* b, int32_t cols_b,
                                    const int32_t* group_sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
                                    uint8_t* qb, float* sb, mg_stream_t stream) {
-  if (G < 1 || G > 65535) return fail(MG_EINVAL, "G=%d outside [1, 65535]", G);
-  if (rows < 0) return fail(MG_EINVAL, "rows < 0");
+  if (G < 1 || G > MG_MAX_EXPERTS) return fail(MG_EINVAL, "G=%d outside [1, %d]", G, MG_MAX_EXPERTS);
+  if (rows < 0 || rows >= kMaxRows) return fail(MG_EINVAL, "rows out of range");
   if (!a || !qa || !sa || !group_sizes) return fail(MG_EINVAL, "NULL tensor argument");
   const bool dual = b != nullptr;
   if (dual != (qb != nullptr) || dual != (sb != nullptr)) return fail(MG_EINVAL, "b, qb, sb must be all set or all NULL");

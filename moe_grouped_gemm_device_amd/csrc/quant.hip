@@ -14,6 +14,7 @@
 // All three kernels are HBM-bound: each element is read twice (amax pass,
 // cast pass; the second read mostly hits cache) and written once as a byte.
 #include "kernels.h"
+#include "worklist.h"
 
 namespace mg {
 
@@ -114,38 +115,142 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int32_t cols, i
 }
 
 // ---------------------------------------------------------------------------
-// K4: per-group colwise, single or dual.  Grid (column blocks of 64, groups);
-// a workgroup owns 64 columns of one group (of tensor a, then of tensor b in
-// the same launch).  Rows are walked in 64-row slabs aligned to 64; each
-// thread covers 8 columns x 2 rows of a slab.  Pass 1 reduces the column
-// amax; pass 2 scales, converts, transposes the 64x64 byte slab in LDS and
-// writes each column's 64 rows as 16-byte pieces (byte stores where a piece
-// straddles the group's first or last row, since neighbouring groups are
-// written by other workgroups).
+// K4: per-group colwise, single or dual.  The unit of work is a tile of 64
+// columns x 256 rows of one group: the device group table cuts every group's
+// rows into 256-row chunks, so a large group spreads over many workgroups
+// (with Zipf-skewed loads one group can hold a sixth of the rows).  Four
+// launches on the stream:
+//   1. zero the scale arrays, which hold column amax bits until step 4;
+//   2. per tile: column |x| max, folded in with an integer atomic max on the
+//      fp32 bits (non-negative floats order like their bit patterns);
+//   3. per tile, walked in reverse order so that the second read meets the
+//      most recently read rows still in cache: the scale from the finished
+//      amax, the cast, a transpose through LDS and column-major 16-byte
+//      stores (byte stores only where a run starts or ends inside a 16-byte
+//      piece shared with a neighbouring group);
+//   4. amax -> scale.
+// Codes of rows past the groups are not written.
 // ---------------------------------------------------------------------------
-constexpr int CW = 64;   // columns per workgroup
-constexpr int RS = 64;   // rows per slab
+constexpr int QC_COLS = 64;    // columns per tile
+constexpr int QC_ROWS = 256;   // rows per tile (chunk of a group)
 
-__device__ void colwise_one(const uint16_t* __restrict__ x, int32_t cols, int64_t rows, int64_t r0,
-                            int64_t r1, int g, int cb, uint8_t* __restrict__ q, float* __restrict__ sc,
-                            uint8_t (*tile)[RS + 16], uint32_t* s_red, float* s_scale) {
+struct ColwiseArgs {
+  const uint16_t* x[2];
+  int32_t cols[2];
+  uint8_t* q[2];
+  uint32_t* s[2];    // scale arrays [G][cols], amax bits until the last launch
+  const int32_t* sizes;
+  int32_t G;
+  int32_t ntensors;
+  int64_t rows;
+};
+
+// Chunks of a group are its intersections with the global 256-row blocks,
+// so interior chunk edges fall on 256-row boundaries (16-byte aligned in the
+// column-major output when the row count is a multiple of 16) and only a
+// group's own first and last rows can share a 16-byte piece with another
+// group.  Rewrites tab.tstart with these chunk counts (build_group_table must
+// have filled off/eff); called by all threads.
+__device__ inline void colwise_chunk_table(GroupTable& tab, int32_t G) {
   const int tid = threadIdx.x;
-  const int cchunk = tid & 7;          // which 8-column chunk
-  const int rsub = tid >> 3;           // 0..31: row within half-slab
-  const int c0 = cb * CW;
-  const int col = c0 + cchunk * 8;
-  const bool col_ok = col < cols;
-  const int64_t start = r0 & ~(int64_t)(RS - 1);
-
-  // pass 1: column amax over the group's rows
-  uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t base = start; base < r1; base += RS) {
+  const int per = (G + kTableThreads - 1) / kTableThreads;
+  const int g0 = tid * per;
+  int32_t cnt[4];
+  int64_t local = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t r = base + rsub + 32 * h;
-      if (col_ok && r >= r0 && r < r1) {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + r * cols + col);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int i = 0; i < 4; ++i) {
+    cnt[i] = 0;
+    if (i < per && g0 + i < G) {
+      const int32_t off = tab.off[g0 + i], eff = tab.eff[g0 + i];
+      if (eff > 0) cnt[i] = (int32_t)(((int64_t)off + eff - 1) / QC_ROWS - off / QC_ROWS + 1);
+      local += cnt[i];
+    }
+  }
+  const int64_t incl = block_incl_scan64(local, tab.scratch);
+  int32_t run = (int32_t)(incl - local);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < per && g0 + i < G) {
+      tab.tstart[g0 + i] = run;
+      run += cnt[i];
+    }
+  }
+  if (tid == (G - 1) / per) tab.tstart[G] = (int32_t)incl;
+  __syncthreads();
+}
+
+// Chunk -> {group, first row, rows}.
+__device__ inline int4 colwise_chunk(const GroupTable& tab, int32_t G, int32_t chunk) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {   // last group whose first chunk is <= chunk
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab.tstart[mid] <= chunk) lo = mid; else hi = mid - 1;
+  }
+  const int64_t off = tab.off[lo], end = off + tab.eff[lo];
+  const int64_t b0 = (off / QC_ROWS + (chunk - tab.tstart[lo])) * (int64_t)QC_ROWS;
+  const int64_t r0 = b0 > off ? b0 : off;
+  const int64_t r1 = b0 + QC_ROWS < end ? b0 + QC_ROWS : end;
+  return make_int4(lo, (int)r0, (int)(r1 - r0), 0);
+}
+
+// Tile index -> (tensor, chunk, column block); consecutive tiles share rows.
+__device__ inline void colwise_tile(const ColwiseArgs& a, int64_t nch, int64_t item, int& t, int32_t& chunk,
+                                    int& cb) {
+  const int64_t cba = cdiv(a.cols[0], QC_COLS);
+  t = 0;
+  if (item >= nch * cba) {
+    item -= nch * cba;
+    t = 1;
+  }
+  const int64_t cbs = cdiv(a.cols[t], QC_COLS);
+  chunk = (int32_t)(item / cbs);
+  cb = (int)(item - (int64_t)chunk * cbs);
+}
+
+__device__ inline int64_t colwise_tiles(const ColwiseArgs& a, int64_t nch) {
+  int64_t n = nch * cdiv(a.cols[0], QC_COLS);
+  if (a.ntensors > 1) n += nch * cdiv(a.cols[1], QC_COLS);
+  return n;
+}
+
+__global__ void __launch_bounds__(256) colwise_zero_kernel(ColwiseArgs a) {
+  for (int t = 0; t < a.ntensors; ++t) {
+    const int64_t n = (int64_t)a.G * a.cols[t];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) a.s[t][i] = 0u;
+  }
+}
+
+__global__ void __launch_bounds__(256) colwise_amax_kernel(ColwiseArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
+  __shared__ uint32_t red[4][QC_COLS];
+  const GroupTable tab = carve_table(table_lds, a.G);
+  GroupTable tabw = tab;
+  build_group_table(a.sizes, a.G, a.rows, QC_ROWS, false, tabw);
+  colwise_chunk_table(tabw, a.G);
+  const int64_t nch = tab.tstart[a.G];
+  const int64_t n = colwise_tiles(a, nch);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cc = tid & 7, rs = tid >> 3;   // 8-column chunk, row within 32
+  for (int64_t item = blockIdx.x; item < n; item += gridDim.x) {
+    int t, cb;
+    int32_t chunk;
+    colwise_tile(a, nch, item, t, chunk, cb);
+    const int4 e = colwise_chunk(tab, a.G, chunk);
+    const int cols = a.cols[t];
+    const int c = cb * QC_COLS + cc * 8;
+    const uint16_t* x = a.x[t] + (int64_t)e.y * cols + c;
+    uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (c < cols) {
+      // all loads issue together: rows past the chunk re-read its first row
+      uint4 v[QC_ROWS / 32];
+#pragma unroll
+      for (int j = 0; j < QC_ROWS / 32; ++j) {
+        const int r = rs + 32 * j;
+        v[j] = *reinterpret_cast<const uint4*>(x + (int64_t)(r < e.z ? r : 0) * cols);
+      }
+#pragma unroll
+      for (int j = 0; j < QC_ROWS / 32; ++j) {
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           m[2 * i] = max(m[2 * i], (w[i] & 0x7FFFu) << 16);
@@ -153,68 +258,128 @@ __device__ void colwise_one(const uint16_t* __restrict__ x, int32_t cols, int64_
         }
       }
     }
-  }
-  // reduce over the 32 threads sharing a column chunk: lanes differing in
-  // bits 3..5 within a wave by shuffles, then across the 4 waves in LDS
+    // reduce over the 32 threads sharing a column chunk: lanes that differ in
+    // bits 3..5 by shuffles, then the 4 waves through LDS
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t v = m[i];
-    v = max(v, (uint32_t)__shfl_xor((int)v, 8, kWave));
-    v = max(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
-    v = max(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
-    m[i] = v;
-  }
-  const int wave = tid >> 6, lane = tid & 63;
-  if (lane < 8) {
+    for (int i = 0; i < 8; ++i) {
+      uint32_t v = m[i];
+      v = max(v, (uint32_t)__shfl_xor((int)v, 8, kWave));
+      v = max(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
+      v = max(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
+      m[i] = v;
+    }
+    if (lane < 8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_red[wave * CW + lane * 8 + i] = m[i];
-  }
-  __syncthreads();
-  if (tid < CW) {
-    const uint32_t a = max(max(s_red[tid], s_red[CW + tid]), max(s_red[2 * CW + tid], s_red[3 * CW + tid]));
-    const float s = fp8_scale_from_amax(__uint_as_float(a));
-    s_scale[tid] = s;
-    if (c0 + tid < cols) sc[(int64_t)g * cols + c0 + tid] = s;
-  }
-  __syncthreads();
-  float sv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sv[i] = s_scale[cchunk * 8 + i];
-
-  // pass 2: cast, transpose through LDS, column-major store
-  for (int64_t base = start; base < r1; base += RS) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rr = rsub + 32 * h;
-      const int64_t r = base + rr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col_ok && r >= r0 && r < r1) v = *reinterpret_cast<const uint4*>(x + r * cols + col);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = clamp448(bf16_to_f32(w[i] & 0xFFFFu) * sv[2 * i]);
-        const float hi = clamp448(bf16_to_f32(w[i] >> 16) * sv[2 * i + 1]);
-        const uint32_t codes = __builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0u, false);
-        tile[cchunk * 8 + 2 * i][rr] = (uint8_t)(codes & 0xFF);
-        tile[cchunk * 8 + 2 * i + 1][rr] = (uint8_t)(codes >> 8 & 0xFF);
-      }
+      for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
     }
     __syncthreads();
-    {
-      // 64 columns x 4 pieces of 16 rows
-      const int c = tid >> 2, piece = tid & 3;
-      const int64_t rp = base + piece * 16;
-      if (c0 + c < cols && rp < r1 && rp + 16 > r0) {
-        uint8_t* dst = q + (int64_t)(c0 + c) * rows + rp;
-        const uint8_t* src = &tile[c][piece * 16];
-        const bool whole = rp >= r0 && rp + 16 <= r1 && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0);
-        if (whole) {
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-        } else {
-          for (int b = 0; b < 16; ++b) {
-            const int64_t r = rp + b;
-            if (r >= r0 && r < r1) dst[b] = src[b];
-          }
+    if (tid < QC_COLS) {
+      const uint32_t v = max(max(red[0][tid], red[1][tid]), max(red[2][tid], red[3][tid]));
+      const int col = cb * QC_COLS + tid;
+      if (col < cols && v != 0u) atomicMax(a.s[t] + (int64_t)e.x * cols + col, v);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(256) colwise_cast_kernel(ColwiseArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
+  // tile[c][r]: code of row r of column c.  Rows of 276 bytes: the dword
+  // writes below (4 rows of one column per lane) hit 64 distinct banks.
+  constexpr int TROW = QC_ROWS + 20;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[QC_COLS][TROW];
+  __shared__ float sc[QC_COLS];
+  __shared__ int sh[QC_COLS];
+  const GroupTable tab = carve_table(table_lds, a.G);
+  GroupTable tabw = tab;
+  build_group_table(a.sizes, a.G, a.rows, QC_ROWS, false, tabw);
+  colwise_chunk_table(tabw, a.G);
+  const int64_t nch = tab.tstart[a.G];
+  const int64_t n = colwise_tiles(a, nch);
+  const int tid = threadIdx.x;
+  const int cc = tid & 7, rq = tid >> 3;   // 8-column chunk, row quad within 128 rows
+  for (int64_t item = n - 1 - blockIdx.x; item >= 0; item -= gridDim.x) {
+    int t, cb;
+    int32_t chunk;
+    colwise_tile(a, nch, item, t, chunk, cb);
+    const int4 e = colwise_chunk(tab, a.G, chunk);
+    const int cols = a.cols[t];
+    const int64_t M = a.rows;
+    if (tid < QC_COLS) {
+      const int col = cb * QC_COLS + tid;
+      float v = 0.f;
+      if (col < cols) v = fp8_scale_from_amax(__uint_as_float(a.s[t][(int64_t)e.x * cols + col]));
+      sc[tid] = v;
+      // byte offset of the column's first row within its 16-byte piece
+      sh[tid] = (int)((reinterpret_cast<uintptr_t>(a.q[t]) + (uint64_t)((int64_t)col * M + e.y)) & 15u);
+    }
+    __syncthreads();
+    const int c = cb * QC_COLS + cc * 8;
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = sc[cc * 8 + i];
+    const uint16_t* x = a.x[t] + (int64_t)e.y * cols + c;
+    // the whole tile's loads first (rows past the chunk re-read its first row)
+    constexpr int HALVES = QC_ROWS / 128;
+    uint4 vv[HALVES][4];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 128 * h + 4 * rq + k;
+        vv[h][k] = make_uint4(0, 0, 0, 0);
+        if (c < cols) vv[h][k] = *reinterpret_cast<const uint4*>(x + (int64_t)(r < e.z ? r : 0) * cols);
+      }
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+      const int r0 = 128 * h + 4 * rq;
+      // codes of 4 rows x 8 columns; column i's 4 codes form one dword
+      uint32_t col4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w[4] = {vv[h][k].x, vv[h][k].y, vv[h][k].z, vv[h][k].w};
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float f0 = clamp448(bf16_to_f32(w[i / 2] & 0xFFFFu) * sv[i]);
+          const float f1 = clamp448(bf16_to_f32(w[i / 2] >> 16) * sv[i + 1]);
+          const uint32_t codes = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0u, false);
+          col4[i] |= (codes & 0xFFu) << (8 * k);
+          col4[i + 1] |= (codes >> 8 & 0xFFu) << (8 * k);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&tile[cc * 8 + i][r0]) = col4[i];
+    }
+    __syncthreads();
+    // Column-major stores.  Column cl's rows [0, e.z) start at global byte
+    // address A = col * M + row0 (plus the base), which sits s0 bytes into a
+    // 16-byte piece; piece p covers rows [16 p - s0, 16 p - s0 + 16).  Its
+    // bytes come from the tile by a byte funnel shift of aligned dwords.
+    constexpr int PIECES = QC_ROWS / 16 + 1;
+    for (int qi = tid; qi < QC_COLS * PIECES; qi += 256) {
+      const int cl = qi / PIECES, p = qi - cl * PIECES;
+      const int col = cb * QC_COLS + cl;
+      if (col >= cols) continue;
+      const int s0 = sh[cl];
+      const int lo = p * 16 - s0, hi = lo + 16;   // rows of this piece
+      if (hi <= 0 || lo >= e.z) continue;
+      uint8_t* dst = a.q[t] + (int64_t)col * M + e.y + lo;   // 16-byte aligned
+      if (lo >= 0 && hi <= e.z) {
+        const int d0 = lo >> 2, sb = lo & 3;   // first dword, byte shift
+        const uint32_t* trow = reinterpret_cast<const uint32_t*>(&tile[cl][0]);
+        uint32_t w[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) w[j] = trow[d0 + j < TROW / 4 ? d0 + j : TROW / 4 - 1];
+        uint4 out;
+        out.x = __builtin_amdgcn_alignbyte(w[1], w[0], sb);
+        out.y = __builtin_amdgcn_alignbyte(w[2], w[1], sb);
+        out.z = __builtin_amdgcn_alignbyte(w[3], w[2], sb);
+        out.w = __builtin_amdgcn_alignbyte(w[4], w[3], sb);
+        *reinterpret_cast<uint4*>(dst) = out;
+      } else {
+        for (int b = 0; b < 16; ++b) {
+          const int r = lo + b;
+          if (r >= 0 && r < e.z) dst[b] = tile[cl][r];
         }
       }
     }
@@ -222,43 +387,40 @@ __device__ void colwise_one(const uint16_t* __restrict__ x, int32_t cols, int64_
   }
 }
 
-__global__ void __launch_bounds__(256) quant_colwise_kernel(const uint16_t* __restrict__ a, int32_t cols_a,
-                                                           const uint16_t* __restrict__ b, int32_t cols_b,
-                                                           const int32_t* __restrict__ sizes, int32_t G,
-                                                           int64_t rows, uint8_t* __restrict__ qa,
-                                                           float* __restrict__ sa, uint8_t* __restrict__ qb,
-                                                           float* __restrict__ sb) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[CW][RS + 16];
-  __shared__ uint32_t s_red[4 * CW];
-  __shared__ float s_scale[CW];
-  __shared__ int64_t s_r[2];
-  const int g = blockIdx.y;
-  const int cb = blockIdx.x;
-  if (threadIdx.x == 0) {
-    // group bounds: exclusive prefix of the (clamped) sizes
-    int64_t off = 0;
-    for (int h = 0; h < g; ++h) off += sizes[h] > 0 ? sizes[h] : 0;
-    int64_t end = off + (sizes[g] > 0 ? sizes[g] : 0);
-    s_r[0] = off < rows ? off : rows;
-    s_r[1] = end < rows ? end : rows;
-  }
-  __syncthreads();
-  const int64_t r0 = s_r[0], r1 = s_r[1];
-  if (cb * CW < cols_a)
-    colwise_one(a, cols_a, rows, r0, r1, g, cb, qa, sa, tile, s_red, s_scale);
-  if (b != nullptr && cb * CW < cols_b) {
-    __syncthreads();
-    colwise_one(b, cols_b, rows, r0, r1, g, cb, qb, sb, tile, s_red, s_scale);
+__global__ void __launch_bounds__(256) colwise_finalize_kernel(ColwiseArgs a) {
+  for (int t = 0; t < a.ntensors; ++t) {
+    const int64_t n = (int64_t)a.G * a.cols[t];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+      a.s[t][i] = __float_as_uint(fp8_scale_from_amax(__uint_as_float(a.s[t][i])));
   }
 }
 
 hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_t* b, int32_t cols_b,
                                 const int32_t* sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
                                 uint8_t* qb, float* sb, hipStream_t stream) {
-  const int32_t cmax = (b != nullptr && cols_b > cols_a) ? cols_b : cols_a;
-  dim3 grid((unsigned)cdiv(cmax, CW), (unsigned)G);
-  hipLaunchKernelGGL(quant_colwise_kernel, grid, dim3(256), 0, stream, a, cols_a, b, cols_b, sizes, G, rows,
-                     qa, sa, qb, sb);
+  ColwiseArgs x;
+  x.x[0] = a;
+  x.cols[0] = cols_a;
+  x.q[0] = qa;
+  x.s[0] = reinterpret_cast<uint32_t*>(sa);
+  x.ntensors = b != nullptr ? 2 : 1;
+  x.x[1] = b;
+  x.cols[1] = b != nullptr ? cols_b : 0;
+  x.q[1] = qb;
+  x.s[1] = reinterpret_cast<uint32_t*>(sb);
+  x.sizes = sizes;
+  x.G = G;
+  x.rows = rows;
+  const int64_t scale_words = (int64_t)G * (cols_a + x.cols[1]);
+  const int small = (int)(cdiv(scale_words, 256) < 1024 ? cdiv(scale_words, 256) : 1024);
+  const int grid = device_cu_count() * 8;
+  const size_t dyn = (size_t)table_lds_bytes(G);
+  hipLaunchKernelGGL(colwise_zero_kernel, dim3(small), dim3(256), 0, stream, x);
+  if (rows > 0) {
+    hipLaunchKernelGGL(colwise_amax_kernel, dim3(grid), dim3(256), dyn, stream, x);
+    hipLaunchKernelGGL(colwise_cast_kernel, dim3(grid), dim3(256), dyn, stream, x);
+  }
+  hipLaunchKernelGGL(colwise_finalize_kernel, dim3(small), dim3(256), 0, stream, x);
   return hipGetLastError();
 }
 
