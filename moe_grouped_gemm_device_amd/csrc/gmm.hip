@@ -53,6 +53,7 @@
 namespace mg {
 
 constexpr int kThreads = 256;   // 4 waves: 2 (M) x 2 (N)
+constexpr uint32_t kRasterM = 8;  // row tiles per raster block (fixed-M item order)
 
 template <int ELEM> struct ElemTraits;
 template <> struct ElemTraits<EL_BF16> {
@@ -130,6 +131,15 @@ __device__ inline void dma16(const i32x4& r, uint32_t lds, uint32_t voff) {
                  : "v"(voff), "s"(lds), "s"(r)
                  : "memory");
   }
+}
+
+// 4 bytes per lane from global memory to LDS: lane l writes lds + 4 l.
+__device__ inline void dma4(const i32x4& r, uint32_t lds, uint32_t voff) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tbuffer_load_dword %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "v"(voff), "s"(lds), "s"(r)
+               : "memory");
 }
 
 // Wait until at most VM vector-memory operations of this wave are still in
@@ -298,21 +308,36 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
   const uint32_t w = (uint32_t)w64;
   int nt;
   if (KIND == FIXED_M) {
-    const uint32_t mt = w / (uint32_t)n_tiles;
-    nt = (int)(w - mt * (uint32_t)n_tiles);
-    if (prev != nullptr && prev->mt == (int)mt) {
-      it = *prev;
-    } else {
-      const int4 e = fixed_m_entry(tab, a.E, BM, (int32_t)mt);
-      it.g = uni(e.x);
-      it.rowbase = uni(e.y);
-      it.m_valid = uni(e.z);
-      it.c_lo = 0;
-      it.c_hi = a.Kc;
-      it.c_begin = 0;
-      it.nsteps = (int)cdiv(a.Kc, BK);
-      it.mt = (int)mt;
+    // Items run group by group; inside a group, in blocks of kRasterM row
+    // tiles, column tile outermost: the workgroups of one XCD, which take
+    // consecutive items at the same time, then share each weight slice
+    // among kRasterM row tiles and each activation slice among the block's
+    // column tiles.
+    const uint32_t ntu = (uint32_t)n_tiles;
+    int lo = 0, hi = a.E - 1;
+    while (lo < hi) {   // last group whose first item is <= w
+      const int mid = (lo + hi + 1) >> 1;
+      if ((uint32_t)tab.tstart[mid] * ntu <= w) lo = mid; else hi = mid - 1;
     }
+    const int g = uni(lo);
+    const int32_t t0 = uni(tab.tstart[g]);
+    const uint32_t mtg = (uint32_t)(uni(tab.tstart[g + 1]) - t0);
+    const uint32_t local = w - (uint32_t)t0 * ntu;
+    const uint32_t blk = local / (kRasterM * ntu);
+    const uint32_t rem = local - blk * kRasterM * ntu;
+    const uint32_t mb = mtg - blk * kRasterM < kRasterM ? mtg - blk * kRasterM : kRasterM;
+    nt = (int)(rem / mb);
+    const int ml = (int)(blk * kRasterM + (rem - (uint32_t)nt * mb));
+    const int32_t eff = uni(tab.eff[g]);
+    it.g = g;
+    it.rowbase = (int64_t)uni(tab.off[g]) + (int64_t)ml * BM;
+    it.m_valid = eff - ml * BM < BM ? eff - ml * BM : BM;
+    it.c_lo = 0;
+    it.c_hi = a.Kc;
+    it.c_begin = 0;
+    it.nsteps = (int)cdiv(a.Kc, BK);
+    it.mt = t0 + ml;
+    (void)prev;
   } else {
     const uint32_t per = (uint32_t)m_tiles_dk * (uint32_t)n_tiles;
     const uint32_t gi = w / per;
@@ -381,6 +406,10 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   constexpr bool MASK_BYTES = (ELEM == EL_FP8) && (KIND == DYNAMIC_K);
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
+  // fp8: the tile's row and column scales, fetched by LDS DMA at the start of
+  // its last k-step (a compiler-issued load would make the compiler drain
+  // every LDS-DMA transfer in flight before the epilogue could use it)
+  __shared__ __attribute__((aligned(16))) float scl[EPI == EPI_NONE ? 4 : BM + BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -402,44 +431,72 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   int b = blockIdx.x;
   if ((G & 7) == 0) b = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // FIXED_M: this workgroup's range [p0, p1) of the L (item, k-step)
-  // positions.  Only GS = min(G, L) workgroups take part, so every range is
-  // non-empty and the pieces of a split tile are exactly the workgroups
-  // whose ranges meet it.
+  // Fixed-M schedule: whole tiles dealt round-robin (item b + k G) for all
+  // but the last one or two rounds' worth -- workgroups on whole tiles run in
+  // lockstep, so operand slices they share are fetched once per XCD -- then
+  // stream-K over the rest: the L = (items - D) * S (item, k-step) positions
+  // of items [D, items) are cut into GS = min(G, L) equal ranges, one per
+  // workgroup [p0, p1), so every such range is non-empty and the pieces of a
+  // split tile are exactly the workgroups whose ranges meet it.
   const int S = (KIND == FIXED_M) ? (int)cdiv(a.Kc, BK) : 1;
-  const int64_t L = items * S;
+  const int64_t rounds = items / G;
+  const int64_t D = (KIND == FIXED_M && rounds >= 2) ? (rounds - 1) * G : 0;
+  const int64_t L = (items - D) * S;
   const int64_t GS = L < G ? L : G;
-  if (KIND == FIXED_M ? b >= GS : b >= items) return;
-  const int64_t p0 = (KIND == FIXED_M) ? (int64_t)b * L / GS : 0;
-  const int64_t p1 = (KIND == FIXED_M) ? (int64_t)(b + 1) * L / GS : 0;
-
+  if (KIND == FIXED_M ? (b >= D && b >= GS) : b >= items) return;
+  const int64_t p0 = (KIND == FIXED_M && b < GS) ? D * S + (int64_t)b * L / GS : 0;
+  const int64_t p1 = (KIND == FIXED_M && b < GS) ? D * S + (int64_t)(b + 1) * L / GS : 0;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(a.B);
   auto fetch = [&](int64_t w, const Item* prev) {
     return get_item<BM, BN, KIND, ELEM, BK>(a, tab, w, n_tiles, m_tiles_dk, prev);
   };
-  // k-steps of item w this workgroup runs end at (exclusive)
-  auto item_end = [&](int64_t w, const Item& it) -> int {
-    if constexpr (KIND == FIXED_M) {
-      const int64_t e = p1 - w * S;
-      return e < S ? (int)e : S;
-    } else {
-      return it.nsteps;
-    }
+  // The workgroup's sequence of (item, first k-step, end k-step); the end of
+  // a dynamic-K item comes from the item (-1 here).
+  struct Pos {
+    int64_t w;
+    int s, e;
   };
-  auto next_item = [&](int64_t w) -> int64_t { return KIND == FIXED_M ? w + 1 : w + G; };
-  auto has_item = [&](int64_t w) -> bool { return KIND == FIXED_M ? w * S < p1 : w < items; };
+  auto sk_pos = [&](int64_t w, int64_t from) -> Pos {
+    const int64_t e = p1 - w * S;
+    return Pos{w, (int)(from - w * S), (int)(e < S ? e : S)};
+  };
+  auto first_pos = [&]() -> Pos {
+    if (KIND == DYNAMIC_K) return Pos{b, 0, -1};
+    if (b < D) return Pos{b, 0, S};
+    return sk_pos(p0 / S, p0);
+  };
+  auto next_pos = [&](int64_t w, Pos& out) -> bool {
+    if (KIND == DYNAMIC_K) {
+      if (w + G >= items) return false;
+      out = Pos{w + G, 0, -1};
+      return true;
+    }
+    if (w < D) {
+      if (w + G < D) {
+        out = Pos{w + G, 0, S};
+        return true;
+      }
+      if (b >= GS) return false;
+      out = sk_pos(p0 / S, p0);
+      return true;
+    }
+    if ((w + 1) * S >= p1) return false;
+    out = sk_pos(w + 1, (w + 1) * S);
+    return true;
+  };
 
   // load cursor (NS - 1 positions ahead of the compute cursor)
-  int64_t lw = (KIND == FIXED_M) ? p0 / S : b;
-  int ls = (KIND == FIXED_M) ? (int)(p0 - lw * S) : 0;
+  const Pos fp = first_pos();
+  int64_t lw = fp.w;
+  int ls = fp.s;
   Item li = fetch(lw, nullptr);
-  int lend = item_end(lw, li);
+  int lend = fp.e < 0 ? li.nsteps : fp.e;
   bool ldone = false;
   ATile at;
   BTile bt;
   auto setup = [&](const Item& it) {
-    at.setup(wave, lane, a.a_ld, A_KC ? it.m_valid : it.m_valid);
+    at.setup(wave, lane, a.a_ld, it.m_valid);
     bt.setup(wave, lane, a.b_ld, it.n_valid);
   };
   setup(li);
@@ -492,21 +549,44 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     if (q < LA) at.issue(q, x.ra, x.st, wave, lane, x.lo, x.hi, x.edge);
     else bt.issue(q - LA, x.rb, x.st + A_BYTES, wave, lane, x.lo, x.hi, x.edge);
   };
+  // Scale DMAs for the compute cursor's tile (EPI != NONE): BM row scales,
+  // then BN column scales, 64 floats per instruction; instruction k goes to
+  // wave k % 4.  Rows and columns outside the tile read as 0.
+  constexpr int NSC = (BM + BN) / 64;
+  auto issue_scales = [&](const Item& it) {
+    if constexpr (EPI != EPI_NONE) {
+      const float* rows = a.sa + ((EPI == EPI_ROW_COL) ? it.rowbase : (int64_t)it.g * a.Mout + it.rowbase);
+      const float* cols = a.sb + (int64_t)it.g * a.Nout + it.n0;
+      const i32x4 rr = make_rsrc_words(rows, (int64_t)it.m_valid * 4);
+      const i32x4 rc = make_rsrc_words(cols, (int64_t)it.n_valid * 4);
+      const uint32_t base = lds_address(reinterpret_cast<uint8_t*>(scl));
+#pragma unroll
+      for (int k = 0; k < (NSC + 3) / 4; ++k) {
+        const int ins = wave + 4 * k;
+        if (ins < NSC) {
+          const bool is_row = ins < BM / 64;
+          const int first = is_row ? ins * 64 : ins * 64 - BM;
+          dma4(is_row ? rr : rc, base + ins * 256, (uint32_t)((first + lane) * 4));
+        }
+      }
+    }
+  };
+
   auto advance_load = [&]() {
     if (ldone) return;
     if (ls + 1 < lend) {
       ++ls;
       return;
     }
-    const int64_t nw = next_item(lw);
-    if (!has_item(nw)) {
+    Pos np;
+    if (!next_pos(lw, np)) {
       ldone = true;
       return;
     }
-    lw = nw;
-    ls = 0;
-    li = fetch(nw, &li);
-    lend = item_end(nw, li);
+    lw = np.w;
+    ls = np.s;
+    li = fetch(np.w, &li);
+    lend = np.e < 0 ? li.nsteps : np.e;
     setup(li);
   };
 
@@ -527,6 +607,11 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   static_assert(LPS % T::KSUB == 0, "transfers per sub-step");
   auto compute = [&](const uint8_t* As, const LoadCtx& lx) {
     const uint8_t* Bs = As + A_BYTES;
+    // The fragment addresses below are loop-invariant; hoisted, they would
+    // hold 24-48 VGPRs across the K loop and push the kernel into spills.
+    // An opaque copy of the lane index makes them cheap per-step arithmetic.
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     int mlo = 0, mhi = BK;
     if constexpr (MASK_BYTES) {
       const int64_t c0 = ci.c_begin + (int64_t)cs * BK;
@@ -605,24 +690,19 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     uint16_t* stg = reinterpret_cast<uint16_t*>(st + wave * WREG);
     float* rsc = reinterpret_cast<float*>(st + 4 * WREG);   // [BM] 1 / row scale
     float* csc = rsc + BM;                                  // [BN] 1 / column scale
-    lds_sync();   // every wave is done reading st
     if constexpr (EPI != EPI_NONE) {
+      // every wave is done reading st, and the scale DMAs issued before this
+      // k-step's LPS tile transfers (and whatever the stream-K combine
+      // issued since, which it waited for) have landed
+      wait_vm_sync<LPS>();
       for (int idx = tid; idx < BM + BN; idx += kThreads) {
-        if (idx < BM) {
-          float v = 0.f;
-          if (idx < it.m_valid) {
-            const int64_t r = (EPI == EPI_ROW_COL) ? it.rowbase + idx : (int64_t)it.g * a.Mout + it.rowbase + idx;
-            v = 1.f / a.sa[r];
-          }
-          rsc[idx] = v;
-        } else {
-          const int c = idx - BM;
-          float v = 0.f;
-          if (c < it.n_valid) v = 1.f / a.sb[(int64_t)it.g * a.Nout + it.n0 + c];
-          csc[c] = v;
-        }
+        const float v = scl[idx];
+        if (idx < BM) rsc[idx] = v != 0.f ? 1.f / v : 0.f;
+        else csc[idx - BM] = v != 0.f ? 1.f / v : 0.f;
       }
       lds_sync();
+    } else {
+      lds_sync();   // every wave is done reading st
     }
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(reinterpret_cast<uint16_t*>(a.C) + (int64_t)it.g * a.c_gs + it.rowbase * a.c_ld + it.n0, 0x7FFFFFFF);
@@ -689,31 +769,37 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   // operand load on that XCD would go back to HBM.)
   constexpr int PART_BYTES = BM * BN * 4;
   constexpr int WAVE_BYTES = TI * TJ * 4096;   // 16 floats x 64 lanes per block
-  auto wg_of = [&](int64_t pos) -> int { return (int)(((pos + 1) * GS - 1) / L); };
+  // (positions here are absolute; the stream-K ranges start at D * S)
+  auto wg_of = [&](int64_t pos) -> int { return (int)(((pos - D * S + 1) * GS - 1) / L); };
   auto part_rsrc = [&](int bb, int64_t w) {
-    const int64_t first = ((int64_t)bb * L / GS) / S;   // first item in bb's range
+    const int64_t first = (D * S + (int64_t)bb * L / GS) / S;   // first item in bb's range
     const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sk_part) +
                           (int64_t)(2 * bb + (first == w ? 0 : 1)) * PART_BYTES + wave * WAVE_BYTES;
     return make_rsrc(base, WAVE_BYTES);
   };
+  // Partial tiles in the MFMA register layout: 16 bytes per lane and
+  // element quad, a 1 KB block per (i, j, q).  The block offset goes in the
+  // instruction's scalar offset, so no per-block address stays live in a
+  // VGPR across the K loop.
   auto part_io = [&](bool store, const __amdgpu_buffer_rsrc_t& r, const Item& it, bool add) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const bool ok = wm * WM + 32 * i + (lane & 31) < it.m_valid;
+      const uint32_t vo = ok ? (uint32_t)(lane * 16) : kOOB;
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t vo = ok ? (uint32_t)((((i * TJ + j) * 4 + q) * 64 + lane) * 16) : kOOB;
+          const int so = ((i * TJ + j) * 4 + q) * 1024;
           if (store) {
             i32x4 v;
             v[0] = __float_as_int(acc[i][j][4 * q]);
             v[1] = __float_as_int(acc[i][j][4 * q + 1]);
             v[2] = __float_as_int(acc[i][j][4 * q + 2]);
             v[3] = __float_as_int(acc[i][j][4 * q + 3]);
-            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)vo, 0, kPolicyDevice);
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)vo, so, kPolicyDevice);
           } else {
-            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, 0, kPolicyDevice);
+            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, so, kPolicyDevice);
             if (add) {
               acc[i][j][4 * q] += __int_as_float(v[0]);
               acc[i][j][4 * q + 1] += __int_as_float(v[1]);
@@ -799,6 +885,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
       else wait_vm_sync<(NS - 2) * LPS>();
       epi_prev = false;
+      if (EPI != EPI_NONE && cs + 1 == cend) issue_scales(ci);
       const LoadCtx lx = prepare_loads(smem + lstage * STAGE);
       lstage = lstage + 1 == NS ? 0 : lstage + 1;
       compute(smem + stage * STAGE, lx);   // also issues the loads of lx
@@ -807,18 +894,18 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       stage = stage + 1 == NS ? 0 : stage + 1;
     }
     bool write = true;
-    if constexpr (KIND == FIXED_M) write = sk_combine(ci, cw);
+    if constexpr (KIND == FIXED_M) write = cw < D || sk_combine(ci, cw);
     if (write) {
       epilogue(smem + last_stage * STAGE, ci);
       epi_prev = true;
     }
     zero_acc();
-    const int64_t nw = next_item(cw);
-    if (!has_item(nw)) break;
-    cw = nw;
-    cs = 0;
-    ci = fetch(nw, &ci);
-    cend = item_end(nw, ci);
+    Pos np;
+    if (!next_pos(cw, np)) break;
+    cw = np.w;
+    cs = np.s;
+    ci = fetch(np.w, &ci);
+    cend = np.e < 0 ? ci.nsteps : np.e;
   }
   wait_vm_all();   // no LDS-DMA transfer may outlive the workgroup
 }
