@@ -431,19 +431,38 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   int b = blockIdx.x;
   if ((G & 7) == 0) b = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // Fixed-M schedule: whole tiles dealt round-robin (item b + k G) for all
-  // but the last one or two rounds' worth -- workgroups on whole tiles run in
-  // lockstep, so operand slices they share are fetched once per XCD -- then
-  // stream-K over the rest: the L = (items - D) * S (item, k-step) positions
-  // of items [D, items) are cut into GS = min(G, L) equal ranges, one per
-  // workgroup [p0, p1), so every such range is non-empty and the pieces of a
-  // split tile are exactly the workgroups whose ranges meet it.
+  // Fixed-M schedule: rounds of G whole tiles first -- workgroups on whole
+  // tiles run in lockstep, so operand slices they share are fetched once per
+  // XCD -- then stream-K over the rest: the L = (items - D) * S (item,
+  // k-step) positions of items [D, items) are cut into GS = min(G, L) equal
+  // ranges, one per workgroup [p0, p1), so every such range is non-empty and
+  // the pieces of a split tile are exactly the workgroups whose ranges meet
+  // it.  Splitting a tile costs its last piece a reload of the other pieces'
+  // fp32 partial tiles at the end of its range (about as long as 10-15
+  // k-steps when the operand streams saturate HBM), so when the last round
+  // would still keep at least 5/8 of the grid busy every tile stays whole
+  // (D = items); otherwise the last one or two rounds' worth goes to
+  // stream-K.  A partial last round is spread evenly over the XCDs, each
+  // taking a run of consecutive tiles (tiles of one expert share X rows).
   const int S = (KIND == FIXED_M) ? (int)cdiv(a.Kc, BK) : 1;
-  const int64_t rounds = items / G;
-  const int64_t D = (KIND == FIXED_M && rounds >= 2) ? (rounds - 1) * G : 0;
+  const int64_t full = items / G, rem = items - full * G;
+  const bool whole = rem == 0 || rem * 8 >= (int64_t)G * 5;
+  const int64_t D = (KIND != FIXED_M) ? 0 : whole ? items : (full >= 2 ? (full - 1) * G : 0);
   const int64_t L = (items - D) * S;
   const int64_t GS = L < G ? L : G;
-  if (KIND == FIXED_M ? (b >= D && b >= GS) : b >= items) return;
+  // item of data-parallel round r for this workgroup, or -1
+  auto dp_item = [&](int64_t r) -> int64_t {
+    const int64_t base = r * G;
+    if (base + G <= D) return base + b;
+    const int64_t n = D - base;
+    if (n <= 0) return -1;
+    if ((G & 7) != 0) return b < n ? base + b : -1;
+    const int64_t C = (n + 7) >> 3;
+    const int64_t j = blockIdx.x >> 3, slot = (int64_t)(blockIdx.x & 7) * C + j;
+    return (j < C && slot < n) ? base + slot : -1;
+  };
+  const int64_t dp0 = (KIND == FIXED_M) ? dp_item(0) : -1;
+  if (KIND == FIXED_M ? (dp0 < 0 && b >= GS) : b >= items) return;
   const int64_t p0 = (KIND == FIXED_M && b < GS) ? D * S + (int64_t)b * L / GS : 0;
   const int64_t p1 = (KIND == FIXED_M && b < GS) ? D * S + (int64_t)(b + 1) * L / GS : 0;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
@@ -463,7 +482,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   };
   auto first_pos = [&]() -> Pos {
     if (KIND == DYNAMIC_K) return Pos{b, 0, -1};
-    if (b < D) return Pos{b, 0, S};
+    if (dp0 >= 0) return Pos{dp0, 0, S};
     return sk_pos(p0 / S, p0);
   };
   auto next_pos = [&](int64_t w, Pos& out) -> bool {
@@ -473,8 +492,10 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       return true;
     }
     if (w < D) {
-      if (w + G < D) {
-        out = Pos{w + G, 0, S};
+      const int64_t r = (w >> 32) == 0 ? (int64_t)((uint32_t)w / (uint32_t)G) : w / G;
+      const int64_t nw = dp_item(r + 1);
+      if (nw >= 0) {
+        out = Pos{nw, 0, S};
         return true;
       }
       if (b >= GS) return false;
