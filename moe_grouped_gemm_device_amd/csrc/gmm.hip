@@ -431,8 +431,8 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   int b = blockIdx.x;
   if ((G & 7) == 0) b = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // Fixed-M schedule: rounds of G whole tiles first -- workgroups on whole
-  // tiles run in lockstep, so operand slices they share are fetched once per
+  // Fixed-M schedule: whole tiles first -- workgroups on whole tiles of one
+  // XCD run in lockstep, so operand slices they share are fetched once per
   // XCD -- then stream-K over the rest: the L = (items - D) * S (item,
   // k-step) positions of items [D, items) are cut into GS = min(G, L) equal
   // ranges, one per workgroup [p0, p1), so every such range is non-empty and
@@ -442,27 +442,33 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   // k-steps when the operand streams saturate HBM), so when the last round
   // would still keep at least 5/8 of the grid busy every tile stays whole
   // (D = items); otherwise the last one or two rounds' worth goes to
-  // stream-K.  A partial last round is spread evenly over the XCDs, each
-  // taking a run of consecutive tiles (tiles of one expert share X rows).
+  // stream-K.  Dynamic-K items are all whole.
   const int S = (KIND == FIXED_M) ? (int)cdiv(a.Kc, BK) : 1;
   const int64_t full = items / G, rem = items - full * G;
   const bool whole = rem == 0 || rem * 8 >= (int64_t)G * 5;
-  const int64_t D = (KIND != FIXED_M) ? 0 : whole ? items : (full >= 2 ? (full - 1) * G : 0);
+  const int64_t D = (KIND != FIXED_M || whole) ? items : (full >= 2 ? (full - 1) * G : 0);
   const int64_t L = (items - D) * S;
   const int64_t GS = L < G ? L : G;
-  // item of data-parallel round r for this workgroup, or -1
-  auto dp_item = [&](int64_t r) -> int64_t {
-    const int64_t base = r * G;
-    if (base + G <= D) return base + b;
-    const int64_t n = D - base;
-    if (n <= 0) return -1;
-    if ((G & 7) != 0) return b < n ? base + b : -1;
-    const int64_t C = (n + 7) >> 3;
-    const int64_t j = blockIdx.x >> 3, slot = (int64_t)(blockIdx.x & 7) * C + j;
-    return (j < C && slot < n) ? base + slot : -1;
+  // Whole items [0, D): XCD x owns the contiguous eighth [c0, c1) and its
+  // G / 8 workgroups take it round-robin, so each XCD's L2 serves one run
+  // of consecutive items (for the balanced dW, one expert per XCD) and a
+  // partial last round is spread evenly over the XCDs.  dp_item(k) is the
+  // workgroup's k-th whole item, or -1.
+  const bool xcd_split = (G & 7) == 0;
+  const int64_t gx = xcd_split ? (G >> 3) : G;
+  const int64_t dj = xcd_split ? (int64_t)(blockIdx.x >> 3) : b;
+  const int64_t c0 = xcd_split ? ((int64_t)(blockIdx.x & 7) * D) >> 3 : 0;
+  const int64_t c1 = xcd_split ? ((int64_t)((blockIdx.x & 7) + 1) * D) >> 3 : D;
+  auto dp_item = [&](int64_t k) -> int64_t {
+    const int64_t w = c0 + dj + k * gx;
+    return w < c1 ? w : -1;
   };
-  const int64_t dp0 = (KIND == FIXED_M) ? dp_item(0) : -1;
-  if (KIND == FIXED_M ? (dp0 < 0 && b >= GS) : b >= items) return;
+  auto dp_next = [&](int64_t w) -> int64_t {   // whole item after w (w from dp_item)
+    const int64_t nw = w + gx;
+    return nw < c1 ? nw : -1;
+  };
+  const int64_t dp0 = dp_item(0);
+  if (dp0 < 0 && b >= GS) return;
   const int64_t p0 = (KIND == FIXED_M && b < GS) ? D * S + (int64_t)b * L / GS : 0;
   const int64_t p1 = (KIND == FIXED_M && b < GS) ? D * S + (int64_t)(b + 1) * L / GS : 0;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
@@ -481,21 +487,14 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     return Pos{w, (int)(from - w * S), (int)(e < S ? e : S)};
   };
   auto first_pos = [&]() -> Pos {
-    if (KIND == DYNAMIC_K) return Pos{b, 0, -1};
-    if (dp0 >= 0) return Pos{dp0, 0, S};
+    if (dp0 >= 0) return Pos{dp0, 0, KIND == FIXED_M ? S : -1};
     return sk_pos(p0 / S, p0);
   };
   auto next_pos = [&](int64_t w, Pos& out) -> bool {
-    if (KIND == DYNAMIC_K) {
-      if (w + G >= items) return false;
-      out = Pos{w + G, 0, -1};
-      return true;
-    }
     if (w < D) {
-      const int64_t r = (w >> 32) == 0 ? (int64_t)((uint32_t)w / (uint32_t)G) : w / G;
-      const int64_t nw = dp_item(r + 1);
+      const int64_t nw = dp_next(w);
       if (nw >= 0) {
-        out = Pos{nw, 0, S};
+        out = Pos{nw, 0, KIND == FIXED_M ? S : -1};
         return true;
       }
       if (b >= GS) return false;
