@@ -52,7 +52,6 @@
 
 namespace mg {
 
-constexpr int kThreads = 256;   // 4 waves: 2 (M) x 2 (N)
 constexpr uint32_t kRasterM = 8;  // row tiles per raster block (fixed-M item order)
 
 template <int ELEM> struct ElemTraits;
@@ -85,6 +84,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, kBufFlags);
 }
 
+// Descriptor words (below) as the compiler's buffer resource type.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const i32x4& w) {
+  const uint64_t base = (uint64_t)(uint32_t)w[0] | ((uint64_t)(uint32_t)(w[1] & 0xFFFF) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, w[2], kBufFlags);
+}
+
 // The same descriptor as four words, for the LDS-DMA asm below: base address
 // (48 bits, stride 0), size in bytes, raw-buffer flags.
 __device__ inline i32x4 make_rsrc_words(const void* base, int64_t bytes) {
@@ -98,10 +103,13 @@ __device__ inline i32x4 make_rsrc_words(const void* base, int64_t bytes) {
   return r;
 }
 
-// Cache policy: operands read exactly once (the weights of fixed-M bf16
-// products) are loaded non-temporal; measured on MI355X, a pure stream runs
-// at ~7.0 TB/s that way against ~4.8 TB/s with the default policy.  Operands
-// that other tiles re-read keep the default policy so they stay in L2.
+// Cache policy: operands read exactly once (the weights of a fixed-M bf16
+// product whose expert has a single row tile) are loaded non-temporal;
+// measured on MI355X, a pure stream runs at ~7.0 TB/s that way against
+// ~4.8 TB/s with the default policy.  Operands that other tiles re-read --
+// the weights of an expert with several row tiles, which the raster order
+// hands to workgroups of one XCD at the same time -- keep the default
+// policy so that they are fetched once into L2.
 constexpr int kPolicyCached = 0;
 constexpr int kPolicyStream = 2;   // nt
 constexpr int kPolicyDevice = 16;  // sc1: coherent at device scope (across XCDs)
@@ -130,6 +138,18 @@ __device__ inline void dma16(const i32x4& r, uint32_t lds, uint32_t voff) {
                  : "=&s"(save)
                  : "v"(voff), "s"(lds), "s"(r)
                  : "memory");
+  }
+}
+
+// A tile whose policy is kPolicyStream streams only when nt (a
+// workgroup-uniform choice made per work item); otherwise it is cached.
+template <int POL>
+__device__ inline void dma_pol(const i32x4& r, uint32_t lds, uint32_t voff, bool nt) {
+  if constexpr (POL == kPolicyStream) {
+    if (nt) dma16<kPolicyStream>(r, lds, voff);
+    else dma16<kPolicyCached>(r, lds, voff);
+  } else {
+    dma16<POL>(r, lds, voff);
   }
 }
 
@@ -178,11 +198,11 @@ __device__ inline int64_t uni64(int64_t v) {
 // Contraction-contiguous operand: R rows x 128 bytes (BK elements); row r at
 // r * 128, its 16-byte chunk c at slot swz_chunk(r, c).  Each 1 KB block
 // (8 rows) is one DMA instruction of one wave.
-template <int R, int ELEM, int POL>
+template <int R, int ELEM, int POL, int NW>
 struct KcTile {
   using T = ElemTraits<ELEM>;
   static constexpr int BYTES = R * 128;
-  static constexpr int LPT = BYTES / (1024 * 4);   // DMA instructions per thread per k-step
+  static constexpr int LPT = BYTES / (1024 * NW);   // DMA instructions per thread per k-step
   static_assert(LPT >= 1, "tile too small");
   uint32_t voff[LPT];
 
@@ -197,17 +217,22 @@ struct KcTile {
       voff[i] = row < rows_valid ? (uint32_t)(row * ld * T::ESZ + chunk_of(wave, lane, i) * 16) : kOOB;
     }
   }
-  // DMA i of this thread's k-step share; only chunks meeting the contraction
-  // range [lo, hi) (relative to the k-step; workgroup-uniform) are fetched.
-  // (edge: the k-step is cut by the range; otherwise every chunk is inside.)
-  __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int lane, int lo, int hi,
-                               bool edge) const {
+  // Source offset of transfer i of this thread's k-step share; only chunks
+  // meeting the contraction range [lo, hi) (relative to the k-step;
+  // workgroup-uniform) are fetched.  (edge: the k-step is cut by the range;
+  // otherwise every chunk is inside.)  The transfer lands at LDS byte
+  // (wave * LPT + i) * 1024 + 16 * lane of the tile.
+  __device__ inline uint32_t offset(int i, int wave, int lane, int lo, int hi, bool edge) const {
     uint32_t vo = voff[i];
     if (edge) {
       const int c = chunk_of(wave, lane, i) * T::EPC;
       vo = ((c + T::EPC > lo) & (c < hi)) ? vo : kOOB;
     }
-    dma16<POL>(r, tile + (wave * LPT + i) * 1024, vo);
+    return vo;
+  }
+  __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int lane, int lo, int hi,
+                               bool edge, bool nt) const {
+    dma_pol<POL>(r, tile + (wave * LPT + i) * 1024, offset(i, wave, lane, lo, hi, edge), nt);
   }
 };
 
@@ -215,12 +240,12 @@ struct KcTile {
 // rows of R values in their natural layout, R * 2 bytes per row, 16-byte
 // chunk c of row r at slot c ^ (4 * (r % 4)); the MFMA fragments are read
 // with the transposing LDS load, see frag_nt.
-template <int R, int POL>
+template <int R, int POL, int NW>
 struct NtTile {
   static constexpr int BYTES = 64 * R * 2;
   static constexpr int CPR = R / 8;        // chunks per row
   static constexpr int RPB = 64 / CPR;     // rows per 1 KB block
-  static constexpr int LPT = BYTES / (1024 * 4);
+  static constexpr int LPT = BYTES / (1024 * NW);
   static_assert(CPR >= 16 && CPR <= 64 && LPT >= 1, "tile shape");
   uint32_t voff[LPT];
 
@@ -235,8 +260,9 @@ struct NtTile {
       voff[i] = ch * 8 < cols_valid ? (uint32_t)((row * ld + ch * 8) * 2) : kOOB;
     }
   }
-  __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int, int, int, bool) const {
-    dma16<POL>(r, tile + (wave * LPT + i) * 1024, voff[i]);
+  __device__ inline uint32_t offset(int i, int, int, int, int, bool) const { return voff[i]; }
+  __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int, int, int, bool, bool nt) const {
+    dma_pol<POL>(r, tile + (wave * LPT + i) * 1024, voff[i], nt);
   }
 };
 
@@ -254,7 +280,7 @@ __device__ inline bf16x8 frag_nt(const uint8_t* tile, int ks, int mn0, int lane)
   const int G = lane >> 4, sl = lane & 15;
   const int k0 = ks * 16 + 8 * (G >> 1) + (sl >> 2);
   const int col = mn0 + 16 * (G & 1) + 4 * (sl & 3);
-  const int a0 = NtTile<R, 0>::lds_addr(k0, col);
+  const int a0 = NtTile<R, 0, 4>::lds_addr(k0, col);
   const int a1 = a0 + 4 * R * 2;   // row k0 + 4: same swizzle
   auto p = (__attribute__((address_space(3))) uint8_t*)tile;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + a0));
@@ -262,9 +288,9 @@ __device__ inline bf16x8 frag_nt(const uint8_t* tile, int ks, int mn0, int lane)
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int R, int ELEM, bool KC, int POL> struct TileSel;
-template <int R, int ELEM, int POL> struct TileSel<R, ELEM, true, POL> { using type = KcTile<R, ELEM, POL>; };
-template <int R, int POL> struct TileSel<R, EL_BF16, false, POL> { using type = NtTile<R, POL>; };
+template <int R, int ELEM, bool KC, int POL, int NW> struct TileSel;
+template <int R, int ELEM, int POL, int NW> struct TileSel<R, ELEM, true, POL, NW> { using type = KcTile<R, ELEM, POL, NW>; };
+template <int R, int POL, int NW> struct TileSel<R, EL_BF16, false, POL, NW> { using type = NtTile<R, POL, NW>; };
 
 // Bytes [lo, hi) of a 4-byte word kept, the rest cleared (lo, hi relative to
 // the word; any values).
@@ -296,6 +322,7 @@ struct Item {
   int64_t c_lo, c_hi, c_begin;
   int nsteps;       // k-steps (>= 1; an empty dW group runs one all-zero step)
   int mt;           // FIXED_M: row tile (work-list entry) of the item
+  bool b_stream;    // B is read by this item only (its expert has one row tile)
 };
 
 // Work item w.  Work-item counts stay below 2^31 (the host bounds every
@@ -337,6 +364,7 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
     it.c_begin = 0;
     it.nsteps = (int)cdiv(a.Kc, BK);
     it.mt = t0 + ml;
+    it.b_stream = mtg <= 1;
     (void)prev;
   } else {
     const uint32_t per = (uint32_t)m_tiles_dk * (uint32_t)n_tiles;
@@ -360,6 +388,7 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
     const int64_t span = it.c_hi - it.c_begin;
     it.nsteps = span > 0 ? (int)cdiv(span, BK) : 1;
     it.mt = (int)mt;
+    it.b_stream = false;
   }
   it.n0 = nt * BN;
   it.n_valid = a.Nout - it.n0;
@@ -369,35 +398,41 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
-__global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
+template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI, int NW, bool REG>
+__global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   using T = ElemTraits<ELEM>;
   constexpr int BK = T::BK;
-  constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile (2 x 2 waves)
+  constexpr int kThreads = NW * 64;
+  constexpr int WGN = NW / 2;               // waves: 2 along M x NW / 2 along N
+  constexpr int WM = BM / 2, WN = BN / WGN; // wave sub-tile
   constexpr int TI = WM / 32, TJ = WN / 32;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int POL_A = kPolicyCached;
   constexpr int POL_B = (KIND == FIXED_M && ELEM == EL_BF16) ? kPolicyStream : kPolicyCached;
-  using ATile = typename TileSel<BM, ELEM, A_KC, POL_A>::type;
-  using BTile = typename TileSel<BN, ELEM, B_KC, POL_B>::type;
+  using ATile = typename TileSel<BM, ELEM, A_KC, POL_A, NW>::type;
+  using BTile = typename TileSel<BN, ELEM, B_KC, POL_B, NW>::type;
   static_assert(ATile::BYTES == A_BYTES && BTile::BYTES == B_BYTES, "tile bytes");
   constexpr int LPS = ATile::LPT + BTile::LPT;   // DMA instructions per thread per k-step
   // Epilogue staging in the stage just consumed: each wave stages its own
-  // WM x WN sub-tile, ECW columns at a time, in a private region (bf16 rows
-  // of ECW + 8 elements), so the waves need no barrier among themselves;
-  // then (fp8) the reciprocal row and column scales of the tile.
+  // WM x WN sub-tile, an ERW x ECW block at a time, in a private region
+  // (bf16 rows of ECW + 8 elements), so the waves need no barrier among
+  // themselves; then (fp8) the reciprocal row and column scales of the tile.
+  // Whole sub-tile rows (ECW = WN) are preferred over whole columns: the
+  // stores then write full 128-byte lines.
   constexpr int SC_BYTES = (EPI == EPI_NONE) ? 0 : (BM + BN) * 4;
-  constexpr int ECW = (4 * WM * (WN + 8) * 2 + SC_BYTES <= STAGE)     ? WN
-                      : (4 * WM * (WN / 2 + 8) * 2 + SC_BYTES <= STAGE) ? WN / 2
-                                                                        : WN / 4;
+  constexpr bool FIT_ALL = NW * WM * (WN + 8) * 2 + SC_BYTES <= STAGE;
+  constexpr bool FIT_ROWS = NW * 32 * (WN + 8) * 2 + SC_BYTES <= STAGE;
+  constexpr int ERW = FIT_ALL ? WM : 32;
+  constexpr int ECW = (FIT_ALL || FIT_ROWS) ? WN : (NW * 32 * (WN / 2 + 8) * 2 + SC_BYTES <= STAGE) ? WN / 2 : WN / 4;
   constexpr int SROW = ECW + 8;
-  constexpr int WREG = WM * SROW * 2;            // bytes of one wave's staging region
-  constexpr int PASSES = WN / ECW;
-  constexpr int SPP = WM * ECW / 8 / kWave;      // 16-byte stores per lane per pass
+  constexpr int WREG = ERW * SROW * 2;           // bytes of one wave's staging region
+  constexpr int CPASS = WN / ECW;                // column blocks
+  constexpr int PASSES = (WM / ERW) * CPASS;
+  constexpr int SPP = ERW * ECW / 8 / kWave;     // 16-byte stores per lane per pass
   constexpr int NST = PASSES * SPP;              // per epilogue
-  static_assert(ECW >= 32 && ECW % 32 == 0 && 4 * WREG + SC_BYTES <= STAGE, "staging does not fit");
-  static_assert(SPP >= 1 && (WM * ECW / 8) % kWave == 0, "store split");
+  static_assert(ECW >= 32 && ECW % 32 == 0 && NW * WREG + SC_BYTES <= STAGE, "staging does not fit");
+  static_assert(SPP >= 1 && (ERW * ECW / 8) % kWave == 0, "store split");
   static_assert((NS - 2) * LPS + NST <= 63, "vmcnt range");
   static_assert(NS >= 2, "at least double buffering");
   static_assert(KIND == DYNAMIC_K || (int64_t)BM * BN * 4 <= kSkPartBytes, "partial tile size");
@@ -414,7 +449,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uni(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // prologue: the group table (offsets, tiles or dynamic-K order) in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
@@ -449,12 +484,14 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   const int64_t D = (KIND != FIXED_M || whole) ? items : (full >= 2 ? (full - 1) * G : 0);
   const int64_t L = (items - D) * S;
   const int64_t GS = L < G ? L : G;
-  // Whole items [0, D): XCD x owns the contiguous eighth [c0, c1) and its
-  // G / 8 workgroups take it round-robin, so each XCD's L2 serves one run
-  // of consecutive items (for the balanced dW, one expert per XCD) and a
-  // partial last round is spread evenly over the XCDs.  dp_item(k) is the
-  // workgroup's k-th whole item, or -1.
-  const bool xcd_split = (G & 7) == 0;
+  // Fixed-M whole items [0, D) (all of equal length): XCD x owns the
+  // contiguous eighth [c0, c1) and its G / 8 workgroups take it round-robin,
+  // so each XCD's L2 serves one run of consecutive items and a partial last
+  // round is spread evenly over the XCDs.  Dynamic-K items differ in length
+  // (groups come largest first) and are dealt round-robin over the whole
+  // grid, longest first.  dp_item(k) is the workgroup's k-th whole item, or
+  // -1.
+  const bool xcd_split = KIND == FIXED_M && (G & 7) == 0;
   const int64_t gx = xcd_split ? (G >> 3) : G;
   const int64_t dj = xcd_split ? (int64_t)(blockIdx.x >> 3) : b;
   const int64_t c0 = xcd_split ? ((int64_t)(blockIdx.x & 7) * D) >> 3 : 0;
@@ -535,8 +572,9 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   struct LoadCtx {
     i32x4 ra, rb;
     int lo, hi;
-    bool edge;
+    bool edge, nt;
     uint32_t st;
+    uint8_t* stp;   // the target stage (register path)
   };
   auto prepare_loads = [&](uint8_t* st) -> LoadCtx {
     const Item& it = li;
@@ -561,13 +599,38 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     x.lo = lo64 < -BK ? -BK : (lo64 > 2 * BK ? 2 * BK : (int)lo64);
     x.hi = hi64 < -BK ? -BK : (hi64 > 2 * BK ? 2 * BK : (int)hi64);
     x.edge = x.lo > 0 || x.hi < BK;
+    x.nt = it.b_stream;
     x.st = lds_address(st);
+    x.stp = st;
     return x;
   };
   constexpr int LA = ATile::LPT;
+  // Register path (REG): the same transfers as buffer loads into VGPRs,
+  // written to the stage by ds_write_b128 once the k-step's MFMAs are issued
+  // (the address unit moves ordinary loads faster than LDS-DMA ones; the
+  // price is LPS x 4 VGPRs and a lookahead of one k-step).
+  i32x4 rbuf[REG ? LPS : 1];
   auto issue_one = [&](const LoadCtx& x, int q) {
-    if (q < LA) at.issue(q, x.ra, x.st, wave, lane, x.lo, x.hi, x.edge);
-    else bt.issue(q - LA, x.rb, x.st + A_BYTES, wave, lane, x.lo, x.hi, x.edge);
+    if constexpr (REG) {
+      const bool isa = q < LA;
+      const uint32_t vo = isa ? at.offset(q, wave, lane, x.lo, x.hi, x.edge)
+                              : bt.offset(q - LA, wave, lane, x.lo, x.hi, x.edge);
+      const __amdgpu_buffer_rsrc_t r = rsrc_of(isa ? x.ra : x.rb);
+      if (!isa && POL_B == kPolicyStream && x.nt) rbuf[q] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, 0, kPolicyStream);
+      else rbuf[q] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, 0, kPolicyCached);
+    } else {
+      if (q < LA) at.issue(q, x.ra, x.st, wave, lane, x.lo, x.hi, x.edge, false);
+      else bt.issue(q - LA, x.rb, x.st + A_BYTES, wave, lane, x.lo, x.hi, x.edge, x.nt);
+    }
+  };
+  auto write_stage = [&](const LoadCtx& x) {   // register path: the loads of x into their stage
+    if constexpr (REG) {
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) {
+        const int blk = q < LA ? wave * LA + q : A_BYTES / 1024 + wave * (LPS - LA) + (q - LA);
+        *reinterpret_cast<i32x4*>(x.stp + blk * 1024 + lane * 16) = rbuf[q];
+      }
+    }
   };
   // Scale DMAs for the compute cursor's tile (EPI != NONE): BM row scales,
   // then BN column scales, 64 floats per instruction; instruction k goes to
@@ -581,8 +644,8 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       const i32x4 rc = make_rsrc_words(cols, (int64_t)it.n_valid * 4);
       const uint32_t base = lds_address(reinterpret_cast<uint8_t*>(scl));
 #pragma unroll
-      for (int k = 0; k < (NSC + 3) / 4; ++k) {
-        const int ins = wave + 4 * k;
+      for (int k = 0; k < (NSC + NW - 1) / NW; ++k) {
+        const int ins = wave + NW * k;
         if (ins < NSC) {
           const bool is_row = ins < BM / 64;
           const int first = is_row ? ins * 64 : ins * 64 - BM;
@@ -623,8 +686,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   // acc[i][j] holds the transposed 32 x 32 block: lane l has output row
   // wm * WM + 32 i + l % 32 and columns wn * WN + 32 j + 8 q + 4 (l / 32) + r
   // in element 4 q + r.
-  constexpr int QPS = LPS / T::KSUB;   // transfers issued per MFMA sub-step
-  static_assert(LPS % T::KSUB == 0, "transfers per sub-step");
+  // transfers issued in MFMA sub-step ks: [ks * LPS / KSUB, (ks + 1) * LPS / KSUB)
   auto compute = [&](const uint8_t* As, const LoadCtx& lx) {
     const uint8_t* Bs = As + A_BYTES;
     // The fragment addresses below are loop-invariant; hoisted, they would
@@ -669,7 +731,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
           for (int j = 0; j < TJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int q = ks * QPS; q < (ks + 1) * QPS; ++q) issue_one(lx, q);
+        for (int q = ks * LPS / T::KSUB; q < (ks + 1) * LPS / T::KSUB; ++q) issue_one(lx, q);
       } else {
         i32x8 af[TI], bfr[TJ];
         const int ch = 4 * ks + 2 * (lane >> 5);
@@ -697,7 +759,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0,
                                                                          127, 0, 127);
 #pragma unroll
-        for (int q = ks * QPS; q < (ks + 1) * QPS; ++q) issue_one(lx, q);
+        for (int q = ks * LPS / T::KSUB; q < (ks + 1) * LPS / T::KSUB; ++q) issue_one(lx, q);
       }
     }
   };
@@ -708,7 +770,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
   // out of range).
   auto epilogue = [&](uint8_t* st, const Item& it) {
     uint16_t* stg = reinterpret_cast<uint16_t*>(st + wave * WREG);
-    float* rsc = reinterpret_cast<float*>(st + 4 * WREG);   // [BM] 1 / row scale
+    float* rsc = reinterpret_cast<float*>(st + NW * WREG);  // [BM] 1 / row scale
     float* csc = rsc + BM;                                  // [BN] 1 / column scale
     if constexpr (EPI != EPI_NONE) {
       // every wave is done reading st, and the scale DMAs issued before this
@@ -729,11 +791,13 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     const int r0 = wm * WM, c0 = wn * WN;   // the wave's sub-tile
 #pragma unroll
     for (int e = 0; e < PASSES; ++e) {
+      const int er = e / CPASS, ec = e % CPASS;   // row block, column block of the pass
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        if (32 * j / ECW != e) continue;
+        if (32 * j / ECW != ec) continue;
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
+          if (32 * i / ERW != er) continue;
           const int rw = 32 * i + (lane & 31);
           float rs = 1.f;
           if constexpr (EPI != EPI_NONE) rs = rsc[r0 + rw];
@@ -752,7 +816,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
             uint2 pk;
             pk.x = pack_bf16x2_hw(v0, v1);
             pk.y = pack_bf16x2_hw(v2, v3);
-            *reinterpret_cast<uint2*>(stg + rw * SROW + (cw - e * ECW)) = pk;
+            *reinterpret_cast<uint2*>(stg + (rw - er * ERW) * SROW + (cw - ec * ECW)) = pk;
           }
         }
       }
@@ -764,7 +828,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
         const int q = lane + k * kWave;
         const int rw = q / (ECW / 8), ch = q % (ECW / 8);
         const uint4 v = *reinterpret_cast<const uint4*>(stg + rw * SROW + ch * 8);
-        const int row = r0 + rw, col = c0 + e * ECW + ch * 8;
+        const int row = r0 + er * ERW + rw, col = c0 + ec * ECW + ch * 8;
         const uint32_t vo = (row < it.m_valid && col < it.n_valid) ? (uint32_t)((row * a.c_ld + col) * 2) : kOOB;
         i32x4 d;
         d[0] = (int)v.x;
@@ -890,6 +954,7 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
     const LoadCtx lx = prepare_loads(smem + u * STAGE);
 #pragma unroll
     for (int q = 0; q < LPS; ++q) issue_one(lx, q);
+    write_stage(lx);
     advance_load();
   }
   int stage = 0;            // stage holding the compute cursor's k-step
@@ -902,13 +967,15 @@ __global__ void __launch_bounds__(kThreads) gmm_kernel(GemmArgs a) {
       // this thread's DMA for the current stage has landed (only the next
       // NS - 2 stages' loads and the last epilogue's stores may be in
       // flight), and every wave is past the previous k-step
-      if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
+      if constexpr (REG) lds_sync();   // the stage's ds_writes are done in every wave
+      else if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
       else wait_vm_sync<(NS - 2) * LPS>();
       epi_prev = false;
       if (EPI != EPI_NONE && cs + 1 == cend) issue_scales(ci);
       const LoadCtx lx = prepare_loads(smem + lstage * STAGE);
       lstage = lstage + 1 == NS ? 0 : lstage + 1;
       compute(smem + stage * STAGE, lx);   // also issues the loads of lx
+      write_stage(lx);
       advance_load();                      // only now: setup() replaces the tiles' offsets
       last_stage = stage;
       stage = stage + 1 == NS ? 0 : stage + 1;
@@ -962,10 +1029,12 @@ int device_cu_count() {
   return cached[dev];
 }
 
+constexpr int kGemmWaves = 8;   // waves per workgroup
+
 int gemm_tile_m(int kind) { (void)kind; return 128; }
 int gemm_tile_n(int kind) { (void)kind; return 256; }
 
-template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI>
+template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI, int NW, bool REG = false>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
   using T = ElemTraits<ELEM>;
   // host bound on the work: fixed-M tiles cover at most
@@ -974,7 +1043,7 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
   if (KIND == FIXED_M) work = fixed_m_capacity(a.total_rows, a.E, BM) * cdiv(a.Nout, BN) * cdiv(a.Kc, T::BK);
   else work = (int64_t)a.E * cdiv(a.Mout, BM) * cdiv(a.Nout, BN);
   if (work <= 0) return hipSuccess;
-  auto kern = gmm_kernel<BM, BN, NS, A_KC, B_KC, KIND, ELEM, EPI>;
+  auto kern = gmm_kernel<BM, BN, NS, A_KC, B_KC, KIND, ELEM, EPI, NW, REG>;
   const int dyn = table_lds_bytes(a.E);
   static int configured = 0;   // dynamic LDS size already allowed
   if (configured == 0) {
@@ -986,7 +1055,7 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
   int64_t slots = device_cu_count();
   if (KIND == FIXED_M && slots > kSkMaxGrid) slots = kSkMaxGrid;
   const int grid = (int)(work < slots ? work : slots);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), (size_t)dyn, stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), (size_t)dyn, stream, a);
   return hipGetLastError();
 }
 
@@ -994,16 +1063,16 @@ hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t strea
   if (L.elem == EL_BF16) {
     if (L.kind == FIXED_M) {
       if (!L.a_kc) return hipErrorInvalidValue;
-      if (L.b_kc) return launch_one<128, 256, 3, true, true, FIXED_M, EL_BF16, EPI_NONE>(a, stream);
-      return launch_one<128, 256, 3, true, false, FIXED_M, EL_BF16, EPI_NONE>(a, stream);
+      if (L.b_kc) return launch_one<128, 256, 3, true, true, FIXED_M, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
+      return launch_one<128, 256, 3, true, false, FIXED_M, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
     }
-    if (!L.a_kc && !L.b_kc) return launch_one<128, 256, 3, false, false, DYNAMIC_K, EL_BF16, EPI_NONE>(a, stream);
+    if (!L.a_kc && !L.b_kc) return launch_one<128, 256, 3, false, false, DYNAMIC_K, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
     return hipErrorInvalidValue;
   }
   if (L.elem == EL_FP8) {
     if (!L.a_kc || !L.b_kc) return hipErrorInvalidValue;
-    if (L.kind == FIXED_M) return launch_one<128, 256, 3, true, true, FIXED_M, EL_FP8, EPI_ROW_COL>(a, stream);
-    return launch_one<128, 256, 3, true, true, DYNAMIC_K, EL_FP8, EPI_GROUP>(a, stream);
+    if (L.kind == FIXED_M) return launch_one<128, 256, 3, true, true, FIXED_M, EL_FP8, EPI_ROW_COL, kGemmWaves>(a, stream);
+    return launch_one<128, 256, 3, true, true, DYNAMIC_K, EL_FP8, EPI_GROUP, kGemmWaves>(a, stream);
   }
   return hipErrorInvalidValue;
 }
