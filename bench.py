@@ -160,9 +160,9 @@ def run_gpu(args, torch, mg):
     bytes_per = algorithmic_bytes(E, M, K, N)
     dom = max(avg_ms, key=avg_ms.get)
     achieved = bytes_per[dom] / (avg_ms[dom] * 1e-3) / 1e9
-    kernel_names = {"fwd": "gmm_kernel<128,256,3,true,false,FIXED_M,bf16> (forward: X rows k-contiguous, W [K,N])",
-                    "dx": "gmm_kernel<128,256,3,true,true,FIXED_M,bf16> (dX: dY rows, W rows contraction-contiguous)",
-                    "dw": "gmm_kernel<128,256,3,false,false,DYNAMIC_K,bf16> (dW: X and dY row-contiguous)"}
+    kernel_names = {"fwd": "gmm_kernel<128,256,3,true,false,FIXED_M,bf16,8 waves> (forward: X rows k-contiguous, W [K,N])",
+                    "dx": "gmm_kernel<128,256,3,true,true,FIXED_M,bf16,8 waves> (dX: dY rows, W rows contraction-contiguous)",
+                    "dw": "gmm_kernel<128,256,3,false,false,DYNAMIC_K,bf16,8 waves> (dW: X and dY row-contiguous)"}
     roofline = {
         "bound": "hbm",
         "kernel": kernel_names[dom],

@@ -84,12 +84,6 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, kBufFlags);
 }
 
-// Descriptor words (below) as the compiler's buffer resource type.
-__device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const i32x4& w) {
-  const uint64_t base = (uint64_t)(uint32_t)w[0] | ((uint64_t)(uint32_t)(w[1] & 0xFFFF) << 32);
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, w[2], kBufFlags);
-}
-
 // The same descriptor as four words, for the LDS-DMA asm below: base address
 // (48 bits, stride 0), size in bytes, raw-buffer flags.
 __device__ inline i32x4 make_rsrc_words(const void* base, int64_t bytes) {
@@ -260,7 +254,6 @@ struct NtTile {
       voff[i] = ch * 8 < cols_valid ? (uint32_t)((row * ld + ch * 8) * 2) : kOOB;
     }
   }
-  __device__ inline uint32_t offset(int i, int, int, int, int, bool) const { return voff[i]; }
   __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int, int, int, bool, bool nt) const {
     dma_pol<POL>(r, tile + (wave * LPT + i) * 1024, voff[i], nt);
   }
@@ -398,7 +391,7 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI, int NW, bool REG>
+template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI, int NW>
 __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   using T = ElemTraits<ELEM>;
   constexpr int BK = T::BK;
@@ -574,7 +567,6 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     int lo, hi;
     bool edge, nt;
     uint32_t st;
-    uint8_t* stp;   // the target stage (register path)
   };
   auto prepare_loads = [&](uint8_t* st) -> LoadCtx {
     const Item& it = li;
@@ -601,36 +593,12 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     x.edge = x.lo > 0 || x.hi < BK;
     x.nt = it.b_stream;
     x.st = lds_address(st);
-    x.stp = st;
     return x;
   };
   constexpr int LA = ATile::LPT;
-  // Register path (REG): the same transfers as buffer loads into VGPRs,
-  // written to the stage by ds_write_b128 once the k-step's MFMAs are issued
-  // (the address unit moves ordinary loads faster than LDS-DMA ones; the
-  // price is LPS x 4 VGPRs and a lookahead of one k-step).
-  i32x4 rbuf[REG ? LPS : 1];
   auto issue_one = [&](const LoadCtx& x, int q) {
-    if constexpr (REG) {
-      const bool isa = q < LA;
-      const uint32_t vo = isa ? at.offset(q, wave, lane, x.lo, x.hi, x.edge)
-                              : bt.offset(q - LA, wave, lane, x.lo, x.hi, x.edge);
-      const __amdgpu_buffer_rsrc_t r = rsrc_of(isa ? x.ra : x.rb);
-      if (!isa && POL_B == kPolicyStream && x.nt) rbuf[q] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, 0, kPolicyStream);
-      else rbuf[q] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, 0, kPolicyCached);
-    } else {
-      if (q < LA) at.issue(q, x.ra, x.st, wave, lane, x.lo, x.hi, x.edge, false);
-      else bt.issue(q - LA, x.rb, x.st + A_BYTES, wave, lane, x.lo, x.hi, x.edge, x.nt);
-    }
-  };
-  auto write_stage = [&](const LoadCtx& x) {   // register path: the loads of x into their stage
-    if constexpr (REG) {
-#pragma unroll
-      for (int q = 0; q < LPS; ++q) {
-        const int blk = q < LA ? wave * LA + q : A_BYTES / 1024 + wave * (LPS - LA) + (q - LA);
-        *reinterpret_cast<i32x4*>(x.stp + blk * 1024 + lane * 16) = rbuf[q];
-      }
-    }
+    if (q < LA) at.issue(q, x.ra, x.st, wave, lane, x.lo, x.hi, x.edge, false);
+    else bt.issue(q - LA, x.rb, x.st + A_BYTES, wave, lane, x.lo, x.hi, x.edge, x.nt);
   };
   // Scale DMAs for the compute cursor's tile (EPI != NONE): BM row scales,
   // then BN column scales, 64 floats per instruction; instruction k goes to
@@ -954,7 +922,6 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     const LoadCtx lx = prepare_loads(smem + u * STAGE);
 #pragma unroll
     for (int q = 0; q < LPS; ++q) issue_one(lx, q);
-    write_stage(lx);
     advance_load();
   }
   int stage = 0;            // stage holding the compute cursor's k-step
@@ -967,15 +934,13 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
       // this thread's DMA for the current stage has landed (only the next
       // NS - 2 stages' loads and the last epilogue's stores may be in
       // flight), and every wave is past the previous k-step
-      if constexpr (REG) lds_sync();   // the stage's ds_writes are done in every wave
-      else if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
+      if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
       else wait_vm_sync<(NS - 2) * LPS>();
       epi_prev = false;
       if (EPI != EPI_NONE && cs + 1 == cend) issue_scales(ci);
       const LoadCtx lx = prepare_loads(smem + lstage * STAGE);
       lstage = lstage + 1 == NS ? 0 : lstage + 1;
       compute(smem + stage * STAGE, lx);   // also issues the loads of lx
-      write_stage(lx);
       advance_load();                      // only now: setup() replaces the tiles' offsets
       last_stage = stage;
       stage = stage + 1 == NS ? 0 : stage + 1;
@@ -1034,7 +999,7 @@ constexpr int kGemmWaves = 8;   // waves per workgroup
 int gemm_tile_m(int kind) { (void)kind; return 128; }
 int gemm_tile_n(int kind) { (void)kind; return 256; }
 
-template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI, int NW, bool REG = false>
+template <int BM, int BN, int NS, bool A_KC, bool B_KC, int KIND, int ELEM, int EPI, int NW>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
   using T = ElemTraits<ELEM>;
   // host bound on the work: fixed-M tiles cover at most
@@ -1043,7 +1008,7 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
   if (KIND == FIXED_M) work = fixed_m_capacity(a.total_rows, a.E, BM) * cdiv(a.Nout, BN) * cdiv(a.Kc, T::BK);
   else work = (int64_t)a.E * cdiv(a.Mout, BM) * cdiv(a.Nout, BN);
   if (work <= 0) return hipSuccess;
-  auto kern = gmm_kernel<BM, BN, NS, A_KC, B_KC, KIND, ELEM, EPI, NW, REG>;
+  auto kern = gmm_kernel<BM, BN, NS, A_KC, B_KC, KIND, ELEM, EPI, NW>;
   const int dyn = table_lds_bytes(a.E);
   static int configured = 0;   // dynamic LDS size already allowed
   if (configured == 0) {
