@@ -74,8 +74,68 @@ __device__ inline int64_t block_incl_scan64(int64_t x, int64_t* s_wave) {
 // thread) an error code: 0, 1 (a negative size) or 2 (sizes sum past
 // total_M).  want_order builds the dynamic-K ordering (O(E^2/256) work)
 // instead of the fixed-M tile starts.
+// Up to 64 groups, one per lane of wave 0: no workgroup-wide scans, one
+// barrier.  The running sum of the sizes saturates at total_M + 1 (every
+// partial sum then fits 32 bits, and min(sum, total_M) and "sum > total_M"
+// are unchanged), so the results equal the general path's.
+__device__ inline int build_group_table_wave(const int32_t* __restrict__ sizes, int E, int64_t total_M, int bm,
+                                             bool want_order, GroupTable t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x < kWave) {
+    const bool mine = lane < E;
+    const int32_t raw = mine ? sizes[lane] : 0;
+    const uint32_t cap = (uint32_t)(total_M + 1);   // total_M < 2^31
+    const uint32_t v0 = raw > 0 ? ((uint32_t)raw < cap ? (uint32_t)raw : cap) : 0u;
+    uint32_t incl = v0;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)incl, d, kWave);
+      if (lane >= d) {
+        const uint64_t sum = (uint64_t)incl + o;
+        incl = sum < cap ? (uint32_t)sum : cap;
+      }
+    }
+    const uint32_t excl = (uint32_t)__shfl_up((int)incl, 1, kWave);
+    const uint32_t tm = (uint32_t)total_M;
+    const uint32_t a = lane == 0 ? 0u : (excl < tm ? excl : tm);
+    const uint32_t b = incl < tm ? incl : tm;
+    const int32_t eff = mine ? (int32_t)(b - a) : 0;
+    const int32_t tiles = (int32_t)(((uint32_t)eff + (uint32_t)bm - 1u) / (uint32_t)bm);
+    int32_t tincl = tiles;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t o = __shfl_up(tincl, d, kWave);
+      if (lane >= d) tincl += o;
+    }
+    if (mine) {
+      t.off[lane] = (int32_t)a;
+      t.eff[lane] = eff;
+      if (!want_order) t.tstart[lane] = tincl - tiles;
+    }
+    const uint32_t total = (uint32_t)__shfl((int)incl, E - 1, kWave);
+    if (lane == E - 1) {
+      t.off[E] = (int32_t)(total < tm ? total : tm);
+      if (!want_order) t.tstart[E] = tincl;
+    }
+    const bool any_neg = __ballot(mine && raw < 0) != 0;
+    const bool any_over = total > tm;
+    if (want_order) {   // every lane of the wave takes part in the shuffles
+      int rank = 0;
+      for (int h = 0; h < E; ++h) {
+        const int32_t e = __shfl(eff, h, kWave);
+        rank += (e > eff) || (e == eff && h < lane);
+      }
+      if (mine) t.order[rank] = lane;
+    }
+    if (lane == 0) t.scratch[15] = any_neg ? 1 : any_over ? 2 : 0;
+  }
+  __syncthreads();
+  return (int)t.scratch[15];
+}
+
 __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E, int64_t total_M, int bm,
                                         bool want_order, GroupTable t) {
+  if (E <= kWave) return build_group_table_wave(sizes, E, total_M, bm, want_order, t);
   const int tid = threadIdx.x;
   const int per = (E + kTableThreads - 1) / kTableThreads;   // groups per thread (<= 4)
   const int g0 = tid * per;

@@ -24,6 +24,7 @@ def _gpu():
 @pytest.mark.parametrize("E,total,bm,seed", [
     (4, 37, 16, 0), (8, 1024, 128, 1), (128, 1, 32, 2), (128, 16, 32, 3), (128, 128, 32, 4),
     (64, 5000, 128, 5), (1024, 20000, 16, 6), (1, 0, 128, 7), (7, 3, 1, 8), (300, 777, 64, 9),
+    (65, 5000, 128, 10), (63, 999, 16, 11), (1, 77, 16, 12),
 ])
 def test_builder_fixed_m_bit_exact(E, total, bm, seed):
     sizes = wl.random_group_sizes(E, total, seed, zero_frac=0.5)
@@ -35,7 +36,8 @@ def test_builder_fixed_m_bit_exact(E, total, bm, seed):
     np.testing.assert_array_equal(host(ent)[:n_ref], ent_ref)
 
 
-@pytest.mark.parametrize("E,total,seed", [(8, 1024, 0), (64, 98304, 1), (1024, 3000, 2), (3, 0, 3), (128, 1, 4)])
+@pytest.mark.parametrize("E,total,seed", [(8, 1024, 0), (64, 98304, 1), (1024, 3000, 2), (3, 0, 3), (128, 1, 4),
+                                          (65, 4000, 5), (1, 9, 6)])
 def test_builder_dynamic_k_bit_exact(E, total, seed):
     sizes = wl.random_group_sizes(E, total, seed, zero_frac=0.3)
     sizes[: E // 3] = sizes[0]   # ties
@@ -53,7 +55,8 @@ def test_builder_flags_bad_sizes_without_writing_out_of_bounds():
     w = torch.zeros(E, K, N, dtype=torch.bfloat16, device="cuda")
     canary = torch.full((M + 64, N), 7.0, dtype=torch.bfloat16, device="cuda")
     y = canary[:M]
-    for sizes, code in [([10, -5, 20, 30], 1), ([40, 40, 0, 0], 2)]:
+    big = 2**31 - 1   # running sums past int32: the error is still "sum past total_M"
+    for sizes, code in [([10, -5, 20, 30], 1), ([40, 40, 0, 0], 2), ([big, big, big, 0], 2), ([big, -1, big, 3], 1)]:
         ws = mg.workspace(E, M)
         mg.workspace_clear(ws)
         mg.gmm_fwd(x, w, dev(np.array(sizes, np.int32)), out=y, ws=ws)
@@ -65,6 +68,25 @@ def test_builder_flags_bad_sizes_without_writing_out_of_bounds():
     mg.gmm_fwd(x, w, dev(np.array([10, 20, 30, 4], np.int32)), out=y, ws=ws)
     torch.cuda.synchronize()
     assert mg.workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("E", [64, 65])   # one-wave table build, and the workgroup-wide one
+def test_builder_flags_survive_int32_running_sums(E):
+    M, K, N = 64, 64, 64
+    big = 2**31 - 1
+    x = torch.zeros(M, K, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(E, K, N, dtype=torch.bfloat16, device="cuda")
+    canary = torch.full((M + 64, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = canary[:M]
+    over = [big, big, big] + [0] * (E - 3)
+    neg = [big, -1] + [1] * (E - 2)
+    for sizes, code in [(over, 2), (neg, 1)]:
+        ws = mg.workspace(E, M)
+        mg.workspace_clear(ws)
+        mg.gmm_fwd(x, w, dev(np.array(sizes, np.int32)), out=y, ws=ws)
+        torch.cuda.synchronize()
+        assert mg.workspace_error(ws) == code
+        assert (canary[M:] == 7.0).all()
 
 
 # --------------------------------------------------------------------------
