@@ -200,8 +200,9 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w,
  *       nibble and k = 2i+1 in its high nibble
  *   sw  bf16 [E][K/128][N], one scale per 128-long chunk of K
  *   y   bf16 [total_M, N]
- * K must be a multiple of 128 and N a multiple of 8.  Only non-empty
- * groups are visited. */
+ * K must be a multiple of 128 and N a multiple of 8; K*N and
+ * total_M*max(K, N) must stay below 2^31 (MG_EUNSUPPORTED otherwise).  Only
+ * non-empty groups are visited. */
 int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4,
                  const void* sw, const int32_t* group_sizes, int32_t E,
                  int64_t total_M, int32_t K, int32_t N, void* y, void* ws,

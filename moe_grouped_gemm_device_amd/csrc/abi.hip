@@ -388,6 +388,7 @@ int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4, const vo
   if (rc) return rc;
   if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
   if (K % 128 || N % 8) return fail(MG_EUNSUPPORTED, "K must be a multiple of 128 and N of 8");
+  if ((rc = check_extents(total_M, K, N, 1))) return rc;   // 32-bit offsets into X and one expert's weights
   if (total_M == 0) return ok();
   if (!xq || !sx || !w4 || !sw || !y) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(xq) || !aligned16(w4)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");

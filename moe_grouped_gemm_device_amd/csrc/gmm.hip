@@ -10,20 +10,21 @@
 // are visited (FBGEMM PR "F8I4 Grouped Gemm Optimization for Sparse M").
 //
 // Design (CDNA4):
-//  * 256 threads = 4 waves in a 2 x 2 arrangement; a wave owns a
-//    (BM/2) x (BN/2) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16,
-//    or v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales for e4m3).
-//    Output tiles are 128 x 256 (a 256 x 256 dW tile would not fit its
-//    accumulators beside the rest without spills): for
-//    these skinny products a CU's vector-memory path (its L1 keeps a bounded
-//    number of line requests in flight) limits throughput before HBM does,
-//    and every re-read of the shared operand costs as much as a fresh weight
-//    byte, so wider tiles mean fewer bytes per CU.
+//  * 512 threads = 8 waves in a 2 (M) x 4 (N) arrangement over a 128 x 256
+//    output tile; a wave owns a 64 x 64 block of 32 x 32 MFMA tiles
+//    (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4 with
+//    unit block scales for e4m3): 64 fp32 accumulators per lane, so every
+//    instantiation fits in the 256 VGPRs a wave gets at two waves per SIMD.
+//    Eight waves rather than four: a CU's address unit turns LDS-DMA
+//    instructions into memory requests at a bounded rate per wave, and with
+//    four waves that rate, not HBM, capped the L2-resident operand streams.
+//    (A 256 x 256 tile, which would halve operand traffic per flop, does not
+//    fit its accumulators beside the rest without spills at either width.)
 //  * Operand tiles move global -> LDS by the buffer unit's LDS-DMA path
 //    (buffer_load_dwordx4 ... lds, 16 bytes per lane), never through VGPRs.
-//    NS k-steps are in flight in LDS; with no register staging the large
-//    accumulator blocks fit.  Synchronisation is explicit: a vmcnt wait sized
-//    to the loads issued after the stage being consumed, then s_barrier.
+//    NS k-steps are in flight in LDS.  Synchronisation is explicit: a vmcnt
+//    wait sized to the loads issued after the stage being consumed, then
+//    s_barrier.
 //  * Operands whose contraction index is contiguous (X rows, W as [N, K],
 //    fp8 column-major codes) use 128-byte LDS rows with 16-byte chunks
 //    XOR-swizzled by row, read by ds_read_b128; operands whose contraction
@@ -34,17 +35,21 @@
 //    swizzled.
 //  * The MFMAs take their operands swapped (C^T blocks), so a lane holds four
 //    consecutive output columns of one row: the epilogue writes 8-byte runs
-//    into an LDS staging area (the stage just consumed) and 16-byte
-//    coalesced non-temporal buffer stores go to HBM.
-//  * Fixed-M products are balanced stream-K style: the (tile, k-step)
-//    positions of all work items form one sequence cut into G equal ranges,
-//    one per workgroup.  A tile split between workgroups is summed in a fixed
+//    into an LDS staging area (the stage just consumed), a wave's 32 rows at
+//    a time, and 16-byte non-temporal buffer stores write whole 128-byte
+//    line segments to HBM.
+//  * Fixed-M products run whole tiles, one contiguous run of tiles per XCD,
+//    and balance the last round or two stream-K style: the (tile, k-step)
+//    positions left form one sequence cut into equal ranges, one per
+//    workgroup.  A tile split between workgroups is summed in a fixed
 //    order: each piece stores its fp32 partial tile in the workspace and
 //    bumps the tile's counter; the piece that arrives last adds all pieces in
 //    workgroup order, runs the epilogue and resets the counter.  Nobody waits
-//    for anybody, so the persistent grid cannot deadlock.
-//  * dW work items are whole tiles dealt round-robin; loads run ahead across
-//    item boundaries.
+//    for anybody, so the persistent grid cannot deadlock.  When whole tiles
+//    alone keep most of the grid busy, no tile is split (re-reading a split
+//    tile's partials costs more than the idle workgroups).
+//  * dW work items are whole tiles dealt round-robin, largest groups first;
+//    loads run ahead across item boundaries.
 //  * Consecutive logical workgroups sit on one XCD (dispatch deals
 //    workgroups round-robin to the 8 XCDs), so neighbouring tiles share L2.
 #include "kernels.h"

@@ -108,6 +108,8 @@ def test_fp8_and_f8i4_reject_unsupported_alignment(lib):
                            _p(0x10000), need, None) == mg.MG_EUNSUPPORTED   # ld % 16
     assert lib.gmm_fwd_f8i4(_p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 4, 64, 192, 64, _p(FAKE),
                             _p(0x10000), need, None) == mg.MG_EUNSUPPORTED  # K % 128
+    assert lib.gmm_fwd_f8i4(_p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 4, 64, 65536, 65536, _p(FAKE),
+                            _p(0x10000), need, None) == mg.MG_EUNSUPPORTED  # one expert's weights past 2 GiB
     assert lib.gmm_bwd_fp8(None, None, None, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 4, 40, 64, 64,
                            None, _p(FAKE), _p(0x10000), lib.mg_workspace_bytes(4, 40),
                            None) == mg.MG_EUNSUPPORTED                   # dw needs total_M % 16
