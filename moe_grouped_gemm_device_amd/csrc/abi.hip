@@ -501,10 +501,6 @@ int moe_unpermute(const void* y_sorted, const int32_t* inv_pos, const float* top
                   int32_t top_k, int32_t hidden, void* out, mg_stream_t stream) {
   if (T < 0 || top_k < 1 || hidden < 1) return fail(MG_EINVAL, "T >= 0, top_k >= 1, hidden >= 1 required");
   if (hidden % 8) return fail(MG_EUNSUPPORTED, "hidden must be a multiple of 8");
-  if (T > 65535) {
-    // grid.y limit
-    return fail(MG_EUNSUPPORTED, "T must be <= 65535 per call");
-  }
   if (T == 0) return ok();
   if (!y_sorted || !inv_pos || !out) return fail(MG_EINVAL, "NULL tensor argument");
   if (!aligned16(y_sorted) || !aligned16(out)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");

@@ -204,34 +204,35 @@ __global__ void __launch_bounds__(256) unpermute_kernel(const uint16_t* __restri
                                                        const int32_t* __restrict__ inv,
                                                        const float* __restrict__ w, int64_t T, int32_t k,
                                                        int32_t hidden, uint16_t* __restrict__ out) {
-  const int64_t t = blockIdx.y;
   const int ch = blockIdx.x * 256 + threadIdx.x;
   if (ch * 8 >= hidden) return;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const int32_t pos = inv[t * k + j];
-    if (pos < 0) continue;
-    const float wt = w ? w[t * k + j] : 1.f;
-    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)pos * hidden + ch * 8);
-    const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {   // grid rows stride over the tokens
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const int32_t pos = inv[t * k + j];
+      if (pos < 0) continue;
+      const float wt = w ? w[t * k + j] : 1.f;
+      const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)pos * hidden + ch * 8);
+      const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += wt * bf16_to_f32(ww[i] & 0xFFFFu);
-      acc[2 * i + 1] += wt * bf16_to_f32(ww[i] >> 16);
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wt * bf16_to_f32(ww[i] & 0xFFFFu);
+        acc[2 * i + 1] += wt * bf16_to_f32(ww[i] >> 16);
+      }
     }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(out + t * hidden + ch * 8) = o;
   }
-  uint4 o;
-  o.x = pack_bf16x2(acc[0], acc[1]);
-  o.y = pack_bf16x2(acc[2], acc[3]);
-  o.z = pack_bf16x2(acc[4], acc[5]);
-  o.w = pack_bf16x2(acc[6], acc[7]);
-  *reinterpret_cast<uint4*>(out + t * hidden + ch * 8) = o;
 }
 
 hipError_t launch_moe_unpermute(const uint16_t* y, const int32_t* inv, const float* w, int64_t T, int32_t k,
                                 int32_t hidden, uint16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  dim3 grid((unsigned)cdiv(hidden / 8, 256), (unsigned)T);
+  dim3 grid((unsigned)cdiv(hidden / 8, 256), (unsigned)(T < 65535 ? T : 65535));   // grid y is at most 65535
   hipLaunchKernelGGL(unpermute_kernel, grid, dim3(256), 0, stream, y, inv, w, T, k, hidden, out);
   return hipGetLastError();
 }

@@ -141,6 +141,26 @@ def test_bf16_gmm_matches_oracle(E, M, K, N, seed, trans_b):
         assert (dw[g] == 0).all()
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (1280, 5120, 256),   # 200 tiles on 256 workgroups: whole tiles, partial last round spread over the XCDs
+    (4352, 4096, 256),   # 544 tiles: one whole round, then stream-K over the last 288 tiles (2-3 pieces each)
+    (384, 1024, 1024),   # 12 tiles: stream-K only, 16 k-steps each cut into many pieces
+])
+def test_fixed_m_schedule_paths(M, N, K):
+    """One group, so the tile count is chosen exactly; forward and dX take
+    every schedule the fixed-M kernel has on a full 256-CU grid."""
+    sizes = np.array([M], np.int32)
+    X = wl.normal_bf16((M, K), 1.0, 7, wl.T_X)
+    W = wl.normal_bf16((1, K, N), 0.5, 7, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, 7, wl.T_DY)
+    x, w, dy, gs = bf16_dev(X), bf16_dev(W), bf16_dev(dY), dev(sizes)
+    y = mg.gmm_fwd(x, w, gs)
+    dx, _ = mg.gmm_bwd(dy, x, w, gs, need_dw=False)
+    torch.cuda.synchronize()
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(y)), oracle.gmm_fwd_bf16(X, W, sizes)) <= BF16_TOL
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(dx)), oracle.gmm_dx_bf16(dY, W, sizes)) <= BF16_TOL
+
+
 def test_rows_past_the_groups_are_untouched():
     E, M, K, N = 4, 200, 64, 64
     sizes = np.array([30, 0, 50, 20], np.int32)     # sum 100 < 200

@@ -85,6 +85,21 @@ def test_silu_mul_and_unpermute():
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
 
 
+def test_unpermute_past_one_grid_row_per_token():
+    """More tokens than the 65535 workgroup rows of one launch: the rows
+    stride over the tokens."""
+    T, k, H = 70001, 1, 16
+    rng = np.random.default_rng(3)
+    inv = rng.permutation(T).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    y = wl.normal_bf16((T, H), 1.0, 3, wl.T_DY)
+    out = mg.moe_unpermute(bf16_dev(y), dev(inv), dev(w), T, k)
+    torch.cuda.synchronize()
+    ref = oracle.unpermute(oracle.bf16_to_f64(y), inv, w, T, k)
+    got = oracle.bf16_to_f64(bf16_host(out))
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
+
+
 @pytest.mark.parametrize("T,bm", [(1, 16), (64, 16), (200, 32)])
 def test_fused_moe_small_matches_oracle(T, bm):
     E, k, H, I = 8, 2, 256, 128
