@@ -183,6 +183,8 @@ __device__ inline uint32_t pack_bf16x2_hw(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+template <bool B> struct BoolConst { static constexpr bool value = B; };
+
 __device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ inline int64_t uni64(int64_t v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
@@ -486,19 +488,25 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // contiguous eighth [c0, c1) and its G / 8 workgroups take it round-robin,
   // so each XCD's L2 serves one run of consecutive items and a partial last
   // round is spread evenly over the XCDs.  Dynamic-K items differ in length
-  // (groups come largest first) and are dealt round-robin over the whole
-  // grid, longest first.  dp_item(k) is the workgroup's k-th whole item, or
-  // -1.
+  // (groups come largest first) and are dealt over the whole grid, longest
+  // first, in snake order.  dp_item(k) is the workgroup's k-th whole item,
+  // or -1.
   const bool xcd_split = KIND == FIXED_M && (G & 7) == 0;
   const int64_t gx = xcd_split ? (G >> 3) : G;
   const int64_t dj = xcd_split ? (int64_t)(blockIdx.x >> 3) : b;
   const int64_t c0 = xcd_split ? ((int64_t)(blockIdx.x & 7) * D) >> 3 : 0;
   const int64_t c1 = xcd_split ? ((int64_t)((blockIdx.x & 7) + 1) * D) >> 3 : D;
   auto dp_item = [&](int64_t k) -> int64_t {
-    const int64_t w = c0 + dj + k * gx;
+    // dynamic-K: odd rounds run backwards (snake), so the workgroups that
+    // drew the longest items of one round draw the shortest of the next
+    const int64_t w = (KIND == DYNAMIC_K && (k & 1)) ? k * G + (G - 1 - b) : c0 + dj + k * gx;
     return w < c1 ? w : -1;
   };
   auto dp_next = [&](int64_t w) -> int64_t {   // whole item after w (w from dp_item)
+    if constexpr (KIND == DYNAMIC_K) {
+      const int64_t k = (w >> 32) == 0 ? (int64_t)((uint32_t)w / (uint32_t)G) : w / G;
+      return dp_item(k + 1);
+    }
     const int64_t nw = w + gx;
     return nw < c1 ? nw : -1;
   };
@@ -660,21 +668,18 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // wm * WM + 32 i + l % 32 and columns wn * WN + 32 j + 8 q + 4 (l / 32) + r
   // in element 4 q + r.
   // transfers issued in MFMA sub-step ks: [ks * LPS / KSUB, (ks + 1) * LPS / KSUB)
-  auto compute = [&](const uint8_t* As, const LoadCtx& lx) {
+  // The k-step body, in two instantiations: EDGE (fp8 dW, a k-step cut by
+  // the group's contraction range: bytes outside it are cleared in the
+  // fragments) and the plain one every other k-step runs, which then carries
+  // none of the masking arithmetic.
+  auto compute_body = [&](const uint8_t* As, const LoadCtx& lx, auto edge_c, int mlo, int mhi) {
+    constexpr bool EDGE = decltype(edge_c)::value;
     const uint8_t* Bs = As + A_BYTES;
     // The fragment addresses below are loop-invariant; hoisted, they would
     // hold 24-48 VGPRs across the K loop and push the kernel into spills.
     // An opaque copy of the lane index makes them cheap per-step arithmetic.
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
-    int mlo = 0, mhi = BK;
-    if constexpr (MASK_BYTES) {
-      const int64_t c0 = ci.c_begin + (int64_t)cs * BK;
-      const int64_t lo64 = ci.c_lo - c0, hi64 = ci.c_hi - c0;
-      mlo = lo64 < 0 ? 0 : (lo64 > BK ? BK : (int)lo64);
-      mhi = hi64 < 0 ? 0 : (hi64 > BK ? BK : (int)hi64);
-    }
-    const bool edge = MASK_BYTES && (mlo > 0 || mhi < BK);
 #pragma unroll
     for (int ks = 0; ks < T::KSUB; ++ks) {
       if constexpr (ELEM == EL_BF16) {
@@ -715,7 +720,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
           const i32x4 lo = *reinterpret_cast<const i32x4*>(As + lds_off(row, ch));
           const i32x4 hi = *reinterpret_cast<const i32x4*>(As + lds_off(row, ch + 1));
           af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          if (edge) af[i] = mask_frag8(af[i], k0, mlo, mhi);
+          if constexpr (EDGE) af[i] = mask_frag8(af[i], k0, mlo, mhi);
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
@@ -723,7 +728,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
           const i32x4 lo = *reinterpret_cast<const i32x4*>(Bs + lds_off(row, ch));
           const i32x4 hi = *reinterpret_cast<const i32x4*>(Bs + lds_off(row, ch + 1));
           bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          if (edge) bfr[j] = mask_frag8(bfr[j], k0, mlo, mhi);
+          if constexpr (EDGE) bfr[j] = mask_frag8(bfr[j], k0, mlo, mhi);
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i)
@@ -735,6 +740,19 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
         for (int q = ks * LPS / T::KSUB; q < (ks + 1) * LPS / T::KSUB; ++q) issue_one(lx, q);
       }
     }
+  };
+  auto compute = [&](const uint8_t* As, const LoadCtx& lx) {
+    if constexpr (MASK_BYTES) {
+      const int64_t c0 = ci.c_begin + (int64_t)cs * BK;
+      const int64_t lo64 = ci.c_lo - c0, hi64 = ci.c_hi - c0;
+      const int mlo = lo64 < 0 ? 0 : (lo64 > BK ? BK : (int)lo64);
+      const int mhi = hi64 < 0 ? 0 : (hi64 > BK ? BK : (int)hi64);
+      if (mlo > 0 || mhi < BK) {
+        compute_body(As, lx, BoolConst<true>{}, mlo, mhi);
+        return;
+      }
+    }
+    compute_body(As, lx, BoolConst<false>{}, 0, BK);
   };
 
   // Epilogue into the stage st just consumed: (fp8: scales), bf16 rounding,
