@@ -484,14 +484,17 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   const int64_t D = (KIND != FIXED_M || whole) ? items : (full >= 2 ? (full - 1) * G : 0);
   const int64_t L = (items - D) * S;
   const int64_t GS = L < G ? L : G;
-  // Fixed-M whole items [0, D) (all of equal length): XCD x owns the
-  // contiguous eighth [c0, c1) and its G / 8 workgroups take it round-robin,
-  // so each XCD's L2 serves one run of consecutive items and a partial last
-  // round is spread evenly over the XCDs.  Dynamic-K items differ in length
-  // (groups come largest first) and are dealt over the whole grid, longest
-  // first, in snake order.  dp_item(k) is the workgroup's k-th whole item,
-  // or -1.
-  const bool xcd_split = KIND == FIXED_M && (G & 7) == 0;
+  // Whole items [0, D) of equal length (fixed-M tiles; dynamic-K tiles when
+  // every group has the same size): XCD x owns the contiguous eighth
+  // [c0, c1) and its G / 8 workgroups take it round-robin, so each XCD's L2
+  // serves one run of consecutive items (for a balanced dW, one expert's X
+  // and dY rows per XCD) and a partial last round is spread evenly over the
+  // XCDs.  Dynamic-K items of unequal length (groups come largest first) are
+  // dealt over the whole grid, longest first, in snake order.  dp_item(k) is
+  // the workgroup's k-th whole item, or -1.
+  bool equal_items = KIND == FIXED_M;
+  if constexpr (KIND == DYNAMIC_K) equal_items = uni(tab.eff[uni(tab.order[0])]) == uni(tab.eff[uni(tab.order[a.E - 1])]);
+  const bool xcd_split = equal_items && (G & 7) == 0;
   const int64_t gx = xcd_split ? (G >> 3) : G;
   const int64_t dj = xcd_split ? (int64_t)(blockIdx.x >> 3) : b;
   const int64_t c0 = xcd_split ? ((int64_t)(blockIdx.x & 7) * D) >> 3 : 0;
@@ -499,11 +502,11 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   auto dp_item = [&](int64_t k) -> int64_t {
     // dynamic-K: odd rounds run backwards (snake), so the workgroups that
     // drew the longest items of one round draw the shortest of the next
-    const int64_t w = (KIND == DYNAMIC_K && (k & 1)) ? k * G + (G - 1 - b) : c0 + dj + k * gx;
+    const int64_t w = (KIND == DYNAMIC_K && !xcd_split && (k & 1)) ? k * G + (G - 1 - b) : c0 + dj + k * gx;
     return w < c1 ? w : -1;
   };
   auto dp_next = [&](int64_t w) -> int64_t {   // whole item after w (w from dp_item)
-    if constexpr (KIND == DYNAMIC_K) {
+    if (KIND == DYNAMIC_K && !xcd_split) {
       const int64_t k = (w >> 32) == 0 ? (int64_t)((uint32_t)w / (uint32_t)G) : w / G;
       return dp_item(k + 1);
     }
