@@ -13,9 +13,11 @@
 //   1. per chunk of pairs: stable rank of every pair among the chunk's pairs
 //      with the same expert, and the chunk's per-expert counts;
 //   2. one workgroup: per-expert totals, padded run starts, per-chunk bases,
-//      block -> expert table, padded sizes, padded length;
+//      block -> expert table, padded sizes, padded length, and the sentinel
+//      in every slot no pair will take (each run's padding and the tail up
+//      to the capacity);
 //   3. scatter: position = base[chunk][expert] + rank; inverse positions.
-// The sentinel fill runs first; the gather of X rows runs last.
+// The gather of X rows runs last.
 #include "kernels.h"
 
 namespace mg {
@@ -78,7 +80,9 @@ __global__ void __launch_bounds__(1024) perm_plan_kernel(int32_t E, int32_t bloc
                                                         int32_t* __restrict__ chunk_counts,
                                                         int32_t* __restrict__ expert_ids, int64_t nblk,
                                                         int32_t* __restrict__ ntpp,
-                                                        int32_t* __restrict__ padded) {
+                                                        int32_t* __restrict__ padded,
+                                                        int32_t* __restrict__ sorted_ids, int64_t cap,
+                                                        int32_t sentinel) {
   __shared__ int32_t s_start[kMaxExperts + 1];
   __shared__ int32_t s_blk[kMaxExperts + 1];
   const int e = threadIdx.x;
@@ -113,11 +117,10 @@ __global__ void __launch_bounds__(1024) perm_plan_kernel(int32_t E, int32_t bloc
       base += cnt;
     }
     for (int32_t b = s_blk[e]; b < s_blk[e + 1] && b < nblk; ++b) expert_ids[b] = e;
+    // this run's padding (after its base + total pairs) takes the sentinel
+    for (int32_t i = base; i < s_start[e + 1] && i < cap; ++i) sorted_ids[i] = sentinel;
   }
-}
-
-__global__ void __launch_bounds__(256) fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+  for (int64_t i = (int64_t)s_start[E] + threadIdx.x; i < cap; i += blockDim.x) sorted_ids[i] = sentinel;
 }
 
 __global__ void __launch_bounds__(256) perm_scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
@@ -177,15 +180,11 @@ hipError_t launch_moe_permute_ws(const int32_t* ids, int64_t T, int32_t k, int32
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   int32_t* rank = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(ws) + align_up(nchunks * E * 4, 256));
 
-  if (cap > 0) {
-    const int fill_grid = (int)(cdiv(cap, 256) < 4096 ? cdiv(cap, 256) : 4096);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_grid), dim3(256), 0, stream, sorted_ids, cap, (int32_t)P);
-  }
   hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(PT), (size_t)E * 4, stream, ids, P, E,
                      chunk, counts, rank);
   int plan_threads = (int)align_up(E, kWave);
   hipLaunchKernelGGL(perm_plan_kernel, dim3(1), dim3(plan_threads), 0, stream, E, block_m, nchunks, counts,
-                     expert_ids, nblk, ntpp, padded);
+                     expert_ids, nblk, ntpp, padded, sorted_ids, cap, (int32_t)P);
   if (P > 0)
     hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)cdiv(P, 256)), dim3(256), 0, stream, ids, P, E,
                        chunk, counts, rank, sorted_ids, inv);
