@@ -411,7 +411,7 @@ def main():
                     help="only run each product and a known-size copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the grouped GEMM runs on one device's share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
