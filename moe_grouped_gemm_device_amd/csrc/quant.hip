@@ -193,25 +193,30 @@ __device__ inline int4 colwise_chunk(const GroupTable& tab, int32_t G, int32_t c
   return make_int4(lo, (int)r0, (int)(r1 - r0), 0);
 }
 
-// Tile index -> (tensor, chunk, column block); consecutive tiles share rows.
+// Tile index -> (tensor, chunk, block of W columns); consecutive tiles share
+// rows.
+template <int W>
 __device__ inline void colwise_tile(const ColwiseArgs& a, int64_t nch, int64_t item, int& t, int32_t& chunk,
                                     int& cb) {
-  const int64_t cba = cdiv(a.cols[0], QC_COLS);
+  const int64_t cba = cdiv(a.cols[0], W);
   t = 0;
   if (item >= nch * cba) {
     item -= nch * cba;
     t = 1;
   }
-  const int64_t cbs = cdiv(a.cols[t], QC_COLS);
+  const int64_t cbs = cdiv(a.cols[t], W);
   chunk = (int32_t)(item / cbs);
   cb = (int)(item - (int64_t)chunk * cbs);
 }
 
+template <int W>
 __device__ inline int64_t colwise_tiles(const ColwiseArgs& a, int64_t nch) {
-  int64_t n = nch * cdiv(a.cols[0], QC_COLS);
-  if (a.ntensors > 1) n += nch * cdiv(a.cols[1], QC_COLS);
+  int64_t n = nch * cdiv(a.cols[0], W);
+  if (a.ntensors > 1) n += nch * cdiv(a.cols[1], W);
   return n;
 }
+
+constexpr int QA_COLS = 256;   // columns per amax tile: a wave reads two 512-byte row runs per load
 
 __global__ void __launch_bounds__(256) colwise_zero_kernel(ColwiseArgs a) {
   for (int t = 0; t < a.ntensors; ++t) {
@@ -222,60 +227,58 @@ __global__ void __launch_bounds__(256) colwise_zero_kernel(ColwiseArgs a) {
 
 __global__ void __launch_bounds__(256) colwise_amax_kernel(ColwiseArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
-  __shared__ uint32_t red[4][QC_COLS];
+  __shared__ uint32_t red[4][QA_COLS];
   const GroupTable tab = carve_table(table_lds, a.G);
   GroupTable tabw = tab;
   build_group_table(a.sizes, a.G, a.rows, QC_ROWS, false, tabw);
   colwise_chunk_table(tabw, a.G);
   const int64_t nch = tab.tstart[a.G];
-  const int64_t n = colwise_tiles(a, nch);
+  const int64_t n = colwise_tiles<QA_COLS>(a, nch);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cc = tid & 7, rs = tid >> 3;   // 8-column chunk, row within 32
+  const int cc = tid & 31, rg = tid >> 5;   // 8-column chunk of the tile, row group (rows rg + 8 j)
   for (int64_t item = blockIdx.x; item < n; item += gridDim.x) {
     int t, cb;
     int32_t chunk;
-    colwise_tile(a, nch, item, t, chunk, cb);
+    colwise_tile<QA_COLS>(a, nch, item, t, chunk, cb);
     const int4 e = colwise_chunk(tab, a.G, chunk);
     const int cols = a.cols[t];
-    const int c = cb * QC_COLS + cc * 8;
+    const int c = cb * QA_COLS + cc * 8;
     const uint16_t* x = a.x[t] + (int64_t)e.y * cols + c;
     uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (c < cols) {
-      // all loads issue together: rows past the chunk re-read its first row
-      uint4 v[QC_ROWS / 32];
+      // 32 rows per thread, 8 loads in flight at a time; rows past the chunk
+      // re-read its first row
 #pragma unroll
-      for (int j = 0; j < QC_ROWS / 32; ++j) {
-        const int r = rs + 32 * j;
-        v[j] = *reinterpret_cast<const uint4*>(x + (int64_t)(r < e.z ? r : 0) * cols);
-      }
+      for (int jb = 0; jb < QC_ROWS / 8; jb += 8) {
+        uint4 v[8];
 #pragma unroll
-      for (int j = 0; j < QC_ROWS / 32; ++j) {
-        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        for (int j = 0; j < 8; ++j) {
+          const int r = rg + 8 * (jb + j);
+          v[j] = *reinterpret_cast<const uint4*>(x + (int64_t)(r < e.z ? r : 0) * cols);
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          m[2 * i] = max(m[2 * i], (w[i] & 0x7FFFu) << 16);
-          m[2 * i + 1] = max(m[2 * i + 1], (w[i] >> 16 & 0x7FFFu) << 16);
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            m[2 * i] = max(m[2 * i], (w[i] & 0x7FFFu) << 16);
+            m[2 * i + 1] = max(m[2 * i + 1], (w[i] >> 16 & 0x7FFFu) << 16);
+          }
         }
       }
     }
-    // reduce over the 32 threads sharing a column chunk: lanes that differ in
-    // bits 3..5 by shuffles, then the 4 waves through LDS
+    // reduce over the 8 row groups: the two of a wave by a shuffle, then the
+    // 4 waves through LDS
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t v = m[i];
-      v = max(v, (uint32_t)__shfl_xor((int)v, 8, kWave));
-      v = max(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
-      v = max(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
-      m[i] = v;
-    }
-    if (lane < 8) {
+    for (int i = 0; i < 8; ++i) m[i] = max(m[i], (uint32_t)__shfl_xor((int)m[i], 32, kWave));
+    if (lane < 32) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
     }
     __syncthreads();
-    if (tid < QC_COLS) {
+    {
       const uint32_t v = max(max(red[0][tid], red[1][tid]), max(red[2][tid], red[3][tid]));
-      const int col = cb * QC_COLS + tid;
+      const int col = cb * QA_COLS + tid;
       if (col < cols && v != 0u) atomicMax(a.s[t] + (int64_t)e.x * cols + col, v);
     }
     __syncthreads();
@@ -295,13 +298,13 @@ __global__ void __launch_bounds__(256) colwise_cast_kernel(ColwiseArgs a) {
   build_group_table(a.sizes, a.G, a.rows, QC_ROWS, false, tabw);
   colwise_chunk_table(tabw, a.G);
   const int64_t nch = tab.tstart[a.G];
-  const int64_t n = colwise_tiles(a, nch);
+  const int64_t n = colwise_tiles<QC_COLS>(a, nch);
   const int tid = threadIdx.x;
   const int cc = tid & 7, rq = tid >> 3;   // 8-column chunk, row quad within 128 rows
   for (int64_t item = n - 1 - blockIdx.x; item >= 0; item -= gridDim.x) {
     int t, cb;
     int32_t chunk;
-    colwise_tile(a, nch, item, t, chunk, cb);
+    colwise_tile<QC_COLS>(a, nch, item, t, chunk, cb);
     const int4 e = colwise_chunk(tab, a.G, chunk);
     const int cols = a.cols[t];
     const int64_t M = a.rows;
