@@ -49,7 +49,10 @@
 //    alone keep most of the grid busy, no tile is split (re-reading a split
 //    tile's partials costs more than the idle workgroups).
 //  * dW work items are whole tiles dealt round-robin, largest groups first;
-//    loads run ahead across item boundaries.
+//    loads run ahead across item boundaries.  When groups are short (a few
+//    k-steps per item) dW uses 256 x 256 tiles with two LDS stages: each
+//    wave then owns 128 x 64 outputs (128 accumulators), which fits because
+//    the dynamic-K kernel carries no stream-K state.
 //  * Consecutive logical workgroups sit on one XCD (dispatch deals
 //    workgroups round-robin to the 8 XCDs), so neighbouring tiles share L2.
 #include "kernels.h"
@@ -57,7 +60,7 @@
 
 namespace mg {
 
-constexpr uint32_t kRasterM = 8;  // row tiles per raster block (fixed-M item order)
+constexpr uint32_t kRasterM = 12;  // most row tiles per raster block (fixed-M item order)
 
 template <int ELEM> struct ElemTraits;
 template <> struct ElemTraits<EL_BF16> {
@@ -335,8 +338,8 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
   const uint32_t w = (uint32_t)w64;
   int nt;
   if (KIND == FIXED_M) {
-    // Items run group by group; inside a group, in blocks of kRasterM row
-    // tiles, column tile outermost: the workgroups of one XCD, which take
+    // Items run group by group; inside a group, in blocks of up to kRasterM
+    // row tiles, column tile outermost: the workgroups of one XCD, which take
     // consecutive items at the same time, then share each weight slice
     // among kRasterM row tiles and each activation slice among the block's
     // column tiles.
@@ -350,11 +353,17 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
     const int32_t t0 = uni(tab.tstart[g]);
     const uint32_t mtg = (uint32_t)(uni(tab.tstart[g + 1]) - t0);
     const uint32_t local = w - (uint32_t)t0 * ntu;
-    const uint32_t blk = local / (kRasterM * ntu);
-    const uint32_t rem = local - blk * kRasterM * ntu;
-    const uint32_t mb = mtg - blk * kRasterM < kRasterM ? mtg - blk * kRasterM : kRasterM;
+    // block height: the group's row tiles cut into the fewest blocks of at
+    // most kRasterM, all of one height but the last (an expert with 9 row
+    // tiles runs as one block, so its weights are streamed once, not twice)
+    const uint32_t mtg1 = mtg > 0 ? mtg : 1;
+    const uint32_t nblk = (mtg1 + kRasterM - 1) / kRasterM;
+    const uint32_t rb = (mtg1 + nblk - 1) / nblk;
+    const uint32_t blk = local / (rb * ntu);
+    const uint32_t rem = local - blk * rb * ntu;
+    const uint32_t mb = mtg - blk * rb < rb ? mtg - blk * rb : rb;
     nt = (int)(rem / mb);
-    const int ml = (int)(blk * kRasterM + (rem - (uint32_t)nt * mb));
+    const int ml = (int)(blk * rb + (rem - (uint32_t)nt * mb));
     const int32_t eff = uni(tab.eff[g]);
     it.g = g;
     it.rowbase = (int64_t)uni(tab.off[g]) + (int64_t)ml * BM;
@@ -1057,7 +1066,17 @@ hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t strea
       if (L.b_kc) return launch_one<128, 256, 3, true, true, FIXED_M, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
       return launch_one<128, 256, 3, true, false, FIXED_M, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
     }
-    if (!L.a_kc && !L.b_kc) return launch_one<128, 256, 3, false, false, DYNAMIC_K, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
+    if (!L.a_kc && !L.b_kc) {
+      // Short contractions (at most 256 rows per group on average, so a few
+      // k-steps per item): 256 x 256 tiles, two stages.  Every item's
+      // operands then cross from L2 to LDS once per 256 x 256 outputs
+      // instead of once per 128 x 256, and the one k-step in flight costs
+      // little when items are that short.  Long contractions keep three
+      // stages, which 256 x 256 tiles cannot fit in LDS.
+      if (a.total_rows <= 256 * (int64_t)a.E)
+        return launch_one<256, 256, 2, false, false, DYNAMIC_K, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
+      return launch_one<128, 256, 3, false, false, DYNAMIC_K, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
+    }
     return hipErrorInvalidValue;
   }
   if (L.elem == EL_FP8) {

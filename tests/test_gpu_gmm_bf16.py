@@ -124,6 +124,10 @@ def test_tiny_config_forward_and_backward():
     (1, 129, 64, 128, 2),       # one group: plain GEMM
     (17, 700, 72, 40, 3),       # many groups, some empty
     (8, 1024, 256, 384, 4),     # balanced
+    # more than 256 rows per group on average: dW on 128 x 256 tiles with
+    # three stages (the cases above take the 256 x 256 two-stage dW tiles)
+    (2, 1100, 136, 392, 5),
+    (3, 2000, 72, 264, 6),
 ])
 def test_bf16_gmm_matches_oracle(E, M, K, N, seed, trans_b):
     sizes = wl.random_group_sizes(E, M, seed, zero_frac=0.25) if E > 1 else np.array([M], np.int32)
