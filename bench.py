@@ -162,7 +162,7 @@ def run_gpu(args, torch, mg):
     achieved = bytes_per[dom] / (avg_ms[dom] * 1e-3) / 1e9
     kernel_names = {"fwd": "gmm_kernel<128,256,3,true,false,FIXED_M,bf16,8 waves> (forward: X rows k-contiguous, W [K,N])",
                     "dx": "gmm_kernel<128,256,3,true,true,FIXED_M,bf16,8 waves> (dX: dY rows, W rows contraction-contiguous)",
-                    "dw": "gmm_kernel<128,256,3,false,false,DYNAMIC_K,bf16,8 waves> (dW: X and dY row-contiguous)"}
+                    "dw": "gmm_kernel<256,256,2,false,false,DYNAMIC_K,bf16,8 waves> (dW: X and dY row-contiguous)"}
     roofline = {
         "bound": "hbm",
         "kernel": kernel_names[dom],
@@ -271,16 +271,17 @@ def _row(what, us, amount, unit, peak):
             "frac": round(achieved / peak, 4)}
 
 
-def row_measurements(torch, mg):
-    """Each hot-path step of the fp8 training layer (DeepSeek-MoE-16B share:
+def _row_cases(torch, mg):
+    """The hot-path steps of the fp8 training layer (DeepSeek-MoE-16B share:
     16384 tokens, 64 experts, top-6 with Zipf(1.1) loads, hidden 2048,
     expert intermediate 1408) and of the token-sorted Mixtral-8x7B expert FFN
-    (T=4096, top-2 of 8, hidden 4096, intermediate 14336), timed on its own
-    against its roofline.  Inputs: seeded synthetic bf16 N(0,1) activations
+    (T=4096, top-2 of 8, hidden 4096, intermediate 14336), one at a time.
+    Yields (key, what, fn, amount, unit, peak, reps); fn runs the step once
+    and must be used before the next case is drawn (later cases may free or
+    overwrite its inputs).  Inputs: seeded synthetic bf16 N(0,1) activations
     and N(0,0.02) weights."""
     import numpy as np
     import workloads as wl
-    rows = {}
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
     # ---- fp8 layer share (configuration: DeepSeek-MoE-16B-shaped) ----------
@@ -295,37 +296,35 @@ def row_measurements(torch, mg):
     ws = mg.workspace(E, M)
     xq = torch.empty(M, H, dtype=torch.uint8, device="cuda")
     sx = torch.empty(M, dtype=torch.float32, device="cuda")
-    us = _timeit(torch, lambda: mg.quantize_rowwise_fp8(X, q=xq, scales=sx))
-    rows["A5_quantize_rowwise_fp8"] = _row(f"X [{M},{H}] bf16 -> e4m3 + row scales", us,
-                                           M * H * 3 + M * 4, "GB/s", PEAK_HBM_GBS)
+    yield ("A5_quantize_rowwise_fp8", f"X [{M},{H}] bf16 -> e4m3 + row scales",
+           lambda: mg.quantize_rowwise_fp8(X, q=xq, scales=sx), M * H * 3 + M * 4, "GB/s", PEAK_HBM_GBS, 10)
     cq = (torch.zeros(I, M, dtype=torch.uint8, device="cuda"), torch.empty(E, I, dtype=torch.float32, device="cuda"),
           torch.zeros(H, M, dtype=torch.uint8, device="cuda"), torch.empty(E, H, dtype=torch.float32, device="cuda"))
-    us = _timeit(torch, lambda: mg.quantize_colwise_per_group_fp8(dY, sizes, b=X, out=cq))
-    rows["A6_quantize_colwise_dual"] = _row(f"dY [{M},{I}] and X [{M},{H}], {E} Zipf groups -> column-major e4m3",
-                                            us, M * (I + H) * 3 + E * (I + H) * 4, "GB/s", PEAK_HBM_GBS)
+    yield ("A6_quantize_colwise_dual", f"dY [{M},{I}] and X [{M},{H}], {E} Zipf groups -> column-major e4m3",
+           lambda: mg.quantize_colwise_per_group_fp8(dY, sizes, b=X, out=cq),
+           M * (I + H) * 3 + E * (I + H) * 4, "GB/s", PEAK_HBM_GBS, 10)
     dyc, sdyc, xc, sxc = cq
     wq_c, sw_c = mg.quantize_colwise_per_group_fp8(W.reshape(E * H, I),
                                                    torch.full((E,), H, dtype=torch.int32, device="cuda"))
     y = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
-    us = _timeit(torch, lambda: mg.gmm_fwd_fp8(xq, sx, wq_c, sw_c, E * H, H, sizes, I, out=y, ws=ws))
-    rows["A7_fp8_gmm_fwd"] = _row(f"Y [{M},{I}] = Xq . Wq_g, K={H}", us, 2.0 * M * H * I, "TFLOP/s", PEAK_FP8_TFLOPS)
+    yield ("A7_fp8_gmm_fwd", f"Y [{M},{I}] = Xq . Wq_g, K={H}",
+           lambda: mg.gmm_fwd_fp8(xq, sx, wq_c, sw_c, E * H, H, sizes, I, out=y, ws=ws),
+           2.0 * M * H * I, "TFLOP/s", PEAK_FP8_TFLOPS, 10)
     dyq = torch.empty(M, I, dtype=torch.uint8, device="cuda")
     sdy = torch.empty(M, dtype=torch.float32, device="cuda")
     mg.quantize_rowwise_fp8(dY, q=dyq, scales=sdy)
     wq_r, sw_r = mg.quantize_rowwise_fp8(W.reshape(E * H, I))
     dxo = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
-    us = _timeit(torch, lambda: mg.gmm_bwd_fp8(sizes, H, I, dyq=dyq, sdy=sdy, wq=wq_r, sw=sw_r, w_ld=I,
-                                               w_expert_stride=H * I, need_dw=False, dx=dxo, ws=ws))
-    rows["A7_fp8_gmm_dx"] = _row(f"dX [{M},{H}] = dYq . Wq_g^T, contraction {I}", us, 2.0 * M * H * I,
-                                 "TFLOP/s", PEAK_FP8_TFLOPS)
+    yield ("A7_fp8_gmm_dx", f"dX [{M},{H}] = dYq . Wq_g^T, contraction {I}",
+           lambda: mg.gmm_bwd_fp8(sizes, H, I, dyq=dyq, sdy=sdy, wq=wq_r, sw=sw_r, w_ld=I,
+                                  w_expert_stride=H * I, need_dw=False, dx=dxo, ws=ws),
+           2.0 * M * H * I, "TFLOP/s", PEAK_FP8_TFLOPS, 10)
     dwo = torch.empty(E, H, I, dtype=torch.bfloat16, device="cuda")
-    us = _timeit(torch, lambda: mg.gmm_bwd_fp8(sizes, H, I, xc=xc, sxc=sxc, dyc=dyc, sdyc=sdyc, need_dx=False,
-                                               dw=dwo, ws=ws))
-    rows["A7_fp8_gmm_dw"] = _row(f"dW [{E},{H},{I}] = Xq_g^T . dYq_g (dynamic K)", us, 2.0 * M * H * I,
-                                 "TFLOP/s", PEAK_FP8_TFLOPS)
-    us = _timeit(torch, lambda: mg.build_worklist(mg.MG_WL_FIXED_M, sizes, M, 128))
-    rows["A1_builder"] = {"what": f"work list for {E} groups, total_M={M}, 128-row tiles (own launch)",
-                          "us": round(us, 2)}
+    yield ("A7_fp8_gmm_dw", f"dW [{E},{H},{I}] = Xq_g^T . dYq_g (dynamic K)",
+           lambda: mg.gmm_bwd_fp8(sizes, H, I, xc=xc, sxc=sxc, dyc=dyc, sdyc=sdyc, need_dx=False, dw=dwo, ws=ws),
+           2.0 * M * H * I, "TFLOP/s", PEAK_FP8_TFLOPS, 10)
+    yield ("A1_builder", f"work list for {E} groups, total_M={M}, 128-row tiles (own launch)",
+           lambda: mg.build_worklist(mg.MG_WL_FIXED_M, sizes, M, 128), None, None, None, 10)
     del X, dY, W, xq, dyq, cq, wq_c, wq_r, y, dxo, dwo, ws
     torch.cuda.empty_cache()
     # ---- token-sorted fused FFN (configuration: Mixtral-8x7B-shaped) -------
@@ -338,40 +337,80 @@ def row_measurements(torch, mg):
     w2 = (torch.randn(E, I, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
     bm = 128
     p = mg.moe_permute(ids, E, bm, x=x)
-    us = _timeit(torch, lambda: mg.moe_permute(ids, E, bm, x=x))
     ntpp = int(p["num_tokens_post_padded"].item())
-    rows["A9_moe_permute"] = _row(f"align + gather of {T}x{k} routed rows, hidden {H}, block_m {bm}", us,
-                                  T * H * 2 + ntpp * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS)
+    yield ("A9_moe_permute", f"align + gather of {T}x{k} routed rows, hidden {H}, block_m {bm}",
+           lambda: mg.moe_permute(ids, E, bm, x=x), T * H * 2 + ntpp * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
     xs, psz = p["x_sorted"], p["padded_sizes"]
     wsf = mg.workspace(E, xs.shape[0])
     h1 = torch.empty(xs.shape[0], 2 * I, dtype=torch.bfloat16, device="cuda")
-    us = _timeit(torch, lambda: mg.gmm_fwd(xs, w1, psz, out=h1, ws=wsf), reps=5)
-    rows["A10_gemm1"] = _row(f"H1 = X_sorted . W1_e, {ntpp} padded rows, K={H}, N={2 * I} (useful flops of {T * k} rows)",
-                             us, 2.0 * T * k * H * 2 * I, "TFLOP/s", PEAK_BF16_TFLOPS)
+    yield ("A10_gemm1", f"H1 = X_sorted . W1_e, {ntpp} padded rows, K={H}, N={2 * I} (useful flops of {T * k} rows)",
+           lambda: mg.gmm_fwd(xs, w1, psz, out=h1, ws=wsf), 2.0 * T * k * H * 2 * I, "TFLOP/s", PEAK_BF16_TFLOPS, 5)
     act = torch.empty(xs.shape[0], I, dtype=torch.bfloat16, device="cuda")
-    us = _timeit(torch, lambda: mg.silu_mul(h1, out=act))
-    rows["A11_silu_mul"] = _row(f"silu(H1[:, :I]) * H1[:, I:], {xs.shape[0]} rows, I={I}", us,
-                                xs.shape[0] * I * 6, "GB/s", PEAK_HBM_GBS)
+    yield ("A11_silu_mul", f"silu(H1[:, :I]) * H1[:, I:], {xs.shape[0]} rows, I={I}",
+           lambda: mg.silu_mul(h1, out=act), xs.shape[0] * I * 6, "GB/s", PEAK_HBM_GBS, 10)
     y2 = torch.empty(xs.shape[0], H, dtype=torch.bfloat16, device="cuda")
-    us = _timeit(torch, lambda: mg.gmm_fwd(act, w2, psz, out=y2, ws=wsf), reps=5)
-    rows["A12_gemm2"] = _row(f"Y2 = act . W2_e, K={I}, N={H} (useful flops of {T * k} rows)", us,
-                             2.0 * T * k * I * H, "TFLOP/s", PEAK_BF16_TFLOPS)
+    yield ("A12_gemm2", f"Y2 = act . W2_e, K={I}, N={H} (useful flops of {T * k} rows)",
+           lambda: mg.gmm_fwd(act, w2, psz, out=y2, ws=wsf), 2.0 * T * k * I * H, "TFLOP/s", PEAK_BF16_TFLOPS, 5)
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
-    us = _timeit(torch, lambda: mg.moe_unpermute(y2, p["inv"], wts, T, k, out=out))
-    rows["A13_moe_unpermute"] = _row(f"top-{k} weighted combine of {T * k} rows, hidden {H}", us,
-                                     T * k * H * 2 + T * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS)
-    us = _timeit(torch, lambda: mg.fused_moe(x, w1, w2, ids, wts, block_m=bm, ws=wsf), reps=3)
-    rows["C3_fused_ffn_T4096"] = _row("permute -> GEMM1 -> SiLU*mul -> GEMM2 -> combine, end to end", us,
-                                      2.0 * T * k * H * 3 * I, "TFLOP/s", PEAK_BF16_TFLOPS)
+    yield ("A13_moe_unpermute", f"top-{k} weighted combine of {T * k} rows, hidden {H}",
+           lambda: mg.moe_unpermute(y2, p["inv"], wts, T, k, out=out),
+           T * k * H * 2 + T * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
+    yield ("C3_fused_ffn_T4096", "permute -> GEMM1 -> SiLU*mul -> GEMM2 -> combine, end to end",
+           lambda: mg.fused_moe(x, w1, w2, ids, wts, block_m=bm, ws=wsf), 2.0 * T * k * H * 3 * I,
+           "TFLOP/s", PEAK_BF16_TFLOPS, 3)
     for Tsmall in (1, 64):
         sub_ids, sub_w = ids[:Tsmall].contiguous(), wts[:Tsmall].contiguous()
         xsub = x[:Tsmall].contiguous()
-        us = _timeit(torch, lambda: mg.fused_moe(xsub, w1, w2, sub_ids, sub_w, ws=wsf), reps=5)
         experts = int(torch.unique(sub_ids).numel())
-        rows[f"C3_fused_ffn_T{Tsmall}"] = _row(
-            f"end to end, {experts} experts touched: weight bytes of those experts", us,
-            experts * (H * 2 * I + I * H) * 2, "GB/s", PEAK_HBM_GBS)
+        yield (f"C3_fused_ffn_T{Tsmall}", f"end to end, {experts} experts touched: weight bytes of those experts",
+               lambda: mg.fused_moe(xsub, w1, w2, sub_ids, sub_w, ws=wsf),
+               experts * (H * 2 * I + I * H) * 2, "GB/s", PEAK_HBM_GBS, 5)
+
+
+def row_measurements(torch, mg):
+    """Each case of _row_cases timed on its own against its roofline."""
+    rows = {}
+    for key, what, fn, amount, unit, peak, reps in _row_cases(torch, mg):
+        us = _timeit(torch, fn, reps=reps)
+        rows[key] = _row(what, us, amount, unit, peak) if amount is not None else {"what": what, "us": round(us, 2)}
     return rows
+
+
+def counter_probe(torch, mg):
+    """Runs every hot-path step three times, untimed, for rocprofv3 counter
+    passes (--pmc): the balanced step's three products, a 256 MiB device copy
+    (the calibration of FETCH_SIZE / WRITE_SIZE), then every case of
+    _row_cases.  Before each batch a one-element fill (torch's FillFunctor)
+    marks where the batch starts in the dispatch sequence (no other fp64
+    fill runs here); the batch names are printed in order."""
+    names = []
+    marker = torch.empty(1, dtype=torch.float64, device="cuda")
+
+    def batch(name, fn):
+        marker.fill_(len(names))
+        names.append(name)
+        for _ in range(3):
+            fn()
+
+    E, M, K, N = 8, 1024, 4096, 6400
+    d = balanced_inputs(torch, mg, E, M, K, N)
+    x, w, dy, sizes = d["x"], d["w"], d["dy"], d["sizes"]
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty_like(w)
+    ws = mg.workspace(E, M)
+    batch("C2_fwd", lambda: mg.gmm_fwd(x, w, sizes, out=y, ws=ws))
+    batch("C2_dx", lambda: mg.gmm_bwd(dy, x, w, sizes, need_dw=False, dx=dx, ws=ws))
+    batch("C2_dw", lambda: mg.gmm_bwd(dy, x, w, sizes, need_dx=False, dw=dw, ws=ws))
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    batch("copy_256MiB", lambda: dst.copy_(src))
+    del d, x, w, dy, y, dx, dw, src, dst
+    torch.cuda.empty_cache()
+    for key, what, fn, amount, unit, peak, reps in _row_cases(torch, mg):
+        batch(key, fn)
+    torch.cuda.synchronize()
+    log("counter probe batches: " + ",".join(names))
 
 
 def cpu_baseline(host):
@@ -409,6 +448,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other configurations")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run each product and a known-size copy (for rocprofv3 --pmc passes)")
+    ap.add_argument("--counter-probe", action="store_true",
+                    help="only run every hot-path step three times, with batch markers (for rocprofv3 passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -424,6 +465,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(torch, mg)
+        return
+    if args.counter_probe:
+        counter_probe(torch, mg)
         return
     r = run_gpu(args, torch, mg)
     out = {
