@@ -340,11 +340,15 @@ def _row_cases(torch, mg):
     ntpp = int(p["num_tokens_post_padded"].item())
     yield ("A9_moe_permute", f"align + gather of {T}x{k} routed rows, hidden {H}, block_m {bm}",
            lambda: mg.moe_permute(ids, E, bm, x=x), T * H * 2 + ntpp * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
-    xs, psz = p["x_sorted"], p["padded_sizes"]
+    yield ("A9_moe_align", f"align only (what the fused path runs): {T}x{k} routed rows, block_m {bm}",
+           lambda: mg.moe_permute(ids, E, bm), T * k * 4 * 3 + ntpp * 4, "GB/s", PEAK_HBM_GBS, 10)
+    xs, psz, sids = p["x_sorted"], p["padded_sizes"], p["sorted_token_ids"]
     wsf = mg.workspace(E, xs.shape[0])
     h1 = torch.empty(xs.shape[0], 2 * I, dtype=torch.bfloat16, device="cuda")
-    yield ("A10_gemm1", f"H1 = X_sorted . W1_e, {ntpp} padded rows, K={H}, N={2 * I} (useful flops of {T * k} rows)",
-           lambda: mg.gmm_fwd(xs, w1, psz, out=h1, ws=wsf), 2.0 * T * k * H * 2 * I, "TFLOP/s", PEAK_BF16_TFLOPS, 5)
+    yield ("A10_gemm1", f"H1 = X[sorted_ids / {k}] . W1_e (gather in the A load), {ntpp} padded rows, K={H}, "
+                        f"N={2 * I} (useful flops of {T * k} rows)",
+           lambda: mg.gmm_fwd_gather(x, sids, k, w1, psz, out=h1, ws=wsf), 2.0 * T * k * H * 2 * I, "TFLOP/s",
+           PEAK_BF16_TFLOPS, 5)
     act = torch.empty(xs.shape[0], I, dtype=torch.bfloat16, device="cuda")
     yield ("A11_silu_mul", f"silu(H1[:, :I]) * H1[:, I:], {xs.shape[0]} rows, I={I}",
            lambda: mg.silu_mul(h1, out=act), xs.shape[0] * I * 6, "GB/s", PEAK_HBM_GBS, 10)
@@ -355,7 +359,7 @@ def _row_cases(torch, mg):
     yield ("A13_moe_unpermute", f"top-{k} weighted combine of {T * k} rows, hidden {H}",
            lambda: mg.moe_unpermute(y2, p["inv"], wts, T, k, out=out),
            T * k * H * 2 + T * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
-    yield ("C3_fused_ffn_T4096", "permute -> GEMM1 -> SiLU*mul -> GEMM2 -> combine, end to end",
+    yield ("C3_fused_ffn_T4096", "align -> gathered GEMM1 -> SiLU*mul -> GEMM2 -> combine, end to end",
            lambda: mg.fused_moe(x, w1, w2, ids, wts, block_m=bm, ws=wsf), 2.0 * T * k * H * 3 * I,
            "TFLOP/s", PEAK_BF16_TFLOPS, 3)
     for Tsmall in (1, 64):

@@ -132,6 +132,26 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes,
             int32_t E, int64_t total_M, int32_t K, int32_t N, int32_t trans_b,
             void* y, void* ws, size_t ws_bytes, mg_stream_t stream);
 
+/* gmm_fwd over token-sorted rows, with the gather fused into the A-operand
+ * load ([FMOE] fused_moe_kernel: the A rows of a block are found through
+ * sorted_token_ids // top_k, so no sorted copy of x is made):
+ *   y[r, :] = x[sorted_token_ids[r] / top_k, :] . W[g(r)]
+ * for the rows r of the groups (group_sizes, normally moe_permute's
+ * padded_group_sizes, summing to at most total_M); a row whose id is
+ * >= T*top_k (moe_permute's padding sentinel) is a zero row.
+ *   x                bf16 [T, K] row-major (the unsorted tokens)
+ *   sorted_token_ids int32 [>= total_M], device (moe_permute's output)
+ *   w, trans_b, y    as for gmm_fwd; y is bf16 [total_M, N], rows past the
+ *                    groups untouched.
+ * The result is bit-identical to gmm_fwd over moe_permute's x_sorted.
+ * Errors as gmm_fwd, plus MG_EINVAL for T < 0, top_k < 1 or
+ * T*top_k > 2^24, and MG_EUNSUPPORTED for T*K*2 bytes past 2 GiB. */
+int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids,
+                   int32_t top_k, const void* w, const int32_t* group_sizes,
+                   int32_t E, int64_t total_M, int32_t K, int32_t N,
+                   int32_t trans_b, void* y, void* ws, size_t ws_bytes,
+                   mg_stream_t stream);
+
 /* Backward of gmm_fwd for an upstream gradient dy [total_M, N]:
  *   dx[r, :] = dy[r, :] . W[g(r)]^T          (bf16 [total_M, K]; may be NULL)
  *   dw[g]    = X_g^T . dY_g                   (bf16, laid out like w; may be

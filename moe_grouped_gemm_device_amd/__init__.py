@@ -43,6 +43,7 @@ _SIGS = {
     "mg_workspace_clear": (ctypes.c_int, [_P, _P]),
     "gmm_build_worklist": (ctypes.c_int, [_I32, _P, _I32, _I64, _I32, _P, _P, _P, _I64, _P]),
     "gmm_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "gmm_fwd_gather": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "gmm_fwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_bwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
@@ -162,6 +163,31 @@ def gmm_fwd(x, w, group_sizes, trans_b=False, out=None, ws=None, stream=None):
     ws = workspace(E, M, x.device) if ws is None else ws
     _call("gmm_fwd", _ptr(x), _ptr(w), _ptr(group_sizes), E, M, K, N, int(bool(trans_b)), _ptr(y),
           _ptr(ws), ws.numel(), _stream(stream))
+    return y
+
+
+def gmm_fwd_gather(x, sorted_token_ids, top_k, w, group_sizes, trans_b=False, out=None, ws=None, stream=None):
+    """y[r] = x[sorted_token_ids[r] // top_k] @ w[g(r)] over the token-sorted
+    rows (zero rows for the padding sentinel); y has one row per entry of
+    sorted_token_ids.  The same result as gmm_fwd over moe_permute's
+    x_sorted, without that copy."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(sorted_token_ids, torch.int32, "sorted_token_ids", 1)
+    _need(w, torch.bfloat16, "w", 3)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    T, K = x.shape
+    M = sorted_token_ids.numel()
+    E = w.shape[0]
+    N = w.shape[1] if trans_b else w.shape[2]
+    if (w.shape[2] if trans_b else w.shape[1]) != K or group_sizes.numel() != E:
+        raise ValueError("shape mismatch between x, w and group_sizes")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, torch.bfloat16, "out", 2)
+    if y.shape[0] < M:
+        raise ValueError("out has fewer rows than sorted_token_ids")
+    ws = workspace(E, M, x.device) if ws is None else ws
+    _call("gmm_fwd_gather", _ptr(x), T, _ptr(sorted_token_ids), int(top_k), _ptr(w), _ptr(group_sizes), E, M, K,
+          N, int(bool(trans_b)), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
     return y
 
 
@@ -367,17 +393,19 @@ def silu_mul(h, out=None, stream=None):
 
 
 def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, ws=None, stream=None):
-    """Token-sorted MoE expert FFN: permute -> gmm(W1) -> SiLU*mul -> gmm(W2)
-    -> top-k weighted combine.  w1 [E, H, 2I], w2 [E, I, H] bf16."""
+    """Token-sorted MoE expert FFN: align -> gmm(W1) over the token rows
+    looked up through the sorted order -> SiLU*mul -> gmm(W2) -> top-k
+    weighted combine.  w1 [E, H, 2I], w2 [E, I, H] bf16."""
     T, k = topk_ids.shape
     E = w1.shape[0]
     if block_m is None:
         block_m = 16 if T * k <= 64 * E else 128
-    p = moe_permute(topk_ids, E, block_m, x=x, stream=stream)
-    xs = p["x_sorted"]
+    p = moe_permute(topk_ids, E, block_m, stream=stream)
+    ids = p["sorted_token_ids"]
     sizes = p["padded_sizes"]
-    ws = workspace(E, xs.shape[0], x.device) if ws is None else ws
-    h1 = gmm_fwd(xs, w1, sizes, ws=ws, stream=stream)
+    ws = workspace(E, ids.numel(), x.device) if ws is None else ws
+    # GEMM1 reads the token rows through the sorted order (no sorted copy)
+    h1 = gmm_fwd_gather(x, ids, k, w1, sizes, ws=ws, stream=stream)
     act = silu_mul(h1, stream=stream)
     y2 = gmm_fwd(act, w2, sizes, ws=ws, stream=stream)
     return moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream), p

@@ -176,6 +176,46 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E,
   return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd");
 }
 
+int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids, int32_t top_k, const void* w,
+                   const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K, int32_t N, int32_t trans_b,
+                   void* y, void* ws, size_t ws_bytes, mg_stream_t stream) {
+  int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
+  if (rc) return rc;
+  if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
+  if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "K and N must be multiples of 8");
+  if (T < 0 || top_k < 1 || T * (int64_t)top_k > ((int64_t)1 << 24))
+    return fail(MG_EINVAL, "T=%lld, top_k=%d: need T >= 0, top_k >= 1, T*top_k <= 2^24", (long long)T, top_k);
+  if ((rc = check_extents(total_M, K, N, 2))) return rc;
+  if ((rc = check_extents(T, K, N, 2))) return rc;
+  if (total_M == 0) return ok();
+  if (!x || !w || !y || !sorted_token_ids) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  GemmArgs a = blank_args();
+  a.A = x;
+  a.a_ld = K;
+  a.gather = sorted_token_ids;
+  a.gather_div = top_k;
+  a.gather_limit = (int32_t)(T * top_k);
+  a.B = w;
+  a.b_ld = trans_b ? K : N;
+  a.b_gs = (int64_t)K * N;
+  a.C = y;
+  a.c_ld = N;
+  a.c_gs = 0;
+  a.Nout = N;
+  a.Kc = K;
+  a.E = E;
+  a.total_rows = total_M;
+  a.sizes = group_sizes;
+  attach_ws(a, ws);
+  GemmLaunch L;
+  L.kind = FIXED_M;
+  L.elem = EL_BF16;
+  L.a_kc = true;
+  L.b_kc = trans_b != 0;
+  return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd_gather");
+}
+
 int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_sizes, int32_t E,
             int64_t total_M, int32_t K, int32_t N, int32_t trans_b, void* dx, void* dw, void* ws,
             size_t ws_bytes, mg_stream_t stream) {

@@ -221,6 +221,32 @@ struct KcTile {
       voff[i] = row < rows_valid ? (uint32_t)(row * ld * T::ESZ + chunk_of(wave, lane, i) * 16) : kOOB;
     }
   }
+  // The same with the tile's rows looked up: row r is source row
+  // ids[r] / div, or zeros when ids[r] >= limit (the source holds fewer
+  // than 2^31 bytes, checked on the host).  The 8 ids of a DMA block are
+  // read with scalar loads (their wait is on the scalar counter, so the
+  // LDS-DMA transfers in flight are not drained), from addresses clamped to
+  // the tile's valid rows, and each lane picks its row's id.
+  __device__ inline void setup_gather(int wave, int lane, int64_t ld, int rows_valid, const int32_t* ids, int div,
+                                      int limit) {
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    const cptr cids = (cptr)ids;
+    const int sel = lane >> 3;   // the lane's row within its 8-row block
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int r0 = 8 * (wave * LPT + i);
+      int id = limit;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int rq = r0 + q < rows_valid ? r0 + q : rows_valid - 1;
+        const int v = cids[rq];
+        id = sel == q ? v : id;
+      }
+      const int row = row_of(wave, lane, i);
+      if (row >= rows_valid) id = limit;
+      voff[i] = (id >= 0 && id < limit) ? (uint32_t)((id / div) * ld * T::ESZ + chunk_of(wave, lane, i) * 16) : kOOB;
+    }
+  }
   // Source offset of transfer i of this thread's k-step share; only chunks
   // meeting the contraction range [lo, hi) (relative to the k-step;
   // workgroup-uniform) are fetched.  (edge: the k-step is cut by the range;
@@ -570,8 +596,17 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   bool ldone = false;
   ATile at;
   BTile bt;
+  // fixed-M products with a contraction-contiguous bf16 A may take their A
+  // rows through a gather index (workgroup-uniform choice)
+  constexpr bool CAN_GATHER = KIND == FIXED_M && A_KC && ELEM == EL_BF16;
+  const bool gather = CAN_GATHER && a.gather != nullptr;
   auto setup = [&](const Item& it) {
-    at.setup(wave, lane, a.a_ld, it.m_valid);
+    if constexpr (CAN_GATHER) {
+      if (gather) at.setup_gather(wave, lane, a.a_ld, it.m_valid, a.gather + it.rowbase, a.gather_div, a.gather_limit);
+      else at.setup(wave, lane, a.a_ld, it.m_valid);
+    } else {
+      at.setup(wave, lane, a.a_ld, it.m_valid);
+    }
     bt.setup(wave, lane, a.b_ld, it.n_valid);
   };
   setup(li);
@@ -600,7 +635,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     if constexpr (A_KC) {
       int64_t ext = 0x7FFFFFFF;
       if (KIND == DYNAMIC_K) ext = it.c_hi <= it.c_lo ? 0 : (int64_t)(it.m_valid - 1) * a.a_ld + (a.total_rows - c0);
-      x.ra = make_rsrc_words(Ab + (it.rowbase * a.a_ld + c0) * T::ESZ, ldone ? 0 : ext);
+      const int64_t arow = gather ? 0 : it.rowbase;   // gathered rows carry their row in the offset
+      x.ra = make_rsrc_words(Ab + (arow * a.a_ld + c0) * T::ESZ, ldone ? 0 : ext);
     } else {
       x.ra = make_rsrc_words(Ab + (c0 * a.a_ld + it.rowbase) * 2, ldone ? 0 : (it.c_hi - c0) * a.a_ld * 2);
     }

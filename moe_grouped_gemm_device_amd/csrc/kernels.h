@@ -63,6 +63,13 @@ struct GemmArgs {
   // partial tiles per workgroup
   int32_t* sk_ctr;
   float* sk_part;
+  // FIXED_M, bf16, A contraction-contiguous only: when gather is set, row r
+  // of A is row gather[r] / gather_div of the matrix at A (a token row
+  // looked up through the token-sorted order), and a zero row when
+  // gather[r] >= gather_limit (the padding sentinel)
+  const int32_t* gather;
+  int32_t gather_div;
+  int32_t gather_limit;
 };
 
 struct GemmLaunch {

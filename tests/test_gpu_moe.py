@@ -111,3 +111,31 @@ def test_fused_moe_small_matches_oracle(T, bm):
     torch.cuda.synchronize()
     ref, _ = oracle.fused_moe(x, w1, w2, ids, w, bm)
     assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T,k,E,bm,K,N,trans_b", [
+    (1, 2, 8, 16, 256, 128, False),       # one token: two rows, the rest of each block is padding
+    (64, 2, 8, 16, 136, 264, True),
+    (300, 6, 64, 32, 200, 392, False),    # many experts, some empty
+    (1500, 2, 8, 128, 1024, 512, False),  # several row tiles per expert
+])
+def test_gmm_fwd_gather_equals_the_sorted_copy(T, k, E, bm, K, N, trans_b):
+    """GEMM over token rows looked up through sorted_token_ids // top_k is
+    bit-identical to the GEMM over the gathered copy, and matches the oracle
+    on the gathered rows (padding rows are zero rows)."""
+    rng = np.random.default_rng(T + K)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = wl.normal_bf16((T, K), 1.0, 7, wl.T_X)
+    W = wl.stacked_normal_bf16(E, (N, K) if trans_b else (K, N), 0.5, 7, wl.T_W)
+    p = mg.moe_permute(dev(ids), E, bm, x=bf16_dev(x))
+    sizes = p["padded_sizes"]
+    w = bf16_dev(W)
+    y_copy = mg.gmm_fwd(p["x_sorted"], w, sizes, trans_b=trans_b)
+    y_gath = mg.gmm_fwd_gather(bf16_dev(x), p["sorted_token_ids"], k, w, sizes, trans_b=trans_b)
+    torch.cuda.synchronize()
+    n = int(host(p["num_tokens_post_padded"])[0])
+    np.testing.assert_array_equal(bf16_host(y_gath)[:n], bf16_host(y_copy)[:n])
+    al = oracle.moe_align(ids, E, bm)
+    xs = oracle.gather_rows(x, k, al["sorted_token_ids"])[:n]
+    ref = oracle.gmm_fwd_bf16(xs, W, al["padded_sizes"], trans_b=trans_b)
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(y_gath)[:n]), ref) <= BF16_TOL
