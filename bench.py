@@ -350,6 +350,10 @@ def _row_cases(torch, mg):
            lambda: mg.gmm_fwd_gather(x, sids, k, w1, psz, out=h1, ws=wsf), 2.0 * T * k * H * 2 * I, "TFLOP/s",
            PEAK_BF16_TFLOPS, 5)
     act = torch.empty(xs.shape[0], I, dtype=torch.bfloat16, device="cuda")
+    yield ("A10_A11_gemm1_silu_fused", f"act = silu*mul(X[sorted_ids / {k}] . W1_e) in one kernel (what the fused path "
+                                       f"runs), {ntpp} padded rows, K={H}, 2I={2 * I} (useful flops of {T * k} rows)",
+           lambda: mg.gmm_fwd_silu_mul(x, w1, psz, sorted_token_ids=sids, top_k=k, out=act, ws=wsf),
+           2.0 * T * k * H * 2 * I, "TFLOP/s", PEAK_BF16_TFLOPS, 5)
     yield ("A11_silu_mul", f"silu(H1[:, :I]) * H1[:, I:], {xs.shape[0]} rows, I={I}",
            lambda: mg.silu_mul(h1, out=act), xs.shape[0] * I * 6, "GB/s", PEAK_HBM_GBS, 10)
     y2 = torch.empty(xs.shape[0], H, dtype=torch.bfloat16, device="cuda")
@@ -359,7 +363,7 @@ def _row_cases(torch, mg):
     yield ("A13_moe_unpermute", f"top-{k} weighted combine of {T * k} rows, hidden {H}",
            lambda: mg.moe_unpermute(y2, p["inv"], wts, T, k, out=out),
            T * k * H * 2 + T * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
-    yield ("C3_fused_ffn_T4096", "align -> gathered GEMM1 -> SiLU*mul -> GEMM2 -> combine, end to end",
+    yield ("C3_fused_ffn_T4096", "align -> gathered GEMM1 with SiLU*mul epilogue -> GEMM2 -> combine, end to end",
            lambda: mg.fused_moe(x, w1, w2, ids, wts, block_m=bm, ws=wsf), 2.0 * T * k * H * 3 * I,
            "TFLOP/s", PEAK_BF16_TFLOPS, 3)
     for Tsmall in (1, 64):

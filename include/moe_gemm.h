@@ -152,6 +152,23 @@ int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids,
                    int32_t trans_b, void* y, void* ws, size_t ws_bytes,
                    mg_stream_t stream);
 
+/* The expert FFN's first GEMM with SiLU-and-mul in its epilogue ([FMOE]
+ * fused_moe: silu_and_mul of the gate and up halves of the first GEMM's
+ * output, applied here before that output ever reaches memory):
+ *   h[r, :]   = A[r, :] . W1[g(r)]          (fp32 accumulate, rounded to bf16)
+ *   act[r, n] = bf16( silu(h[r, n]) * h[r, I + n] ),  silu(v) = v / (1 + e^-v)
+ * with A[r, :] = x[sorted_token_ids[r] / top_k, :] (zero row for ids
+ * >= T*top_k) when sorted_token_ids is non-NULL, else x[r, :].
+ *   x     bf16 [T, K] (gathered) or [total_M, K] row-major
+ *   w1    bf16 [E, K, 2I] (gate columns 0..I-1, up columns I..2I-1)
+ *   act   bf16 [total_M, I]; rows past the groups untouched
+ * Bit-identical to gmm_fwd (or gmm_fwd_gather) into h followed by silu_mul.
+ * Errors as gmm_fwd_gather; K and I must be multiples of 8. */
+int gmm_fwd_silu_mul(const void* x, int64_t T, const int32_t* sorted_token_ids,
+                     int32_t top_k, const void* w1, const int32_t* group_sizes,
+                     int32_t E, int64_t total_M, int32_t K, int32_t I,
+                     void* act, void* ws, size_t ws_bytes, mg_stream_t stream);
+
 /* Backward of gmm_fwd for an upstream gradient dy [total_M, N]:
  *   dx[r, :] = dy[r, :] . W[g(r)]^T          (bf16 [total_M, K]; may be NULL)
  *   dw[g]    = X_g^T . dY_g                   (bf16, laid out like w; may be

@@ -216,6 +216,52 @@ int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids, in
   return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd_gather");
 }
 
+int gmm_fwd_silu_mul(const void* x, int64_t T, const int32_t* sorted_token_ids, int32_t top_k, const void* w1,
+                     const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K, int32_t I, void* act,
+                     void* ws, size_t ws_bytes, mg_stream_t stream) {
+  int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
+  if (rc) return rc;
+  if (K < 1 || I < 1) return fail(MG_EINVAL, "K and I must be positive");
+  if (K % 8 || I % 8) return fail(MG_EUNSUPPORTED, "K and I must be multiples of 8");
+  if (I > (1 << 30)) return fail(MG_EUNSUPPORTED, "I too large");
+  if ((rc = check_extents(total_M, K, 2 * I, 2))) return rc;
+  if (sorted_token_ids) {
+    if (T < 0 || top_k < 1 || T * (int64_t)top_k > ((int64_t)1 << 24))
+      return fail(MG_EINVAL, "T=%lld, top_k=%d: need T >= 0, top_k >= 1, T*top_k <= 2^24", (long long)T, top_k);
+    if ((rc = check_extents(T, K, 2 * I, 2))) return rc;
+  }
+  if (total_M == 0) return ok();
+  if (!x || !w1 || !act) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(act)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  GemmArgs a = blank_args();
+  a.A = x;
+  a.a_ld = K;
+  if (sorted_token_ids) {
+    a.gather = sorted_token_ids;
+    a.gather_div = top_k;
+    a.gather_limit = (int32_t)(T * top_k);
+  }
+  a.B = w1;
+  a.b_ld = 2 * (int64_t)I;       // W1[g, k, n]: gate columns 0..I-1, up columns I..2I-1
+  a.b_gs = (int64_t)K * 2 * I;
+  a.C = act;
+  a.c_ld = I;
+  a.c_gs = 0;
+  a.Nout = I;
+  a.Kc = K;
+  a.E = E;
+  a.total_rows = total_M;
+  a.sizes = group_sizes;
+  attach_ws(a, ws);
+  GemmLaunch L;
+  L.kind = FIXED_M;
+  L.elem = EL_BF16;
+  L.a_kc = true;
+  L.b_kc = false;
+  L.swiglu = true;
+  return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd_silu_mul");
+}
+
 int gmm_bwd(const void* dy, const void* x, const void* w, const int32_t* group_sizes, int32_t E,
             int64_t total_M, int32_t K, int32_t N, int32_t trans_b, void* dx, void* dw, void* ws,
             size_t ws_bytes, mg_stream_t stream) {

@@ -290,6 +290,20 @@ struct NtTile {
       voff[i] = ch * 8 < cols_valid ? (uint32_t)((row * ld + ch * 8) * 2) : kOOB;
     }
   }
+  // Paired columns: the first R / 2 columns of the tile are columns 0.. of
+  // the operand (from the tile origin), the last R / 2 are columns
+  // half_off + R / 2.. (the up block of a fused gate/up weight); a column
+  // pair exists when its first-half column is below cols_valid.
+  __device__ inline void setup_paired(int wave, int lane, int64_t ld, int cols_valid, int half_off) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int row = (wave * LPT + i) * RPB + lane / CPR;
+      const int ch = (lane % CPR) ^ (4 * (row & 3));
+      const int hc = ch % (CPR / 2);
+      const int col = ch * 8 + (ch >= CPR / 2 ? half_off : 0);
+      voff[i] = hc * 8 < cols_valid ? (uint32_t)((row * ld + col) * 2) : kOOB;
+    }
+  }
   __device__ inline void issue(int i, const i32x4& r, uint32_t tile, int wave, int, int, int, bool, bool nt) const {
     dma_pol<POL>(r, tile + (wave * LPT + i) * 1024, voff[i], nt);
   }
@@ -455,7 +469,13 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // themselves; then (fp8) the reciprocal row and column scales of the tile.
   // Whole sub-tile rows (ECW = WN) are preferred over whole columns: the
   // stores then write full 128-byte lines.
-  constexpr int SC_BYTES = (EPI == EPI_NONE) ? 0 : (BM + BN) * 4;
+  // epilogues that apply fp8 scales; EPI_SWIGLU pairs gate and up columns
+  constexpr bool SCALED = EPI == EPI_ROW_COL || EPI == EPI_GROUP;
+  constexpr bool SWIGLU = EPI == EPI_SWIGLU;
+  static_assert(!SWIGLU || (KIND == FIXED_M && ELEM == EL_BF16 && !B_KC && NW == 8 && BN == 256 && BM == 128),
+                "the paired gate/up epilogue is built for bf16 fixed-M 128 x 256 tiles with B as [K, N]");
+  constexpr int BNE = SWIGLU ? BN / 2 : BN;   // output columns per tile
+  constexpr int SC_BYTES = SCALED ? (BM + BN) * 4 : 0;
   constexpr bool FIT_ALL = NW * WM * (WN + 8) * 2 + SC_BYTES <= STAGE;
   constexpr bool FIT_ROWS = NW * 32 * (WN + 8) * 2 + SC_BYTES <= STAGE;
   constexpr int ERW = FIT_ALL ? WM : 32;
@@ -479,7 +499,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // fp8: the tile's row and column scales, fetched by LDS DMA at the start of
   // its last k-step (a compiler-issued load would make the compiler drain
   // every LDS-DMA transfer in flight before the epilogue could use it)
-  __shared__ __attribute__((aligned(16))) float scl[EPI == EPI_NONE ? 4 : BM + BN];
+  __shared__ __attribute__((aligned(16))) float scl[SCALED ? BM + BN : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -492,7 +512,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   const int err = build_group_table(a.sizes, a.E, a.total_rows, BM, KIND == DYNAMIC_K, tab);
   if (err != 0 && blockIdx.x == 0 && tid == 0 && a.err != nullptr) *a.err = err;
 
-  const int n_tiles = (int)cdiv(a.Nout, BN);
+  const int n_tiles = (int)cdiv(a.Nout, BNE);
   const int m_tiles_dk = (KIND == DYNAMIC_K) ? (int)cdiv(a.Mout, BM) : 1;
   const int64_t items = uni64((KIND == FIXED_M) ? (int64_t)tab.tstart[a.E] * n_tiles
                                                 : (int64_t)a.E * m_tiles_dk * n_tiles);
@@ -555,7 +575,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(a.B);
   auto fetch = [&](int64_t w, const Item* prev) {
-    return get_item<BM, BN, KIND, ELEM, BK>(a, tab, w, n_tiles, m_tiles_dk, prev);
+    return get_item<BM, BNE, KIND, ELEM, BK>(a, tab, w, n_tiles, m_tiles_dk, prev);
   };
   // The workgroup's sequence of (item, first k-step, end k-step); the end of
   // a dynamic-K item comes from the item (-1 here).
@@ -607,7 +627,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     } else {
       at.setup(wave, lane, a.a_ld, it.m_valid);
     }
-    bt.setup(wave, lane, a.b_ld, it.n_valid);
+    if constexpr (SWIGLU) bt.setup_paired(wave, lane, a.b_ld, it.n_valid, a.Nout - BNE);
+    else bt.setup(wave, lane, a.b_ld, it.n_valid);
   };
   setup(li);
   // compute cursor
@@ -666,7 +687,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // wave k % 4.  Rows and columns outside the tile read as 0.
   constexpr int NSC = (BM + BN) / 64;
   auto issue_scales = [&](const Item& it) {
-    if constexpr (EPI != EPI_NONE) {
+    if constexpr (SCALED) {
       const float* rows = a.sa + ((EPI == EPI_ROW_COL) ? it.rowbase : (int64_t)it.g * a.Mout + it.rowbase);
       const float* cols = a.sb + (int64_t)it.g * a.Nout + it.n0;
       const i32x4 rr = make_rsrc_words(rows, (int64_t)it.m_valid * 4);
@@ -808,10 +829,84 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // exactly NST vector-memory stores per lane (lanes outside the tile store
   // out of range).
   auto epilogue = [&](uint8_t* st, const Item& it) {
+    if constexpr (SWIGLU) {
+      // Waves 0-1 of each row half hold gate columns, waves 2-3 the up
+      // columns at the same positions (same lane layout).  Per 32-row block:
+      // the gate waves hand their bf16-rounded values to the up waves
+      // through LDS (lane-contiguous dwords, conflict-free), the up waves
+      // form act = silu(g) * u in fp32 from the bf16 values, round it and
+      // stage it for 16-byte stores of whole row segments.  Every wave
+      // issues the same NST stores (the gate waves' out of range), so the
+      // main loop's vector-memory waits count alike in all waves.
+      static_assert(NST == TI * 4 && WGN == 4 && TJ == 2 && WN == 64, "paired epilogue shape");
+      lds_sync();   // every wave is done reading st
+      uint32_t* xch = reinterpret_cast<uint32_t*>(st);   // [4 gate waves][16 dwords][64 lanes]
+      const bool up = wn >= 2;
+      const int pair = wm * 2 + (wn & 1);
+      uint16_t* stg_up = reinterpret_cast<uint16_t*>(st + 4 * 16 * 64 * 4) + pair * 32 * SROW;
+      const __amdgpu_buffer_rsrc_t cr =
+          make_rsrc(reinterpret_cast<uint16_t*>(a.C) + it.rowbase * a.c_ld + it.n0, 0x7FFFFFFF);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        if (!up) {
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int d = 0; d < 8; ++d)
+              xch[(pair * 16 + j * 8 + d) * 64 + lane] = pack_bf16x2_hw(acc[i][j][2 * d], acc[i][j][2 * d + 1]);
+        }
+        lds_sync();
+        if (up) {
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t g01 = xch[(pair * 16 + j * 8 + 2 * q) * 64 + lane];
+              const uint32_t g23 = xch[(pair * 16 + j * 8 + 2 * q + 1) * 64 + lane];
+              const uint32_t u01 = pack_bf16x2_hw(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+              const uint32_t u23 = pack_bf16x2_hw(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              const float g[4] = {bf16_to_f32(g01 & 0xFFFFu), bf16_to_f32(g01 >> 16), bf16_to_f32(g23 & 0xFFFFu),
+                                  bf16_to_f32(g23 >> 16)};
+              const float u[4] = {bf16_to_f32(u01 & 0xFFFFu), bf16_to_f32(u01 >> 16), bf16_to_f32(u23 & 0xFFFFu),
+                                  bf16_to_f32(u23 >> 16)};
+              float v[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] = g[r] / (1.f + expf(-g[r])) * u[r];
+              uint2 pk;
+              pk.x = pack_bf16x2(v[0], v[1]);
+              pk.y = pack_bf16x2(v[2], v[3]);
+              const int cw = 32 * j + 8 * q + 4 * (lane >> 5);
+              *reinterpret_cast<uint2*>(stg_up + (lane & 31) * SROW + cw) = pk;
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int q = lane + k * kWave;
+          const int rw = q >> 3, ch = q & 7;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          uint32_t vo = kOOB;
+          if (up) {
+            v = *reinterpret_cast<const uint4*>(stg_up + rw * SROW + ch * 8);
+            const int row = wm * WM + 32 * i + rw, col = (wn - 2) * WN + ch * 8;
+            vo = (row < it.m_valid && col < it.n_valid) ? (uint32_t)((row * a.c_ld + col) * 2) : kOOB;
+          }
+          i32x4 d;
+          d[0] = (int)v.x;
+          d[1] = (int)v.y;
+          d[2] = (int)v.z;
+          d[3] = (int)v.w;
+          __builtin_amdgcn_raw_buffer_store_b128(d, cr, (int)vo, 0, kPolicyStream);
+        }
+        lds_sync();   // exchange and staging are free for the next block
+      }
+      return;
+    }
     uint16_t* stg = reinterpret_cast<uint16_t*>(st + wave * WREG);
     float* rsc = reinterpret_cast<float*>(st + NW * WREG);  // [BM] 1 / row scale
     float* csc = rsc + BM;                                  // [BN] 1 / column scale
-    if constexpr (EPI != EPI_NONE) {
+    if constexpr (SCALED) {
       // every wave is done reading st, and the scale DMAs issued before this
       // k-step's LPS tile transfers (and whatever the stream-K combine
       // issued since, which it waited for) have landed
@@ -839,13 +934,13 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
           if (32 * i / ERW != er) continue;
           const int rw = 32 * i + (lane & 31);
           float rs = 1.f;
-          if constexpr (EPI != EPI_NONE) rs = rsc[r0 + rw];
+          if constexpr (SCALED) rs = rsc[r0 + rw];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int cw = 32 * j + 8 * q + 4 * (lane >> 5);   // column in the sub-tile
             float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
             float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-            if constexpr (EPI != EPI_NONE) {
+            if constexpr (SCALED) {
               const f32x4 cs4 = *reinterpret_cast<const f32x4*>(csc + c0 + cw);
               v0 = (v0 * cs4[0]) * rs;
               v1 = (v1 * cs4[1]) * rs;
@@ -1008,7 +1103,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
       if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
       else wait_vm_sync<(NS - 2) * LPS>();
       epi_prev = false;
-      if (EPI != EPI_NONE && cs + 1 == cend) issue_scales(ci);
+      if (SCALED && cs + 1 == cend) issue_scales(ci);
       const LoadCtx lx = prepare_loads(smem + lstage * STAGE);
       lstage = lstage + 1 == NS ? 0 : lstage + 1;
       compute(smem + stage * STAGE, lx);   // also issues the loads of lx
@@ -1076,7 +1171,7 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
   // host bound on the work: fixed-M tiles cover at most
   // floor(total_M / BM) + min(total_M, E) row slices
   int64_t work;
-  if (KIND == FIXED_M) work = fixed_m_capacity(a.total_rows, a.E, BM) * cdiv(a.Nout, BN) * cdiv(a.Kc, T::BK);
+  if (KIND == FIXED_M) work = fixed_m_capacity(a.total_rows, a.E, BM) * cdiv(a.Nout, EPI == EPI_SWIGLU ? BN / 2 : BN) * cdiv(a.Kc, T::BK);
   else work = (int64_t)a.E * cdiv(a.Mout, BM) * cdiv(a.Nout, BN);
   if (work <= 0) return hipSuccess;
   auto kern = gmm_kernel<BM, BN, NS, A_KC, B_KC, KIND, ELEM, EPI, NW>;
@@ -1099,6 +1194,10 @@ hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t strea
   if (L.elem == EL_BF16) {
     if (L.kind == FIXED_M) {
       if (!L.a_kc) return hipErrorInvalidValue;
+      if (L.swiglu) {
+        if (L.b_kc) return hipErrorInvalidValue;
+        return launch_one<128, 256, 3, true, false, FIXED_M, EL_BF16, EPI_SWIGLU, kGemmWaves>(a, stream);
+      }
       if (L.b_kc) return launch_one<128, 256, 3, true, true, FIXED_M, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
       return launch_one<128, 256, 3, true, false, FIXED_M, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);
     }

@@ -36,7 +36,11 @@ hipError_t launch_build_worklist(const BuildArgs& a, hipStream_t stream);
 // ---------------------------------------------------------------------------
 enum Kind { FIXED_M = 0, DYNAMIC_K = 1 };
 enum Elem { EL_BF16 = 0, EL_FP8 = 1, EL_I4 = 2 };
-enum Epi { EPI_NONE = 0, EPI_ROW_COL = 1, EPI_GROUP = 2 };
+// EPI_SWIGLU (bf16 fixed-M, B as [K, N]): the tile's 256 columns are 128
+// gate columns n0.. and the matching 128 up columns I + n0.. of B, and the
+// output is act[r, n] = silu(h[r, n]) * h[r, I + n] with h rounded to bf16
+// first (I = the output width, Nout)
+enum Epi { EPI_NONE = 0, EPI_ROW_COL = 1, EPI_GROUP = 2, EPI_SWIGLU = 3 };
 
 struct GemmArgs {
   const void* A;
@@ -76,6 +80,7 @@ struct GemmLaunch {
   int kind;      // Kind
   int elem;      // Elem of A (B is the same except EL_I4)
   bool a_kc, b_kc;
+  bool swiglu = false;   // EPI_SWIGLU epilogue (bf16 fixed-M, b_kc false)
 };
 
 // Output tile of the GEMM kernel for a launch (rows x columns).

@@ -139,3 +139,45 @@ def test_gmm_fwd_gather_equals_the_sorted_copy(T, k, E, bm, K, N, trans_b):
     xs = oracle.gather_rows(x, k, al["sorted_token_ids"])[:n]
     ref = oracle.gmm_fwd_bf16(xs, W, al["padded_sizes"], trans_b=trans_b)
     assert rel_fro(oracle.bf16_to_f64(bf16_host(y_gath)[:n]), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("case", [
+    dict(E=3, M=300, K=136, I=136, gather=None),            # two column tiles, the second 8 wide
+    dict(E=5, M=700, K=64, I=264, gather=None),
+    dict(E=8, T=64, k=2, bm=16, K=256, I=128, gather=True),
+    dict(E=64, T=300, k=6, bm=32, K=200, I=392, gather=True),
+    dict(E=8, T=1500, k=2, bm=128, K=512, I=1024, gather=True),
+])
+def test_gmm_fwd_silu_mul_equals_the_unfused_steps(case):
+    """The GEMM with SiLU-and-mul in its epilogue is bit-identical to the GEMM
+    into h followed by the silu_mul kernel, with and without the gathered A
+    rows, and matches the oracle's silu_mul of the oracle GEMM."""
+    E, K, I = case["E"], case["K"], case["I"]
+    W1 = wl.stacked_normal_bf16(E, (K, 2 * I), 0.3, 11, wl.T_W1)
+    w1 = bf16_dev(W1)
+    if case["gather"]:
+        T, k, bm = case["T"], case["k"], case["bm"]
+        rng = np.random.default_rng(T)
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        x = wl.normal_bf16((T, K), 1.0, 11, wl.T_X)
+        p = mg.moe_permute(dev(ids), E, bm)
+        sizes, sids = p["padded_sizes"], p["sorted_token_ids"]
+        h = mg.gmm_fwd_gather(bf16_dev(x), sids, k, w1, sizes)
+        act = mg.gmm_fwd_silu_mul(bf16_dev(x), w1, sizes, sorted_token_ids=sids, top_k=k)
+        n = int(host(p["num_tokens_post_padded"])[0])
+        al = oracle.moe_align(ids, E, bm)
+        xa = oracle.gather_rows(x, k, al["sorted_token_ids"])[:n]
+        osz = al["padded_sizes"]
+    else:
+        M = case["M"]
+        osz = wl.random_group_sizes(E, M, 11, zero_frac=0.25)
+        x = wl.normal_bf16((M, K), 1.0, 11, wl.T_X)
+        sizes = dev(osz)
+        h = mg.gmm_fwd(bf16_dev(x), w1, sizes)
+        act = mg.gmm_fwd_silu_mul(bf16_dev(x), w1, sizes)
+        n, xa = M, x
+    ref_act = mg.silu_mul(h[:n].contiguous())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_host(act)[:n], bf16_host(ref_act))
+    ref = oracle.silu_mul(oracle.gmm_fwd_bf16(xa, W1, osz))
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(act)[:n]), ref) <= 1e-2
