@@ -14,9 +14,9 @@ the source pages:
 * FP8 rowwise and per-group colwise quantizers -- torchao commit "Optimize
   FP8 MoE backward pass" (commit message; colwise kernel in
   bench_colwise_block_configs.py);
-* token permutation, SiLU-and-mul and the top-k weighted sum -- applied-ai
-  issue "Column-major fused MoE" (moe_align_block_size docstring and example,
-  fused_moe).
+* router (softmax, top-k, optional renormalization), token permutation,
+  SiLU-and-mul and the top-k weighted sum -- applied-ai issue "Column-major
+  fused MoE" (moe_align_block_size docstring and example, fused_moe).
 
 Pins: every function here is checked by the ``-m "not gpu"`` tests against
 closed forms, library routines, brute force and the pages' worked example.
@@ -72,6 +72,7 @@ def _declare(lib):
         "or_gather_rows": (None, [_P, _I64, _I32, _I64, _P, _I64, _P]),
         "or_silu_mul": (None, [_P, _I64, _I64, _P]),
         "or_unpermute": (None, [_P, _P, _P, _I64, _I32, _I64, _P]),
+        "or_route_topk": (None, [_P, _I64, _I32, _I32, _I32, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -342,6 +343,18 @@ def silu_mul(h):
     act = np.empty((R, I2 // 2), np.float64)
     _lib().or_silu_mul(_ptr(h), R, I2 // 2, _ptr(act))
     return act
+
+
+def route_topk(logits, top_k, renormalize=False):
+    """fp32 logits [T, E] -> (ids int32 [T, top_k], weights fp64 [T, top_k]):
+    the top_k experts by probability, descending, ties to the lower index;
+    weights softmax probabilities (divided by their sum if renormalize)."""
+    z = _c(logits, np.float32)
+    T, E = z.shape
+    ids = np.empty((T, top_k), np.int32)
+    w = np.empty((T, top_k), np.float64)
+    _lib().or_route_topk(_ptr(z), T, E, top_k, int(bool(renormalize)), _ptr(ids), _ptr(w))
+    return ids, w
 
 
 def unpermute(Y, inv, weights, T, k):

@@ -495,3 +495,38 @@ void or_unpermute(const double* Y, const int32_t* inv, const float* w,
       out[t * H + h] = acc;
     }
 }
+
+/* Router: probabilities p = softmax(logits) in fp64 over each token's E
+ * logits; the token's experts are the top_k largest, in descending order
+ * ([P3] fused_moe: softmax of the gating output in fp32, then topk, then an
+ * optional division by the sum of the chosen weights).  The integer decision
+ * is taken on the fp32 logits themselves (softmax is increasing, so the
+ * order is the same), ties to the lower expert index; weights are
+ * p[id] (divided by their sum when renormalize). */
+void or_route_topk(const float* logits, int64_t T, int32_t E, int32_t top_k,
+                   int32_t renormalize, int32_t* ids, double* weights) {
+  for (int64_t t = 0; t < T; ++t) {
+    const float* z = logits + t * E;
+    double mx = -INFINITY;
+    for (int32_t e = 0; e < E; ++e)
+      if ((double)z[e] > mx) mx = (double)z[e];
+    double sum = 0.0;
+    for (int32_t e = 0; e < E; ++e) sum += exp((double)z[e] - mx);
+    double chosen = 0.0;
+    for (int32_t j = 0; j < top_k; ++j) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        int taken = 0;
+        for (int32_t i = 0; i < j; ++i)
+          if (ids[t * top_k + i] == e) taken = 1;
+        if (taken) continue;
+        if (best < 0 || z[e] > z[best]) best = e;
+      }
+      ids[t * top_k + j] = best;
+      weights[t * top_k + j] = exp((double)z[best] - mx) / sum;
+      chosen += weights[t * top_k + j];
+    }
+    if (renormalize)
+      for (int32_t j = 0; j < top_k; ++j) weights[t * top_k + j] /= chosen;
+  }
+}

@@ -426,3 +426,58 @@ def test_fused_moe_single_expert_is_dense_ffn():
     a = (torch.nn.functional.silu(h[:, :I]) * h[:, I:]).to(torch.bfloat16).double()
     y = (a @ W2).to(torch.bfloat16).double()
     np.testing.assert_allclose(out, y.numpy(), rtol=2 ** -7, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# Router: softmax -> top-k -> optional renormalization (applied-ai issue
+# "Column-major fused MoE", fused_moe)
+# --------------------------------------------------------------------------
+
+def test_route_topk_known_probabilities():
+    """Logits ln 1, ln 2, ln 5 give probabilities 1/8, 2/8, 5/8 exactly (up to
+    the fp32 rounding of the logarithms); top-2 renormalized is 5/7, 2/7."""
+    z = np.log(np.array([[1.0, 2.0, 5.0]])).astype(np.float32)
+    ids, w = oracle.route_topk(z, 2)
+    np.testing.assert_array_equal(ids, [[2, 1]])
+    np.testing.assert_allclose(w, [[5 / 8, 2 / 8]], rtol=1e-6)
+    ids, w = oracle.route_topk(z, 2, renormalize=True)
+    np.testing.assert_allclose(w, [[5 / 7, 2 / 7]], rtol=1e-6)
+
+
+def test_route_topk_two_experts_is_the_logistic():
+    """With two experts the larger probability is the logistic function of
+    the logit difference."""
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal((50, 2)).astype(np.float32)
+    ids, w = oracle.route_topk(z, 1)
+    d = np.abs(z[:, 0].astype(np.float64) - z[:, 1].astype(np.float64))
+    np.testing.assert_allclose(w[:, 0], 1.0 / (1.0 + np.exp(-d)), rtol=1e-12)
+    np.testing.assert_array_equal(ids[:, 0], np.where(z[:, 1] > z[:, 0], 1, 0))
+
+
+def test_route_topk_matches_a_full_sort_and_is_shift_invariant():
+    """ids equal a full lexicographic sort by (-logit, index) on small random
+    inputs with repeated values; adding a constant to a token's logits
+    changes nothing; k = E with renormalization sums to 1 and puts all
+    experts in descending order."""
+    rng = np.random.default_rng(1)
+    z = rng.integers(-3, 4, size=(40, 9)).astype(np.float32)   # many ties
+    for k in (1, 3, 9):
+        ids, w = oracle.route_topk(z, k)
+        for t in range(z.shape[0]):
+            order = sorted(range(9), key=lambda e: (-z[t, e], e))[:k]
+            assert list(ids[t]) == order
+        assert np.all(np.diff(w, axis=1) <= 0)
+        ids2, w2 = oracle.route_topk(z + np.float32(2.0), k)
+        np.testing.assert_array_equal(ids2, ids)
+        np.testing.assert_allclose(w2, w, rtol=1e-12)
+    ids, w = oracle.route_topk(z, 9, renormalize=True)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-12)
+    assert all(sorted(r) == list(range(9)) for r in ids)
+
+
+def test_route_topk_equal_logits():
+    """All logits equal: experts 0..k-1 in order, each with probability 1/E."""
+    ids, w = oracle.route_topk(np.zeros((3, 6), np.float32), 4)
+    np.testing.assert_array_equal(ids, np.tile(np.arange(4), (3, 1)))
+    np.testing.assert_allclose(w, 1 / 6, rtol=1e-15)
