@@ -335,6 +335,9 @@ def _row_cases(torch, mg):
     x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
     w1 = (torch.randn(E, H, 2 * I, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
     w2 = (torch.randn(E, I, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    logits = torch.randn(T, E, generator=g, device="cuda")
+    yield ("A0_route_topk", f"router: fp32 softmax + top-{k} of {T}x{E} logits (renormalized)",
+           lambda: mg.route_topk(logits, k, renormalize=True), T * E * 4 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
     bm = 128
     p = mg.moe_permute(ids, E, bm, x=x)
     ntpp = int(p["num_tokens_post_padded"].item())

@@ -284,6 +284,24 @@ int quantize_int4_weights(const void* w, int32_t E, int32_t K, int32_t N,
 /* Token permutation for the token-sorted fused path ([FMOE]).               */
 /* ------------------------------------------------------------------------ */
 
+/* Router ([FMOE] fused_moe: softmax of the gating output in fp32, topk,
+ * then, with renormalize, division by the sum of the chosen weights).  Per
+ * token t:
+ *   p = softmax(logits[t, :]) in fp32
+ *   topk_ids[t, j]     = the j-th largest expert by probability (j ascending
+ *                        = descending probability; ties to the lower index)
+ *   topk_weights[t, j] = p[topk_ids[t, j]] (divided by the sum over j of
+ *                        those when renormalize != 0)
+ * logits fp32 [T, E] row-major; topk_ids int32 [T, top_k]; topk_weights
+ * fp32 [T, top_k]; all device memory, caller-owned.  The choice is made on
+ * the logits themselves (softmax is increasing), so ids are exactly those
+ * of the fp32 logits.  One wave per token, no workspace.  Errors: T < 0,
+ * E outside [1, MG_MAX_EXPERTS], top_k outside [1, min(E, 64)], NULL
+ * pointers with T > 0 -> MG_EINVAL. */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t top_k,
+                   int32_t renormalize, int32_t* topk_ids, float* topk_weights,
+                   mg_stream_t stream);
+
 /* Capacity helpers: sorted_token_ids holds T*k + E*(block_m-1) entries;
  * expert_ids holds ceil(that / block_m). */
 int64_t moe_sorted_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m);

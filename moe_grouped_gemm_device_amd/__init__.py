@@ -59,6 +59,7 @@ _SIGS = {
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_unpermute": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "silu_mul": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "moe_route_topk": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "mg_last_error": (ctypes.c_char_p, []),
     "mg_version": (ctypes.c_char_p, []),
 }
@@ -396,6 +397,20 @@ def moe_permute(topk_ids, E, block_m, x=None, ws=None, stream=None):
           _stream(stream))
     return dict(sorted_token_ids=sorted_ids[:cap], expert_ids=expert_ids[:nblk], num_tokens_post_padded=ntpp,
                 inv=inv[:T * k], padded_sizes=padded, x_sorted=None if xs is None else xs[:cap])
+
+
+def route_topk(logits, top_k, renormalize=False, stream=None):
+    """Router: fp32 softmax of each token's logits, its top_k experts in
+    descending order (ties to the lower index) and their probabilities
+    (divided by their sum with renormalize).  Returns (topk_ids int32 [T, k],
+    topk_weights fp32 [T, k])."""
+    _need(logits, torch.float32, "logits", 2)
+    T, E = logits.shape
+    ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    _call("moe_route_topk", _ptr(logits), T, E, int(top_k), int(bool(renormalize)), _ptr(ids), _ptr(w),
+          _stream(stream))
+    return ids, w
 
 
 def moe_unpermute(y_sorted, inv, topk_weights, T, k, out=None, stream=None):

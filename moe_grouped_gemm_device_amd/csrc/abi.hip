@@ -595,6 +595,17 @@ int moe_unpermute(const void* y_sorted, const int32_t* inv_pos, const float* top
                     "moe_unpermute");
 }
 
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t renormalize,
+                   int32_t* topk_ids, float* topk_weights, mg_stream_t stream) {
+  if (T < 0) return fail(MG_EINVAL, "T=%lld must be >= 0", (long long)T);
+  if (E < 1 || E > MG_MAX_EXPERTS) return fail(MG_EINVAL, "E=%d outside [1, %d]", E, MG_MAX_EXPERTS);
+  if (top_k < 1 || top_k > E || top_k > 64) return fail(MG_EINVAL, "top_k=%d outside [1, min(E, 64)]", top_k);
+  if (T == 0) return ok();
+  if (!logits || !topk_ids || !topk_weights) return fail(MG_EINVAL, "NULL tensor argument");
+  return hip_status(launch_route_topk(logits, T, E, top_k, renormalize != 0, topk_ids, topk_weights, S(stream)),
+                    "moe_route_topk");
+}
+
 int silu_mul(const void* h, int64_t rows, int32_t inter, void* act, mg_stream_t stream) {
   if (rows < 0 || inter < 1) return fail(MG_EINVAL, "rows >= 0 and inter >= 1 required");
   if (inter % 8) return fail(MG_EUNSUPPORTED, "inter must be a multiple of 8");

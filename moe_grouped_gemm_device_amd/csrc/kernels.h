@@ -118,6 +118,8 @@ hipError_t launch_moe_permute_ws(const int32_t* topk_ids, int64_t T, int32_t k, 
 hipError_t launch_moe_unpermute(const uint16_t* y, const int32_t* inv, const float* w,
                                 int64_t T, int32_t k, int32_t hidden, uint16_t* out,
                                 hipStream_t stream);
+hipError_t launch_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t renorm, int32_t* ids,
+                             float* wts, hipStream_t stream);
 hipError_t launch_silu_mul(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* act,
                            hipStream_t stream);
 

@@ -271,3 +271,104 @@ hipError_t launch_silu_mul(const uint16_t* h, int64_t rows, int32_t inter, uint1
 }
 
 }  // namespace mg
+
+namespace mg {
+
+// ---------------------------------------------------------------------------
+// K0: router.  Per token: softmax of its E logits in fp32, its top_k experts
+// in descending order and their probabilities, optionally divided by their
+// sum (applied-ai issue "Column-major fused MoE", fused_moe: fp32 softmax of
+// the gating output, topk, renormalize).  One wave per token, VPL logits per
+// lane.  The experts are chosen on the logits (softmax is increasing, so the
+// order is that of the probabilities), ties to the lower expert index.  The
+// max and sum are butterfly reductions, identical in every lane.
+// ---------------------------------------------------------------------------
+template <int VPL>
+__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int64_t T, int32_t E,
+                                                          int32_t k, int32_t renorm, int32_t* __restrict__ ids,
+                                                          float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += stride) {
+    const float* z = logits + t * E;
+    float v[VPL], ex[VPL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? z[e] : -INFINITY;
+      mx = fmaxf(mx, v[i]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      ex[i] = (lane + 64 * i < E) ? expf(v[i] - mx) : 0.f;
+      s += ex[i];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    uint32_t taken = 0;       // bit i: this lane's logit i is chosen
+    float chosen = 0.f;       // sum of the chosen probabilities, j ascending
+    int my_id = 0;            // lane j keeps the j-th choice
+    float my_w = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;    // no candidate
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !((taken >> i) & 1u) && (bi == 0x7FFFFFFF || v[i] > bv)) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        const bool better = oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+        if (better) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      // bi is the same in every lane; its owner marks it and supplies exp
+      const int owner = bi & 63, slot = bi >> 6;
+      float mine = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (i == slot) mine = ex[i];
+      if (lane == owner) taken |= 1u << slot;
+      const float p = __shfl(mine, owner, 64) / s;
+      if (lane == j) {
+        my_id = bi;
+        my_w = p;
+      }
+      chosen += p;
+    }
+    if (renorm) my_w = my_w / chosen;
+    if (lane < k) {
+      ids[t * k + lane] = my_id;
+      wts[t * k + lane] = my_w;
+    }
+  }
+}
+
+hipError_t launch_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t renorm, int32_t* ids,
+                             float* wts, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int64_t want = (T + 3) / 4;
+  const int blocks = (int)(want < 16384 ? want : 16384);
+  const int vpl = (E + 63) / 64;
+  if (vpl <= 1) hipLaunchKernelGGL(route_topk_kernel<1>, dim3(blocks), dim3(256), 0, stream, logits, T, E, k, renorm, ids, wts);
+  else if (vpl <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, dim3(blocks), dim3(256), 0, stream, logits, T, E, k, renorm, ids, wts);
+  else if (vpl <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, dim3(blocks), dim3(256), 0, stream, logits, T, E, k, renorm, ids, wts);
+  else if (vpl <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, dim3(blocks), dim3(256), 0, stream, logits, T, E, k, renorm, ids, wts);
+  else if (vpl <= 16) hipLaunchKernelGGL(route_topk_kernel<16>, dim3(blocks), dim3(256), 0, stream, logits, T, E, k, renorm, ids, wts);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mg

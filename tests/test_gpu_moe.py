@@ -181,3 +181,40 @@ def test_gmm_fwd_silu_mul_equals_the_unfused_steps(case):
     np.testing.assert_array_equal(bf16_host(act)[:n], bf16_host(ref_act))
     ref = oracle.silu_mul(oracle.gmm_fwd_bf16(xa, W1, osz))
     assert rel_fro(oracle.bf16_to_f64(bf16_host(act)[:n]), ref) <= 1e-2
+
+
+@pytest.mark.parametrize("T,E,k,renorm", [
+    (1, 8, 2, False), (4096, 8, 2, False), (16384, 64, 6, True), (300, 1024, 8, True),
+    (77, 65, 3, False), (50, 130, 64, True), (10, 3, 3, True),
+])
+def test_route_topk_matches_oracle(T, E, k, renorm):
+    """Expert ids bit-exact (the choice is made on the fp32 logits on both
+    sides, ties to the lower index: a quarter of the logits are rounded to
+    integers so ties occur); probabilities within fp32 rounding of the fp64
+    softmax."""
+    rng = np.random.default_rng(T + E)
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    z[:, : max(E // 4, 1)] = np.round(z[:, : max(E // 4, 1)])
+    ids, w = mg.route_topk(dev(z), k, renormalize=renorm)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route_topk(z, k, renormalize=renorm)
+    np.testing.assert_array_equal(host(ids), ref_ids)
+    np.testing.assert_allclose(host(w), ref_w, rtol=1e-5, atol=1e-30)
+
+
+def test_router_feeds_the_fused_path():
+    """Router logits -> device top-k -> align -> fused FFN, against the oracle
+    taking the same steps."""
+    T, E, k, H, I = 96, 8, 2, 256, 128
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    x = wl.normal_bf16((T, H), 1.0, 5, wl.T_X)
+    w1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.05, 5, wl.T_W1)
+    w2 = wl.stacked_normal_bf16(E, (I, H), 0.05, 5, wl.T_W2)
+    ids, w = mg.route_topk(dev(z), k, renormalize=True)
+    out, _ = mg.fused_moe(bf16_dev(x), bf16_dev(w1), bf16_dev(w2), ids, w, block_m=16)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route_topk(z, k, renormalize=True)
+    np.testing.assert_array_equal(host(ids), ref_ids)
+    ref, _ = oracle.fused_moe(x, w1, w2, ref_ids, ref_w.astype(np.float32), 16)
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), ref) <= BF16_TOL
