@@ -376,6 +376,21 @@ def _row_cases(torch, mg):
         yield (f"C3_fused_ffn_T{Tsmall}", f"end to end, {experts} experts touched: weight bytes of those experts",
                lambda: mg.fused_moe(xsub, w1, w2, sub_ids, sub_w, ws=wsf),
                experts * (H * 2 * I + I * H) * 2, "GB/s", PEAK_HBM_GBS, 5)
+    # the same FFN with int4 expert weights (per-128-K bf16 scales) and fp8
+    # activations, decode-sized token counts
+    w1_4, s1 = mg.quantize_int4_weights(w1)
+    w2_4, s2 = mg.quantize_int4_weights(w2)
+    del w1, w2
+    torch.cuda.empty_cache()
+    for Tsmall in (1, 64):
+        sub_ids, sub_w = ids[:Tsmall].contiguous(), wts[:Tsmall].contiguous()
+        xsub = x[:Tsmall].contiguous()
+        experts = int(torch.unique(sub_ids).numel())
+        int4_bytes = experts * ((H * 2 * I + I * H) // 2 + (H // 128 * 2 * I + I // 128 * H) * 2)
+        yield (f"C3xC4_fused_ffn_f8i4_T{Tsmall}",
+               f"int4-weight FFN end to end, {experts} experts touched: int4 weight and scale bytes of those experts",
+               lambda: mg.fused_moe_f8i4(xsub, w1_4, s1, w2_4, s2, sub_ids, sub_w, ws=wsf),
+               int4_bytes, "GB/s", PEAK_HBM_GBS, 5)
 
 
 def row_measurements(torch, mg):

@@ -399,6 +399,30 @@ def moe_permute(topk_ids, E, block_m, x=None, ws=None, stream=None):
                 inv=inv[:T * k], padded_sizes=padded, x_sorted=None if xs is None else xs[:cap])
 
 
+def fused_moe_f8i4(x, w1_4, s1, w2_4, s2, topk_ids, topk_weights, block_m=16, ws=None, stream=None):
+    """Token-sorted MoE expert FFN with int4 expert weights and fp8
+    activations, for decode-sized token counts: align + gather -> rowwise
+    e4m3 quantization -> F8I4 GEMM1 -> SiLU*mul -> rowwise e4m3 quantization
+    -> F8I4 GEMM2 -> top-k weighted combine.  Weights as quantize_int4_weights
+    returns them: w1_4 uint8 [E, 2I, H/2] with s1 bf16 [E, H/128, 2I] (from
+    W1 [E, H, 2I]), w2_4 uint8 [E, H, I/2] with s2 bf16 [E, I/128, H] (from
+    W2 [E, I, H]).  Every weight tile is streamed once per 32 sorted rows, so
+    this path suits small T; large T belongs on the bf16 or fp8 kernels.
+    Returns (out bf16 [T, H], dict of the intermediates)."""
+    T, k = topk_ids.shape
+    E = w1_4.shape[0]
+    p = moe_permute(topk_ids, E, block_m, x=x, stream=stream)
+    xs, sizes = p["x_sorted"], p["padded_sizes"]
+    ws = workspace(E, xs.shape[0], x.device) if ws is None else ws
+    xq, sx = quantize_rowwise_fp8(xs, stream=stream)
+    h1 = gmm_fwd_f8i4(xq, sx, w1_4, s1, sizes, ws=ws, stream=stream)
+    act = silu_mul(h1, stream=stream)
+    aq, sa = quantize_rowwise_fp8(act, stream=stream)
+    y2 = gmm_fwd_f8i4(aq, sa, w2_4, s2, sizes, ws=ws, stream=stream)
+    out = moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream)
+    return out, dict(permute=p, xq=xq, sx=sx, h1=h1, act=act, aq=aq, sa=sa, y2=y2)
+
+
 def route_topk(logits, top_k, renormalize=False, stream=None):
     """Router: fp32 softmax of each token's logits, its top_k experts in
     descending order (ties to the lower index) and their probabilities

@@ -218,3 +218,46 @@ def test_router_feeds_the_fused_path():
     np.testing.assert_array_equal(host(ids), ref_ids)
     ref, _ = oracle.fused_moe(x, w1, w2, ref_ids, ref_w.astype(np.float32), 16)
     assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_fused_moe_f8i4_stages_match_the_oracle(T):
+    """The int4-weight fused FFN, stage by stage, against the oracle fed the
+    same quantized operands: the int4 weights and the e4m3 codes of the
+    gathered rows and of the activations are bit-exact; each F8I4 GEMM is
+    within the fp8 tolerance of the oracle's fp64 product of the dequantized
+    operands; SiLU*mul and the combine within bf16 rounding."""
+    E, k, H, I, bm = 8, 2, 256, 256, 16
+    ids, w = wl.softmax_topk_routing(T, E, k, 3)
+    x = wl.normal_bf16((T, H), 1.0, 3, wl.T_X)
+    W1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.05, 3, wl.T_W1)
+    W2 = wl.stacked_normal_bf16(E, (I, H), 0.05, 3, wl.T_W2)
+    w1_4, s1 = mg.quantize_int4_weights(bf16_dev(W1))
+    w2_4, s2 = mg.quantize_int4_weights(bf16_dev(W2))
+    out, st = mg.fused_moe_f8i4(bf16_dev(x), w1_4, s1, w2_4, s2, dev(ids), dev(w), block_m=bm)
+    torch.cuda.synchronize()
+    p1, q1 = oracle.quant_int4(oracle.bf16_to_f64(W1), 128)
+    p2, q2 = oracle.quant_int4(oracle.bf16_to_f64(W2), 128)
+    np.testing.assert_array_equal(host(w1_4), p1)
+    np.testing.assert_array_equal(bf16_host(s1), q1)
+    np.testing.assert_array_equal(host(w2_4), p2)
+    np.testing.assert_array_equal(bf16_host(s2), q2)
+    al = oracle.moe_align(ids, E, bm)
+    n, sizes = al["num_tokens_post_padded"], al["padded_sizes"]
+    xq, sx = oracle.quant_rowwise(oracle.gather_rows(x, k, al["sorted_token_ids"])[:n])
+    np.testing.assert_array_equal(host(st["xq"])[:n], xq)
+    np.testing.assert_array_equal(host(st["sx"])[:n], sx)
+    h1_ref = oracle.gmm_fwd(oracle.dequant_rowwise(xq, sx), oracle.dequant_int4(p1, q1, 128), sizes)
+    h1 = bf16_host(st["h1"])[:n]
+    assert rel_fro(oracle.bf16_to_f64(h1), h1_ref) <= 2e-2
+    act_ref = oracle.silu_mul(oracle.bf16_to_f64(h1))
+    act = bf16_host(st["act"])[:n]
+    assert rel_fro(oracle.bf16_to_f64(act), act_ref) <= 4e-3
+    aq, sa = oracle.quant_rowwise(act)
+    np.testing.assert_array_equal(host(st["aq"])[:n], aq)
+    np.testing.assert_array_equal(host(st["sa"])[:n], sa)
+    y2_ref = oracle.gmm_fwd(oracle.dequant_rowwise(aq, sa), oracle.dequant_int4(p2, q2, 128), sizes)
+    y2 = bf16_host(st["y2"])[:n]
+    assert rel_fro(oracle.bf16_to_f64(y2), y2_ref) <= 2e-2
+    out_ref = oracle.unpermute(oracle.bf16_to_f64(y2), al["inv"], w, T, k)
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), out_ref) <= BF16_TOL
