@@ -14,8 +14,13 @@
 // values) with two byte permutes, and runs the fp8 MFMA per 128-long K chunk
 // into a fresh accumulator that is then scaled by that chunk's bf16 weight
 // scale (keeping the dequantization exact) and added to the running sum.
-// The four waves of a workgroup split K; their partial tiles are summed in
-// LDS, divided by the row scale of the activations and rounded to bf16.
+// The waves of a workgroup (8 for contractions of 64 or more chunks, else 4)
+// split K.  Each wave requests the operands of its next chunk before it
+// computes the current one, so two chunks stream per wave; the loads' offsets
+// are opaque to the compiler, which would otherwise branch around the
+// out-of-range loads and drain every load in flight.  The partial tiles are
+// summed in LDS in wave order, divided by the row scale of the activations
+// and rounded to bf16.
 #include "kernels.h"
 #include "worklist.h"
 
@@ -54,7 +59,6 @@ __device__ inline i32x8 i4x32_to_e4m3(const uint4& w) {
 
 constexpr int F_BM = kF8I4RowTile;
 constexpr int F_BN = 32;
-constexpr int F_UNROLL = 1;   // K chunks whose operands are requested together
 constexpr uint32_t F_OOB = 0x80000000u;   // offset past any buffer: the load returns zeros
 
 __device__ inline __amdgpu_buffer_rsrc_t f_rsrc(const void* base, int64_t bytes) {
@@ -62,8 +66,22 @@ __device__ inline __amdgpu_buffer_rsrc_t f_rsrc(const void* base, int64_t bytes)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, 0x00020000);
 }
 
-__global__ void __launch_bounds__(256) f8i4_kernel(GemmArgs a) {
-  __shared__ float red[4][F_BM * F_BN];
+
+// One 128-long K chunk of a wave's work: the two 64-long halves of the
+// weight fragment (int4, 16 bytes each), the chunk's bf16 weight scale, and
+// the two matching fp8 activation fragments.
+struct F8I4Chunk {
+  i32x4 w[2];
+  float sc;
+  i32x8 x[2];
+};
+
+// F_WAVES waves per workgroup, each owning a contiguous run of K chunks: 8
+// for long contractions (many chunks per wave to keep streaming), 4
+// otherwise (less reduction work per tile).
+template <int F_WAVES>
+__global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
+  __shared__ float red[F_WAVES][F_BM * F_BN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.Kc;
   const int N = a.Nout;
@@ -83,7 +101,7 @@ __global__ void __launch_bounds__(256) f8i4_kernel(GemmArgs a) {
   const uint8_t* w4 = reinterpret_cast<const uint8_t*>(a.B);
 
   // chunk range of this wave
-  const int per = (nchunk + 3) / 4;
+  const int per = (nchunk + F_WAVES - 1) / F_WAVES;
   const int j0 = wave * per;
   const int j1 = j0 + per < nchunk ? j0 + per : nchunk;
 
@@ -108,70 +126,76 @@ __global__ void __launch_bounds__(256) f8i4_kernel(GemmArgs a) {
     const uint32_t xrow = (uint32_t)((row0 + col) * (int64_t)K);
     const uint32_t srow = (uint32_t)((n0 + col) * 2);
 
+    // Requests every operand of chunk j (zeros past the wave's range).  The
+    // weights keep the default cache policy although they are read once: a
+    // lane's 16 bytes are a quarter of a 64-byte run whose 128-byte line the
+    // next chunk reads too, and non-temporal loads fetched such lines from
+    // HBM twice (measured: 1.9 -> 3.0 TB/s at 16 routed rows over 128
+    // experts).
+    auto load = [&](int j, F8I4Chunk& c) {
+      const bool live = j < j1;
+      // k = 128 j + 64 s + 32 half .. +32  ->  weight bytes (128 j + 64 s + 32 half) / 2
+      uint32_t wo = (live && col_ok) ? wrow + j * 64 + half * 16 : F_OOB;
+      asm volatile("" : "+v"(wo));   // opaque: no per-lane branch around the loads
+      c.w[0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
+      c.w[1] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 32, 0);
+      uint32_t so = (live && col_ok) ? srow + (uint32_t)j * (uint32_t)N * 2u : F_OOB;
+      asm volatile("" : "+v"(so));
+      c.sc = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)so, 0, 0));
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        uint32_t xo = (live && row_ok) ? xrow + j * 128 + sh * 64 + half * 32 : F_OOB;
+        asm volatile("" : "+v"(xo));
+        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 0, 0);
+        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 16, 0);
+        c.x[sh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    // chunk product into a fresh accumulator, scaled by the chunk's weight
+    // scale and added to the running sum
+    auto compute = [&](const F8I4Chunk& c) {
+      f32x16 part;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[v] = 0.f;
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const uint4 wq = make_uint4((uint32_t)c.w[sh][0], (uint32_t)c.w[sh][1], (uint32_t)c.w[sh][2],
+                                    (uint32_t)c.w[sh][3]);
+        const i32x8 bf = i4x32_to_e4m3(wq);
+        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(c.x[sh], bf, part, 0, 0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] += part[v] * c.sc;
+    };
 
-    for (int jb = j0; jb < j1; jb += F_UNROLL) {
-      // the batch's weights, chunk scales and activation fragments, all in
-      // flight before the first MFMA.  The weights keep the default cache
-      // policy although they are read once: a lane's 16 bytes are a quarter
-      // of a 64-byte run whose 128-byte line the next chunk reads too, and
-      // non-temporal loads fetched such lines from HBM twice (measured:
-      // 1.9 -> 3.0 TB/s at 16 routed rows over 128 experts).
-      i32x4 wv[F_UNROLL][2];
-      float sc[F_UNROLL];
-      i32x8 af[F_UNROLL][2];
-#pragma unroll
-      for (int u = 0; u < F_UNROLL; ++u) {
-        const int j = jb + u;
-        const bool live = j < j1;
-        // k = 128 j + 64 s + 32 half .. +32  ->  weight bytes (128 j + 64 s + 32 half) / 2
-        const uint32_t wo = (live && col_ok) ? wrow + j * 64 + half * 16 : F_OOB;
-        wv[u][0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
-        wv[u][1] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(wo == F_OOB ? F_OOB : wo + 32), 0, 0);
-        const uint32_t so = (live && col_ok) ? srow + (uint32_t)j * (uint32_t)N * 2u : F_OOB;
-        sc[u] = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)so, 0, 0));
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const uint32_t xo = (live && row_ok) ? xrow + j * 128 + sh * 64 + half * 32 : F_OOB;
-          const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 0, 0);
-          const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xo == F_OOB ? F_OOB : xo + 16), 0, 0);
-          af[u][sh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < F_UNROLL; ++u) {
-        if (jb + u < j1) {
-          f32x16 part;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) part[v] = 0.f;
-#pragma unroll
-          for (int sh = 0; sh < 2; ++sh) {
-            const uint4 wq = make_uint4((uint32_t)wv[u][sh][0], (uint32_t)wv[u][sh][1], (uint32_t)wv[u][sh][2],
-                                        (uint32_t)wv[u][sh][3]);
-            const i32x8 bf = i4x32_to_e4m3(wq);
-            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[u][sh], bf, part, 0, 0, 0, 127, 0, 127);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[v] += part[v] * sc[u];
-        }
-      }
+    // Two chunks in flight: chunk j + 1's operands are requested before
+    // chunk j is computed, so each wave keeps its next weight run streaming
+    // while the MFMAs of the current one run.
+    F8I4Chunk c0, c1;
+    load(j0, c0);
+    for (int j = j0; j < j1; j += 2) {
+      load(j + 1, c1);
+      compute(c0);
+      load(j + 2, c0);
+      if (j + 1 < j1) compute(c1);
     }
 
-    // cross-wave reduction of the four K slices
+    // cross-wave reduction of the K slices, in a fixed order
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = 8 * (v >> 2) + 4 * half + (v & 3);
       red[wave][r * F_BN + col] = acc[v];
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < (F_BM * F_BN) / 256; ++i) {
-      const int idx = tid + i * 256;
+    for (int idx = tid; idx < F_BM * F_BN; idx += F_WAVES * 64) {
       const int r = idx / F_BN, c = idx % F_BN;
       if (r < m_valid && n0 + c < N) {
-        const float sum = (red[0][idx] + red[1][idx]) + (red[2][idx] + red[3][idx]);
+        float sum = red[0][idx];
+#pragma unroll
+        for (int q = 1; q < F_WAVES; ++q) sum += red[q][idx];
         const float y = sum * (1.f / a.sa[row0 + r]);
         reinterpret_cast<uint16_t*>(a.C)[(row0 + r) * a.c_ld + n0 + c] = (uint16_t)f32_to_bf16_rne(y);
       }
@@ -183,9 +207,15 @@ __global__ void __launch_bounds__(256) f8i4_kernel(GemmArgs a) {
 hipError_t launch_f8i4(const GemmArgs& a, int64_t cap_entries, hipStream_t stream) {
   const int64_t max_items = cap_entries * cdiv(a.Nout, F_BN);
   if (max_items <= 0) return hipSuccess;
-  const int64_t slots = (int64_t)device_cu_count() * 8;   // 8 workgroups per CU: more loads in flight
+  // the register budget allows 4 waves per SIMD: 2 workgroups of 8 waves or
+  // 4 of 4 waves per CU, with as many again queued behind them
+  const bool wide = a.Kc / 128 >= 64;
+  const int64_t slots = (int64_t)device_cu_count() * (wide ? 4 : 8);
   const int grid = (int)(max_items < slots ? max_items : slots);
-  hipLaunchKernelGGL(f8i4_kernel, dim3(grid), dim3(256), (size_t)table_lds_bytes(a.E), stream, a);
+  if (wide)
+    hipLaunchKernelGGL(f8i4_kernel<8>, dim3(grid), dim3(8 * 64), (size_t)table_lds_bytes(a.E), stream, a);
+  else
+    hipLaunchKernelGGL(f8i4_kernel<4>, dim3(grid), dim3(4 * 64), (size_t)table_lds_bytes(a.E), stream, a);
   return hipGetLastError();
 }
 

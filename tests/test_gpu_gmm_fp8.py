@@ -86,7 +86,9 @@ def _f8i4_case(E, total_M, K, N, seed):
 
 
 @pytest.mark.parametrize("E,total_M,K,N,seed", [(8, 5, 256, 64, 0), (16, 100, 512, 136, 1), (128, 1, 5120, 8192, 2),
-                                                (128, 16, 5120, 8192, 3)])
+                                                (128, 16, 5120, 8192, 3),
+                                                # 70 chunks: the 8-wave kernel, 9 chunks per wave but 7 in the last
+                                                (4, 7, 8960, 96, 4)])
 def test_f8i4_sparse_m(E, total_M, K, N, seed):
     got, ref = _f8i4_case(E, total_M, K, N, seed)
     assert rel_fro(got, ref) <= FP8_TOL
