@@ -136,3 +136,38 @@ def test_permute_rejects_bad_arguments(lib):
     assert lib.moe_block_capacity(4, 3, 4, 4) == 6
     assert lib.moe_unpermute(_p(FAKE), _p(FAKE), None, 4, 2, 12, _p(FAKE), None) == mg.MG_EUNSUPPORTED
     assert lib.silu_mul(_p(FAKE), 4, 12, _p(FAKE), None) == mg.MG_EUNSUPPORTED
+
+
+def test_gathered_and_silu_gemms_reject_bad_arguments(lib):
+    need = lib.mg_workspace_bytes(4, 64)
+    ws = _p(0x10000)
+    # gmm_fwd_gather(x, T, ids, top_k, w, sizes, E, total_M, K, N, trans_b, y, ws, ws_bytes, stream)
+    g = lambda T, k, ids, K, N, wsb: lib.gmm_fwd_gather(_p(FAKE), T, ids, k, _p(FAKE), _p(FAKE), 4, 64, K, N, 0,
+                                                       _p(FAKE), ws, wsb, None)
+    assert g(32, 0, _p(FAKE), 64, 64, need) == mg.MG_EINVAL               # top_k < 1
+    assert g(-1, 2, _p(FAKE), 64, 64, need) == mg.MG_EINVAL               # T < 0
+    assert g(1 << 23, 4, _p(FAKE), 64, 64, need) == mg.MG_EINVAL          # T*top_k past 2^24
+    assert g(32, 2, None, 64, 64, need) == mg.MG_EINVAL                   # no sorted ids
+    assert g(32, 2, _p(FAKE), 60, 64, need) == mg.MG_EUNSUPPORTED         # K % 8
+    assert g(32, 2, _p(FAKE), 64, 64, need - 1) == mg.MG_EWORKSPACE
+    assert g(1 << 20, 2, _p(FAKE), 4096, 64, need) == mg.MG_EUNSUPPORTED  # x past 2 GiB
+    # gmm_fwd_silu_mul(x, T, ids, top_k, w1, sizes, E, total_M, K, I, act, ws, ws_bytes, stream)
+    s = lambda ids, k, K, I, wsb: lib.gmm_fwd_silu_mul(_p(FAKE), 32, ids, k, _p(FAKE), _p(FAKE), 4, 64, K, I,
+                                                      _p(FAKE), ws, wsb, None)
+    assert s(None, 1, 64, 36, need) == mg.MG_EUNSUPPORTED                 # I % 8
+    assert s(None, 1, 0, 64, need) == mg.MG_EINVAL                        # K = 0
+    assert s(_p(FAKE), 0, 64, 64, need) == mg.MG_EINVAL                   # gathered, top_k < 1
+    assert s(None, 1, 64, 64, need - 1) == mg.MG_EWORKSPACE
+    assert lib.gmm_fwd_silu_mul(None, 32, None, 1, _p(FAKE), _p(FAKE), 4, 64, 64, 64, _p(FAKE), ws, need,
+                                None) == mg.MG_EINVAL                   # no x
+
+
+def test_router_rejects_bad_arguments(lib):
+    r = lambda T, E, k, ids: lib.moe_route_topk(_p(FAKE), T, E, k, 0, ids, _p(FAKE), None)
+    assert r(-1, 8, 2, _p(FAKE)) == mg.MG_EINVAL
+    assert r(16, 0, 1, _p(FAKE)) == mg.MG_EINVAL
+    assert r(16, 1025, 2, _p(FAKE)) == mg.MG_EINVAL
+    assert r(16, 8, 9, _p(FAKE)) == mg.MG_EINVAL          # top_k > E
+    assert r(16, 128, 65, _p(FAKE)) == mg.MG_EINVAL       # top_k > 64
+    assert r(16, 8, 2, None) == mg.MG_EINVAL
+    assert r(0, 8, 2, None) == mg.MG_OK                   # nothing to route
