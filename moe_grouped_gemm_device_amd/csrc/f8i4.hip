@@ -32,28 +32,31 @@ constexpr uint32_t kPosHi = 0x4E4C4A48u;   // 4, 5, 6, 7  -> 48 4A 4C 4E
 constexpr uint32_t kNegLo = 0xCACCCED0u;   // -8,-7,-6,-5 -> D0 CE CC CA
 constexpr uint32_t kNegHi = 0xB8C0C4C8u;   // -4,-3,-2,-1 -> C8 C4 C0 B8
 
-// Four nibbles (in the low 16 bits of v) -> four e4m3 codes.
-__device__ inline uint32_t nib4_to_e4m3(uint32_t v) {
-  // spread nibbles into bytes: byte i = nibble i
-  const uint32_t sel = (v & 0xFu) | ((v >> 4 & 0xFu) << 8) | ((v >> 8 & 0xFu) << 16) | ((v >> 12 & 0xFu) << 24);
-  const uint32_t idx = sel & 0x07070707u;
+// Four bytes holding nibble values 0..15 -> their four e4m3 codes: one byte
+// permute into the table of 0..7, one into that of -8..-1, and a byte mask
+// from bit 3 to choose between them.
+__device__ inline uint32_t nibble_bytes_to_e4m3(uint32_t x) {
+  const uint32_t idx = x & 0x07070707u;
   const uint32_t pos = __builtin_amdgcn_perm(kPosHi, kPosLo, idx);
   const uint32_t neg = __builtin_amdgcn_perm(kNegHi, kNegLo, idx);
-  const uint32_t m = ((sel >> 3) & 0x01010101u) * 0xFFu;
+  const uint32_t s = (x >> 3) & 0x01010101u;
+  const uint32_t m = (s << 8) - s;   // 0xFF in the bytes whose bit 3 is set
   return (pos & ~m) | (neg & m);
 }
 
 // 16 bytes = 32 nibbles (k ascending, low nibble first) -> 32 e4m3 codes.
+// Per 4-byte word: the low nibbles (even k) and high nibbles (odd k) are
+// converted as two words of bytes, then interleaved back into k order.
 __device__ inline i32x8 i4x32_to_e4m3(const uint4& w) {
+  const uint32_t src[4] = {w.x, w.y, w.z, w.w};
   i32x8 r;
-  r[0] = (int)nib4_to_e4m3(w.x & 0xFFFFu);
-  r[1] = (int)nib4_to_e4m3(w.x >> 16);
-  r[2] = (int)nib4_to_e4m3(w.y & 0xFFFFu);
-  r[3] = (int)nib4_to_e4m3(w.y >> 16);
-  r[4] = (int)nib4_to_e4m3(w.z & 0xFFFFu);
-  r[5] = (int)nib4_to_e4m3(w.z >> 16);
-  r[6] = (int)nib4_to_e4m3(w.w & 0xFFFFu);
-  r[7] = (int)nib4_to_e4m3(w.w >> 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t even = nibble_bytes_to_e4m3(src[i] & 0x0F0F0F0Fu);
+    const uint32_t odd = nibble_bytes_to_e4m3((src[i] >> 4) & 0x0F0F0F0Fu);
+    r[2 * i] = (int)__builtin_amdgcn_perm(odd, even, 0x05010400u);       // k = 8i .. 8i+3
+    r[2 * i + 1] = (int)__builtin_amdgcn_perm(odd, even, 0x07030602u);   // k = 8i+4 .. 8i+7
+  }
   return r;
 }
 
