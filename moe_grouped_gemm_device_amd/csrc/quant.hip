@@ -216,6 +216,16 @@ __device__ inline int64_t colwise_tiles(const ColwiseArgs& a, int64_t nch) {
   return n;
 }
 
+// Workgroups that take part in a persistent loop over n equal items: with
+// r = ceil(n / grid) rounds, ceil(n / r) workgroups suffice, and every round
+// but the last keeps all of them busy.
+__device__ inline int64_t balanced_active(int64_t n) {
+  const int64_t G = gridDim.x;
+  if (n <= 0) return 0;
+  const int64_t rounds = (n + G - 1) / G;
+  return (n + rounds - 1) / rounds;
+}
+
 constexpr int QA_COLS = 256;   // columns per amax tile: a wave reads two 512-byte row runs per load
 
 __global__ void __launch_bounds__(256) colwise_zero_kernel(ColwiseArgs a) {
@@ -236,7 +246,11 @@ __global__ void __launch_bounds__(256) colwise_amax_kernel(ColwiseArgs a) {
   const int64_t n = colwise_tiles<QA_COLS>(a, nch);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cc = tid & 31, rg = tid >> 5;   // 8-column chunk of the tile, row group (rows rg + 8 j)
-  for (int64_t item = blockIdx.x; item < n; item += gridDim.x) {
+  // balanced rounds: the fewest workgroups that take the tiles in as many
+  // rounds as the grid needs, so no round runs with most of the grid idle
+  const int64_t active = balanced_active(n);
+  if ((int64_t)blockIdx.x >= active) return;
+  for (int64_t item = blockIdx.x; item < n; item += active) {
     int t, cb;
     int32_t chunk;
     colwise_tile<QA_COLS>(a, nch, item, t, chunk, cb);
@@ -301,7 +315,9 @@ __global__ void __launch_bounds__(256) colwise_cast_kernel(ColwiseArgs a) {
   const int64_t n = colwise_tiles<QC_COLS>(a, nch);
   const int tid = threadIdx.x;
   const int cc = tid & 7, rq = tid >> 3;   // 8-column chunk, row quad within 128 rows
-  for (int64_t item = n - 1 - blockIdx.x; item >= 0; item -= gridDim.x) {
+  const int64_t active = balanced_active(n);   // as in the amax pass
+  if ((int64_t)blockIdx.x >= active) return;
+  for (int64_t item = n - 1 - blockIdx.x; item >= 0; item -= active) {
     int t, cb;
     int32_t chunk;
     colwise_tile<QC_COLS>(a, nch, item, t, chunk, cb);
