@@ -135,17 +135,28 @@ def test_f8i4_128_rows_full_size_sampled():
 # (a token's output depends on its own rows only).
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T", [1, 64])
-def test_fused_ffn_mixtral_full_size_sampled(T):
-    E, k, H, I = 8, 2, 4096, 14336
-    ids, w = wl.softmax_topk_routing(T, E, k, 0)
-    x = wl.normal_bf16((T, H), 1.0, 0, wl.T_X)
+@pytest.fixture(scope="module")
+def mixtral_weights():
+    """W1 [8, 4096, 28672] and W2 [8, 14336, 4096] bf16 N(0, 0.02), host bits
+    and device copies, generated once for the module."""
+    E, H, I = 8, 4096, 14336
     w1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.02, 0, wl.T_W1)
     w2 = wl.stacked_normal_bf16(E, (I, H), 0.02, 0, wl.T_W2)
-    out, _ = mg.fused_moe(bf16_dev(x), bf16_dev(w1), bf16_dev(w2), dev(ids), dev(w))
+    return w1, w2, bf16_dev(w1), bf16_dev(w2)
+
+
+@pytest.mark.parametrize("T", [1, 64, 4096])   # block_m 16, 16 and 128 (the benchmarked launch)
+def test_fused_ffn_mixtral_full_size_sampled(T, mixtral_weights):
+    E, k, H, I = 8, 2, 4096, 14336
+    w1, w2, w1d, w2d = mixtral_weights
+    ids, w = wl.softmax_topk_routing(T, E, k, 0)
+    x = wl.normal_bf16((T, H), 1.0, 0, wl.T_X)
+    out, _ = mg.fused_moe(bf16_dev(x), w1d, w2d, dev(ids), dev(w))
     torch.cuda.synchronize()
     got = _f64(out)
     toks = np.unique(np.random.default_rng(1).choice(T, min(T, 4), replace=False))
+    if T > 64:
+        toks = np.unique(np.concatenate([toks, [0, T - 1]]))   # first and last token too
     for t in toks:
         used = np.unique(ids[t])
         remap = np.searchsorted(used, ids[t:t + 1])
