@@ -10,7 +10,7 @@ import torch
 import moe_grouped_gemm_device_amd as mg
 import oracle
 import workloads as wl
-from gpu_util import BF16_TOL, FP8_TOL, bf16_dev, bf16_host, dev, gpu, rel_fro, require_gpu
+from gpu_util import BF16_TOL, FP8_TOL, bf16_dev, bf16_host, dev, gpu, host, rel_fro, require_gpu
 
 pytestmark = gpu
 
@@ -162,4 +162,59 @@ def test_fused_ffn_mixtral_full_size_sampled(T, mixtral_weights):
         remap = np.searchsorted(used, ids[t:t + 1])
         ref, _ = oracle.fused_moe(x[t:t + 1], np.ascontiguousarray(w1[used]), np.ascontiguousarray(w2[used]),
                                   remap.astype(np.int32), w[t:t + 1], 1)
+        assert rel_fro(got[t:t + 1], ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_fused_ffn_f8i4_mixtral_full_size_sampled(T, mixtral_weights):
+    """The int4-weight fused FFN at the Mixtral shapes, stage by stage at
+    the sorted rows of sampled tokens, against the oracle fed the same
+    quantized operands: e4m3 codes and int4 weights bit-exact, the two F8I4
+    GEMMs within the fp8 tolerance, SiLU*mul and the combine within bf16
+    rounding."""
+    E, k, H, I = 8, 2, 4096, 14336
+    w1, w2, w1d, w2d = mixtral_weights
+    ids, w = wl.softmax_topk_routing(T, E, k, 0)
+    x = wl.normal_bf16((T, H), 1.0, 0, wl.T_X)
+    w1_4, s1 = mg.quantize_int4_weights(w1d)
+    w2_4, s2 = mg.quantize_int4_weights(w2d)
+    out, st = mg.fused_moe_f8i4(bf16_dev(x), w1_4, s1, w2_4, s2, dev(ids), dev(w))
+    torch.cuda.synchronize()
+    inv = host(st["permute"]["inv"])
+    xq, sx, aq, sa = host(st["xq"]), host(st["sx"]), host(st["aq"]), host(st["sa"])
+    h1, act, y2 = bf16_host(st["h1"]), bf16_host(st["act"]), bf16_host(st["y2"])
+    got = _f64(out)
+    codes = {}   # expert -> GPU int4 codes and scales of W1 and W2, checked bit-exact once
+
+    def expert_codes(e):
+        if e not in codes:
+            q1, c1 = oracle.quant_int4(oracle.bf16_to_f64(w1[e:e + 1]), 128)
+            q2, c2 = oracle.quant_int4(oracle.bf16_to_f64(w2[e:e + 1]), 128)
+            got_codes = (host(w1_4[e:e + 1]), bf16_host(s1[e:e + 1]), host(w2_4[e:e + 1]), bf16_host(s2[e:e + 1]))
+            for a, b in zip(got_codes, (q1, c1, q2, c2)):
+                np.testing.assert_array_equal(a, b)
+            codes[e] = got_codes
+        return codes[e]
+
+    one = np.array([1], np.int32)
+    toks = np.unique(np.random.default_rng(2).choice(T, min(T, 2), replace=False))
+    for t in toks:
+        y2_rows = []
+        for j in range(k):
+            e, p = int(ids[t, j]), int(inv[t * k + j])
+            q1, c1, q2, c2 = expert_codes(e)
+            rq, rs = oracle.quant_rowwise(x[t:t + 1])
+            np.testing.assert_array_equal(xq[p:p + 1], rq)
+            np.testing.assert_array_equal(sx[p:p + 1], rs)
+            h_ref = oracle.gmm_fwd(oracle.dequant_rowwise(rq, rs), oracle.dequant_int4(q1, c1, 128), one)
+            assert rel_fro(oracle.bf16_to_f64(h1[p:p + 1]), h_ref) <= FP8_TOL
+            act_ref = oracle.silu_mul(oracle.bf16_to_f64(h1[p:p + 1]))
+            assert rel_fro(oracle.bf16_to_f64(act[p:p + 1]), act_ref) <= 4e-3
+            aq_ref, as_ref = oracle.quant_rowwise(act[p:p + 1])
+            np.testing.assert_array_equal(aq[p:p + 1], aq_ref)
+            np.testing.assert_array_equal(sa[p:p + 1], as_ref)
+            y_ref = oracle.gmm_fwd(oracle.dequant_rowwise(aq_ref, as_ref), oracle.dequant_int4(q2, c2, 128), one)
+            assert rel_fro(oracle.bf16_to_f64(y2[p:p + 1]), y_ref) <= FP8_TOL
+            y2_rows.append(oracle.bf16_to_f64(y2[p:p + 1]))
+        ref = sum(float(w[t, j]) * y2_rows[j] for j in range(k))
         assert rel_fro(got[t:t + 1], ref) <= BF16_TOL
