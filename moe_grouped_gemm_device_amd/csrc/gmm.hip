@@ -126,17 +126,20 @@ __device__ inline uint32_t lds_address(uint8_t* p) { return (uint32_t)(uintptr_t
 // stage a transfer targets, so with the builtin it drains every transfer in
 // flight before each LDS read, which would serialise the K pipeline.  The
 // waits that order these transfers are all explicit (wait_vm_sync).  M0,
-// which supplies the LDS address, is restored before the statement ends.
+// which supplies the LDS address, is restored before the statement ends.  A
+// wait state separates the M0 write from the transfer that reads it (the
+// GFX9-family hazard between an SALU write of M0 and an LDS DMA, which the
+// compiler cannot see inside the asm).
 template <int POL>
 __device__ inline void dma16(const i32x4& r, uint32_t lds, uint32_t voff) {
   uint32_t save;
   if constexpr (POL == kPolicyStream) {
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(save)
                  : "v"(voff), "s"(lds), "s"(r)
                  : "memory");
   } else {
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(save)
                  : "v"(voff), "s"(lds), "s"(r)
                  : "memory");
@@ -158,7 +161,7 @@ __device__ inline void dma_pol(const i32x4& r, uint32_t lds, uint32_t voff, bool
 // 4 bytes per lane from global memory to LDS: lane l writes lds + 4 l.
 __device__ inline void dma4(const i32x4& r, uint32_t lds, uint32_t voff) {
   uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tbuffer_load_dword %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
                : "=&s"(save)
                : "v"(voff), "s"(lds), "s"(r)
                : "memory");
