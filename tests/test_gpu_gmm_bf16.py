@@ -250,3 +250,53 @@ def test_balanced_config_full_size():
     colsum = Xf.reshape(E, 128, K).sum(axis=1)
     assert rel_fro(dwh[:, :, 0], colsum) <= BF16_TOL
     assert (dwh == dwh[:, :, :1]).all()
+
+
+def test_captured_step_replays_bitwise():
+    """The library's calls are legal under stream capture (no allocation, no
+    synchronization, no memset): a captured forward + dX + dW, plus both
+    fp8 quantizers, replayed several times with eager work between the
+    replays, reproduces the eager outputs bit for bit each time."""
+    E, M, K, N = 5, 300, 128, 192
+    sizes = wl.random_group_sizes(E, M, 4, zero_frac=0.2)
+    X = wl.normal_bf16((M, K), 1.0, 4, wl.T_X)
+    W = wl.normal_bf16((E, K, N), 0.5, 4, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, 4, wl.T_DY)
+    x, w, dy, gs = bf16_dev(X), bf16_dev(W), bf16_dev(dY), dev(sizes)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty_like(w)
+    xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    cq = (torch.zeros(N, M, dtype=torch.uint8, device="cuda"), torch.empty(E, N, dtype=torch.float32, device="cuda"))
+    ws = mg.workspace(E, M)
+
+    def step():
+        mg.gmm_fwd(x, w, gs, out=y, ws=ws)
+        mg.gmm_bwd(dy, x, w, gs, need_dw=False, dx=dx, ws=ws)
+        mg.gmm_bwd(dy, x, w, gs, need_dx=False, dw=dw, ws=ws)
+        mg.quantize_rowwise_fp8(x, q=xq, scales=sx)
+        mg.quantize_colwise_per_group_fp8(dy, gs, out=cq)
+
+    outs = (y, dx, dw, xq, sx, cq[0], cq[1])
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            assert torch.equal(t, r)
+        step()   # eager work between the replays
+        torch.cuda.synchronize()
