@@ -8,8 +8,9 @@
 // fused_moe applies silu_and_mul between the two GEMMs and sums the top-k
 // expert outputs of every token.
 //
-// The alignment is a stable counting sort in three small kernels with no
-// device-to-host traffic:
+// The alignment is a stable counting sort with no device-to-host traffic.
+// Up to 1024 pairs it runs in one workgroup (perm_small_kernel); beyond, in
+// three small kernels:
 //   1. per chunk of pairs: stable rank of every pair among the chunk's pairs
 //      with the same expert, and the chunk's per-expert counts;
 //   2. one workgroup: per-expert totals, padded run starts, per-chunk bases,
@@ -157,6 +158,94 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(const uint16_t* __rest
   *reinterpret_cast<uint4*>(out + row * hidden + ch * 8) = v;
 }
 
+// Small routings (at most 1024 pairs, decode-sized) in one workgroup and one
+// launch: the stable ranks of perm_rank (ballot matching inside a wave,
+// waves advancing the per-expert cursors in order), the plan of
+// perm_plan and the scatter, with the ranks kept in registers.
+constexpr int kPermSmall = 1024;
+
+__global__ void __launch_bounds__(kPermSmall) perm_small_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                               int32_t E, int32_t block_m,
+                                                               int32_t* __restrict__ expert_ids, int64_t nblk,
+                                                               int32_t* __restrict__ ntpp,
+                                                               int32_t* __restrict__ padded,
+                                                               int32_t* __restrict__ sorted_ids, int64_t cap,
+                                                               int32_t* __restrict__ inv, int32_t sentinel) {
+  __shared__ int32_t cursor[kMaxExperts];
+  __shared__ int32_t s_start[kMaxExperts + 1];
+  __shared__ int32_t s_blk[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kPermSmall) cursor[e] = 0;
+  __syncthreads();
+  // stable rank of pair tid among the earlier pairs of its expert
+  const int f = tid;
+  int e = -1;
+  if (f < P) {
+    e = ids[f];
+    if (e < 0 || e >= E) e = -1;
+  }
+  uint64_t active = __ballot(e >= 0);
+  int my_rank = 0, my_cnt = 0, my_leader = 0;
+  while (active) {
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    const int el = __shfl(e, leader, kWave);
+    const uint64_t m = __ballot(e == el) & active;
+    if ((m >> lane) & 1) {
+      my_rank = __popcll(m & ((1ull << lane) - 1));
+      my_cnt = __popcll(m);
+      my_leader = leader;
+    }
+    active &= ~m;
+  }
+  int base = 0;
+  for (int w = 0; w < kPermSmall / kWave; ++w) {
+    if (wave == w && e >= 0 && lane == my_leader) {
+      base = cursor[e];
+      cursor[e] = base + my_cnt;
+    }
+    __syncthreads();
+  }
+  const int rank = __shfl(base, my_leader, kWave) + my_rank;
+  // plan: padded run sizes, their starts (serial scan by thread 0, E adds),
+  // the block -> expert table, the sentinel in every slot no pair takes
+  int32_t pad = 0;
+  if (tid < E) {
+    pad = (cursor[tid] + block_m - 1) / block_m * block_m;
+    padded[tid] = pad;
+    s_start[tid] = pad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0, blk = 0;
+    for (int h = 0; h < E; ++h) {
+      const int32_t p = s_start[h];
+      s_start[h] = run;
+      s_blk[h] = blk;
+      run += p;
+      blk += p / block_m;
+    }
+    s_start[E] = run;
+    s_blk[E] = blk;
+    *ntpp = run;
+  }
+  __syncthreads();
+  if (tid < E) {
+    for (int32_t b = s_blk[tid]; b < s_blk[tid + 1] && b < nblk; ++b) expert_ids[b] = tid;
+    for (int32_t i = s_start[tid] + cursor[tid]; i < s_start[tid + 1] && i < cap; ++i) sorted_ids[i] = sentinel;
+  }
+  for (int64_t i = (int64_t)s_start[E] + tid; i < cap; i += kPermSmall) sorted_ids[i] = sentinel;
+  // scatter
+  if (f < P) {
+    if (e >= 0) {
+      const int32_t pos = s_start[e] + rank;
+      sorted_ids[pos] = (int32_t)f;
+      inv[f] = pos;
+    } else {
+      inv[f] = -1;
+    }
+  }
+}
+
 static int64_t perm_chunk(int64_t P, int32_t E) {
   // keep nchunks * E <= 2^20 so the count table stays small
   int64_t chunk = 1024;
@@ -180,14 +269,18 @@ hipError_t launch_moe_permute_ws(const int32_t* ids, int64_t T, int32_t k, int32
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   int32_t* rank = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(ws) + align_up(nchunks * E * 4, 256));
 
-  hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(PT), (size_t)E * 4, stream, ids, P, E,
-                     chunk, counts, rank);
-  int plan_threads = (int)align_up(E, kWave);
-  hipLaunchKernelGGL(perm_plan_kernel, dim3(1), dim3(plan_threads), 0, stream, E, block_m, nchunks, counts,
-                     expert_ids, nblk, ntpp, padded, sorted_ids, cap, (int32_t)P);
-  if (P > 0)
+  if (P <= kPermSmall) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(kPermSmall), 0, stream, ids, P, E, block_m, expert_ids,
+                       nblk, ntpp, padded, sorted_ids, cap, inv, (int32_t)P);
+  } else {
+    hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(PT), (size_t)E * 4, stream, ids, P, E,
+                       chunk, counts, rank);
+    int plan_threads = (int)align_up(E, kWave);
+    hipLaunchKernelGGL(perm_plan_kernel, dim3(1), dim3(plan_threads), 0, stream, E, block_m, nchunks, counts,
+                       expert_ids, nblk, ntpp, padded, sorted_ids, cap, (int32_t)P);
     hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)cdiv(P, 256)), dim3(256), 0, stream, ids, P, E,
                        chunk, counts, rank, sorted_ids, inv);
+  }
   if (x != nullptr && x_sorted != nullptr && cap > 0) {
     const int64_t n = cap * (hidden / 8);
     hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, x, P, k,

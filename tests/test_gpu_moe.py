@@ -48,6 +48,8 @@ def test_permute_worked_example():
 @pytest.mark.parametrize("T,k,E,bm,seed", [
     (1, 2, 8, 16, 0), (64, 2, 8, 16, 1), (4096, 2, 8, 128, 2), (37, 6, 64, 16, 3), (16384, 6, 64, 128, 4),
     (5, 1, 3, 1, 5), (3000, 4, 1024, 32, 6),
+    # both sides of the one-workgroup path's limit of 1024 pairs
+    (512, 2, 8, 16, 7), (1025, 1, 8, 16, 8), (171, 6, 1024, 8, 9), (128, 8, 1024, 1, 10), (1024, 1, 1, 64, 11),
 ])
 def test_permute_random(T, k, E, bm, seed):
     rng = np.random.default_rng(seed)
@@ -59,6 +61,9 @@ def test_permute_random(T, k, E, bm, seed):
 def test_permute_skewed_routing():
     ids = wl.zipf_topk_routing(2000, 64, 6, 1.1, 0)
     _check_permute(ids, 64, 64)
+    # one-workgroup path: many pairs of one expert spread over all waves
+    ids = wl.zipf_topk_routing(170, 64, 6, 1.1, 1)
+    _check_permute(ids, 64, 16)
 
 
 def test_silu_mul_and_unpermute():
