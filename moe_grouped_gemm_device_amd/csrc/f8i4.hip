@@ -15,7 +15,11 @@
 // into a fresh accumulator that is then scaled by that chunk's bf16 weight
 // scale (keeping the dequantization exact) and added to the running sum.
 // The waves of a workgroup (8 for contractions of 64 or more chunks, else 4)
-// split K.  Each wave requests the operands of its next chunk before it
+// split K.  When the items are too few to give every slot of the grid one
+// (one or two routed rows over a narrow N), K is also split across
+// workgroups: each piece stores its fp32 partial tile in the workspace, and
+// the last piece to arrive adds them all in piece order (the same bits
+// whatever the arrival order) and writes the output.  Each wave requests the operands of its next chunk before it
 // computes the current one, so two chunks stream per wave; the loads' offsets
 // are opaque to the compiler, which would otherwise branch around the
 // out-of-range loads and drain every load in flight.  The partial tiles are
@@ -63,6 +67,8 @@ __device__ inline i32x8 i4x32_to_e4m3(const uint4& w) {
 constexpr int F_BM = kF8I4RowTile;
 constexpr int F_BN = 32;
 constexpr uint32_t F_OOB = 0x80000000u;   // offset past any buffer: the load returns zeros
+constexpr int F_DEVICE = 16;              // sc1: coherent at device scope (across XCDs)
+constexpr int F_SPLIT_ROUNDS = 1;         // K pieces fill this many waves of the grid's slots
 
 __device__ inline __amdgpu_buffer_rsrc_t f_rsrc(const void* base, int64_t bytes) {
   const int32_t nr = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
@@ -85,6 +91,7 @@ struct F8I4Chunk {
 template <int F_WAVES>
 __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
   __shared__ float red[F_WAVES][F_BM * F_BN];
+  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.Kc;
   const int N = a.Nout;
@@ -103,15 +110,30 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t xr = f_rsrc(a.A, a.total_rows * (int64_t)K);
   const uint8_t* w4 = reinterpret_cast<const uint8_t*>(a.B);
 
-  // chunk range of this wave
-  const int per = (nchunk + F_WAVES - 1) / F_WAVES;
-  const int j0 = wave * per;
-  const int j1 = j0 + per < nchunk ? j0 + per : nchunk;
+  // K pieces per item: more than one only while the items leave slots idle,
+  // each wave keeps at least two chunks, and every item has an arrival
+  // counter of its own in the workspace
+  int S = 1;
+  if (items > 0 && items <= kSkMaxGrid && items * 2 <= (int64_t)gridDim.x * F_SPLIT_ROUNDS) {
+    S = (int)((int64_t)gridDim.x * F_SPLIT_ROUNDS / items);
+    const int smax = nchunk / (2 * F_WAVES);
+    if (S > smax) S = smax;
+    if (S < 1) S = 1;
+  }
+  const int64_t units = items * S;
+  // chunk range of a wave: piece s, wave q -> run s * F_WAVES + q
+  const int per = (nchunk + S * F_WAVES - 1) / (S * F_WAVES);
+  const __amdgpu_buffer_rsrc_t pr = f_rsrc(a.sk_part, units * (int64_t)(F_BM * F_BN * 4));
 
   int64_t first = blockIdx.x;
   if ((gridDim.x & 7) == 0) first = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
 
-  for (int64_t w = first; w < items; w += gridDim.x) {
+  for (int64_t u = first; u < units; u += gridDim.x) {
+    const int64_t w = u / S;
+    const int piece = (int)(u - w * S);
+    const int jr = (piece * F_WAVES + wave) * per;
+    const int j0 = jr < nchunk ? jr : nchunk;
+    const int j1 = j0 + per < nchunk ? j0 + per : nchunk;
     const int64_t mt = w / n_tiles;
     const int nt = (int)(w - mt * n_tiles);
     const int4 e = fixed_m_entry(tab, a.E, F_BM, (int32_t)mt);
@@ -193,14 +215,53 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
       red[wave][r * F_BN + col] = acc[v];
     }
     __syncthreads();
-    for (int idx = tid; idx < F_BM * F_BN; idx += F_WAVES * 64) {
-      const int r = idx / F_BN, c = idx % F_BN;
-      if (r < m_valid && n0 + c < N) {
-        float sum = red[0][idx];
+    if (S == 1) {
+      for (int idx = tid; idx < F_BM * F_BN; idx += F_WAVES * 64) {
+        const int r = idx / F_BN, c = idx % F_BN;
+        if (r < m_valid && n0 + c < N) {
+          float sum = red[0][idx];
 #pragma unroll
-        for (int q = 1; q < F_WAVES; ++q) sum += red[q][idx];
-        const float y = sum * (1.f / a.sa[row0 + r]);
-        reinterpret_cast<uint16_t*>(a.C)[(row0 + r) * a.c_ld + n0 + c] = (uint16_t)f32_to_bf16_rne(y);
+          for (int q = 1; q < F_WAVES; ++q) sum += red[q][idx];
+          const float y = sum * (1.f / a.sa[row0 + r]);
+          reinterpret_cast<uint16_t*>(a.C)[(row0 + r) * a.c_ld + n0 + c] = (uint16_t)f32_to_bf16_rne(y);
+        }
+      }
+    } else {
+      // this piece's partial tile -> workspace slot u (item w's pieces are
+      // slots w * S .. w * S + S - 1)
+      for (int idx = tid; idx < F_BM * F_BN; idx += F_WAVES * 64) {
+        const int r = idx / F_BN, c = idx % F_BN;
+        if (r < m_valid && n0 + c < N) {
+          float sum = red[0][idx];
+#pragma unroll
+          for (int q = 1; q < F_WAVES; ++q) sum += red[q][idx];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(sum), pr, (int)((u * (F_BM * F_BN) + idx) * 4), 0,
+                                                F_DEVICE);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the partial has reached the coherence point
+      __syncthreads();
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(a.sk_ctr + w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == S - 1;
+        if (last) __hip_atomic_store(a.sk_ctr + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+      }
+      __syncthreads();
+      if (s_last) {
+        for (int idx = tid; idx < F_BM * F_BN; idx += F_WAVES * 64) {
+          const int r = idx / F_BN, c = idx % F_BN;
+          if (r < m_valid && n0 + c < N) {
+            float sum = 0.f;
+            for (int q = 0; q < S; ++q) {
+              const float v = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                  pr, (int)(((w * S + q) * (F_BM * F_BN) + idx) * 4), 0, F_DEVICE));
+              sum = q == 0 ? v : sum + v;
+            }
+            const float y = sum * (1.f / a.sa[row0 + r]);
+            reinterpret_cast<uint16_t*>(a.C)[(row0 + r) * a.c_ld + n0 + c] = (uint16_t)f32_to_bf16_rne(y);
+          }
+        }
       }
     }
     __syncthreads();
@@ -214,6 +275,11 @@ hipError_t launch_f8i4(const GemmArgs& a, int64_t cap_entries, hipStream_t strea
   // 4 of 4 waves per CU, with as many again queued behind them
   const bool wide = a.Kc / 128 >= 64;
   const int64_t slots = (int64_t)device_cu_count() * (wide ? 4 : 8);
+  // The grid follows the host's bound on the items (the capacity of the
+  // sorted rows), so K pieces appear where the real items are fewer than
+  // half of it: routed decode steps, whose sorted buffer has room for every
+  // expert.  A grid widened for pieces beyond that bound measured slower (a
+  // routed row over 128 experts, K=5120, N=8192: 19.4 -> 26.8 us).
   const int grid = (int)(max_items < slots ? max_items : slots);
   if (wide)
     hipLaunchKernelGGL(f8i4_kernel<8>, dim3(grid), dim3(8 * 64), (size_t)table_lds_bytes(a.E), stream, a);
