@@ -106,11 +106,60 @@ __global__ void __launch_bounds__(256) quant_rowwise_kernel(const uint16_t* __re
     *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(*reinterpret_cast<const uint4*>(xr + ch * 8), s);
 }
 
+// Few long rows (the sorted activations of a decode step: about a hundred
+// rows of 4096-14336): a wave per row would leave most compute units idle
+// and stream each row through one wave, so here a workgroup takes a row,
+// held in the registers of its 256 threads.  The amax is a max, so scale
+// and codes are the same bits as the wave-per-row kernel's.
+constexpr int RCH_WG = 8;              // chunks per thread held in registers
+constexpr int64_t kRowwiseWgRows = 1024;
+constexpr int32_t kRowwiseWgCols = 2048;
+
+__global__ void __launch_bounds__(256) quant_rowwise_wg_kernel(const uint16_t* __restrict__ x, int32_t cols,
+                                                              int64_t ld, uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales) {
+  __shared__ uint32_t wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * ld;
+  uint8_t* qr = q + row * (int64_t)cols;
+  const int nch = cols >> 3;
+  uint4 held[RCH_WG];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < RCH_WG; ++i) {
+    const int ch = tid + i * 256;
+    held[i] = make_uint4(0, 0, 0, 0);
+    if (ch < nch) {
+      held[i] = *reinterpret_cast<const uint4*>(xr + ch * 8);
+      m = max(m, chunk_absmax_bits(held[i]));
+    }
+  }
+  for (int ch = tid + RCH_WG * 256; ch < nch; ch += 256)
+    m = max(m, chunk_absmax_bits(*reinterpret_cast<const uint4*>(xr + ch * 8)));
+  m = wave_max_u32(m);
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float s = fp8_scale_from_amax(__uint_as_float(m));
+  if (tid == 0) scales[row] = s;
+#pragma unroll
+  for (int i = 0; i < RCH_WG; ++i) {
+    const int ch = tid + i * 256;
+    if (ch < nch) *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(held[i], s);
+  }
+  for (int ch = tid + RCH_WG * 256; ch < nch; ch += 256)
+    *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(*reinterpret_cast<const uint4*>(xr + ch * 8), s);
+}
+
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int32_t cols, int64_t ld, uint8_t* q,
                                 float* s, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rowwise_kernel, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, stream, x, rows,
-                     cols, ld, q, s);
+  if (rows <= kRowwiseWgRows && cols >= kRowwiseWgCols)
+    hipLaunchKernelGGL(quant_rowwise_wg_kernel, dim3((unsigned)rows), dim3(256), 0, stream, x, cols, ld, q, s);
+  else
+    hipLaunchKernelGGL(quant_rowwise_kernel, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, stream, x, rows,
+                       cols, ld, q, s);
   return hipGetLastError();
 }
 

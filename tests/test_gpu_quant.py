@@ -58,7 +58,10 @@ def test_rowwise_each_bf16_value_against_many_scales():
 
 
 @pytest.mark.parametrize("rows,cols,ld", [(1, 8, 8), (37, 200, 208), (4096, 2048, 2048), (64, 14336, 14336),
-                                          (3, 8192 + 8, 8192 + 8)])
+                                          (3, 8192 + 8, 8192 + 8),
+                                          # both sides of the workgroup-per-row kernel's limits
+                                          (1024, 2048, 2056), (1025, 2048, 2048), (122, 2040, 2040),
+                                          (5, 20480, 20480)])
 def test_rowwise_shapes(rows, cols, ld):
     full = wl.normal_bf16((rows, ld), 1.0, rows, wl.T_X)
     full[rows // 2] = 0
