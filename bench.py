@@ -376,6 +376,24 @@ def _row_cases(torch, mg):
         yield (f"C3_fused_ffn_T{Tsmall}", f"end to end, {experts} experts touched: weight bytes of those experts",
                lambda: mg.fused_moe(xsub, w1, w2, sub_ids, sub_w, ws=wsf),
                experts * (H * 2 * I + I * H) * 2, "GB/s", PEAK_HBM_GBS, 5)
+    # the same FFN with e4m3 expert weights (one scale per expert and output
+    # column) and e4m3 activations
+    w1q, s1q = mg.quantize_fp8_expert_weights(w1)
+    w2q, s2q = mg.quantize_fp8_expert_weights(w2)
+    yield ("C3_fused_ffn_fp8_T4096", "fp8-weight FFN end to end: align + gather -> e4m3 rows -> fp8 GEMM1 -> "
+                                     "SiLU*mul -> e4m3 -> fp8 GEMM2 -> combine",
+           lambda: mg.fused_moe_fp8(x, w1q, s1q, w2q, s2q, ids, wts, ws=wsf), 2.0 * T * k * H * 3 * I,
+           "TFLOP/s", PEAK_FP8_TFLOPS, 3)
+    for Tsmall in (1, 64):
+        sub_ids, sub_w = ids[:Tsmall].contiguous(), wts[:Tsmall].contiguous()
+        xsub = x[:Tsmall].contiguous()
+        experts = int(torch.unique(sub_ids).numel())
+        yield (f"C3_fused_ffn_fp8_T{Tsmall}",
+               f"fp8-weight FFN end to end, {experts} experts touched: e4m3 weight bytes of those experts",
+               lambda: mg.fused_moe_fp8(xsub, w1q, s1q, w2q, s2q, sub_ids, sub_w, ws=wsf),
+               experts * (H * 2 * I + I * H), "GB/s", PEAK_HBM_GBS, 5)
+    del w1q, w2q
+    torch.cuda.empty_cache()
     # the same FFN with int4 expert weights (per-128-K bf16 scales) and fp8
     # activations, decode-sized token counts
     w1_4, s1 = mg.quantize_int4_weights(w1)

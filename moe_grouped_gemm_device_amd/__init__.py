@@ -423,6 +423,47 @@ def fused_moe_f8i4(x, w1_4, s1, w2_4, s2, topk_ids, topk_weights, block_m=16, ws
     return out, dict(permute=p, xq=xq, sx=sx, h1=h1, act=act, aq=aq, sa=sa, y2=y2)
 
 
+def quantize_fp8_expert_weights(w, stream=None):
+    """Expert weights w bf16 [E, K, N] -> (wq uint8 [N, E*K], sw fp32 [E, N]):
+    column-major e4m3 codes with one power-of-two scale per (expert, output
+    column) over its K weights.  This is the per-group colwise quantizer on w
+    viewed as [E*K, N] with E groups of K rows; gmm_fwd_fp8 takes the result
+    with w_ld = E*K and w_expert_stride = K."""
+    _need(w, torch.bfloat16, "w", 3)
+    E, K, N = w.shape
+    sizes = torch.full((E,), K, dtype=torch.int32, device=w.device)
+    return quantize_colwise_per_group_fp8(w.reshape(E * K, N), sizes, stream=stream)
+
+
+def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=None, stream=None):
+    """Token-sorted MoE expert FFN with e4m3 expert weights and
+    activations: align + gather -> rowwise e4m3 of the sorted rows -> fp8
+    GEMM1 (row scales x per-(expert, column) weight scales) -> SiLU*mul ->
+    rowwise e4m3 of the activations -> fp8 GEMM2 -> top-k weighted combine.
+    Weights as quantize_fp8_expert_weights returns them: w1q uint8 [2I, E*H]
+    with s1 fp32 [E, 2I] (from W1 [E, H, 2I]), w2q uint8 [H, E*I] with s2
+    fp32 [E, H] (from W2 [E, I, H]).  Returns (out bf16 [T, H], dict of the
+    intermediates)."""
+    T, k = topk_ids.shape
+    E, two_i = s1.shape
+    H = x.shape[1]
+    inter = two_i // 2
+    if s2.shape != (E, H) or w1q.shape != (two_i, E * H) or w2q.shape != (H, E * inter):
+        raise ValueError("fp8 expert weights do not match x and each other")
+    if block_m is None:
+        block_m = 16 if T * k <= 64 * E else 128
+    p = moe_permute(topk_ids, E, block_m, x=x, stream=stream)
+    xs, sizes = p["x_sorted"], p["padded_sizes"]
+    ws = workspace(E, xs.shape[0], x.device) if ws is None else ws
+    xq, sx = quantize_rowwise_fp8(xs, stream=stream)
+    h1 = gmm_fwd_fp8(xq, sx, w1q, s1, E * H, H, sizes, two_i, ws=ws, stream=stream)
+    act = silu_mul(h1, stream=stream)
+    aq, sa = quantize_rowwise_fp8(act, stream=stream)
+    y2 = gmm_fwd_fp8(aq, sa, w2q, s2, E * inter, inter, sizes, H, ws=ws, stream=stream)
+    out = moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream)
+    return out, dict(permute=p, xq=xq, sx=sx, h1=h1, act=act, aq=aq, sa=sa, y2=y2)
+
+
 def route_topk(logits, top_k, renormalize=False, stream=None):
     """Router: fp32 softmax of each token's logits, its top_k experts in
     descending order (ties to the lower index) and their probabilities

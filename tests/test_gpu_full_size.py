@@ -218,3 +218,60 @@ def test_fused_ffn_f8i4_mixtral_full_size_sampled(T, mixtral_weights):
             y2_rows.append(oracle.bf16_to_f64(y2[p:p + 1]))
         ref = sum(float(w[t, j]) * y2_rows[j] for j in range(k))
         assert rel_fro(got[t:t + 1], ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [1, 64, 4096])   # block_m 16, 16 and 128
+def test_fused_ffn_fp8_mixtral_full_size_sampled(T, mixtral_weights):
+    """The fp8-weight fused FFN at the Mixtral shapes, stage by stage at the
+    sorted rows of sampled tokens, against the oracle fed the same quantized
+    operands: weight codes, per-(expert, column) scales and activation codes
+    bit-exact, the two fp8 GEMMs within the fp8 tolerance, SiLU*mul and the
+    combine within bf16 rounding."""
+    E, k, H, I = 8, 2, 4096, 14336
+    w1, w2, w1d, w2d = mixtral_weights
+    ids, w = wl.softmax_topk_routing(T, E, k, 0)
+    x = wl.normal_bf16((T, H), 1.0, 0, wl.T_X)
+    w1q, s1 = mg.quantize_fp8_expert_weights(w1d)
+    w2q, s2 = mg.quantize_fp8_expert_weights(w2d)
+    out, st = mg.fused_moe_fp8(bf16_dev(x), w1q, s1, w2q, s2, dev(ids), dev(w))
+    torch.cuda.synchronize()
+    inv = host(st["permute"]["inv"])
+    xq, sx, aq, sa = host(st["xq"]), host(st["sx"]), host(st["aq"]), host(st["sa"])
+    h1, act, y2 = bf16_host(st["h1"]), bf16_host(st["act"]), bf16_host(st["y2"])
+    got = _f64(out)
+    one = np.array([1], np.int32)
+    deq = {}   # expert -> dequantized W1 and W2 of the GPU codes, checked bit-exact once
+
+    def expert_weights(e):
+        if e not in deq:
+            q1, c1 = oracle.quant_colwise(w1[e], np.array([H], np.int32))
+            q2, c2 = oracle.quant_colwise(w2[e], np.array([I], np.int32))
+            np.testing.assert_array_equal(host(w1q[:, e * H:(e + 1) * H]), q1)
+            np.testing.assert_array_equal(host(s1[e:e + 1]), c1)
+            np.testing.assert_array_equal(host(w2q[:, e * I:(e + 1) * I]), q2)
+            np.testing.assert_array_equal(host(s2[e:e + 1]), c2)
+            deq[e] = (oracle.dequant_colwise(q1, c1, np.array([H], np.int32)).reshape(1, H, 2 * I),
+                      oracle.dequant_colwise(q2, c2, np.array([I], np.int32)).reshape(1, I, H))
+        return deq[e]
+
+    toks = np.unique(np.random.default_rng(3).choice(T, min(T, 2), replace=False))
+    for t in toks:
+        y2_rows = []
+        for j in range(k):
+            e, p = int(ids[t, j]), int(inv[t * k + j])
+            d1, d2 = expert_weights(e)
+            rq, rs = oracle.quant_rowwise(x[t:t + 1])
+            np.testing.assert_array_equal(xq[p:p + 1], rq)
+            np.testing.assert_array_equal(sx[p:p + 1], rs)
+            h_ref = oracle.gmm_fwd(oracle.dequant_rowwise(rq, rs), d1, one)
+            assert rel_fro(oracle.bf16_to_f64(h1[p:p + 1]), h_ref) <= FP8_TOL
+            act_ref = oracle.silu_mul(oracle.bf16_to_f64(h1[p:p + 1]))
+            assert rel_fro(oracle.bf16_to_f64(act[p:p + 1]), act_ref) <= 4e-3
+            aq_ref, as_ref = oracle.quant_rowwise(act[p:p + 1])
+            np.testing.assert_array_equal(aq[p:p + 1], aq_ref)
+            np.testing.assert_array_equal(sa[p:p + 1], as_ref)
+            y_ref = oracle.gmm_fwd(oracle.dequant_rowwise(aq_ref, as_ref), d2, one)
+            assert rel_fro(oracle.bf16_to_f64(y2[p:p + 1]), y_ref) <= FP8_TOL
+            y2_rows.append(oracle.bf16_to_f64(y2[p:p + 1]))
+        ref = sum(float(w[t, j]) * y2_rows[j] for j in range(k))
+        assert rel_fro(got[t:t + 1], ref) <= BF16_TOL

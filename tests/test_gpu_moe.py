@@ -266,3 +266,51 @@ def test_fused_moe_f8i4_stages_match_the_oracle(T):
     assert rel_fro(oracle.bf16_to_f64(y2), y2_ref) <= 2e-2
     out_ref = oracle.unpermute(oracle.bf16_to_f64(y2), al["inv"], w, T, k)
     assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), out_ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [1, 64, 300])
+def test_fused_moe_fp8_stages_match_the_oracle(T):
+    """The fp8-weight fused FFN, stage by stage, against the oracle fed the
+    same quantized operands: the weight codes and per-(expert, column)
+    scales, and the e4m3 codes of the gathered rows and of the activations,
+    bit-exact; each fp8 GEMM within the fp8 tolerance of the oracle's fp64
+    product of the dequantized operands; SiLU*mul and the combine within
+    bf16 rounding.  T=300 takes 128-row blocks."""
+    E, k, H, I = 8, 2, 256, 384
+    ids, w = wl.softmax_topk_routing(T, E, k, 5)
+    x = wl.normal_bf16((T, H), 1.0, 5, wl.T_X)
+    W1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.05, 5, wl.T_W1)
+    W2 = wl.stacked_normal_bf16(E, (I, H), 0.05, 5, wl.T_W2)
+    w1q, s1 = mg.quantize_fp8_expert_weights(bf16_dev(W1))
+    w2q, s2 = mg.quantize_fp8_expert_weights(bf16_dev(W2))
+    out, st = mg.fused_moe_fp8(bf16_dev(x), w1q, s1, w2q, s2, dev(ids), dev(w))
+    torch.cuda.synchronize()
+    bm = 16 if T * k <= 64 * E else 128
+    full = lambda n: np.full(E, n, np.int32)
+    p1, q1 = oracle.quant_colwise(W1.reshape(E * H, 2 * I), full(H))
+    p2, q2 = oracle.quant_colwise(W2.reshape(E * I, H), full(I))
+    np.testing.assert_array_equal(host(w1q), p1)
+    np.testing.assert_array_equal(host(s1), q1)
+    np.testing.assert_array_equal(host(w2q), p2)
+    np.testing.assert_array_equal(host(s2), q2)
+    al = oracle.moe_align(ids, E, bm)
+    n, sizes = al["num_tokens_post_padded"], al["padded_sizes"]
+    xq, sx = oracle.quant_rowwise(oracle.gather_rows(x, k, al["sorted_token_ids"])[:n])
+    np.testing.assert_array_equal(host(st["xq"])[:n], xq)
+    np.testing.assert_array_equal(host(st["sx"])[:n], sx)
+    h1_ref = oracle.gmm_fwd(oracle.dequant_rowwise(xq, sx),
+                            oracle.dequant_colwise(p1, q1, full(H)).reshape(E, H, 2 * I), sizes)
+    h1 = bf16_host(st["h1"])[:n]
+    assert rel_fro(oracle.bf16_to_f64(h1), h1_ref) <= 2e-2
+    act_ref = oracle.silu_mul(oracle.bf16_to_f64(h1))
+    act = bf16_host(st["act"])[:n]
+    assert rel_fro(oracle.bf16_to_f64(act), act_ref) <= 4e-3
+    aq, sa = oracle.quant_rowwise(act)
+    np.testing.assert_array_equal(host(st["aq"])[:n], aq)
+    np.testing.assert_array_equal(host(st["sa"])[:n], sa)
+    y2_ref = oracle.gmm_fwd(oracle.dequant_rowwise(aq, sa),
+                            oracle.dequant_colwise(p2, q2, full(I)).reshape(E, I, H), sizes)
+    y2 = bf16_host(st["y2"])[:n]
+    assert rel_fro(oracle.bf16_to_f64(y2), y2_ref) <= 2e-2
+    out_ref = oracle.unpermute(oracle.bf16_to_f64(y2), al["inv"], w, T, k)
+    assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), out_ref) <= BF16_TOL
