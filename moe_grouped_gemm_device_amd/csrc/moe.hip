@@ -87,9 +87,21 @@ __global__ void __launch_bounds__(1024) perm_plan_kernel(int32_t E, int32_t bloc
   __shared__ int32_t s_start[kMaxExperts + 1];
   __shared__ int32_t s_blk[kMaxExperts + 1];
   const int e = threadIdx.x;
+  // the per-chunk counts are read eight at a time, so that one memory
+  // latency covers eight chunks instead of one
+  constexpr int PB = 8;
   int64_t total = 0;
-  if (e < E)
-    for (int64_t c = 0; c < nchunks; ++c) total += chunk_counts[c * E + e];
+  if (e < E) {
+    int64_t c = 0;
+    for (; c + PB <= nchunks; c += PB) {
+      int32_t v[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) v[u] = chunk_counts[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) total += v[u];
+    }
+    for (; c < nchunks; ++c) total += chunk_counts[c * E + e];
+  }
   const int32_t pad = (int32_t)((total + block_m - 1) / block_m * block_m);
   if (e < E) padded[e] = pad;
   // exclusive scan of padded sizes across experts (E <= 1024; serial in LDS
@@ -112,7 +124,18 @@ __global__ void __launch_bounds__(1024) perm_plan_kernel(int32_t E, int32_t bloc
   __syncthreads();
   if (e < E) {
     int32_t base = s_start[e];
-    for (int64_t c = 0; c < nchunks; ++c) {
+    int64_t c = 0;
+    for (; c + PB <= nchunks; c += PB) {
+      int32_t v[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) v[u] = chunk_counts[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        chunk_counts[(c + u) * E + e] = base;
+        base += v[u];
+      }
+    }
+    for (; c < nchunks; ++c) {
       const int32_t cnt = chunk_counts[c * E + e];
       chunk_counts[c * E + e] = base;
       base += cnt;
