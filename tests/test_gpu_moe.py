@@ -314,3 +314,48 @@ def test_fused_moe_fp8_stages_match_the_oracle(T):
     assert rel_fro(oracle.bf16_to_f64(y2), y2_ref) <= 2e-2
     out_ref = oracle.unpermute(oracle.bf16_to_f64(y2), al["inv"], w, T, k)
     assert rel_fro(oracle.bf16_to_f64(bf16_host(out)), out_ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("path", ["bf16", "fp8", "int4"])
+def test_captured_decode_ffn_replays_bitwise(path):
+    """A one-token fused FFN step captured in a HIP graph (no allocation
+    outside torch's graph pool, no synchronization, no memset): every replay,
+    with eager steps between the replays, reproduces the eager output bit for
+    bit.  At these shapes the int4 path's F8I4 GEMMs split K across
+    workgroups and the bf16 GEMM2 runs stream-K pieces, so the workspace's
+    arrival counters, which reset themselves, are exercised across replays."""
+    E, k, H, I = 8, 2, 2048, 2048
+    ids, w = wl.softmax_topk_routing(1, E, k, 7)
+    x = bf16_dev(wl.normal_bf16((1, H), 1.0, 7, wl.T_X))
+    W1 = bf16_dev(wl.stacked_normal_bf16(E, (H, 2 * I), 0.02, 7, wl.T_W1))
+    W2 = bf16_dev(wl.stacked_normal_bf16(E, (I, H), 0.02, 7, wl.T_W2))
+    ids_d, w_d = dev(ids), dev(w)
+    ws = mg.workspace(E, 256)
+    if path == "bf16":
+        step = lambda: mg.fused_moe(x, W1, W2, ids_d, w_d, ws=ws)[0]
+    elif path == "fp8":
+        w1q, s1 = mg.quantize_fp8_expert_weights(W1)
+        w2q, s2 = mg.quantize_fp8_expert_weights(W2)
+        step = lambda: mg.fused_moe_fp8(x, w1q, s1, w2q, s2, ids_d, w_d, ws=ws)[0]
+    else:
+        w1_4, s1 = mg.quantize_int4_weights(W1)
+        w2_4, s2 = mg.quantize_int4_weights(W2)
+        step = lambda: mg.fused_moe_f8i4(x, w1_4, s1, w2_4, s2, ids_d, w_d, ws=ws)[0]
+    ref = step().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert torch.equal(step(), ref)   # eager work between the replays
+        torch.cuda.synchronize()
