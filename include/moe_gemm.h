@@ -78,8 +78,9 @@ enum {
  * work lists themselves are built in LDS by every kernel's prologue.
  * Depends on host values only; the pointer must be 256-byte aligned.
  * A fresh workspace must be zeroed once before its first use (a
- * zero-filled allocation, or mg_workspace_clear); the GEMM calls leave the
- * counters at zero again when they finish.  Calls that share a workspace
+ * zero-filled allocation, or mg_workspace_clear); the GEMM calls (the
+ * F8I4 call's K split included) leave the counters at zero again when they
+ * finish.  Calls that share a workspace
  * must not overlap in time (enqueue them on one stream): the partial tiles
  * and counters of one call would be taken for another's. */
 size_t mg_workspace_bytes(int32_t E, int64_t total_M);
@@ -239,7 +240,12 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w,
  *   y   bf16 [total_M, N]
  * K must be a multiple of 128 and N a multiple of 8; K*N and
  * total_M*max(K, N) must stay below 2^31 (MG_EUNSUPPORTED otherwise).  Only
- * non-empty groups are visited. */
+ * non-empty groups are visited.  When the (row tile, 32-column) items are
+ * at most 256 and fill at most half the grid, K is split across workgroups:
+ * fp32 partial tiles go to the workspace and one arrival counter per item
+ * is used and left at zero, so the workspace rules above apply here too.
+ * The last piece to arrive adds the partials in piece order, so results do
+ * not depend on the arrival order. */
 int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4,
                  const void* sw, const int32_t* group_sizes, int32_t E,
                  int64_t total_M, int32_t K, int32_t N, void* y, void* ws,
