@@ -64,8 +64,9 @@ def test_fp8_backward(E, M, K, N, seed):
         assert (dwh[g] == 0).all()
 
 
-def _f8i4_case(E, total_M, K, N, seed):
-    counts = wl.uniform_expert_rows(total_M, E, seed)
+def _f8i4_case(E, total_M, K, N, seed, counts=None):
+    if counts is None:
+        counts = wl.uniform_expert_rows(total_M, E, seed)
     X = wl.normal_bf16((total_M, K), 1.0, seed, wl.T_X)
     xq, sx = oracle.quant_rowwise(X)
     Xd = oracle.dequant_rowwise(xq, sx)
@@ -114,3 +115,17 @@ def test_f8i4_one_token_over_128_groups_matches_single_group():
     assert torch.equal(y128, y1)
     ref = oracle.gmm_fwd(oracle.dequant_rowwise(xq, sx), oracle.dequant_int4(p, s, 128), np.array([1]))
     assert rel_fro(_f64(y1), ref) <= FP8_TOL
+
+
+@pytest.mark.parametrize("E,counts,K,N,seed", [
+    # one expert holds every row, the rest are empty: the (row tile,
+    # 32-column) items fill at most half of a grid sized for one tile per
+    # routed row, so K is split across workgroups -- 4 pieces here, with a
+    # ragged row count and a ragged last column slice
+    (8, [0, 0, 5, 0, 0, 0, 0, 0], 4096, 200, 5),      # 4-wave kernel, 32 chunks
+    (8, [0, 0, 0, 0, 0, 0, 0, 9], 8960, 96, 6),       # 8-wave kernel, 70 chunks
+])
+def test_f8i4_k_split_pieces(E, counts, K, N, seed):
+    counts = np.array(counts, np.int32)
+    got, ref = _f8i4_case(E, int(counts.sum()), K, N, seed, counts=counts)
+    assert rel_fro(got, ref) <= FP8_TOL
