@@ -264,6 +264,21 @@ int gmm_fwd_f8i4(const uint8_t* xq, const float* sx, const uint8_t* w4,
 int quantize_rowwise_fp8(const void* x, int64_t rows, int32_t cols, int64_t ld,
                          uint8_t* q, float* scales, mg_stream_t stream);
 
+/* Rowwise of token rows in sorted order ([FMOE] docstring: fused_moe reads A
+ * row sorted_id / top_k and masks the padding sentinel): output row r
+ * quantizes x[sorted_token_ids[r] / top_k], and an entry that is not below
+ * T * top_k (the sentinel) gives a row of zeros (codes 0, the scale of
+ * amax 0), bit for bit what quantize_rowwise_fp8 gives for the rows
+ * moe_permute gathers.
+ *   x                 bf16 [T, cols] contiguous (may be NULL when T == 0)
+ *   sorted_token_ids  int32 [rows] (moe_permute's sorted_token_ids)
+ *   q                 e4m3 [rows, cols] contiguous, scales fp32 [rows]
+ * cols % 8 == 0, top_k >= 1; MG_EINVAL for negative sizes or NULL
+ * pointers, MG_EUNSUPPORTED for misaligned tensors (x 16-byte, q 8-byte). */
+int quantize_rowwise_fp8_gather(const void* x, int64_t T, const int32_t* sorted_token_ids,
+                                int32_t top_k, int64_t rows, int32_t cols, uint8_t* q,
+                                float* scales, mg_stream_t stream);
+
 /* Per-group colwise, single or dual: for each group g and column c of a
  * (and of b, if non-NULL), one scale over the group's rows.  Codes are
  * written column-major: qa[c * rows + r]; scales sa[g * cols_a + c].  b,

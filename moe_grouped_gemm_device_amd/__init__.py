@@ -51,6 +51,7 @@ _SIGS = {
                                    _P, _P, _P, _SZ, _P]),
     "gmm_fwd_f8i4": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "quantize_rowwise_fp8": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P, _P]),
+    "quantize_rowwise_fp8_gather": (ctypes.c_int, [_P, _I64, _P, _I32, _I64, _I32, _P, _P, _P]),
     "quantize_colwise_per_group_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _I32, _I64, _P, _P, _P, _P, _P]),
     "quantize_int4_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "moe_sorted_capacity": (_I64, [_I64, _I32, _I32, _I32]),
@@ -316,6 +317,22 @@ def quantize_rowwise_fp8(x, q=None, scales=None, stream=None):
     return q, scales
 
 
+def quantize_rowwise_fp8_gather(x, sorted_token_ids, top_k, q=None, scales=None, stream=None):
+    """Rowwise e4m3 of the token rows in sorted order: row r quantizes
+    x[sorted_token_ids[r] // top_k]; the padding sentinel (>= T * top_k)
+    gives a row of zeros.  x bf16 [T, C] contiguous.  Returns (codes uint8
+    [rows, C], fp32 scales [rows]), rows = sorted_token_ids.numel()."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(sorted_token_ids, torch.int32, "sorted_token_ids", 1)
+    T, C = x.shape
+    R = sorted_token_ids.numel()
+    q = torch.empty(R, C, dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty(R, dtype=torch.float32, device=x.device) if scales is None else scales
+    _call("quantize_rowwise_fp8_gather", _ptr(x), T, _ptr(sorted_token_ids), int(top_k), R, C, _ptr(q),
+          _ptr(scales), _stream(stream))
+    return q, scales
+
+
 def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None):
     """Per-group colwise quantization of a (and b).  Returns
     (qa [Ca, M] column-major codes, sa [G, Ca]) or, with b,
@@ -401,8 +418,8 @@ def moe_permute(topk_ids, E, block_m, x=None, ws=None, stream=None):
 
 def fused_moe_f8i4(x, w1_4, s1, w2_4, s2, topk_ids, topk_weights, block_m=16, ws=None, stream=None):
     """Token-sorted MoE expert FFN with int4 expert weights and fp8
-    activations, for decode-sized token counts: align + gather -> rowwise
-    e4m3 quantization -> F8I4 GEMM1 -> SiLU*mul -> rowwise e4m3 quantization
+    activations, for decode-sized token counts: align -> rowwise e4m3
+    quantization of the token rows in sorted order -> F8I4 GEMM1 -> SiLU*mul -> rowwise e4m3 quantization
     -> F8I4 GEMM2 -> top-k weighted combine.  Weights as quantize_int4_weights
     returns them: w1_4 uint8 [E, 2I, H/2] with s1 bf16 [E, H/128, 2I] (from
     W1 [E, H, 2I]), w2_4 uint8 [E, H, I/2] with s2 bf16 [E, I/128, H] (from
@@ -411,10 +428,11 @@ def fused_moe_f8i4(x, w1_4, s1, w2_4, s2, topk_ids, topk_weights, block_m=16, ws
     Returns (out bf16 [T, H], dict of the intermediates)."""
     T, k = topk_ids.shape
     E = w1_4.shape[0]
-    p = moe_permute(topk_ids, E, block_m, x=x, stream=stream)
-    xs, sizes = p["x_sorted"], p["padded_sizes"]
-    ws = workspace(E, xs.shape[0], x.device) if ws is None else ws
-    xq, sx = quantize_rowwise_fp8(xs, stream=stream)
+    p = moe_permute(topk_ids, E, block_m, stream=stream)
+    ids, sizes = p["sorted_token_ids"], p["padded_sizes"]
+    ws = workspace(E, ids.numel(), x.device) if ws is None else ws
+    # the token rows are read through the sorted order by the quantizer
+    xq, sx = quantize_rowwise_fp8_gather(x, ids, k, stream=stream)
     h1 = gmm_fwd_f8i4(xq, sx, w1_4, s1, sizes, ws=ws, stream=stream)
     act = silu_mul(h1, stream=stream)
     aq, sa = quantize_rowwise_fp8(act, stream=stream)
@@ -437,8 +455,8 @@ def quantize_fp8_expert_weights(w, stream=None):
 
 def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=None, stream=None):
     """Token-sorted MoE expert FFN with e4m3 expert weights and
-    activations: align + gather -> rowwise e4m3 of the sorted rows -> fp8
-    GEMM1 (row scales x per-(expert, column) weight scales) -> SiLU*mul ->
+    activations: align -> rowwise e4m3 of the token rows in sorted order ->
+    fp8 GEMM1 (row scales x per-(expert, column) weight scales) -> SiLU*mul ->
     rowwise e4m3 of the activations -> fp8 GEMM2 -> top-k weighted combine.
     Weights as quantize_fp8_expert_weights returns them: w1q uint8 [2I, E*H]
     with s1 fp32 [E, 2I] (from W1 [E, H, 2I]), w2q uint8 [H, E*I] with s2
@@ -452,10 +470,11 @@ def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=
         raise ValueError("fp8 expert weights do not match x and each other")
     if block_m is None:
         block_m = 16 if T * k <= 64 * E else 128
-    p = moe_permute(topk_ids, E, block_m, x=x, stream=stream)
-    xs, sizes = p["x_sorted"], p["padded_sizes"]
-    ws = workspace(E, xs.shape[0], x.device) if ws is None else ws
-    xq, sx = quantize_rowwise_fp8(xs, stream=stream)
+    p = moe_permute(topk_ids, E, block_m, stream=stream)
+    ids, sizes = p["sorted_token_ids"], p["padded_sizes"]
+    ws = workspace(E, ids.numel(), x.device) if ws is None else ws
+    # the token rows are read through the sorted order by the quantizer
+    xq, sx = quantize_rowwise_fp8_gather(x, ids, k, stream=stream)
     h1 = gmm_fwd_fp8(xq, sx, w1q, s1, E * H, H, sizes, two_i, ws=ws, stream=stream)
     act = silu_mul(h1, stream=stream)
     aq, sa = quantize_rowwise_fp8(act, stream=stream)

@@ -512,6 +512,20 @@ int quantize_rowwise_fp8(const void* x, int64_t rows, int32_t cols, int64_t ld, 
                     "quantize_rowwise_fp8");
 }
 
+int quantize_rowwise_fp8_gather(const void* x, int64_t T, const int32_t* sorted_token_ids, int32_t top_k,
+                                int64_t rows, int32_t cols, uint8_t* q, float* scales, mg_stream_t stream) {
+  if (rows < 0 || T < 0 || cols < 1) return fail(MG_EINVAL, "rows and T must be >= 0 and cols >= 1");
+  if (top_k < 1) return fail(MG_EINVAL, "top_k must be >= 1");
+  if (cols % 8) return fail(MG_EUNSUPPORTED, "cols must be a multiple of 8");
+  if (rows == 0) return ok();
+  if (!sorted_token_ids || !q || !scales || (T > 0 && !x)) return fail(MG_EINVAL, "NULL tensor argument");
+  if ((x && !aligned16(x)) || (reinterpret_cast<uintptr_t>(q) & 7))
+    return fail(MG_EUNSUPPORTED, "x must be 16-byte and q 8-byte aligned");
+  return hip_status(launch_quant_rowwise(reinterpret_cast<const uint16_t*>(x), rows, cols, cols, q, scales,
+                                         S(stream), sorted_token_ids, top_k, T * (int64_t)top_k),
+                    "quantize_rowwise_fp8_gather");
+}
+
 int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a, const void* b, int32_t cols_b,
                                    const int32_t* group_sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
                                    uint8_t* qb, float* sb, mg_stream_t stream) {

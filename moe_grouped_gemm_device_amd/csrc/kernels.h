@@ -97,8 +97,11 @@ constexpr int kF8I4RowTile = 32;
 // ---------------------------------------------------------------------------
 // K3/K4: fp8 quantizers, int4 weight quantizer
 // ---------------------------------------------------------------------------
+// src (optional): output row r quantizes x[src[r] / top_k], or a row of
+// zeros where src[r] is not below n_pairs.
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int32_t cols,
-                                int64_t ld, uint8_t* q, float* s, hipStream_t stream);
+                                int64_t ld, uint8_t* q, float* s, hipStream_t stream,
+                                const int32_t* src = nullptr, int32_t top_k = 1, int64_t n_pairs = 0);
 hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_t* b,
                                 int32_t cols_b, const int32_t* sizes, int32_t G,
                                 int64_t rows, uint8_t* qa, float* sa, uint8_t* qb,

@@ -71,16 +71,35 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
 // ---------------------------------------------------------------------------
 constexpr int RCH = 8;   // chunks per lane held in registers
 
+// Source row of output row `row`: the row itself, or, with a row list
+// (token rows in sorted order), x[src[row] / top_k], where an entry past the
+// n_pairs (token, slot) pairs -- the padding sentinel -- stands for a row of
+// zeros (nch = 0: nothing is read, amax 0).
+__device__ inline const uint16_t* rowwise_source(const uint16_t* x, int64_t row, int64_t ld,
+                                                 const int32_t* src, int32_t top_k, int64_t n_pairs,
+                                                 int& nch) {
+  if (src == nullptr) return x + row * ld;
+  const int32_t id = src[row];
+  if (id < 0 || id >= n_pairs) {
+    nch = 0;
+    return x;
+  }
+  return x + (int64_t)(id / top_k) * ld;
+}
+
 __global__ void __launch_bounds__(256) quant_rowwise_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                            int32_t cols, int64_t ld,
                                                            uint8_t* __restrict__ q,
-                                                           float* __restrict__ scales) {
+                                                           float* __restrict__ scales,
+                                                           const int32_t* __restrict__ src, int32_t top_k,
+                                                           int64_t n_pairs) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const uint16_t* xr = x + row * ld;
   uint8_t* qr = q + row * (int64_t)cols;
-  const int nch = cols >> 3;   // 16-byte chunks in the row
+  const int ncols = cols >> 3;   // 16-byte chunks in the row
+  int nch = ncols;               // of them read from x
+  const uint16_t* xr = rowwise_source(x, row, ld, src, top_k, n_pairs, nch);
   uint4 held[RCH];
   uint32_t m = 0;
 #pragma unroll
@@ -100,10 +119,11 @@ __global__ void __launch_bounds__(256) quant_rowwise_kernel(const uint16_t* __re
 #pragma unroll
   for (int i = 0; i < RCH; ++i) {
     const int ch = lane + i * kWave;
-    if (ch < nch) *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(held[i], s);
+    if (ch < ncols) *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(held[i], s);
   }
-  for (int ch = lane + RCH * kWave; ch < nch; ch += kWave)
-    *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(*reinterpret_cast<const uint4*>(xr + ch * 8), s);
+  for (int ch = lane + RCH * kWave; ch < ncols; ch += kWave)
+    *reinterpret_cast<uint2*>(qr + ch * 8) =
+        quant_chunk(ch < nch ? *reinterpret_cast<const uint4*>(xr + ch * 8) : make_uint4(0, 0, 0, 0), s);
 }
 
 // Few long rows (the sorted activations of a decode step: about a hundred
@@ -117,13 +137,16 @@ constexpr int32_t kRowwiseWgCols = 2048;
 
 __global__ void __launch_bounds__(256) quant_rowwise_wg_kernel(const uint16_t* __restrict__ x, int32_t cols,
                                                               int64_t ld, uint8_t* __restrict__ q,
-                                                              float* __restrict__ scales) {
+                                                              float* __restrict__ scales,
+                                                              const int32_t* __restrict__ src, int32_t top_k,
+                                                              int64_t n_pairs) {
   __shared__ uint32_t wmax[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
-  const uint16_t* xr = x + row * ld;
   uint8_t* qr = q + row * (int64_t)cols;
-  const int nch = cols >> 3;
+  const int ncols = cols >> 3;
+  int nch = ncols;
+  const uint16_t* xr = rowwise_source(x, row, ld, src, top_k, n_pairs, nch);
   uint4 held[RCH_WG];
   uint32_t m = 0;
 #pragma unroll
@@ -146,20 +169,23 @@ __global__ void __launch_bounds__(256) quant_rowwise_wg_kernel(const uint16_t* _
 #pragma unroll
   for (int i = 0; i < RCH_WG; ++i) {
     const int ch = tid + i * 256;
-    if (ch < nch) *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(held[i], s);
+    if (ch < ncols) *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(held[i], s);
   }
-  for (int ch = tid + RCH_WG * 256; ch < nch; ch += 256)
-    *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(*reinterpret_cast<const uint4*>(xr + ch * 8), s);
+  for (int ch = tid + RCH_WG * 256; ch < ncols; ch += 256)
+    *reinterpret_cast<uint2*>(qr + ch * 8) =
+        quant_chunk(ch < nch ? *reinterpret_cast<const uint4*>(xr + ch * 8) : make_uint4(0, 0, 0, 0), s);
 }
 
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int32_t cols, int64_t ld, uint8_t* q,
-                                float* s, hipStream_t stream) {
+                                float* s, hipStream_t stream, const int32_t* src, int32_t top_k,
+                                int64_t n_pairs) {
   if (rows <= 0) return hipSuccess;
   if (rows <= kRowwiseWgRows && cols >= kRowwiseWgCols)
-    hipLaunchKernelGGL(quant_rowwise_wg_kernel, dim3((unsigned)rows), dim3(256), 0, stream, x, cols, ld, q, s);
+    hipLaunchKernelGGL(quant_rowwise_wg_kernel, dim3((unsigned)rows), dim3(256), 0, stream, x, cols, ld, q, s,
+                       src, top_k, n_pairs);
   else
     hipLaunchKernelGGL(quant_rowwise_kernel, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, stream, x, rows,
-                       cols, ld, q, s);
+                       cols, ld, q, s, src, top_k, n_pairs);
   return hipGetLastError();
 }
 

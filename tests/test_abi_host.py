@@ -123,6 +123,13 @@ def test_quantizers_reject_bad_arguments(lib):
     assert lib.quantize_colwise_per_group_fp8(_p(FAKE), 16, None, 0, _p(FAKE), 0, 64, _p(FAKE), _p(FAKE),
                                               None, None, None) == mg.MG_EINVAL       # G = 0
     assert lib.quantize_int4_weights(_p(FAKE), 2, 100, 16, _p(FAKE), _p(FAKE), None) == mg.MG_EUNSUPPORTED
+    g = lib.quantize_rowwise_fp8_gather
+    assert g(_p(FAKE), 4, _p(FAKE), 2, 8, 12, _p(FAKE), _p(FAKE), None) == mg.MG_EUNSUPPORTED   # cols % 8
+    assert g(_p(FAKE), 4, _p(FAKE), 0, 8, 16, _p(FAKE), _p(FAKE), None) == mg.MG_EINVAL        # top_k 0
+    assert g(_p(FAKE), -1, _p(FAKE), 2, 8, 16, _p(FAKE), _p(FAKE), None) == mg.MG_EINVAL       # T < 0
+    assert g(_p(FAKE), 4, None, 2, 8, 16, _p(FAKE), _p(FAKE), None) == mg.MG_EINVAL            # no ids
+    assert g(None, 4, _p(FAKE), 2, 8, 16, _p(FAKE), _p(FAKE), None) == mg.MG_EINVAL            # no x, T > 0
+    assert g(_p(FAKE), 4, _p(FAKE), 2, 0, 16, None, None, None) == mg.MG_OK                    # no rows
 
 
 def test_permute_rejects_bad_arguments(lib):

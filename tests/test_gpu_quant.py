@@ -129,3 +129,23 @@ def test_int4_quantizer_bit_exact(E, K, N):
     p_ref, s_ref = oracle.quant_int4(oracle.bf16_to_f64(w), 128)
     np.testing.assert_array_equal(bf16_host(sw), s_ref)
     np.testing.assert_array_equal(host(w4), p_ref)
+
+
+@pytest.mark.parametrize("T,k,E,bm,cols", [(1, 2, 8, 16, 4096), (64, 2, 8, 16, 14336), (300, 6, 64, 16, 512),
+                                           (2000, 2, 8, 128, 2048),
+                                           (600, 2, 8, 16, 8192)])   # rows past the register-held chunks
+def test_rowwise_gather_bit_exact(T, k, E, bm, cols):
+    """Rowwise e4m3 of the token rows in sorted order, padding sentinels
+    included, equals the oracle's rowwise quantizer on the oracle's gather,
+    codes and scales bit for bit (few long rows take the workgroup-per-row
+    kernel, many rows the wave-per-row one)."""
+    ids, _ = wl.softmax_topk_routing(T, E, k, cols)
+    x = wl.normal_bf16((T, cols), 1.0, cols, wl.T_X)
+    x[T // 2] = 0
+    al = oracle.moe_align(ids, E, bm)
+    sids = al["sorted_token_ids"]
+    q, s = mg.quantize_rowwise_fp8_gather(bf16_dev(x), dev(sids), k)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rowwise(oracle.gather_rows(x, k, sids))
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(s), s_ref)
