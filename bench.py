@@ -380,8 +380,8 @@ def _row_cases(torch, mg):
     # column) and e4m3 activations
     w1q, s1q = mg.quantize_fp8_expert_weights(w1)
     w2q, s2q = mg.quantize_fp8_expert_weights(w2)
-    yield ("C3_fused_ffn_fp8_T4096", "fp8-weight FFN end to end: align + gather -> e4m3 rows -> fp8 GEMM1 -> "
-                                     "SiLU*mul -> e4m3 -> fp8 GEMM2 -> combine",
+    yield ("C3_fused_ffn_fp8_T4096", "fp8-weight FFN end to end: align -> e4m3 of the token rows in sorted order "
+                                     "-> fp8 GEMM1 -> SiLU*mul -> e4m3 -> fp8 GEMM2 -> combine",
            lambda: mg.fused_moe_fp8(x, w1q, s1q, w2q, s2q, ids, wts, ws=wsf), 2.0 * T * k * H * 3 * I,
            "TFLOP/s", PEAK_FP8_TFLOPS, 3)
     for Tsmall in (1, 64):
