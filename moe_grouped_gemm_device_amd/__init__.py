@@ -116,8 +116,34 @@ def workspace_bytes(E, total_M):
 
 
 def workspace(E, total_M, device="cuda"):
-    """A device workspace big enough for any grouped-GEMM call with E, total_M."""
+    """A fresh, zeroed device workspace big enough for any grouped-GEMM call
+    with E, total_M (its size does not depend on them)."""
     return torch.zeros(max(workspace_bytes(E, total_M), 256), dtype=torch.uint8, device=device)
+
+
+_WS_CACHE = {}
+
+
+def default_workspace(device=None, stream=None):
+    """The workspace a call made without ``ws`` uses: one per (device,
+    stream), zeroed once when first needed and kept.  Its arrival counters
+    return to zero after every call, so it never needs clearing again, and
+    calls on one stream never overlap, so they may share it.  It cannot be
+    created during graph capture: make one eager call on the stream first,
+    or pass ``ws``."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    s = torch.cuda.current_stream(idx) if stream is None else stream
+    key = (idx, s.cuda_stream)
+    ws = _WS_CACHE.get(key)
+    if ws is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("no workspace for this stream yet and the stream is capturing: "
+                               "make one eager call on it first, or pass ws")
+        with torch.cuda.device(idx), torch.cuda.stream(s):
+            ws = torch.zeros(max(workspace_bytes(1, 0), 256), dtype=torch.uint8, device=torch.device("cuda", idx))
+        _WS_CACHE[key] = ws
+    return ws
 
 
 def workspace_error(ws):
@@ -163,7 +189,7 @@ def gmm_fwd(x, w, group_sizes, trans_b=False, out=None, ws=None, stream=None):
         raise ValueError("shape mismatch between x, w and group_sizes")
     y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device) if out is None else out
     _need(y, torch.bfloat16, "out", 2)
-    ws = workspace(E, M, x.device) if ws is None else ws
+    ws = default_workspace(x.device, stream) if ws is None else ws
     _call("gmm_fwd", _ptr(x), _ptr(w), _ptr(group_sizes), E, M, K, N, int(bool(trans_b)), _ptr(y),
           _ptr(ws), ws.numel(), _stream(stream))
     return y
@@ -188,7 +214,7 @@ def gmm_fwd_gather(x, sorted_token_ids, top_k, w, group_sizes, trans_b=False, ou
     _need(y, torch.bfloat16, "out", 2)
     if y.shape[0] < M:
         raise ValueError("out has fewer rows than sorted_token_ids")
-    ws = workspace(E, M, x.device) if ws is None else ws
+    ws = default_workspace(x.device, stream) if ws is None else ws
     _call("gmm_fwd_gather", _ptr(x), T, _ptr(sorted_token_ids), int(top_k), _ptr(w), _ptr(group_sizes), E, M, K,
           N, int(bool(trans_b)), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
     return y
@@ -215,7 +241,7 @@ def gmm_fwd_silu_mul(x, w1, group_sizes, sorted_token_ids=None, top_k=1, out=Non
     _need(y, torch.bfloat16, "out", 2)
     if y.shape[0] < M or y.shape[1] != I:
         raise ValueError("out must be [rows, I]")
-    ws = workspace(E, M, x.device) if ws is None else ws
+    ws = default_workspace(x.device, stream) if ws is None else ws
     _call("gmm_fwd_silu_mul", _ptr(x), T, _ptr(sorted_token_ids), int(top_k), _ptr(w1), _ptr(group_sizes), E, M,
           K, I, _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
     return y
@@ -235,7 +261,7 @@ def gmm_bwd(dy, x, w, group_sizes, trans_b=False, need_dx=True, need_dw=True, dx
         dx = torch.empty(M, K, dtype=torch.bfloat16, device=x.device)
     if need_dw and dw is None:
         dw = torch.empty_like(w)
-    ws = workspace(E, M, x.device) if ws is None else ws
+    ws = default_workspace(x.device, stream) if ws is None else ws
     _call("gmm_bwd", _ptr(dy), _ptr(x), _ptr(w), _ptr(group_sizes), E, M, K, N, int(bool(trans_b)),
           _ptr(dx if need_dx else None), _ptr(dw if need_dw else None), _ptr(ws), ws.numel(), _stream(stream))
     return (dx if need_dx else None), (dw if need_dw else None)
@@ -257,7 +283,7 @@ def gmm_fwd_fp8(xq, sx, wq, sw, w_ld, w_expert_stride, group_sizes, N, out=None,
     M, K = xq.shape
     E = group_sizes.numel()
     y = torch.empty(M, N, dtype=torch.bfloat16, device=xq.device) if out is None else out
-    ws = workspace(E, M, xq.device) if ws is None else ws
+    ws = default_workspace(xq.device, stream) if ws is None else ws
     wd = _fp8w(wq, sw, w_ld, w_expert_stride)
     _call("gmm_fwd_fp8", _ptr(xq), _ptr(sx), ctypes.byref(wd), _ptr(group_sizes), E, M, K, int(N), _ptr(y),
           _ptr(ws), ws.numel(), _stream(stream))
@@ -276,7 +302,7 @@ def gmm_bwd_fp8(group_sizes, K, N, dyq=None, sdy=None, wq=None, sw=None, w_ld=0,
         dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
     if need_dw and dw is None:
         dw = torch.empty(E, K, N, dtype=torch.bfloat16, device=dev)
-    ws = workspace(E, M, dev) if ws is None else ws
+    ws = default_workspace(dev, stream) if ws is None else ws
     wd = _fp8w(wq, sw, w_ld, w_expert_stride) if need_dx else None
     _call("gmm_bwd_fp8", _ptr(dyq), _ptr(sdy), ctypes.byref(wd) if wd is not None else None, _ptr(xc),
           _ptr(sxc), _ptr(dyc), _ptr(sdyc), _ptr(group_sizes), E, M, int(K), int(N),
@@ -296,7 +322,7 @@ def gmm_fwd_f8i4(xq, sx, w4, sw, group_sizes, out=None, ws=None, stream=None):
     if K2 * 2 != K or group_sizes.numel() != E:
         raise ValueError("shape mismatch between xq, w4 and group_sizes")
     y = torch.empty(M, N, dtype=torch.bfloat16, device=xq.device) if out is None else out
-    ws = workspace(E, M, xq.device) if ws is None else ws
+    ws = default_workspace(xq.device, stream) if ws is None else ws
     _call("gmm_fwd_f8i4", _ptr(xq), _ptr(sx), _ptr(w4), _ptr(sw), _ptr(group_sizes), E, M, K, N, _ptr(y),
           _ptr(ws), ws.numel(), _stream(stream))
     return y
@@ -306,13 +332,27 @@ def gmm_fwd_f8i4(xq, sx, w4, sw, group_sizes, out=None, ws=None, stream=None):
 # quantizers
 # --------------------------------------------------------------------------
 
+def _rowwise_outputs(q, scales, R, C, device):
+    """Fresh (codes, scales) for R rows of C values, or the caller's buffers
+    checked for dtype, shape, contiguity and device (the kernels write R * C
+    codes and R scales through them)."""
+    q = torch.empty(R, C, dtype=torch.uint8, device=device) if q is None else q
+    scales = torch.empty(R, dtype=torch.float32, device=device) if scales is None else scales
+    _need(q, torch.uint8, "q", 2)
+    _need(scales, torch.float32, "scales", 1)
+    if tuple(q.shape) != (R, C) or scales.numel() != R:
+        raise ValueError(f"q must be [{R}, {C}] and scales [{R}]")
+    if q.device != device or scales.device != device:
+        raise ValueError("q and scales must be on the input's device")
+    return q, scales
+
+
 def quantize_rowwise_fp8(x, q=None, scales=None, stream=None):
     """bf16 [R, C] -> (e4m3 codes uint8 [R, C], fp32 scales [R])."""
-    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
-        raise ValueError("x must be a bf16 matrix with unit column stride")
+    if x.device.type != "cuda" or x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a device bf16 matrix with unit column stride")
     R, C = x.shape
-    q = torch.empty(R, C, dtype=torch.uint8, device=x.device) if q is None else q
-    scales = torch.empty(R, dtype=torch.float32, device=x.device) if scales is None else scales
+    q, scales = _rowwise_outputs(q, scales, R, C, x.device)
     _call("quantize_rowwise_fp8", _ptr(x), R, C, x.stride(0), _ptr(q), _ptr(scales), _stream(stream))
     return q, scales
 
@@ -326,8 +366,7 @@ def quantize_rowwise_fp8_gather(x, sorted_token_ids, top_k, q=None, scales=None,
     _need(sorted_token_ids, torch.int32, "sorted_token_ids", 1)
     T, C = x.shape
     R = sorted_token_ids.numel()
-    q = torch.empty(R, C, dtype=torch.uint8, device=x.device) if q is None else q
-    scales = torch.empty(R, dtype=torch.float32, device=x.device) if scales is None else scales
+    q, scales = _rowwise_outputs(q, scales, R, C, x.device)
     _call("quantize_rowwise_fp8_gather", _ptr(x), T, _ptr(sorted_token_ids), int(top_k), R, C, _ptr(q),
           _ptr(scales), _stream(stream))
     return q, scales
@@ -336,16 +375,24 @@ def quantize_rowwise_fp8_gather(x, sorted_token_ids, top_k, q=None, scales=None,
 def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None):
     """Per-group colwise quantization of a (and b).  Returns
     (qa [Ca, M] column-major codes, sa [G, Ca]) or, with b,
-    (qa, sa, qb, sb).  Codes of rows past the groups are not written (fresh
-    outputs start zeroed); out=(qa, sa[, qb, sb]) reuses buffers."""
+    (qa, sa, qb, sb).  Codes of rows past the groups are not written (a
+    fresh output holds whatever its allocation held there); out=(qa, sa[,
+    qb, sb]) reuses buffers, checked for dtype, shape and device."""
     _need(a, torch.bfloat16, "a", 2)
     _need(group_sizes, torch.int32, "group_sizes", 1)
     M, Ca = a.shape
     G = group_sizes.numel()
+    def check(q, sc, C, name):
+        _need(q, torch.uint8, "q" + name, 2)
+        _need(sc, torch.float32, "s" + name, 2)
+        if tuple(q.shape) != (C, M) or tuple(sc.shape) != (G, C) or q.device != a.device or sc.device != a.device:
+            raise ValueError(f"q{name} must be [{C}, {M}] and s{name} [{G}, {C}] on the input's device")
+
     if out is not None:
         qa, sa = out[0], out[1]
+        check(qa, sa, Ca, "a")
     else:
-        qa = torch.zeros(Ca, M, dtype=torch.uint8, device=a.device)
+        qa = torch.empty(Ca, M, dtype=torch.uint8, device=a.device)
         sa = torch.empty(G, Ca, dtype=torch.float32, device=a.device)
     qb = sb = None
     Cb = 0
@@ -356,8 +403,9 @@ def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None
         Cb = b.shape[1]
         if out is not None:
             qb, sb = out[2], out[3]
+            check(qb, sb, Cb, "b")
         else:
-            qb = torch.zeros(Cb, M, dtype=torch.uint8, device=a.device)
+            qb = torch.empty(Cb, M, dtype=torch.uint8, device=a.device)
             sb = torch.empty(G, Cb, dtype=torch.float32, device=a.device)
     _call("quantize_colwise_per_group_fp8", _ptr(a), Ca, _ptr(b), Cb, _ptr(group_sizes), G, M, _ptr(qa),
           _ptr(sa), _ptr(qb), _ptr(sb), _stream(stream))
@@ -430,7 +478,7 @@ def fused_moe_f8i4(x, w1_4, s1, w2_4, s2, topk_ids, topk_weights, block_m=16, ws
     E = w1_4.shape[0]
     p = moe_permute(topk_ids, E, block_m, stream=stream)
     ids, sizes = p["sorted_token_ids"], p["padded_sizes"]
-    ws = workspace(E, ids.numel(), x.device) if ws is None else ws
+    ws = default_workspace(x.device, stream) if ws is None else ws
     # the token rows are read through the sorted order by the quantizer
     xq, sx = quantize_rowwise_fp8_gather(x, ids, k, stream=stream)
     h1 = gmm_fwd_f8i4(xq, sx, w1_4, s1, sizes, ws=ws, stream=stream)
@@ -472,7 +520,7 @@ def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=
         block_m = 16 if T * k <= 64 * E else 128
     p = moe_permute(topk_ids, E, block_m, stream=stream)
     ids, sizes = p["sorted_token_ids"], p["padded_sizes"]
-    ws = workspace(E, ids.numel(), x.device) if ws is None else ws
+    ws = default_workspace(x.device, stream) if ws is None else ws
     # the token rows are read through the sorted order by the quantizer
     xq, sx = quantize_rowwise_fp8_gather(x, ids, k, stream=stream)
     h1 = gmm_fwd_fp8(xq, sx, w1q, s1, E * H, H, sizes, two_i, ws=ws, stream=stream)
@@ -530,7 +578,7 @@ def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, ws=None, stream=N
     p = moe_permute(topk_ids, E, block_m, stream=stream)
     ids = p["sorted_token_ids"]
     sizes = p["padded_sizes"]
-    ws = workspace(E, ids.numel(), x.device) if ws is None else ws
+    ws = default_workspace(x.device, stream) if ws is None else ws
     # GEMM1 reads the token rows through the sorted order (no sorted copy)
     # and applies SiLU-and-mul in its epilogue (no [rows, 2I] intermediate)
     act = gmm_fwd_silu_mul(x, w1, sizes, sorted_token_ids=ids, top_k=k, ws=ws, stream=stream)

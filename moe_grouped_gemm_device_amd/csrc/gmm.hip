@@ -492,6 +492,15 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   static_assert(ECW >= 32 && ECW % 32 == 0 && NW * WREG + SC_BYTES <= STAGE, "staging does not fit");
   static_assert(SPP >= 1 && (ERW * ECW / 8) % kWave == 0, "store split");
   static_assert((NS - 2) * LPS + NST <= 63, "vmcnt range");
+  // Vector-memory waits count loads and stores on one counter, and a store
+  // may retire before older loads.  So no wait relies on stores retiring in
+  // order: before an epilogue issues its stores it waits until at most
+  // EPI_VM loads are in flight -- the newest NS - 2 stages, which leaves the
+  // stage the next k-step reads landed, and (fp8) the tile's scale loads,
+  // which only the LPS transfers of its last k-step follow.  The wait at the
+  // top of the next k-step may then allow for the NST stores as well.
+  constexpr int EPI_VM_STAGES = (NS - 2) * LPS;
+  constexpr int EPI_VM = (EPI_VM_STAGES < LPS) ? EPI_VM_STAGES : LPS;
   static_assert(NS >= 2, "at least double buffering");
   static_assert(KIND == DYNAMIC_K || (int64_t)BM * BN * 4 <= kSkPartBytes, "partial tile size");
   // fp8 dW: chunks straddling a group boundary carry bytes of the next
@@ -842,7 +851,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
       // issues the same NST stores (the gate waves' out of range), so the
       // main loop's vector-memory waits count alike in all waves.
       static_assert(NST == TI * 4 && WGN == 4 && TJ == 2 && WN == 64, "paired epilogue shape");
-      lds_sync();   // every wave is done reading st
+      // every wave is done reading st, and the next k-step's stage has landed
+      wait_vm_sync<EPI_VM_STAGES>();
       uint32_t* xch = reinterpret_cast<uint32_t*>(st);   // [4 gate waves][16 dwords][64 lanes]
       const bool up = wn >= 2;
       const int pair = wm * 2 + (wn & 1);
@@ -910,10 +920,10 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     float* rsc = reinterpret_cast<float*>(st + NW * WREG);  // [BM] 1 / row scale
     float* csc = rsc + BM;                                  // [BN] 1 / column scale
     if constexpr (SCALED) {
-      // every wave is done reading st, and the scale DMAs issued before this
-      // k-step's LPS tile transfers (and whatever the stream-K combine
-      // issued since, which it waited for) have landed
-      wait_vm_sync<LPS>();
+      // every wave is done reading st; the scale DMAs, which only this
+      // k-step's LPS tile transfers follow, and the next k-step's stage have
+      // landed (the stream-K combine waited for whatever it issued since)
+      wait_vm_sync<EPI_VM>();
       for (int idx = tid; idx < BM + BN; idx += kThreads) {
         const float v = scl[idx];
         if (idx < BM) rsc[idx] = v != 0.f ? 1.f / v : 0.f;
@@ -921,7 +931,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
       }
       lds_sync();
     } else {
-      lds_sync();   // every wave is done reading st
+      // every wave is done reading st, and the next k-step's stage has landed
+      wait_vm_sync<EPI_VM_STAGES>();
     }
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(reinterpret_cast<uint16_t*>(a.C) + (int64_t)it.g * a.c_gs + it.rowbase * a.c_ld + it.n0, 0x7FFFFFFF);
@@ -1102,7 +1113,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     for (; cs < cend; ++cs) {
       // this thread's DMA for the current stage has landed (only the next
       // NS - 2 stages' loads and the last epilogue's stores may be in
-      // flight), and every wave is past the previous k-step
+      // flight; after an epilogue the stage had landed before its stores
+      // were issued), and every wave is past the previous k-step
       if (epi_prev) wait_vm_sync<(NS - 2) * LPS + NST>();
       else wait_vm_sync<(NS - 2) * LPS>();
       epi_prev = false;

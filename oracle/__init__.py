@@ -370,7 +370,9 @@ def unpermute(Y, inv, weights, T, k):
 def fused_moe(x_bits, w1_bits, w2_bits, topk_ids, topk_weights, block_m):
     """Token-sorted fused MoE, rounding to bf16 only where the pages keep a
     bf16 intermediate (the first GEMM's output, the activation, the second
-    GEMM's output, the final sum).  W1 is [E, H, 2I], W2 is [E, I, H]."""
+    GEMM's output).  The top-k weighted sum is returned in fp64, unrounded:
+    callers compare it with the library's bf16 output, whose own final
+    rounding the tolerance covers.  W1 is [E, H, 2I], W2 is [E, I, H]."""
     E = w1_bits.shape[0]
     T, k = topk_ids.shape
     al = moe_align(topk_ids, E, block_m)

@@ -115,10 +115,29 @@ def test_colwise_rows_outside_groups_untouched():
     M, C = 300, 64
     sizes = np.array([50, 0, 70], np.int32)       # covers 120 rows
     x = wl.normal_bf16((M, C), 1.0, 0, wl.T_X)
-    qa, sa = mg.quantize_colwise_per_group_fp8(bf16_dev(x), dev(sizes))   # qa starts zeroed
+    qa = torch.full((C, M), 0xA5, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(3, C, dtype=torch.float32, device="cuda")
+    mg.quantize_colwise_per_group_fp8(bf16_dev(x), dev(sizes), out=(qa, sa))
     torch.cuda.synchronize()
-    assert (host(qa)[:, 120:] == 0).all()
+    assert (host(qa)[:, 120:] == 0xA5).all()
     _check_colwise(x, sizes, qa, sa)
+
+
+def test_quantizers_reject_mismatched_output_buffers():
+    x = bf16_dev(wl.normal_bf16((64, 32), 1.0, 0, wl.T_X))
+    with pytest.raises(ValueError):
+        mg.quantize_rowwise_fp8(x, q=torch.empty(63, 32, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        mg.quantize_rowwise_fp8(x, scales=torch.empty(64, dtype=torch.float64, device="cuda"))
+    with pytest.raises(ValueError):
+        mg.quantize_rowwise_fp8(x, q=torch.empty(32, 64, dtype=torch.uint8, device="cuda").t())
+    ids = dev(np.arange(64, dtype=np.int32))
+    with pytest.raises(ValueError):
+        mg.quantize_rowwise_fp8_gather(x, ids, 1, scales=torch.empty(10, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        mg.quantize_colwise_per_group_fp8(x, dev(np.array([64], np.int32)),
+                                          out=(torch.empty(32, 60, dtype=torch.uint8, device="cuda"),
+                                               torch.empty(1, 32, dtype=torch.float32, device="cuda")))
 
 
 @pytest.mark.parametrize("E,K,N", [(2, 256, 64), (3, 5120, 136)])
@@ -133,7 +152,8 @@ def test_int4_quantizer_bit_exact(E, K, N):
 
 @pytest.mark.parametrize("T,k,E,bm,cols", [(1, 2, 8, 16, 4096), (64, 2, 8, 16, 14336), (300, 6, 64, 16, 512),
                                            (2000, 2, 8, 128, 2048),
-                                           (600, 2, 8, 16, 8192)])   # rows past the register-held chunks
+                                           (600, 2, 8, 16, 8192),    # rows past the register-held chunks
+                                           (8, 2, 8, 16, 20480)])    # few rows past 16384 columns, sentinels
 def test_rowwise_gather_bit_exact(T, k, E, bm, cols):
     """Rowwise e4m3 of the token rows in sorted order, padding sentinels
     included, equals the oracle's rowwise quantizer on the oracle's gather,

@@ -210,6 +210,80 @@ def test_bf16_encode_matches_torch_on_fp32_inputs():
     np.testing.assert_array_equal(ours, wl.f32_to_bf16_bits(x))
 
 
+def _bf16_nearest_exact(x):
+    """Reference double -> bf16 bits by exact rational arithmetic: the finite
+    bf16 value nearest to x, a tie going to the pattern with an even last
+    bit.  Positive bf16 patterns are ordered like their values, so the two
+    neighbours of |x| come from a binary search over patterns compared as
+    exact fractions; no float rounding enters anywhere.  Defined for |x| up
+    to the largest finite bf16 value."""
+    import struct
+    from fractions import Fraction
+
+    def val(p):   # exact value of a positive finite bf16 pattern
+        return Fraction(struct.unpack("<f", struct.pack("<I", p << 16))[0])
+
+    a = Fraction(abs(x))
+    lo, hi = 0, 0x7F7F            # val(lo) <= a < val(hi) is kept below
+    if a > val(hi):
+        raise ValueError("beyond the largest finite bf16 value")
+    if a == val(hi):
+        p = hi
+    else:
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if val(mid) <= a:
+                lo = mid
+            else:
+                hi = mid
+        dlo, dhi = a - val(lo), val(hi) - a
+        p = lo if dlo < dhi else hi if dhi < dlo else (lo if lo % 2 == 0 else hi)
+    return p | (0x8000 if np.signbit(x) else 0)
+
+
+def _bf16_pin_inputs():
+    """Doubles that are not fp32 values: random magnitudes over the whole
+    normal range, near-ties just above and below bf16 midpoints (off by far
+    less than an fp32 ulp, so rounding through fp32 first lands exactly on
+    the midpoint), subnormals, and the normal/subnormal boundary."""
+    g = np.random.default_rng(7)
+    xs = list(g.standard_normal(3000) * np.exp2(g.uniform(-125, 127, 3000)))
+    base = wl.bf16_bits_to_f32(g.integers(0x0080, 0x7F7F, 600).astype(np.uint16)).astype(np.float64)
+    mids = base + np.exp2(np.floor(np.log2(base)) - 8)        # halfway to the next bf16 value
+    for eps in (2.0 ** -40, 2.0 ** -30, 2.0 ** -26):
+        xs += list(mids * (1 + eps)) + list(mids * (1 - eps))
+    sub = np.exp2(-133.0)                                      # bf16 subnormal spacing
+    ks = g.integers(0, 128, 400).astype(np.float64)
+    xs += list((ks + 0.5) * sub) + list((ks + 0.5) * sub * (1 + 2.0 ** -35)) + list((ks + 0.5) * sub * (1 - 2.0 ** -35))
+    xs += list(g.uniform(0, 128, 400) * sub) + list(g.uniform(0, 1, 100) * sub * 2.0 ** -5)
+    tiny_normal = np.exp2(-126.0)
+    xs += [tiny_normal, tiny_normal * (1 - 2.0 ** -9), tiny_normal * (1 - 2.0 ** -9) * (1 + 2.0 ** -40),
+           tiny_normal * (1 - 2.0 ** -9) * (1 - 2.0 ** -40), tiny_normal * (1 + 2.0 ** -9), 127.5 * sub,
+           0.5 * sub, 0.5 * sub * (1 + 2.0 ** -40), 0.5 * sub * (1 - 2.0 ** -40), 2.0 ** -1000]
+    x = np.array(xs, np.float64)
+    signs = np.where(g.integers(0, 2, x.size) == 1, -1.0, 1.0)
+    return x * signs
+
+
+def test_bf16_encode_of_doubles_is_exact_rounding():
+    """The oracle's double -> bf16 (used on fp64 GEMM results and on the int4
+    scales) equals the exact nearest-even rounding of the double itself."""
+    x = _bf16_pin_inputs()
+    ref = np.array([_bf16_nearest_exact(float(v)) for v in x], np.uint16)
+    np.testing.assert_array_equal(oracle.f64_to_bf16(x), ref)
+
+
+def test_bf16_pin_rejects_rounding_through_fp32():
+    """The inputs above separate correct rounding from double rounding
+    through fp32 (the mistake the pin is there to catch): rounding each
+    double to fp32 first and then to bf16 disagrees with the exact result on
+    many of them."""
+    x = _bf16_pin_inputs()
+    ref = np.array([_bf16_nearest_exact(float(v)) for v in x], np.uint16)
+    via_f32 = wl.f32_to_bf16_bits(x.astype(np.float32))
+    assert int((via_f32 != ref).sum()) >= 200
+
+
 def test_e4m3_decode_matches_torch():
     codes = np.arange(256, dtype=np.uint8)
     vals = oracle.e4m3_to_f64(codes)
