@@ -7,7 +7,8 @@ import torch
 import moe_grouped_gemm_device_amd as mg
 import oracle
 import workloads as wl
-from gpu_util import BF16_TOL, bf16_dev, bf16_host, dev, gpu, host, rel_fro, require_gpu
+from gpu_util import (BF16_TOL, GEMM_BF16, assert_close, bf16_dev, bf16_host, dev, dw_norms, dx_norms, fwd_norms,
+                      gpu, host, require_gpu)
 
 pytestmark = gpu
 
@@ -107,13 +108,20 @@ def _run_all(X, W, dY, sizes, trans_b):
     return f(y), f(dx), dwh
 
 
+def _check_products(y, dx, dw, X, W, dY, sizes):
+    """Y, dX and dW (fp64 of the library's bf16, dW laid out [E, K, N])
+    against the oracle on the same bf16 operands, every element."""
+    Xf, Wf, dYf = (oracle.bf16_to_f64(a) for a in (X, W, dY))
+    assert_close(y, oracle.gmm_fwd(Xf, Wf, sizes), BF16_TOL, GEMM_BF16, "Y", fwd_norms(Xf, Wf, sizes))
+    assert_close(dx, oracle.gmm_dx(dYf, Wf, sizes), BF16_TOL, GEMM_BF16, "dX", dx_norms(dYf, Wf, sizes))
+    assert_close(dw, oracle.gmm_dw(Xf, dYf, sizes), BF16_TOL, GEMM_BF16, "dW", dw_norms(Xf, dYf, sizes))
+
+
 def test_tiny_config_forward_and_backward():
     c = wl.tiny_bf16(seed=0)
     dY = wl.normal_bf16((c["M"], c["N"]), 1.0, 0, wl.T_DY)
     y, dx, dw = _run_all(c["X"], c["W"], dY, c["sizes"], False)
-    assert rel_fro(y, oracle.gmm_fwd_bf16(c["X"], c["W"], c["sizes"])) <= BF16_TOL
-    assert rel_fro(dx, oracle.gmm_dx_bf16(dY, c["W"], c["sizes"])) <= BF16_TOL
-    assert rel_fro(dw, oracle.gmm_dw_bf16(c["X"], dY, c["sizes"])) <= BF16_TOL
+    _check_products(y, dx, dw, c["X"], c["W"], dY, c["sizes"])
     assert (dw[0] == 0).all()   # the empty group
 
 
@@ -137,10 +145,7 @@ def test_bf16_gmm_matches_oracle(E, M, K, N, seed, trans_b):
     W = wl.normal_bf16((E, K, N), 0.5, seed, wl.T_W)
     dY = wl.normal_bf16((M, N), 1.0, seed, wl.T_DY)
     y, dx, dw = _run_all(X, W, dY, sizes, trans_b)
-    assert rel_fro(y, oracle.gmm_fwd_bf16(X, W, sizes)) <= BF16_TOL
-    assert rel_fro(dx, oracle.gmm_dx_bf16(dY, W, sizes)) <= BF16_TOL
-    dw_ref = oracle.gmm_dw_bf16(X, dY, sizes)
-    assert rel_fro(dw, dw_ref) <= BF16_TOL
+    _check_products(y, dx, dw, X, W, dY, sizes)
     for g in np.flatnonzero(sizes == 0):
         assert (dw[g] == 0).all()
 
@@ -161,8 +166,11 @@ def test_fixed_m_schedule_paths(M, N, K):
     y = mg.gmm_fwd(x, w, gs)
     dx, _ = mg.gmm_bwd(dy, x, w, gs, need_dw=False)
     torch.cuda.synchronize()
-    assert rel_fro(oracle.bf16_to_f64(bf16_host(y)), oracle.gmm_fwd_bf16(X, W, sizes)) <= BF16_TOL
-    assert rel_fro(oracle.bf16_to_f64(bf16_host(dx)), oracle.gmm_dx_bf16(dY, W, sizes)) <= BF16_TOL
+    Xf, Wf, dYf = (oracle.bf16_to_f64(a) for a in (X, W, dY))
+    assert_close(oracle.bf16_to_f64(bf16_host(y)), oracle.gmm_fwd(Xf, Wf, sizes), BF16_TOL, GEMM_BF16, "Y",
+                 fwd_norms(Xf, Wf, sizes))
+    assert_close(oracle.bf16_to_f64(bf16_host(dx)), oracle.gmm_dx(dYf, Wf, sizes), BF16_TOL, GEMM_BF16, "dX",
+                 dx_norms(dYf, Wf, sizes))
 
 
 def test_rows_past_the_groups_are_untouched():
@@ -175,7 +183,8 @@ def test_rows_past_the_groups_are_untouched():
     torch.cuda.synchronize()
     yh = oracle.bf16_to_f64(bf16_host(y))
     assert (yh[100:] == 3.0).all()
-    assert rel_fro(yh[:100], oracle.gmm_fwd_bf16(X[:100], W, sizes)) <= BF16_TOL
+    Xf, Wf = oracle.bf16_to_f64(X[:100]), oracle.bf16_to_f64(W)
+    assert_close(yh[:100], oracle.gmm_fwd(Xf, Wf, sizes), BF16_TOL, GEMM_BF16, "Y", fwd_norms(Xf, Wf, sizes))
 
 
 def test_zero_group_insertion_is_bitwise_invariant():
@@ -220,9 +229,9 @@ def test_deterministic_and_empty_total():
 
 def test_balanced_config_full_size():
     """E=8, M=1024 (128 rows each), K=4096, N=6400; X, W uniform[0,1);
-    dY = ones.  dX and dW are checked in full against closed forms the
-    oracle evaluates in fp64 (dX[r,k] = sum_n W[g,k,n]; dW[g,k,n] =
-    sum_{r in g} X[r,k] for every n); Y on sampled rows and columns."""
+    dY = ones.  Every element: Y against the oracle's forward, dX and dW
+    against closed forms evaluated in fp64 (dX[r,k] = sum_n W[g,k,n];
+    dW[g,k,n] = sum_{r in g} X[r,k] for every n)."""
     c = wl.balanced_bf16(seed=0)
     E, M, K, N = c["E"], c["M"], c["K"], c["N"]
     sizes = c["sizes"]
@@ -231,24 +240,17 @@ def test_balanced_config_full_size():
     y = mg.gmm_fwd(x, w, gs)
     dx, dw = mg.gmm_bwd(dy, x, w, gs)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(M, 24, replace=False))
-    cols = np.sort(rng.choice(N, 24, replace=False))
-    # forward on samples: the oracle on the sampled rows and columns
-    sub_sizes = np.array([np.sum((rows >= 128 * g) & (rows < 128 * (g + 1))) for g in range(E)], np.int32)
-    y_ref = oracle.gmm_fwd_bf16(c["X"][rows], np.ascontiguousarray(c["W"][:, :, cols]), sub_sizes)
-    y_got = oracle.bf16_to_f64(bf16_host(y))[np.ix_(rows, cols)]
-    assert rel_fro(y_got, y_ref) <= BF16_TOL
+    Xf, Wf, dYf = (oracle.bf16_to_f64(a) for a in (c["X"], c["W"], c["dY"]))
+    assert_close(oracle.bf16_to_f64(bf16_host(y)), oracle.gmm_fwd(Xf, Wf, sizes), BF16_TOL, GEMM_BF16, "Y",
+                 fwd_norms(Xf, Wf, sizes))
     # dX in full
-    Wf = oracle.bf16_to_f64(c["W"])
     dx_ref = np.repeat(Wf.sum(axis=2), 128, axis=0)
-    del Wf
-    assert rel_fro(oracle.bf16_to_f64(bf16_host(dx)), dx_ref) <= BF16_TOL
+    assert_close(oracle.bf16_to_f64(bf16_host(dx)), dx_ref, BF16_TOL, GEMM_BF16, "dX", dx_norms(dYf, Wf, sizes))
+    del Wf, dx_ref
     # dW: constant along n, equal to the group's column sums of X
     dwh = oracle.bf16_to_f64(bf16_host(dw))
-    Xf = oracle.bf16_to_f64(c["X"])
     colsum = Xf.reshape(E, 128, K).sum(axis=1)
-    assert rel_fro(dwh[:, :, 0], colsum) <= BF16_TOL
+    assert_close(dwh[:, :, :1], colsum[:, :, None], BF16_TOL, GEMM_BF16, "dW", dw_norms(Xf, dYf[:, :1], sizes))
     assert (dwh == dwh[:, :, :1]).all()
 
 
@@ -300,3 +302,55 @@ def test_captured_step_replays_bitwise():
             assert torch.equal(t, r)
         step()   # eager work between the replays
         torch.cuda.synchronize()
+
+
+def test_captured_step_follows_device_sizes_changed_between_replays():
+    """The group sizes are read on the device at run time, never on the host,
+    so one captured forward + dX + dW serves every routing: the sizes (and
+    the token rows) are overwritten in place between replays -- empty
+    groups, a sum below the row count, one group holding everything -- and
+    each replay equals a fresh eager run with the new sizes, bit for bit."""
+    E, M, K, N = 6, 400, 128, 192
+    W = wl.normal_bf16((E, K, N), 0.5, 8, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, 8, wl.T_DY)
+    w, dy = bf16_dev(W), bf16_dev(dY)
+    x = bf16_dev(wl.normal_bf16((M, K), 1.0, 8, wl.T_X))
+    gs = dev(wl.random_group_sizes(E, M, 8))
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty_like(w)
+    ws = mg.workspace(E, M)
+
+    def step():
+        mg.gmm_fwd(x, w, gs, out=y, ws=ws)
+        mg.gmm_bwd(dy, x, w, gs, dx=dx, dw=dw, ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    cases = [wl.random_group_sizes(E, M, 21, zero_frac=0.4), np.array([0, 0, M, 0, 0, 0], np.int32),
+             np.array([10, 0, 130, 7, 0, 53], np.int32), wl.random_group_sizes(E, M, 22)]
+    for i, sizes in enumerate(cases):
+        xs = wl.normal_bf16((M, K), 1.0, 30 + i, wl.T_X)
+        gs.copy_(dev(sizes))
+        x.copy_(bf16_dev(xs))
+        for t in (y, dx, dw):
+            t.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        s = int(sizes.sum())
+        ws2 = mg.workspace(E, M)
+        y_e = mg.gmm_fwd(x, w, dev(sizes), ws=ws2)
+        dx_e, dw_e = mg.gmm_bwd(dy, x, w, dev(sizes), ws=ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(y[:s], y_e[:s]) and torch.equal(dx[:s], dx_e[:s]) and torch.equal(dw, dw_e)
+        assert (y[s:] == 7.0).all() and (dx[s:] == 7.0).all()
+        Xf, Wf = oracle.bf16_to_f64(xs[:s]), oracle.bf16_to_f64(W)
+        assert_close(oracle.bf16_to_f64(bf16_host(y[:s])), oracle.gmm_fwd(Xf, Wf, sizes), BF16_TOL, GEMM_BF16, "Y",
+                     fwd_norms(Xf, Wf, sizes))

@@ -8,7 +8,8 @@ import torch
 import moe_grouped_gemm_device_amd as mg
 import oracle
 import workloads as wl
-from gpu_util import FP8_TOL, bf16_dev, bf16_host, dev, gpu, rel_fro, require_gpu
+from gpu_util import (FP8_TOL, GEMM_FP8, assert_close, bf16_dev, bf16_host, dev, dw_norms, dx_norms, fwd_norms, gpu,
+                      group_rows, require_gpu, vec_norms)
 
 pytestmark = gpu
 
@@ -39,9 +40,9 @@ def test_fp8_forward(E, M, K, N, seed):
     wq, sw = oracle.quant_colwise(W.reshape(E * K, N), np.full(E, K, np.int32))
     y = mg.gmm_fwd_fp8(dev(xq), dev(sx), dev(wq), dev(sw), E * K, K, dev(sizes), N)
     torch.cuda.synchronize()
-    ref = oracle.gmm_fwd(oracle.dequant_rowwise(xq, sx),
-                         oracle.dequant_colwise(wq, sw, np.full(E, K, np.int32)).reshape(E, K, N), sizes)
-    assert rel_fro(_f64(y), ref) <= FP8_TOL
+    A = oracle.dequant_rowwise(xq, sx)
+    Wd = oracle.dequant_colwise(wq, sw, np.full(E, K, np.int32)).reshape(E, K, N)
+    assert_close(_f64(y), oracle.gmm_fwd(A, Wd, sizes), FP8_TOL, GEMM_FP8, "Y", fwd_norms(A, Wd, sizes))
 
 
 @pytest.mark.parametrize("E,M,K,N,seed", [(4, 304, 256, 208, 0), (9, 1008, 136, 384, 1), (16, 2048, 1408, 2048, 3)])
@@ -55,11 +56,11 @@ def test_fp8_backward(E, M, K, N, seed):
                             w_expert_stride=K * N, xc=dev(xc), sxc=dev(sxc), dyc=dev(dyc), sdyc=dev(sdyc))
     torch.cuda.synchronize()
     Wd = oracle.dequant_rowwise(wq, sw).reshape(E, K, N)
-    dx_ref = oracle.gmm_dx(oracle.dequant_rowwise(dyq, sdy), Wd, sizes)
-    assert rel_fro(_f64(dx), dx_ref) <= FP8_TOL
-    dw_ref = oracle.gmm_dw(oracle.dequant_colwise(xc, sxc, sizes), oracle.dequant_colwise(dyc, sdyc, sizes), sizes)
+    dYd = oracle.dequant_rowwise(dyq, sdy)
+    assert_close(_f64(dx), oracle.gmm_dx(dYd, Wd, sizes), FP8_TOL, GEMM_FP8, "dX", dx_norms(dYd, Wd, sizes))
+    Xc, dYc = oracle.dequant_colwise(xc, sxc, sizes), oracle.dequant_colwise(dyc, sdyc, sizes)
     dwh = _f64(dw)
-    assert rel_fro(dwh, dw_ref) <= FP8_TOL
+    assert_close(dwh, oracle.gmm_dw(Xc, dYc, sizes), FP8_TOL, GEMM_FP8, "dW", dw_norms(Xc, dYc, sizes))
     for g in np.flatnonzero(sizes == 0):
         assert (dwh[g] == 0).all()
 
@@ -74,16 +75,19 @@ def _f8i4_case(E, total_M, K, N, seed, counts=None):
     w4 = torch.randint(0, 256, (E, N, K // 2), dtype=torch.uint8, device="cuda")   # never read for empty experts
     sw = torch.randn(E, K // 128, N, device="cuda").to(torch.bfloat16)
     ref = np.zeros((total_M, N))
+    cn = np.zeros((E, N))
     for e in np.flatnonzero(counts):
         We = oracle.bf16_to_f64(wl.normal_bf16((K, N), 0.02, seed, wl.T_W, int(e)))[None]
         p, s = oracle.quant_int4(We, 128)
         w4[e] = dev(p[0])
         sw[e] = bf16_dev(s[0])
         rows = slice(offs[e], offs[e + 1])
-        ref[rows] = oracle.gmm_fwd(Xd[rows], oracle.dequant_int4(p, s, 128), np.array([counts[e]]))
+        Wq = oracle.dequant_int4(p, s, 128)
+        ref[rows] = oracle.gmm_fwd(Xd[rows], Wq, np.array([counts[e]]))
+        cn[e] = vec_norms(Wq[0], 0)
     y = mg.gmm_fwd_f8i4(dev(xq), dev(sx), w4, sw, dev(counts))
     torch.cuda.synchronize()
-    return _f64(y), ref
+    return _f64(y), ref, (vec_norms(Xd, 1), cn, group_rows(counts, total_M))
 
 
 @pytest.mark.parametrize("E,total_M,K,N,seed", [(8, 5, 256, 64, 0), (16, 100, 512, 136, 1), (128, 1, 5120, 8192, 2),
@@ -91,8 +95,8 @@ def _f8i4_case(E, total_M, K, N, seed, counts=None):
                                                 # 70 chunks: the 8-wave kernel, 9 chunks per wave but 7 in the last
                                                 (4, 7, 8960, 96, 4)])
 def test_f8i4_sparse_m(E, total_M, K, N, seed):
-    got, ref = _f8i4_case(E, total_M, K, N, seed)
-    assert rel_fro(got, ref) <= FP8_TOL
+    got, ref, norms = _f8i4_case(E, total_M, K, N, seed)
+    assert_close(got, ref, FP8_TOL, GEMM_FP8, "Y", norms)
 
 
 def test_f8i4_one_token_over_128_groups_matches_single_group():
@@ -113,8 +117,8 @@ def test_f8i4_one_token_over_128_groups_matches_single_group():
     y1 = mg.gmm_fwd_f8i4(dev(xq), dev(sx), dev(p), bf16_dev(s), dev(np.array([1], np.int32)))
     torch.cuda.synchronize()
     assert torch.equal(y128, y1)
-    ref = oracle.gmm_fwd(oracle.dequant_rowwise(xq, sx), oracle.dequant_int4(p, s, 128), np.array([1]))
-    assert rel_fro(_f64(y1), ref) <= FP8_TOL
+    A, Wq = oracle.dequant_rowwise(xq, sx), oracle.dequant_int4(p, s, 128)
+    assert_close(_f64(y1), oracle.gmm_fwd(A, Wq, np.array([1])), FP8_TOL, GEMM_FP8, "Y", fwd_norms(A, Wq, [1]))
 
 
 @pytest.mark.parametrize("E,counts,K,N,seed", [
@@ -127,5 +131,5 @@ def test_f8i4_one_token_over_128_groups_matches_single_group():
 ])
 def test_f8i4_k_split_pieces(E, counts, K, N, seed):
     counts = np.array(counts, np.int32)
-    got, ref = _f8i4_case(E, int(counts.sum()), K, N, seed, counts=counts)
-    assert rel_fro(got, ref) <= FP8_TOL
+    got, ref, norms = _f8i4_case(E, int(counts.sum()), K, N, seed, counts=counts)
+    assert_close(got, ref, FP8_TOL, GEMM_FP8, "Y", norms)
