@@ -163,7 +163,10 @@ int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids,
  *   x     bf16 [T, K] (gathered) or [total_M, K] row-major
  *   w1    bf16 [E, K, 2I] (gate columns 0..I-1, up columns I..2I-1)
  *   act   bf16 [total_M, I]; rows past the groups untouched
- * Bit-identical to gmm_fwd (or gmm_fwd_gather) into h followed by silu_mul.
+ * The same bits as gmm_fwd (or gmm_fwd_gather) into h followed by silu_mul
+ * whenever neither launch splits a tile along K; where the stream-K tail
+ * splits tiles, the split points differ (a tile here pairs gate and up
+ * columns), so h may differ in its last bit before SiLU*mul.
  * Errors as gmm_fwd_gather; K and I must be multiples of 8. */
 int gmm_fwd_silu_mul(const void* x, int64_t T, const int32_t* sorted_token_ids,
                      int32_t top_k, const void* w1, const int32_t* group_sizes,
