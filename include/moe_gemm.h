@@ -133,6 +133,29 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes,
             int32_t E, int64_t total_M, int32_t K, int32_t N, int32_t trans_b,
             void* y, void* ws, size_t ws_bytes, mg_stream_t stream);
 
+/* gmm_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same product and kernels, with the workspace taken from a fixed
+ * device array inside the library (64 MiB + 1280 bytes per device, held
+ * from the first call on that device until the process ends) instead of a
+ * caller's buffer.  The result is bit-identical to gmm_fwd's.
+ *   x, w, group_sizes, E, total_M, K, N, trans_b, y: as for gmm_fwd.
+ * The array's address on the current device (stream must belong to it) is
+ * looked up on the first call there, which also enqueues a fill kernel on
+ * `stream` that zeroes its counters; every call leaves them zero again.
+ * The call allocates and frees nothing.  Every call on one device shares
+ * that device's array: calls that overlap in time on one device (other
+ * streams, other threads) race on it and must not be made.  The sticky
+ * device error word lives in the array and is not readable through this
+ * entry point; violations are still clamped.
+ * Errors as gmm_fwd, plus MG_EWORKSPACE should a call need more scratch
+ * than the array holds (the need depends on host values only), MG_EHIP if
+ * the array's address cannot be found, MG_EUNSUPPORTED for a device index
+ * of 64 or more. */
+int gmm_fwd_noalloc(const void* x, const void* w, const int32_t* group_sizes,
+                    int32_t E, int64_t total_M, int32_t K, int32_t N,
+                    int32_t trans_b, void* y, mg_stream_t stream);
+
 /* gmm_fwd over token-sorted rows, with the gather fused into the A-operand
  * load ([FMOE] fused_moe_kernel: the A rows of a block are found through
  * sorted_token_ids // top_k, so no sorted copy of x is made):

@@ -43,6 +43,7 @@ _SIGS = {
     "mg_workspace_clear": (ctypes.c_int, [_P, _P]),
     "gmm_build_worklist": (ctypes.c_int, [_I32, _P, _I32, _I64, _I32, _P, _P, _P, _I64, _P]),
     "gmm_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "gmm_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P]),
     "gmm_fwd_gather": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_fwd_silu_mul": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
@@ -193,6 +194,24 @@ def gmm_fwd(x, w, group_sizes, trans_b=False, out=None, ws=None, stream=None):
     _call("gmm_fwd", _ptr(x), _ptr(w), _ptr(group_sizes), E, M, K, N, int(bool(trans_b)), _ptr(y),
           _ptr(ws), ws.numel(), _stream(stream))
     return y
+
+
+def gmm_fwd_noalloc(x, w, group_sizes, out, trans_b=False, stream=None):
+    """gmm_fwd with the library's own fixed scratch instead of a workspace:
+    the call allocates nothing (out is required).  Calls on one device must
+    not overlap in time."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w, torch.bfloat16, "w", 3)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    _need(out, torch.bfloat16, "out", 2)
+    M, K = x.shape
+    E = w.shape[0]
+    N = w.shape[1] if trans_b else w.shape[2]
+    if (w.shape[2] if trans_b else w.shape[1]) != K or group_sizes.numel() != E or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch between x, w, group_sizes and out")
+    _call("gmm_fwd_noalloc", _ptr(x), _ptr(w), _ptr(group_sizes), E, M, K, N, int(bool(trans_b)), _ptr(out),
+          _stream(stream))
+    return out
 
 
 def gmm_fwd_gather(x, sorted_token_ids, top_k, w, group_sizes, trans_b=False, out=None, ws=None, stream=None):

@@ -4,11 +4,22 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_gemm.h"
 #include "kernels.h"
 
 using namespace mg;
+
+// Scratch of gmm_fwd_noalloc: one GEMM workspace (error word, stream-K
+// arrival counters, partial tiles: 64 MiB + 1280 bytes) as a file-scope
+// device array, so that entry point allocates nothing.  Each device the
+// library runs on holds its own copy until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it only stands for
+// the symbol): the device's address of its copy comes from
+// hipGetSymbolAddress, once per device, and is kept in noalloc_ptr.
+static constexpr size_t kNoAllocBytes = (size_t)kWsBytes;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
 
 namespace {
 
@@ -84,6 +95,34 @@ GemmArgs blank_args() {
   return a;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[kMaxDevices] = {};
+
+// The current device's scratch address.  On the first call on a device the
+// header and counters are cleared by a fill kernel enqueued on `stream`
+// (a kernel, not a memset, so a capturing stream records a kernel node).
+int noalloc_scratch(void** out, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "gmm_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MG_EUNSUPPORTED, "device %d past the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                           "gmm_fwd_noalloc: hipGetSymbolAddress(scratch)");
+    if ((reinterpret_cast<uintptr_t>(p) & 255) != 0) return fail(MG_EHIP, "gmm_fwd_noalloc: scratch not 256-byte aligned");
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, reinterpret_cast<int32_t*>(p), kWsZeroWords);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "gmm_fwd_noalloc: clearing the scratch");
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return MG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,8 +178,9 @@ int gmm_build_worklist(int32_t kind, const int32_t* group_sizes, int32_t E, int6
 // bf16
 // ---------------------------------------------------------------------------
 
-int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K,
-            int32_t N, int32_t trans_b, void* y, void* ws, size_t ws_bytes, mg_stream_t stream) {
+static int gmm_fwd_with(const void* x, const void* w, const int32_t* group_sizes, int32_t E, int64_t total_M,
+                        int32_t K, int32_t N, int32_t trans_b, void* y, void* ws, size_t ws_bytes, mg_stream_t stream,
+                        const char* name) {
   int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
   if (rc) return rc;
   if (K < 1 || N < 1) return fail(MG_EINVAL, "K and N must be positive");
@@ -173,7 +213,28 @@ int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E,
   L.elem = EL_BF16;
   L.a_kc = true;
   L.b_kc = trans_b != 0;
-  return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd");
+  return hip_status(launch_gemm(L, a, S(stream)), name);
+}
+
+int gmm_fwd(const void* x, const void* w, const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K,
+            int32_t N, int32_t trans_b, void* y, void* ws, size_t ws_bytes, mg_stream_t stream) {
+  return gmm_fwd_with(x, w, group_sizes, E, total_M, K, N, trans_b, y, ws, ws_bytes, stream, "gmm_fwd");
+}
+
+int gmm_fwd_noalloc(const void* x, const void* w, const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K,
+                    int32_t N, int32_t trans_b, void* y, mg_stream_t stream) {
+  // the scratch a call needs depends on host values only; refuse what the
+  // fixed array cannot hold before touching the device
+  if (E < 1 || E > MG_MAX_EXPERTS) return fail(MG_EINVAL, "E=%d outside [1, %d]", E, MG_MAX_EXPERTS);
+  if (total_M < 0 || total_M >= kMaxRows) return fail(MG_EINVAL, "total_M=%lld outside [0, 2^31)", (long long)total_M);
+  const size_t need = (size_t)ws_layout(E, total_M).total;
+  if (need > kNoAllocBytes)
+    return fail(MG_EWORKSPACE, "gmm_fwd_noalloc: needs %zu bytes of scratch, the fixed array holds %zu", need,
+                kNoAllocBytes);
+  void* ws = nullptr;
+  int rc = noalloc_scratch(&ws, S(stream));
+  if (rc) return rc;
+  return gmm_fwd_with(x, w, group_sizes, E, total_M, K, N, trans_b, y, ws, kNoAllocBytes, stream, "gmm_fwd_noalloc");
 }
 
 int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids, int32_t top_k, const void* w,

@@ -50,11 +50,13 @@ struct WsLayout {
   int64_t total;
 };
 
+constexpr int64_t kWsBytes = kWsPartials + 2 * (int64_t)kSkMaxGrid * kSkPartBytes;
+
 __host__ __device__ inline WsLayout ws_layout(int32_t E, int64_t total_M) {
   (void)E;
   (void)total_M;
   WsLayout L;
-  L.total = kWsPartials + 2 * (int64_t)kSkMaxGrid * kSkPartBytes;
+  L.total = kWsBytes;
   return L;
 }
 

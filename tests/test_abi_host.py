@@ -92,6 +92,14 @@ def test_gmm_fwd_rejects_null_and_small_workspace(lib):
                        None) == mg.MG_EINVAL  # misaligned workspace
 
 
+@pytest.mark.parametrize("E,total_M", [(0, 16), (1025, 16), (4, -1), (4, 1 << 31)])
+def test_gmm_fwd_noalloc_rejects_before_any_device_call(lib, E, total_M):
+    """The allocation-free forward refuses out-of-range sizes on the host,
+    before it looks up its scratch array on the device."""
+    rc = lib.gmm_fwd_noalloc(_p(FAKE), _p(FAKE), _p(FAKE), E, total_M, 64, 64, 0, _p(FAKE), None)
+    assert rc == mg.MG_EINVAL and lib.mg_last_error()
+
+
 def test_gmm_bwd_rejects_no_outputs(lib):
     need = lib.mg_workspace_bytes(4, 64)
     rc = lib.gmm_bwd(_p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 4, 64, 64, 64, 0, None, None, _p(0x10000), need, None)
