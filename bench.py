@@ -154,6 +154,16 @@ def run_gpu(args, torch, mg):
         e1.record()
         e1.synchronize()
         avg_ms[name] = e0.elapsed_time(e1) / R
+    launch_stats = {name: launch_percentiles(torch, fn, reps=20) for name, fn in products.items()}
+    # the pages' A100 figure is the total kernel time of 30 forward + backward
+    # iterations: the same 30 steps here, back to back, HIP events around them
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(30):
+        step()
+    e1.record()
+    e1.synchronize()
+    total30_ms = e0.elapsed_time(e1)
     flops_step = 3 * 2.0 * M * K * N
     ms_step = elapsed * 1e3 / args.steps
     tflops = flops_step / (ms_step * 1e-3) / 1e12
@@ -173,9 +183,131 @@ def run_gpu(args, torch, mg):
         "traffic": measured_traffic(dom),
         "algorithmic_bytes_per_launch": bytes_per[dom],
         "avg_launch_us": {k: round(v * 1e3, 2) for k, v in avg_ms.items()},
+        "launch_us_percentiles": launch_stats,
         "mfma_frac": {k: round(2.0 * M * K * N / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) for k, v in avg_ms.items()},
     }
-    return dict(value=tflops, ms_per_step=ms_step, roofline=roofline, E=E, M=M, K=K, N=N, host=d["host"])
+    return dict(value=tflops, ms_per_step=ms_step, roofline=roofline, E=E, M=M, K=K, N=N, host=d["host"],
+                total30_ms=total30_ms)
+
+
+_FLUSH = None
+
+
+def _flush_caches(torch):
+    """Writes 1 GiB, four times the 256 MB Infinity Cache, so the next kernel
+    finds none of its operands cached (L2 and the Infinity Cache)."""
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    _FLUSH.fill_(1)
+
+
+def launch_percentiles(torch, fn, reps=20):
+    """Median, p10 and p90 of single-launch durations (a HIP event pair
+    around each launch), warm (launches back to back) and cold (caches
+    flushed before each launch, outside the events)."""
+    out = {}
+    for cold in (False, True):
+        times = []
+        fn()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            if cold:
+                _flush_caches(torch)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        times.sort()
+        q = lambda f: times[min(len(times) - 1, int(round(f * (len(times) - 1))))]
+        out["cold" if cold else "warm"] = {"median": round(q(0.5), 2), "p10": round(q(0.1), 2), "p90": round(q(0.9), 2)}
+    return out
+
+
+def tiny_latency(torch, mg):
+    """The tiny grouped GEMM (E=4, K=64, N=48, group sizes [0, 20, 9, 8]):
+    forward and backward latency per launch (median, p10, p90)."""
+    import numpy as np
+    import workloads as wl
+    c = wl.tiny_bf16(seed=0)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    x, w, gs = t(c["X"]), t(c["W"]), torch.from_numpy(c["sizes"]).cuda()
+    dy = t(wl.normal_bf16((c["M"], c["N"]), 1.0, 0, wl.T_DY))
+    y = torch.empty(c["M"], c["N"], dtype=torch.bfloat16, device="cuda")
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    ws = mg.workspace(4, c["M"])
+    return {"workload": "E=4, K=64, N=48, group sizes [0,20,9,8] (total_M=37), bf16",
+            "fwd_us": launch_percentiles(torch, lambda: mg.gmm_fwd(x, w, gs, out=y, ws=ws))["warm"],
+            "dx_us": launch_percentiles(torch, lambda: mg.gmm_bwd(dy, x, w, gs, need_dw=False, dx=dx, ws=ws))["warm"],
+            "dw_us": launch_percentiles(torch, lambda: mg.gmm_bwd(dy, x, w, gs, need_dx=False, dw=dw, ws=ws))["warm"]}
+
+
+def measured_peaks(torch):
+    """What this GPU sustains, measured beside the published peaks: device
+    memory streams through torch (copy, read-only sum, write-only fill of
+    1 GiB), and dense GEMMs through the vendor BLAS (torch.matmul in bf16,
+    torch._scaled_mm in e4m3) at 8192 x 8192 x 8192.  Context only: none of
+    these runs any part of the grouped-GEMM path."""
+    def t(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    res = {"copy_GBps": round(2 * n / t(lambda: dst.copy_(src)) / 1e3, 1),
+           "read_GBps": round(n / t(lambda: src.sum()) / 1e3, 1),
+           "write_GBps": round(n / t(lambda: dst.fill_(2.0)) / 1e3, 1)}
+    del src, dst
+    S = 8192
+    a = torch.randn(S, S, device="cuda").to(torch.bfloat16)
+    b = torch.randn(S, S, device="cuda").to(torch.bfloat16)
+    res["bf16_gemm_TFLOPs"] = round(2.0 * S ** 3 / t(lambda: torch.matmul(a, b)) / 1e6, 1)
+    try:
+        a8, b8 = a.to(torch.float8_e4m3fn), b.t().contiguous().to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device="cuda")
+        res["fp8_gemm_TFLOPs"] = round(2.0 * S ** 3 / t(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
+                                                                             out_dtype=torch.bfloat16)) / 1e6, 1)
+    except Exception as e:   # a torch build without the fp8 product
+        res["fp8_gemm_TFLOPs"] = None
+        res["fp8_gemm_error"] = str(e)[:160]
+    res["what"] = ("sustained on this GPU: 1 GiB copy / fp32 sum / fill through torch, and the vendor BLAS at "
+                   "8192^3 (bf16 matmul, e4m3 scaled_mm); published peaks: HBM 8000 GB/s, bf16 2500, fp8 5000 TFLOP/s")
+    return res
+
+
+def graph_replay_latency(torch, fn, reps=50):
+    """Median of the event-timed replay of fn captured in a HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    times = []
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    times.sort()
+    return round(times[len(times) // 2], 2)
 
 
 def sparse_m_latency(torch, mg, reps=50):
@@ -246,6 +378,8 @@ def sparse_m_latency(torch, mg, reps=50):
         touched = int((sz > 0).sum().item())
         res[f"warm_total_M{tm}"] = {"us": round(t, 2), "experts_with_rows": touched,
                                     "hbm_frac": round(touched * bytes_expert / (t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    res["graph_replay_us_total_M1_E128"] = graph_replay_latency(torch, run128)
+    res["graph_replay_us_total_M1_E1"] = graph_replay_latency(torch, run1)
     res["workload"] = "F8I4: E=128, total_M=1 (one routed row), K=5120, N=8192; int4 per-128-K bf16 scales"
     return res
 
@@ -325,7 +459,21 @@ def _row_cases(torch, mg):
            2.0 * M * H * I, "TFLOP/s", PEAK_FP8_TFLOPS, 10)
     yield ("A1_builder", f"work list for {E} groups, total_M={M}, 128-row tiles (own launch)",
            lambda: mg.build_worklist(mg.MG_WL_FIXED_M, sizes, M, 128), None, None, None, 10)
-    del X, dY, W, xq, dyq, cq, wq_c, wq_r, y, dxo, dwo, ws
+    del X, dY, W, xq, dyq, cq, wq_c, wq_r, y, dxo, dwo
+    torch.cuda.empty_cache()
+    # ---- the torchao page's colwise shapes: M=16640 rows, 2048 or 5120
+    # columns, 64 or 128 groups cut at multiples of 16, randn bf16 input
+    for Cp, Gp in ((2048, 64), (5120, 64), (2048, 128), (5120, 128)):
+        Mp = 16640
+        szp = torch.from_numpy(wl.jagged_sizes_multiple_of(Gp, Mp, 16, 0)).cuda()
+        xp = torch.randn(Mp, Cp, generator=g, device="cuda").to(torch.bfloat16)
+        outp = (torch.empty(Cp, Mp, dtype=torch.uint8, device="cuda"),
+                torch.empty(Gp, Cp, dtype=torch.float32, device="cuda"))
+        yield (f"A6_colwise_M{Mp}_C{Cp}_G{Gp}", f"single tensor [{Mp},{Cp}] bf16, {Gp} groups -> column-major e4m3",
+               lambda: mg.quantize_colwise_per_group_fp8(xp, szp, out=outp),
+               Mp * Cp * 3 + Gp * Cp * 4, "GB/s", PEAK_HBM_GBS, 10)
+        del xp, outp
+    del ws
     torch.cuda.empty_cache()
     # ---- token-sorted fused FFN (configuration: Mixtral-8x7B-shaped) -------
     T, E, k, H, I = 4096, 8, 2, 4096, 14336
@@ -412,11 +560,17 @@ def _row_cases(torch, mg):
 
 
 def row_measurements(torch, mg):
-    """Each case of _row_cases timed on its own against its roofline."""
+    """Each case of _row_cases timed on its own against its roofline: the
+    average of back-to-back launches, and for the HBM-bound steps also the
+    median of single launches with the caches flushed before each (cold)."""
     rows = {}
     for key, what, fn, amount, unit, peak, reps in _row_cases(torch, mg):
         us = _timeit(torch, fn, reps=reps)
         rows[key] = _row(what, us, amount, unit, peak) if amount is not None else {"what": what, "us": round(us, 2)}
+        if unit == "GB/s":
+            cold = launch_percentiles(torch, fn, reps=10)["cold"]
+            rows[key]["cold_us"] = cold
+            rows[key]["cold_frac"] = round(amount / cold["median"] / 1e3 / peak, 4)
     return rows
 
 
@@ -457,29 +611,50 @@ def counter_probe(torch, mg):
     log("counter probe batches: " + ",".join(names))
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(host):
-    """The fp64 oracle (unchanged, OpenMP over output rows) running the same
-    step at full size -- forward, dX and dW of the balanced workload --
-    repeated until about 10 s of CPU work (at most 3 steps)."""
+    """The fp64 oracle (unchanged, OpenMP over output rows) timed on the host
+    cores on a bounded sample of the same workload: with every core of the
+    process (up to 16, the GPU machine's share), the whole step -- forward, dX
+    and dW -- once; with one thread, the forward of one group (128 of the
+    1024 rows), the rest of the step being the same loops."""
     import oracle
-    threads = min(os.cpu_count() or 1, 16)
-    used = oracle.set_threads(threads)
+    nproc = os.cpu_count() or 1
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    threads = min(affinity, 16)
     X, W, dY, s = host["X"], host["W"], host["dY"], host["sizes"]
     M, K = X.shape
     N = dY.shape[1]
+    used = oracle.set_threads(threads)
     t0 = time.perf_counter()
-    n = 0
-    while n < 3 and (n == 0 or time.perf_counter() - t0 < 10.0):
-        oracle.gmm_fwd_bf16(X, W, s)
-        oracle.gmm_dx_bf16(dY, W, s)
-        oracle.gmm_dw_bf16(X, dY, s)
-        n += 1
+    oracle.gmm_fwd_bf16(X, W, s)
+    oracle.gmm_dx_bf16(dY, W, s)
+    oracle.gmm_dw_bf16(X, dY, s)
     dt = time.perf_counter() - t0
-    flops = n * 3 * 2.0 * M * K * N
+    flops = 3 * 2.0 * M * K * N
+    oracle.set_threads(1)
+    r1 = int(s[0])
+    t1 = time.perf_counter()
+    oracle.gmm_fwd_bf16(X[:r1], W[:1], s[:1])
+    dt1 = time.perf_counter() - t1
+    oracle.set_threads(used)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": used, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"{n} x the whole step (fwd + dX + dW, M={M}, K={K}, N={N}, E={len(s)}) in fp64, "
-                      "including the bf16 -> fp64 decode of the operands"}
+            "sample": f"the whole step once (fwd + dX + dW, M={M}, K={K}, N={N}, E={len(s)}) in fp64 on {used} "
+                      "threads, including the bf16 -> fp64 decode of the operands",
+            "single_thread": {"value": round(2.0 * r1 * K * N / dt1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                              "seconds": round(dt1, 2),
+                              "sample": f"the forward of one group ({r1} rows, K={K}, N={N}) in fp64 on one thread"},
+            "host_cpus": nproc, "process_cpus": affinity, "cpu_model": _cpu_model()}
 
 
 def main():
@@ -490,6 +665,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse-M latency measurement")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other configurations")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured memory and vendor-BLAS rates")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run each product and a known-size copy (for rocprofv3 --pmc passes)")
     ap.add_argument("--counter-probe", action="store_true",
@@ -532,14 +708,21 @@ def main():
                    "E": r["E"], "M": r["M"], "K": r["K"], "N": r["N"]},
         "mfma_frac": round(r["value"] / PEAK_BF16_TFLOPS, 4),
         "roofline": r["roofline"],
-        "context": "pages: 60 ms total kernel time for 30 fwd+bwd iterations of this workload on A100 (2.0 ms/iter)",
+        "context": "pages: 60 ms total kernel time for 30 fwd+bwd iterations of this workload on A100 (2.0 ms/iter); "
+                   "here: total_kernel_ms_30_iterations",
     }
+    out["total_kernel_ms_30_iterations"] = round(r["total30_ms"], 3)
+    log("tiny-configuration latency")
+    out["tiny_config"] = tiny_latency(torch, mg)
     if not args.no_sparse:
         log("sparse-M latency")
         out["sparse_m"] = sparse_m_latency(torch, mg)
     if not args.no_rows:
         log("per-step rows (fp8 layer share, fused FFN)")
         out["rows"] = row_measurements(torch, mg)
+    if not args.no_peaks:
+        log("measured peaks")
+        out["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(r["host"])
