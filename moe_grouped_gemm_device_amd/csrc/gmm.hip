@@ -61,6 +61,7 @@
 namespace mg {
 
 constexpr uint32_t kRasterM = 12;  // most row tiles per raster block (fixed-M item order)
+constexpr int64_t kDkMinPieceSteps = 8;   // shortest piece of a split dynamic-K contraction (k-steps)
 
 template <int ELEM> struct ElemTraits;
 template <> struct ElemTraits<EL_BF16> {
@@ -369,15 +370,38 @@ struct Item {
   int nsteps;       // k-steps (>= 1; an empty dW group runs one all-zero step)
   int mt;           // FIXED_M: row tile (work-list entry) of the item
   bool b_stream;    // B is read by this item only (its expert has one row tile)
+  // DYNAMIC_K pieces: (pieces the tile's contraction is cut into, 1 when
+  // whole) << 16 | this item's piece; and, for a split tile, (its arrival
+  // counter) << 16 | (the partial slot of its piece 0)
+  int split;
+  int sloc;
+  __device__ int pieces() const { return split >> 16; }
+  __device__ int piece() const { return split & 0xFFFF; }
+  __device__ int ctr() const { return sloc >> 16; }
+  __device__ int slot() const { return sloc & 0xFFFF; }
+};
+
+// Split plan of a dynamic-K launch: the first `groups` entries of the
+// size-descending group order are cut into pieces[i] pieces along their
+// contraction; items_before[i] counts the items of the split groups before
+// order position i (items_before[groups] = all split items).
+constexpr int kDkMaxSplitGroups = 16;
+struct DkSplit {
+  int32_t groups;
+  int32_t pieces[kDkMaxSplitGroups];
+  int32_t items_before[kDkMaxSplitGroups + 1];
+  int32_t slot_before[kDkMaxSplitGroups + 1];
 };
 
 // Work item w.  Work-item counts stay below 2^31 (the host bounds every
 // operand below 2 GiB), so the index arithmetic is 32-bit.  A fixed-M item
 // in the same row tile as `prev` reuses its group lookup.
-template <int BM, int BN, int KIND, int ELEM, int BK>
+template <int BM, int BN, int KIND, int ELEM, int BK, bool SPLIT>
 __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_t w64, int n_tiles, int m_tiles_dk,
-                                const Item* prev) {
+                                const Item* prev, const DkSplit& sp) {
   Item it;
+  it.split = 1 << 16;
+  it.sloc = 0;
   const uint32_t w = (uint32_t)w64;
   int nt;
   if (KIND == FIXED_M) {
@@ -419,9 +443,28 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
     it.b_stream = mtg <= 1;
     (void)prev;
   } else {
+    // items: the pieces of the split groups' tiles (piece outermost, so a
+    // tile's pieces are dealt to different workgroups), then one item per
+    // tile of every other group, in the size-descending group order
     const uint32_t per = (uint32_t)m_tiles_dk * (uint32_t)n_tiles;
-    const uint32_t gi = w / per;
-    const uint32_t rem = w - gi * per;
+    const int ns = SPLIT ? uni(sp.groups) : 0;
+    const uint32_t nsplit = SPLIT ? (uint32_t)uni(sp.items_before[ns]) : 0u;
+    uint32_t gi, rem;
+    if (SPLIT && w < nsplit) {
+      int q = 0;
+      while (q + 1 < ns && (uint32_t)uni(sp.items_before[q + 1]) <= w) ++q;
+      const uint32_t local = w - (uint32_t)uni(sp.items_before[q]);
+      const uint32_t j = local / per;
+      gi = (uint32_t)q;
+      rem = local - j * per;
+      const int pc = uni(sp.pieces[q]);
+      it.split = (pc << 16) | (int)j;
+      it.sloc = ((q * (int)per + (int)rem) << 16) | (uni(sp.slot_before[q]) + (int)rem * pc);
+    } else {
+      const uint32_t w2 = w - nsplit;
+      gi = (uint32_t)ns + w2 / per;
+      rem = w2 - (gi - (uint32_t)ns) * per;
+    }
     const uint32_t mt = rem / (uint32_t)n_tiles;
     nt = (int)(rem - mt * (uint32_t)n_tiles);
     // every field is the same in all lanes (it comes from LDS reads of the
@@ -439,6 +482,12 @@ __device__ inline Item get_item(const GemmArgs& a, const GroupTable& tab, int64_
     it.c_begin = eff > 0 ? start : it.c_hi;
     const int64_t span = it.c_hi - it.c_begin;
     it.nsteps = span > 0 ? (int)cdiv(span, BK) : 1;
+    if (SPLIT && it.pieces() > 1) {   // piece j: k-steps [j n / S, (j + 1) n / S) of the n
+      const int s0 = (int)((int64_t)it.piece() * it.nsteps / it.pieces());
+      const int s1 = (int)((int64_t)(it.piece() + 1) * it.nsteps / it.pieces());
+      it.c_begin += (int64_t)s0 * BK;
+      it.nsteps = s1 - s0;
+    }
     it.mt = (int)mt;
     it.b_stream = false;
   }
@@ -503,6 +552,10 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   constexpr int EPI_VM = (EPI_VM_STAGES < LPS) ? EPI_VM_STAGES : LPS;
   static_assert(NS >= 2, "at least double buffering");
   static_assert(KIND == DYNAMIC_K || (int64_t)BM * BN * 4 <= kSkPartBytes, "partial tile size");
+  // bf16 dynamic-K launches may split long contractions when a partial tile
+  // fits a workspace slot (the fp8 dW kernel, with its group-boundary byte
+  // masks, has no registers left for the combine)
+  constexpr bool DK_SPLIT = KIND == DYNAMIC_K && ELEM == EL_BF16 && (int64_t)BM * BN * 4 <= kSkPartBytes;
   // fp8 dW: chunks straddling a group boundary carry bytes of the next
   // group; they are cleared in the fragments of the boundary k-steps
   constexpr bool MASK_BYTES = (ELEM == EL_FP8) && (KIND == DYNAMIC_K);
@@ -526,9 +579,63 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
 
   const int n_tiles = (int)cdiv(a.Nout, BNE);
   const int m_tiles_dk = (KIND == DYNAMIC_K) ? (int)cdiv(a.Mout, BM) : 1;
-  const int64_t items = uni64((KIND == FIXED_M) ? (int64_t)tab.tstart[a.E] * n_tiles
-                                                : (int64_t)a.E * m_tiles_dk * n_tiles);
   const int G = gridDim.x;
+  // Dynamic-K split plan (grouped_gemm PR review thread: problems sorted by
+  // k, descending, so the longest come first): a group whose contraction is
+  // longer than a workgroup's share of all k-steps is cut into pieces of at
+  // most that share (and of at least kDkMinPieceSteps), so a few very large
+  // groups cannot leave the rest of the grid idle.  Each piece stores its
+  // fp32 partial tile in the workspace; the last to arrive adds all pieces
+  // in piece order (the same bits whatever the arrival order) and writes
+  // the tile.  Split tiles are limited by the workspace: one arrival counter
+  // each (kSkMaxGrid) and one partial slot per piece (2 kSkMaxGrid).  Every
+  // workgroup computes the same plan from the group table.
+  __shared__ DkSplit sp;
+  if constexpr (DK_SPLIT) {
+    auto steps_of = [&](int g) -> int64_t {   // k-steps of group g's contraction
+      const int32_t off = tab.off[g], eff = tab.eff[g];
+      if (eff <= 0) return 1;
+      const int64_t start = (ELEM == EL_FP8) ? ((int64_t)off & ~(int64_t)15) : (int64_t)off;
+      return cdiv((int64_t)off + eff - start, BK);
+    };
+    int64_t mine = 0;
+    for (int g = tid; g < a.E; g += kThreads) mine += steps_of(g);
+    const int64_t all = block_incl_scan64(mine, tab.scratch);   // the last thread's value is the total
+    if (tid == kThreads - 1) tab.scratch[15] = all;
+    __syncthreads();
+    if (tid == 0) {
+      const int per = m_tiles_dk * n_tiles;
+      const int64_t total = tab.scratch[15] * per;
+      int64_t cap = cdiv(total, G);
+      if (cap < kDkMinPieceSteps) cap = kDkMinPieceSteps;
+      int ns = 0, slots = 0;
+      sp.items_before[0] = 0;
+      sp.slot_before[0] = 0;
+      while (ns < kDkMaxSplitGroups && ns < a.E) {
+        const int64_t st = steps_of(tab.order[ns]);
+        int pc = (int)cdiv(st, cap);
+        if (pc > st) pc = (int)st;
+        if (pc < 2) break;
+        if ((ns + 1) * per > kSkMaxGrid) break;            // arrival counters
+        if (slots + pc * per > 2 * kSkMaxGrid) break;       // partial slots
+        sp.pieces[ns] = pc;
+        slots += pc * per;
+        sp.items_before[ns + 1] = sp.items_before[ns] + pc * per;
+        sp.slot_before[ns + 1] = slots;
+        ++ns;
+      }
+      sp.groups = ns;
+    }
+  } else {
+    if (tid == 0) {
+      sp.groups = 0;
+      sp.items_before[0] = 0;
+    }
+  }
+  __syncthreads();
+  const int64_t items = uni64((KIND == FIXED_M) ? (int64_t)tab.tstart[a.E] * n_tiles
+                                                : (int64_t)(a.E - sp.groups) * m_tiles_dk * n_tiles +
+                                                      sp.items_before[sp.groups]);
   // logical workgroup index: consecutive indices on one XCD
   int b = blockIdx.x;
   if ((G & 7) == 0) b = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
@@ -560,7 +667,8 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // dealt over the whole grid, longest first, in snake order.  dp_item(k) is
   // the workgroup's k-th whole item, or -1.
   bool equal_items = KIND == FIXED_M;
-  if constexpr (KIND == DYNAMIC_K) equal_items = uni(tab.eff[uni(tab.order[0])]) == uni(tab.eff[uni(tab.order[a.E - 1])]);
+  if constexpr (KIND == DYNAMIC_K)
+    equal_items = uni(sp.groups) == 0 && uni(tab.eff[uni(tab.order[0])]) == uni(tab.eff[uni(tab.order[a.E - 1])]);
   const bool xcd_split = equal_items && (G & 7) == 0;
   const int64_t gx = xcd_split ? (G >> 3) : G;
   const int64_t dj = xcd_split ? (int64_t)(blockIdx.x >> 3) : b;
@@ -587,7 +695,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(a.B);
   auto fetch = [&](int64_t w, const Item* prev) {
-    return get_item<BM, BNE, KIND, ELEM, BK>(a, tab, w, n_tiles, m_tiles_dk, prev);
+    return get_item<BM, BNE, KIND, ELEM, BK, DK_SPLIT>(a, tab, w, n_tiles, m_tiles_dk, prev, sp);
   };
   // The workgroup's sequence of (item, first k-step, end k-step); the end of
   // a dynamic-K item comes from the item (-1 here).
@@ -1095,6 +1203,31 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     return true;
   };
 
+  // Dynamic-K split tile: every piece stores its partial (slot ci.slot +
+  // piece); the last to arrive sums the pieces in order and writes the tile.
+  // The same device-coherent protocol as the stream-K combine.
+  auto slot_rsrc = [&](int slot) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sk_part) + (int64_t)slot * PART_BYTES + wave * WAVE_BYTES;
+    return make_rsrc(base, WAVE_BYTES);
+  };
+  auto dk_combine = [&](const Item& it) -> bool {
+    int32_t* flag = reinterpret_cast<int32_t*>(tab.scratch);
+    part_io(true, slot_rsrc(it.slot() + it.piece()), it, false);
+    wait_vm_all();   // this wave's partial has reached the coherence point
+    lds_sync();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(a.sk_ctr + it.ctr(), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == it.pieces() - 1;
+      if (last) __hip_atomic_store(a.sk_ctr + it.ctr(), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = last;
+    }
+    lds_sync();
+    if (!uni(*flag)) return false;
+    const int pc = it.pieces();
+    for (int j = 0; j < pc; ++j) part_io(false, slot_rsrc(it.slot() + j), it, j != 0);
+    return true;
+  };
+
   // ---- main loop ----------------------------------------------------------
   // NS - 1 k-steps are loaded ahead; stages are used round-robin.
 #pragma unroll
@@ -1128,6 +1261,9 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
     }
     bool write = true;
     if constexpr (KIND == FIXED_M) write = cw < D || sk_combine(ci, cw);
+    if constexpr (DK_SPLIT) {
+      if (ci.pieces() > 1) write = dk_combine(ci);
+    }
     if (write) {
       epilogue(smem + last_stage * STAGE, ci);
       epi_prev = true;
@@ -1189,6 +1325,9 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
   if (KIND == FIXED_M) work = fixed_m_capacity(a.total_rows, a.E, BM) * cdiv(a.Nout, EPI == EPI_SWIGLU ? BN / 2 : BN) * cdiv(a.Kc, T::BK);
   else work = (int64_t)a.E * cdiv(a.Mout, BM) * cdiv(a.Nout, BN);
   if (work <= 0) return hipSuccess;
+  // a dynamic-K launch whose tiles may be split takes up to 8 workgroups per
+  // tile, so the pieces of a long contraction find idle workgroups
+  if (KIND == DYNAMIC_K && ELEM == EL_BF16 && (int64_t)BM * BN * 4 <= kSkPartBytes) work *= 8;
   auto kern = gmm_kernel<BM, BN, NS, A_KC, B_KC, KIND, ELEM, EPI, NW>;
   const int dyn = table_lds_bytes(a.E);
   static int configured = 0;   // dynamic LDS size already allowed

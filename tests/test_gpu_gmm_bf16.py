@@ -354,3 +354,44 @@ def test_captured_step_follows_device_sizes_changed_between_replays():
         Xf, Wf = oracle.bf16_to_f64(xs[:s]), oracle.bf16_to_f64(W)
         assert_close(oracle.bf16_to_f64(bf16_host(y[:s])), oracle.gmm_fwd(Xf, Wf, sizes), BF16_TOL, GEMM_BF16, "Y",
                      fwd_norms(Xf, Wf, sizes))
+
+
+def _zipf_sizes(E, M, s=1.1):
+    w = 1.0 / np.arange(1, E + 1) ** s
+    sz = np.floor(M * w / w.sum()).astype(np.int32)
+    sz[0] += M - int(sz.sum())
+    return sz
+
+
+@pytest.mark.parametrize("E,sizes,K,N,trans_b", [
+    # one group holds 95% of the rows: its tiles' contraction (60 k-steps)
+    # is cut into 8 pieces summed by the last to arrive
+    (4, [3800, 100, 0, 100], 264, 392, False),
+    (4, [3800, 100, 0, 100], 264, 392, True),
+    # Zipf(1.1) loads over 16 groups
+    (16, "zipf", 136, 200, False),
+    # one very large group among many small ones
+    (64, [20000] + [50] * 63, 128, 128, False),
+])
+def test_dw_split_contraction_skewed_groups(E, sizes, K, N, trans_b):
+    """dW of skewed groups, where the long contractions are split across
+    workgroups, matches the oracle element by element and is the same bits
+    on every run (the pieces are summed in piece order)."""
+    sizes = _zipf_sizes(E, 9000) if sizes == "zipf" else np.array(sizes, np.int32)
+    M = int(sizes.sum())
+    X = wl.normal_bf16((M, K), 1.0, 13, wl.T_X)
+    W = wl.normal_bf16((E, K, N), 0.5, 13, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, 13, wl.T_DY)
+    Wg = np.ascontiguousarray(np.transpose(W, (0, 2, 1))) if trans_b else W
+    x, w, dy, gs = bf16_dev(X), bf16_dev(Wg), bf16_dev(dY), dev(sizes)
+    _, dw1 = mg.gmm_bwd(dy, x, w, gs, trans_b=trans_b, need_dx=False)
+    _, dw2 = mg.gmm_bwd(dy, x, w, gs, trans_b=trans_b, need_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw2)
+    dwh = oracle.bf16_to_f64(bf16_host(dw1))
+    if trans_b:
+        dwh = np.ascontiguousarray(np.transpose(dwh, (0, 2, 1)))
+    Xf, dYf = oracle.bf16_to_f64(X), oracle.bf16_to_f64(dY)
+    assert_close(dwh, oracle.gmm_dw(Xf, dYf, sizes), BF16_TOL, GEMM_BF16, "dW", dw_norms(Xf, dYf, sizes))
+    for g in np.flatnonzero(sizes == 0):
+        assert (dwh[g] == 0).all()
