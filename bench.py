@@ -141,11 +141,29 @@ def run_gpu(args, torch, mg):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # Per-kernel durations: HIP events around R back-to-back launches of each
-    # product (the same launches as in a step), so that only the dispatch gap
-    # between identical kernels is counted besides the kernels themselves.
+    # Per-kernel durations: the same K steps once more, with a HIP event pair
+    # around every launch (on the stream the library launches on), so each
+    # product's average launch duration is measured in the step it belongs
+    # to.  (The timed steps above carry no events: an event marker between
+    # two kernels leaves the GPU idle for a few microseconds.)
+    samples = {name: [] for name in products}
+    pairs = []
+    for _ in range(args.steps):
+        for name, fn in products.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            pairs.append((name, e0, e1))
+    torch.cuda.synchronize()
+    for name, e0, e1 in pairs:
+        samples[name].append(e0.elapsed_time(e1))
+    step_ms = {name: sum(v) / len(v) for name, v in samples.items()}
+    # R launches of one product back to back, one event pair around them
+    # (only the dispatch gap between identical kernels is counted besides the
+    # kernels themselves): the average the roofline uses
     R = max(args.steps, 5)
-    avg_ms = {}
+    b2b_ms = {}
     for name, fn in products.items():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -153,7 +171,8 @@ def run_gpu(args, torch, mg):
             fn()
         e1.record()
         e1.synchronize()
-        avg_ms[name] = e0.elapsed_time(e1) / R
+        b2b_ms[name] = e0.elapsed_time(e1) / R
+    avg_ms = b2b_ms
     launch_stats = {name: launch_percentiles(torch, fn, reps=20) for name, fn in products.items()}
     # the pages' A100 figure is the total kernel time of 30 forward + backward
     # iterations: the same 30 steps here, back to back, HIP events around them
@@ -183,6 +202,10 @@ def run_gpu(args, torch, mg):
         "traffic": measured_traffic(dom),
         "algorithmic_bytes_per_launch": bytes_per[dom],
         "avg_launch_us": {k: round(v * 1e3, 2) for k, v in avg_ms.items()},
+        "avg_launch_us_how": f"{R} launches of each product back to back between one HIP event pair",
+        "avg_launch_us_in_steps": {k: round(v * 1e3, 2) for k, v in step_ms.items()},
+        "avg_launch_us_in_steps_how": f"HIP event pair around every launch of {args.steps} more steps "
+                                      "(fwd, dX, dW in turn)",
         "launch_us_percentiles": launch_stats,
         "mfma_frac": {k: round(2.0 * M * K * N / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) for k, v in avg_ms.items()},
     }
