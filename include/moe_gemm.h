@@ -404,6 +404,17 @@ const char* mg_last_error(void);
 /* Library version string. */
 const char* mg_version(void);
 
+/* Row-tile height (128 or 256) of the most recent grouped-GEMM launch this
+ * thread enqueued through gmm_fwd, gmm_fwd_gather, gmm_fwd_silu_mul,
+ * gmm_bwd, gmm_fwd_fp8 or gmm_bwd_fp8 (the last kernel of a call that
+ * enqueues several), or 0 before the first.  Large fixed-M launches -- at
+ * least two rounds of 256 x 256 tiles on every compute unit, contractions
+ * of 1024 or more, 192 or more rows per group on average -- run on
+ * 256 x 256 tiles with four waves; the rest on 128 x 256 tiles (dW: 128 or
+ * 256 rows) with eight.  The result does not depend on the choice beyond
+ * rounding order.  For diagnostics and tests; reads no device state. */
+int32_t mg_last_gemm_tile_m(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,7 @@ _SIGS = {
     "moe_route_topk": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "mg_last_error": (ctypes.c_char_p, []),
     "mg_version": (ctypes.c_char_p, []),
+    "mg_last_gemm_tile_m": (_I32, []),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -110,6 +111,12 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def last_gemm_tile_m():
+    """Row-tile height (128 or 256) of this thread's most recent grouped-GEMM
+    launch (0 before the first); diagnostics."""
+    return int(lib().mg_last_gemm_tile_m())
 
 
 def workspace_bytes(E, total_M):

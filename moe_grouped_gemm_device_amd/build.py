@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoegemm.so")
-SOURCES = ["abi.hip", "builder.hip", "gmm.hip", "f8i4.hip", "quant.hip", "moe.hip"]
+SOURCES = ["abi.hip", "builder.hip", "gmm.hip", "gmm256.hip", "f8i4.hip", "quant.hip", "moe.hip"]
 ARCH = os.environ.get("MG_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -131,6 +131,8 @@ const char* mg_last_error(void) { return g_err; }
 
 const char* mg_version(void) { return "moe-gemm-gfx950 0.1"; }
 
+int32_t mg_last_gemm_tile_m(void) { return last_gemm_tile_m(); }
+
 size_t mg_workspace_bytes(int32_t E, int64_t total_M) {
   if (E < 1 || E > MG_MAX_EXPERTS || total_M < 0) return 0;
   return (size_t)ws_layout(E, total_M).total;

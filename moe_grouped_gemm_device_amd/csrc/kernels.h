@@ -88,6 +88,12 @@ int gemm_tile_m(int kind);
 int gemm_tile_n(int kind);
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream);
+// The 256 x 256-tile kernel (gmm256.hip) for large fixed-M launches;
+// launch_gemm hands a launch to it when gemm256_eligible says so.
+bool gemm256_eligible(const GemmLaunch& L, const GemmArgs& a);
+// row-tile height of this thread's last launch_gemm (0 before the first)
+int last_gemm_tile_m();
+hipError_t launch_gemm256(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream);
 // The GEMM kernels read every operand's tile base unconditionally, so a
 // DYNAMIC_K launch needs total_M > 0; with no rows, dW is a plain zero fill.
 hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t stream);
