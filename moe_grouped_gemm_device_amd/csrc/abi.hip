@@ -78,6 +78,7 @@ void attach_ws(GemmArgs& a, void* ws) {
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
   a.err = err_word(ws);
   a.sk_ctr = reinterpret_cast<int32_t*>(p + kWsCounters);
+  a.wq = reinterpret_cast<int32_t*>(ws) + kWsQueueWord;
   a.sk_part = reinterpret_cast<float*>(p + kWsPartials);
 }
 

@@ -18,9 +18,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
 
-// Workspace layout (bytes).  The header holds the sticky error word.
+// Workspace layout (bytes).  The header holds the sticky error word and
+// the two counters of a work-queue launch.
 constexpr int64_t kWsHeader = 256;
 constexpr int kWsErrorWord = 0;   // int32 index into the header
+constexpr int kWsQueueWord = 1;   // work-queue counters at words 1 and 9: items handed out, workgroups finished
 constexpr int kMinTileM = 16;     // smallest row tile any kernel uses
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -58,6 +58,9 @@ constexpr int NSCB = NS + 1;          // fp8 scale buffers, used round-robin by 
 constexpr int SROW = 64 + 8;          // epilogue staging row (bf16 elements)
 static_assert(NW * 32 * SROW * 2 <= STAGE, "epilogue staging fits a stage");
 static_assert((NS - 2) * LPW <= 63, "vmcnt range");
+constexpr int64_t PART = 256LL * 256 * 4;   // one fp32 partial tile (split dynamic-K contraction)
+constexpr int PART_SLOTS = (int)(2 * kSkMaxGrid * kSkPartBytes / PART);   // partial slots in the workspace
+constexpr int64_t MIN_PIECE = 8;            // shortest piece of a split contraction (k-steps)
 
 // chunk swizzle of a contraction-contiguous tile: line L holds rows 2L, 2L+1
 __device__ inline int kc_swz(int L) { return (L ^ (L >> 1)) & 3; }
@@ -95,17 +98,19 @@ __device__ inline i32x4 uni4(i32x4 r) {
   return u;
 }
 
-template <bool B_KC, int ELEM, int EPI>
+template <bool B_KC, int ELEM, int EPI, int KIND>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) gmm256_kernel(GemmArgs a) {
   using namespace g256;
   constexpr int ESZ = ELEM == EL_FP8 ? 1 : 2;
   constexpr int EPC = 16 / ESZ;                    // elements per 16-byte chunk
   constexpr int BK = RB / ESZ;                     // contraction elements per k-step
   constexpr int KSUB = ELEM == EL_FP8 ? 1 : 2;     // MFMA sub-steps per k-step
-  constexpr bool SCALED = EPI == EPI_ROW_COL;
+  constexpr bool SCALED = EPI == EPI_ROW_COL || EPI == EPI_GROUP;
+  constexpr bool DK = KIND == DYNAMIC_K;
   constexpr bool SWIGLU = EPI == EPI_SWIGLU;
   constexpr int BNE = SWIGLU ? BN / 2 : BN;        // output columns per tile
-  static_assert(ELEM == EL_BF16 || (B_KC && (EPI == EPI_ROW_COL)), "fp8: both operands k-contiguous, scaled");
+  static_assert(ELEM == EL_BF16 || (B_KC && SCALED), "fp8: both operands k-contiguous, scaled");
+  static_assert(!DK || (ELEM == EL_FP8 && EPI == EPI_GROUP), "dynamic-K: e4m3 with per-group scales");
   static_assert(!SWIGLU || (ELEM == EL_BF16 && !B_KC), "paired gate/up epilogue: bf16, B as [K, N]");
   static_assert(ELEM == EL_FP8 || EPI == EPI_NONE || SWIGLU, "bf16 epilogues");
 
@@ -123,31 +128,147 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
   const GroupTable tab = carve_table(table_lds, a.E);
-  const int err = build_group_table(a.sizes, a.E, a.total_rows, BM, false, tab);
+  const int err = build_group_table(a.sizes, a.E, a.total_rows, BM, DK, tab);
   if (err != 0 && blockIdx.x == 0 && tid == 0 && a.err != nullptr) *a.err = err;
 
   const int n_tiles = (int)cdiv(a.Nout, BNE);
   const int G = gridDim.x;
-  const int64_t items = uni64((int64_t)tab.tstart[a.E] * n_tiles);
-  // XCD x (workgroups dealt round-robin to the 8 XCDs) owns items
-  // [x D / 8, (x + 1) D / 8), taken round-robin by its G / 8 workgroups
-  const bool xcd_split = (G & 7) == 0;
+  const int m_tiles_dk = DK ? (int)cdiv(a.Mout, BM) : 1;
+  // Dynamic-K split plan (grouped_gemm PR review thread: problems sorted by
+  // k, descending): a group whose contraction is longer than a workgroup's
+  // share of all k-steps is cut into pieces of at most that share (and of
+  // at least MIN_PIECE), so a few large groups cannot leave most of the
+  // grid idle.  Each piece stores its fp32 partial tile in the workspace;
+  // the last to arrive adds all pieces in piece order (the same bits
+  // whatever the arrival order) and writes the tile.  Limits: one arrival
+  // counter per split tile (kSkMaxGrid), one partial slot per piece
+  // (PART_SLOTS).  Every workgroup computes the same plan from the table.
+  __shared__ DkSplit sp;
+  if constexpr (DK) {
+    auto steps_of = [&](int g) -> int64_t {   // k-steps of group g's contraction
+      const int32_t off = tab.off[g], eff = tab.eff[g];
+      if (eff <= 0) return 1;
+      const int64_t start = (int64_t)off & ~(int64_t)15;
+      return cdiv((int64_t)off + eff - start, BK);
+    };
+    int64_t mine = 0;
+    for (int g = tid; g < a.E; g += 256) mine += steps_of(g);
+    const int64_t all = block_incl_scan64(mine, tab.scratch);   // the last thread's value is the total
+    if (tid == 255) tab.scratch[15] = all;
+    __syncthreads();
+    if (tid == 0) {
+      const int per = m_tiles_dk * n_tiles;
+      int64_t cap = cdiv(tab.scratch[15] * per, G);
+      if (cap < MIN_PIECE) cap = MIN_PIECE;
+      int ns = 0, slots = 0;
+      sp.items_before[0] = 0;
+      sp.slot_before[0] = 0;
+      while (ns < kDkMaxSplitGroups && ns < a.E) {
+        const int64_t st = steps_of(tab.order[ns]);
+        int pc = (int)cdiv(st, cap);
+        if (pc > st) pc = (int)st;
+        if (pc < 2) break;
+        if ((ns + 1) * per > kSkMaxGrid) break;            // arrival counters
+        if (slots + pc * per > PART_SLOTS) break;           // partial slots
+        sp.pieces[ns] = pc;
+        slots += pc * per;
+        sp.items_before[ns + 1] = sp.items_before[ns] + pc * per;
+        sp.slot_before[ns + 1] = slots;
+        ++ns;
+      }
+      sp.groups = ns;
+    }
+  } else {
+    if (tid == 0) {
+      sp.groups = 0;
+      sp.items_before[0] = 0;
+    }
+  }
+  __syncthreads();
+  const int64_t items = uni64(DK ? (int64_t)(a.E - sp.groups) * m_tiles_dk * n_tiles + sp.items_before[sp.groups]
+                                 : (int64_t)tab.tstart[a.E] * n_tiles);
+  // Items of equal length (fixed-M tiles; dynamic-K tiles when every group
+  // has the same size): XCD x (workgroups are dealt round-robin to the 8
+  // XCDs) owns items [x D / 8, (x + 1) D / 8), taken round-robin by its G / 8
+  // workgroups.  Dynamic-K items of unequal length (groups come largest
+  // first) are dealt over the whole grid in snake order, so the workgroups
+  // that drew a round's longest items draw the next round's shortest.
+  bool equal_items = true;
+  if constexpr (DK)
+    equal_items = uni(sp.groups) == 0 && uni(tab.eff[uni(tab.order[0])]) == uni(tab.eff[uni(tab.order[a.E - 1])]);
+  const bool xcd_split = equal_items && (G & 7) == 0;
+  // Dynamic-K items of unequal length (groups come largest first) come from
+  // a work queue: a workgroup's first item is its own index, and every
+  // further one the next index handed out by an atomic counter in the
+  // workspace, so a workgroup that drew long items draws fewer -- the
+  // longest-first greedy deal.  Thread 0 requests items into a ring in LDS
+  // six ahead of the compute cursor (the load cursor runs at most four
+  // ahead), right after an epilogue: waiting there for the counter's reply
+  // waits for little else, since the next item's loads had the epilogue's
+  // time to land.  The last workgroup to finish resets the counters.
+  // (Tiles handed out this way share no L2 by XCD, which costs against the
+  // static deal when the groups are equal; measured on MI355X with the
+  // Zipf-skewed groups of a DeepSeek-MoE layer share, it still beats the
+  // static longest-first snake deal.)
+  const bool dyn = DK && !equal_items;
+  const bool snake = false;
+  __shared__ int32_t qring[16];   // the workgroup's n-th item at [n % 16] (-1: none)
+  auto grab = [&](int64_t n) __attribute__((always_inline)) {
+    if (tid == 0) {
+      int code = -1;
+      if (n == 0) code = (int)blockIdx.x;
+      else {
+        const int l = G + __hip_atomic_fetch_add(a.wq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (l >= 0 && l < items) code = l;
+      }
+      qring[n & 15] = code;
+    }
+  };
+  // counts this workgroup out; the last one resets the counters
+  auto queue_exit = [&]() __attribute__((always_inline)) {
+    if (dyn && tid == 0) {
+      const int done = __hip_atomic_fetch_add(a.wq + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == G - 1) {
+        __hip_atomic_store(a.wq, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.wq + 8, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  if (dyn) {
+    for (int n = 0; n <= 6; ++n) grab(n);
+    __syncthreads();
+  }
   const int64_t gx = xcd_split ? (G >> 3) : G;
   const int64_t dj = xcd_split ? (int64_t)(blockIdx.x >> 3) : blockIdx.x;
   const int64_t c0 = xcd_split ? ((int64_t)(blockIdx.x & 7) * items) >> 3 : 0;
   const int64_t c1 = xcd_split ? ((int64_t)((blockIdx.x & 7) + 1) * items) >> 3 : items;
-  if (c0 + dj >= c1) return;
-  const int nsteps = (int)cdiv(a.Kc, BK);
-  // (fixed-M items have no split plan; the reference is never read)
-  const DkSplit& no_split = *reinterpret_cast<const DkSplit*>(table_lds);
+  // the workgroup's k-th item (c1 or beyond: none)
+  auto item_of = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
+    if (dyn) {
+      const int code = uni(qring[k & 15]);
+      return code < 0 ? c1 : code;   // none left (or the counter was not zeroed)
+    }
+    if (snake) return k * G + ((k & 1) ? (G - 1 - (int64_t)blockIdx.x) : (int64_t)blockIdx.x);
+    return c0 + dj + k * gx;
+  };
+  if (item_of(0) >= c1) {
+    queue_exit();
+    return;
+  }
   // (every field is workgroup-uniform; said so, so that items live in SGPRs)
   auto fetch = [&](int64_t w) __attribute__((always_inline)) {
-    Item it = get_item<BM, BNE, FIXED_M, ELEM, BK, false, RASTER>(a, tab, w, n_tiles, 1, nullptr, no_split);
+    Item it = get_item<BM, BNE, KIND, ELEM, BK, DK, RASTER>(a, tab, w, n_tiles, m_tiles_dk, nullptr, sp);
     it.g = uni(it.g);
     it.rowbase = uni64(it.rowbase);
     it.m_valid = uni(it.m_valid);
     it.n0 = uni(it.n0);
     it.n_valid = uni(it.n_valid);
+    it.c_lo = uni64(it.c_lo);
+    it.c_hi = uni64(it.c_hi);
+    it.c_begin = uni64(it.c_begin);
+    it.nsteps = uni(it.nsteps);
+    it.split = uni(it.split);
+    it.sloc = uni(it.sloc);
     return it;
   };
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
@@ -229,7 +350,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
 
   // load cursor: item lw, k-step ls
-  int64_t lw = c0 + dj;
+  int64_t lk = 0;               // load cursor: the workgroup's lk-th item, k-step ls
+  int64_t lw = item_of(0);
   int ls = 0;
   Item li = fetch(lw);
   bool ldone = false;
@@ -242,7 +364,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // column scales, 64 per instruction, two instructions per wave
   auto issue_scales = [&](const Item& it, int b) __attribute__((always_inline)) {
     if constexpr (SCALED) {
-      const i32x4 rr = uni4(make_rsrc_words(a.sa + it.rowbase, (int64_t)it.m_valid * 4));
+      const float* rows = a.sa + (DK ? (int64_t)it.g * a.Mout + it.rowbase : it.rowbase);
+      const i32x4 rr = uni4(make_rsrc_words(rows, (int64_t)it.m_valid * 4));
       const i32x4 rc = uni4(make_rsrc_words(a.sb + (int64_t)it.g * a.Nout + it.n0, (int64_t)it.n_valid * 4));
       dma4(rr, sbase + (b * 512 + 64 * wave) * 4, (uint32_t)((64 * wave + lane) * 4));
       dma4(rc, sbase + (b * 512 + 256 + 64 * wave) * 4, (uint32_t)((64 * wave + lane) * 4));
@@ -260,14 +383,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   auto prepare = [&](int st) __attribute__((always_inline)) -> Batch {
     Batch x;
-    const int64_t cb = (int64_t)ls * BK;
-    const int64_t hi64 = (int64_t)a.Kc - cb;
-    const int hi = hi64 > BK ? BK : (int)hi64;
+    // contraction index of the k-step's first element, and the item's range
+    // relative to it (clamped to int)
+    const int64_t cb = li.c_begin + (int64_t)ls * BK;
+    const int64_t lo64 = li.c_lo - cb, hi64 = li.c_hi - cb;
+    const int lo = lo64 < -BK ? -BK : (lo64 > 2 * BK ? 2 * BK : (int)lo64);
+    const int hi = hi64 < -BK ? -BK : (hi64 > 2 * BK ? 2 * BK : (int)hi64);
+    // dynamic-K operands end where the matrix ends; an empty group reads nothing
+    int64_t a_ext = 0x7FFFFFFF, b_ext = 0x7FFFFFFF;
+    if constexpr (DK) {
+      a_ext = li.c_hi <= li.c_lo ? 0 : (int64_t)(li.m_valid - 1) * a.a_ld + (a.total_rows - cb);
+      b_ext = li.c_hi <= li.c_lo ? 0 : (int64_t)(li.n_valid - 1) * a.b_ld + (a.total_rows - cb);
+    }
     const uint8_t* abase = gather ? Ab + cb * ESZ : Ab + (li.rowbase * a.a_ld + cb) * ESZ;
-    x.ra = uni4(make_rsrc_words(abase, ldone ? 0 : 0x7FFFFFFF));
+    x.ra = uni4(make_rsrc_words(abase, ldone ? 0 : a_ext));
     if constexpr (B_KC)
       x.rb = uni4(make_rsrc_words(Bb + ((int64_t)li.g * a.b_gs + (int64_t)li.n0 * a.b_ld + cb) * ESZ,
-                                  ldone ? 0 : 0x7FFFFFFF));
+                                  ldone ? 0 : b_ext));
     else
       x.rb = uni4(make_rsrc_words(Bb + ((int64_t)li.g * a.b_gs + cb * a.b_ld + li.n0) * 2,
                                   ldone ? 0 : ((int64_t)a.Kc - cb) * a.b_ld * 2));
@@ -277,11 +409,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       x.vo[q] = voA[q];
       x.vo[4 + q] = voB[q];
     }
-    if (hi < BK) {   // the k-step the contraction's end cuts: later chunks read zeros
+    if (lo > 0 || hi < BK) {   // a k-step the contraction range cuts: chunks outside it read zeros
 #pragma unroll
       for (int q = 0; q < LPW; ++q) {
         const int c = (int)((chunks >> (2 * q)) & 3u);
-        if (q < 4 || B_KC) x.vo[q] = c * EPC < hi ? x.vo[q] : kOOB;
+        if (q < 4 || B_KC) x.vo[q] = (c * EPC + EPC > lo && c * EPC < hi) ? x.vo[q] : kOOB;
       }
     }
     return x;
@@ -292,12 +424,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   auto advance_load = [&]() __attribute__((always_inline)) {
     if (ldone) return;
-    if (ls + 1 < nsteps) {
+    if (ls + 1 < li.nsteps) {
       ++ls;
       return;
     }
-    const int64_t nw = lw + gx;
-    if (nw >= c1) {
+    const int64_t nw = item_of(++lk);
+    if (nw < 0 || nw >= c1) {   // (negative only from counters the caller failed to zero)
       ldone = true;
       return;
     }
@@ -431,8 +563,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
+  // partial slot of a split dynamic-K tile, this wave's 64 KB of it
+  auto slot_rsrc = [&](int slot) __attribute__((always_inline)) {
+    return make_rsrc(reinterpret_cast<const uint8_t*>(a.sk_part) + (int64_t)slot * PART + wave * (PART / 4), PART / 4);
+  };
+
   // ---- epilogue: the item's output through stage st ----
-  auto epilogue = [&](int st, const Item& it, int sb) __attribute__((always_inline)) {
+  // With npieces > 0 (the last-arriving piece of a split dynamic-K tile)
+  // the values are the sums, in piece order, of the pieces' partial tiles in
+  // slots slot0 .. slot0 + npieces - 1, and acc (already zero) is not read.
+  auto epilogue = [&](int st, const Item& it, int sb, int npieces, int slot0) __attribute__((always_inline)) {
     uint8_t* stg_base = smem + st * STAGE;
     // lane-derived addresses from an opaque copy of the lane index, so they
     // are computed here rather than hoisted and held across the k-loop
@@ -519,13 +659,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       return;
     }
     uint16_t* stg = reinterpret_cast<uint16_t*>(stg_base) + wave * 32 * SROW;
-    const __amdgpu_buffer_rsrc_t cr =
-        make_rsrc(reinterpret_cast<uint16_t*>(a.C) + it.rowbase * a.c_ld + it.n0, 0x7FFFFFFF);
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(
+        reinterpret_cast<uint16_t*>(a.C) + (int64_t)it.g * a.c_gs + it.rowbase * a.c_ld + it.n0, 0x7FFFFFFF);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = e >> 1, h = e & 1;   // 32-row block, 64-column half of the wave's block
       float rs = 1.f;
       if constexpr (SCALED) rs = rcp[wm * 128 + 32 * i + l31];
+      const uint32_t pvo = wm * 128 + 32 * i + l31 < it.m_valid ? (uint32_t)(lane * 16) : kOOB;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * h + jj;
@@ -534,6 +675,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
           const int cw = 32 * jj + 8 * q + 4 * hi;   // column in the 64-wide staging row
           float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
           float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+          if constexpr (DK) {
+            if (npieces > 0) {
+              v0 = v1 = v2 = v3 = 0.f;
+              for (int p = 0; p < npieces; ++p) {
+                const i32x4 pv = __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(slot0 + p), (int)pvo,
+                                                                        ((i * 4 + j) * 4 + q) * 1024, kPolicyDevice);
+                v0 += __int_as_float(pv[0]);
+                v1 += __int_as_float(pv[1]);
+                v2 += __int_as_float(pv[2]);
+                v3 += __int_as_float(pv[3]);
+              }
+            }
+          }
           if constexpr (SCALED) {
             const f32x4 cs4 = *reinterpret_cast<const f32x4*>(rcp + 256 + wn * 128 + 64 * h + cw);
             v0 = (v0 * cs4[0]) * rs;
@@ -570,13 +724,62 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
+  // ---- split dynamic-K tiles: partials and the last-arrival combine ----
+  // Partial tiles in the MFMA register layout, a 64 KB region per wave: 16
+  // bytes per lane and element quad, a 1 KB block per (i, j, q), the block
+  // offset in the instruction's scalar offset.  Stores and loads are
+  // coherent at device scope (sc1), so no cache-wide writeback is needed: a
+  // wait for the stores orders them before the counter update, and loads
+  // after it cannot hit stale lines.
+  auto part_store = [&](const __amdgpu_buffer_rsrc_t& r, const Item& it) __attribute__((always_inline)) {
+    int ln = threadIdx.x & 63;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = wm * 128 + 32 * i + (ln & 31) < it.m_valid;
+      const uint32_t vo = ok ? (uint32_t)(ln * 16) : kOOB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          i32x4 v;
+          v[0] = __float_as_int(acc[i][j][4 * q]);
+          v[1] = __float_as_int(acc[i][j][4 * q + 1]);
+          v[2] = __float_as_int(acc[i][j][4 * q + 2]);
+          v[3] = __float_as_int(acc[i][j][4 * q + 3]);
+          __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)vo, ((i * 4 + j) * 4 + q) * 1024, kPolicyDevice);
+        }
+    }
+  };
+  // A piece of a split tile: store the partial, count the arrival; returns
+  // true for the last piece to arrive, which then writes the tile from the
+  // partials (epilogue with npieces).  The accumulators are zero afterwards.
+  auto dk_arrive = [&](const Item& it) __attribute__((always_inline)) -> bool {
+    int32_t* flag = reinterpret_cast<int32_t*>(tab.scratch);
+    part_store(slot_rsrc(it.slot() + it.piece()), it);
+    zero_acc();
+    wait_vm_all();   // this wave's partial has reached the coherence point
+    lds_sync();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(a.sk_ctr + it.ctr(), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == it.pieces() - 1;
+      if (last) __hip_atomic_store(a.sk_ctr + it.ctr(), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = last;
+    }
+    lds_sync();
+    const bool last = uni(*flag) != 0;
+    lds_sync();   // every wave has read the flag before the next use of the word
+    return last;
+  };
+
   // ---- main loop ----
   // prologue: the first NS k-steps fill every stage
 #pragma unroll
   for (int u = 0; u < NS; ++u) load_step(u);
   wait_vm_sync<(NS - 1) * LPW>();   // B(0)
   int stage = 0;                    // stage of the compute cursor's k-step
-  int64_t cw = c0 + dj;
+  int64_t ck = 0;                   // compute cursor: the workgroup's ck-th item
+  int64_t cw = item_of(0);
   Item ci = fetch(cw);
   int cseq = 0;                     // items finished by the compute cursor
   Frag256<ELEM> F0, F1;
@@ -598,30 +801,72 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     stage = st + 1 == NS ? 0 : st + 1;
   };
+  // Dynamic-K: a k-step that the group's row range cuts (its first and
+  // last) holds bytes of the neighbouring groups in the 16-byte chunks that
+  // straddle the range's ends; they are cleared in the fragments before the
+  // MFMAs.  A lane's fragment covers contraction bytes 32 (lane / 32) + 0..31
+  // of the k-step.
+  auto edge_mask = [&](Frag256<ELEM>& f, int s) __attribute__((always_inline)) {
+    if constexpr (DK) {
+      const int64_t cb = ci.c_begin + (int64_t)s * BK;
+      const int64_t lo64 = ci.c_lo - cb, hi64 = ci.c_hi - cb;
+      const int mlo = lo64 < 0 ? 0 : (lo64 > BK ? BK : (int)lo64);
+      const int mhi = hi64 < 0 ? 0 : (hi64 > BK ? BK : (int)hi64);
+      if (mlo > 0 || mhi < BK) {
+        int ln = threadIdx.x & 63;
+        asm volatile("" : "+v"(ln));
+        const int k0 = 32 * (ln >> 5);
+        uint32_t m[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) m[d] = byte_range_mask(mlo - k0 - 4 * d, mhi - k0 - 4 * d);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            f.a[x][d] = (int)((uint32_t)f.a[x][d] & m[d]);
+            f.b[x][d] = (int)((uint32_t)f.b[x][d] & m[d]);
+          }
+      }
+    }
+  };
   for (;;) {
     // every k-step of the item but the last refills the stage it used
+    const int nst = ci.nsteps;
     if constexpr (KSUB == 2) {
-      for (int s = 0; s + 1 < nsteps; ++s) kstep(F0, F1, BoolConst<false>{});
+      for (int s = 0; s + 1 < nst; ++s) kstep(F0, F1, BoolConst<false>{});
     } else {
       // e4m3: one sub-step per k-step, fragments alternate between F0 and F1
       int s = 0;
-      for (; s + 2 < nsteps; s += 2) {
+      for (; s + 2 < nst; s += 2) {
+        edge_mask(F0, s);
         kstep(F0, F1, BoolConst<false>{});
+        edge_mask(F1, s + 1);
         kstep(F1, F0, BoolConst<false>{});
       }
-      if (s + 1 < nsteps) {
+      if (s + 1 < nst) {
+        edge_mask(F0, s);
         kstep(F0, F1, BoolConst<false>{});
         F0 = F1;   // once per item
       }
     }
     const int st_last = stage;
+    edge_mask(F0, nst - 1);
     kstep(F0, F1, BoolConst<true>{});
     // the last k-step's stage holds the epilogue's staging, then its refill
-    epilogue(st_last, ci, cseq % NSCB);   // (leaves the accumulators zeroed)
+    bool write = true;
+    int npieces = 0;
+    if constexpr (DK) {
+      if (ci.pieces() > 1) {
+        write = dk_arrive(ci);
+        npieces = ci.pieces();
+      }
+    }
+    if (write) epilogue(st_last, ci, cseq % NSCB, npieces, ci.slot());   // (leaves the accumulators zeroed)
+    if (dyn) grab(ck + 7);
     lds_sync();
     load_step(st_last);
-    const int64_t nw = cw + gx;
-    if (nw >= c1) break;
+    const int64_t nw = item_of(++ck);
+    if (nw < 0 || nw >= c1) break;
     cw = nw;
     ci = fetch(cw);
     ++cseq;
@@ -632,17 +877,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     G256_FENCE();
   }
   wait_vm_all();   // no LDS-DMA transfer may outlive the workgroup
+  // every request of this workgroup precedes its exit count, so the last to
+  // count has seen all requests done: the counters start at zero again
+  queue_exit();
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-template <bool B_KC, int ELEM, int EPI>
+template <bool B_KC, int ELEM, int EPI, int KIND>
 static hipError_t launch_256(const GemmArgs& a, hipStream_t stream) {
   const int bne = EPI == EPI_SWIGLU ? 128 : 256;
-  const int64_t work = fixed_m_capacity(a.total_rows, a.E, 256) * cdiv(a.Nout, bne);
+  const int64_t work = KIND == DYNAMIC_K ? (int64_t)a.E * cdiv(a.Mout, 256) * cdiv(a.Nout, 256)
+                                         : fixed_m_capacity(a.total_rows, a.E, 256) * cdiv(a.Nout, bne);
   if (work <= 0) return hipSuccess;
-  auto kern = gmm256_kernel<B_KC, ELEM, EPI>;
+  auto kern = gmm256_kernel<B_KC, ELEM, EPI, KIND>;
   static int configured = 0;
   if (configured == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -657,6 +906,14 @@ static hipError_t launch_256(const GemmArgs& a, hipStream_t stream) {
 }
 
 bool gemm256_eligible(const GemmLaunch& L, const GemmArgs& a) {
+  const int64_t cus = device_cu_count();
+  if (L.kind == DYNAMIC_K) {
+    // e4m3 dW: enough tiles for a few rounds on every CU, and groups of 512
+    // rows on average (8 k-steps per tile)
+    if (L.elem != EL_FP8 || !L.a_kc || !L.b_kc) return false;
+    const int64_t tiles = (int64_t)a.E * cdiv(a.Mout, 256) * cdiv(a.Nout, 256);
+    return tiles >= 2 * cus && a.total_rows >= (int64_t)a.E * 512;
+  }
   if (L.kind != FIXED_M || !L.a_kc) return false;
   if (L.elem == EL_FP8 && !L.b_kc) return false;
   if (L.elem != EL_BF16 && L.elem != EL_FP8) return false;
@@ -665,7 +922,6 @@ bool gemm256_eligible(const GemmLaunch& L, const GemmArgs& a) {
   // contractions that a tile's pipeline fill is small beside its k-steps
   const int bne = L.swiglu ? 128 : 256;
   const int64_t tiles = fixed_m_capacity(a.total_rows, a.E, 256) * cdiv(a.Nout, bne);
-  const int64_t cus = device_cu_count();
   if (tiles < 2 * cus) return false;
   if (a.Kc < 1024) return false;
   // rows per group: 256-row tiles of groups under about 192 rows would be
@@ -676,11 +932,12 @@ bool gemm256_eligible(const GemmLaunch& L, const GemmArgs& a) {
 
 hipError_t launch_gemm256(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream) {
   if (L.elem == EL_BF16) {
-    if (L.swiglu) return launch_256<false, EL_BF16, EPI_SWIGLU>(a, stream);
-    if (L.b_kc) return launch_256<true, EL_BF16, EPI_NONE>(a, stream);
-    return launch_256<false, EL_BF16, EPI_NONE>(a, stream);
+    if (L.swiglu) return launch_256<false, EL_BF16, EPI_SWIGLU, FIXED_M>(a, stream);
+    if (L.b_kc) return launch_256<true, EL_BF16, EPI_NONE, FIXED_M>(a, stream);
+    return launch_256<false, EL_BF16, EPI_NONE, FIXED_M>(a, stream);
   }
-  return launch_256<true, EL_FP8, EPI_ROW_COL>(a, stream);
+  if (L.kind == DYNAMIC_K) return launch_256<true, EL_FP8, EPI_GROUP, DYNAMIC_K>(a, stream);
+  return launch_256<true, EL_FP8, EPI_ROW_COL, FIXED_M>(a, stream);
 }
 
 }  // namespace mg

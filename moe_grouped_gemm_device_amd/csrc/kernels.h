@@ -67,6 +67,10 @@ struct GemmArgs {
   // partial tiles per workgroup
   int32_t* sk_ctr;
   float* sk_part;
+  // work-queue counters: items handed out (word 1 of the workspace header)
+  // and finished workgroups (word 9); zero between calls: the last
+  // workgroup of a launch that uses them resets them
+  int32_t* wq;
   // FIXED_M, bf16, A contraction-contiguous only: when gather is set, row r
   // of A is row gather[r] / gather_div of the matrix at A (a token row
   // looked up through the token-sorted order), and a zero row when

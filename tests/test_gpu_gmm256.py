@@ -7,8 +7,9 @@ matters: the contraction ends inside a k-step, the last column tile is
 partial, group ends cut row tiles, one group is empty.  Covered: bf16 with B
 as [K, N] and as [N, K], dX, e4m3 forward and dX with row and column scales,
 the A rows taken through the token-sorted index with and without the
-SiLU*mul epilogue, and a captured launch replayed after the device group
-sizes change."""
+SiLU*mul epilogue, the e4m3 dynamic-K dW over skewed groups whose row
+ranges start and end inside 16-byte chunks, and a captured launch replayed
+after the device group sizes change."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +18,7 @@ import moe_grouped_gemm_device_amd as mg
 import oracle
 import workloads as wl
 from gpu_util import (BF16_TOL, FP8_TOL, GEMM_BF16, GEMM_FP8, SWIGLU_ELEM, assert_close, bf16_dev, bf16_host, dev,
-                      dx_norms, fwd_norms, gpu, group_rows, require_gpu, vec_norms)
+                      dw_norms, dx_norms, fwd_norms, gpu, group_rows, require_gpu, vec_norms)
 
 pytestmark = gpu
 
@@ -100,6 +101,33 @@ def test_fp8_forward_and_dx():
     A = oracle.dequant_rowwise(dyq, sdy)
     Wr = oracle.dequant_rowwise(wq_r, sw_r).reshape(E, Kq, Nq)
     assert_close(_f64(dx), oracle.gmm_dx(A, Wr, SIZES), FP8_TOL, GEMM_FP8, "dX", dx_norms(A, Wr, SIZES))
+
+
+def test_fp8_dw_skewed_groups():
+    """dW[g] = Xc_g^T . dYc_g over 8 groups of very different sizes (one
+    empty, one of 77 rows), so items are dealt longest first in snake order;
+    group boundaries fall inside 16-byte chunks, whose bytes of the
+    neighbouring groups must not count.  Output 2056 x 2000 per group."""
+    sizes = np.array([3001, 0, 517, 9000, 1203, 77, 4100, 2486], np.int32)
+    E, M, Kq, Nq = len(sizes), int(sizes.sum()), 2056, 2000
+    g = wl.rng(45, wl.T_W)
+    xc, sxc = _codes(g, (Kq, M)), _scales(g, (E, Kq))     # column-major codes, per (group, column)
+    dyc, sdyc = _codes(g, (Nq, M)), _scales(g, (E, Nq))
+    ws = mg.workspace(E, M)
+    args = dict(xc=dev(xc), sxc=dev(sxc), dyc=dev(dyc), sdyc=dev(sdyc), need_dx=False, ws=ws)
+    _, dw = mg.gmm_bwd_fp8(dev(sizes), Kq, Nq, **args)
+    _wide()
+    # the items come from a work queue in the workspace header, and the
+    # split tiles' arrival counters follow it: both are back at zero after
+    # the call, and a second call with the same workspace gives the same bits
+    _, dw2 = mg.gmm_bwd_fp8(dev(sizes), Kq, Nq, **args)
+    torch.cuda.synchronize()
+    assert (ws[:1280].view(torch.int32)[1:] == 0).all()
+    assert torch.equal(dw, dw2)
+    dwh = _f64(dw)
+    Xc, dYc = oracle.dequant_colwise(xc, sxc, sizes), oracle.dequant_colwise(dyc, sdyc, sizes)
+    assert_close(dwh, oracle.gmm_dw(Xc, dYc, sizes), FP8_TOL, GEMM_FP8, "dW", dw_norms(Xc, dYc, sizes))
+    assert (dwh[1] == 0).all()
 
 
 def test_gathered_rows_and_silu_mul_epilogue():
