@@ -37,10 +37,14 @@
 //    32 rows x 64 columns at a time) and writes whole 128-byte row segments;
 //    the transfer that would refill that stage is issued after the
 //    epilogue and a barrier.
-//  * Whole tiles only: each XCD owns a contiguous eighth of the items and
-//    its workgroups take them round-robin; items come in raster blocks of up
-//    to 4 row tiles, so the 32 tiles an XCD runs at once cover about 4 row
-//    tiles x 8 column tiles and share their operand slices in its L2.
+//  * Each XCD owns a contiguous eighth of the tiles and its workgroups take
+//    them round-robin; tiles come in raster blocks of up to 4 row tiles, so
+//    the 32 tiles an XCD runs at once cover about 4 row tiles x 8 column
+//    tiles and share their operand slices in its L2.  When the XCD's last
+//    round would leave most of its workgroups idle (at most a quarter of
+//    them busy), each of that round's tiles is cut along the contraction
+//    into P pieces, one per workgroup: the pieces store fp32 partial tiles
+//    in the workspace and the last to arrive sums them in piece order.
 #include "gemm_dev.h"
 
 namespace mg {
@@ -60,7 +64,8 @@ static_assert(NW * 32 * SROW * 2 <= STAGE, "epilogue staging fits a stage");
 static_assert((NS - 2) * LPW <= 63, "vmcnt range");
 constexpr int64_t PART = 256LL * 256 * 4;   // one fp32 partial tile (split dynamic-K contraction)
 constexpr int PART_SLOTS = (int)(2 * kSkMaxGrid * kSkPartBytes / PART);   // partial slots in the workspace
-constexpr int64_t MIN_PIECE = 8;            // shortest piece of a split contraction (k-steps)
+constexpr int64_t MIN_PIECE = 8;            // shortest piece of a split dynamic-K contraction (k-steps)
+constexpr int64_t TAIL_PIECE = 32;          // shortest piece of a split fixed-M last-round tile (k-steps)
 
 // chunk swizzle of a contraction-contiguous tile: line L holds rows 2L, 2L+1
 __device__ inline int kc_swz(int L) { return (L ^ (L >> 1)) & 3; }
@@ -109,6 +114,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr bool DK = KIND == DYNAMIC_K;
   constexpr bool SWIGLU = EPI == EPI_SWIGLU;
   constexpr int BNE = SWIGLU ? BN / 2 : BN;        // output columns per tile
+  constexpr bool TSPLIT = KIND == FIXED_M && !SWIGLU;   // last-round tiles may be cut into pieces
+  constexpr bool PIECES = DK || TSPLIT;
   static_assert(ELEM == EL_BF16 || (B_KC && SCALED), "fp8: both operands k-contiguous, scaled");
   static_assert(!DK || (ELEM == EL_FP8 && EPI == EPI_GROUP), "dynamic-K: e4m3 with per-group scales");
   static_assert(!SWIGLU || (ELEM == EL_BF16 && !B_KC), "paired gate/up epilogue: bf16, B as [K, N]");
@@ -190,9 +197,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Items of equal length (fixed-M tiles; dynamic-K tiles when every group
   // has the same size): XCD x (workgroups are dealt round-robin to the 8
   // XCDs) owns items [x D / 8, (x + 1) D / 8), taken round-robin by its G / 8
-  // workgroups.  Dynamic-K items of unequal length (groups come largest
-  // first) are dealt over the whole grid in snake order, so the workgroups
-  // that drew a round's longest items draw the next round's shortest.
+  // workgroups.
   bool equal_items = true;
   if constexpr (DK)
     equal_items = uni(sp.groups) == 0 && uni(tab.eff[uni(tab.order[0])]) == uni(tab.eff[uni(tab.order[a.E - 1])]);
@@ -208,10 +213,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // time to land.  The last workgroup to finish resets the counters.
   // (Tiles handed out this way share no L2 by XCD, which costs against the
   // static deal when the groups are equal; measured on MI355X with the
-  // Zipf-skewed groups of a DeepSeek-MoE layer share, it still beats the
-  // static longest-first snake deal.)
+  // Zipf-skewed groups of a DeepSeek-MoE layer share, it still beats a
+  // static longest-first deal.)
   const bool dyn = DK && !equal_items;
-  const bool snake = false;
   __shared__ int32_t qring[16];   // the workgroup's n-th item at [n % 16] (-1: none)
   auto grab = [&](int64_t n) __attribute__((always_inline)) {
     if (tid == 0) {
@@ -242,22 +246,66 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t dj = xcd_split ? (int64_t)(blockIdx.x >> 3) : blockIdx.x;
   const int64_t c0 = xcd_split ? ((int64_t)(blockIdx.x & 7) * items) >> 3 : 0;
   const int64_t c1 = xcd_split ? ((int64_t)((blockIdx.x & 7) + 1) * items) >> 3 : items;
-  // the workgroup's k-th item (c1 or beyond: none)
+  // Fixed-M last round: the XCD's n tiles run as floor(n / gx) full rounds
+  // and a last round of r = n % gx tiles, which at 256 x 256 tiles and long
+  // contractions (the second FFN GEMM) can idle most of the XCD for a whole
+  // tile's time.  With r <= gx / 4, each of those r tiles is cut into P
+  // = min(8, gx / r) pieces of at least TAIL_PIECE k-steps, one piece per
+  // workgroup (piece j of last-round tile t is item code D + j r + t, D the
+  // tile count).  Tile t's arrival counter is x gx + t, its piece j's
+  // partial slot x gx + t P + j: with gx <= 32 every XCD stays inside its
+  // own 32 counters and slots.  (Measured on MI355X: with a quarter of the
+  // XCD or more busy, a last round of whole tiles runs about as fast as the
+  // same work in pieces -- the k-steps of the few busy workgroups speed up
+  // -- and short pieces lose to the partials' round trip.)
+  int64_t whole = c1 - c0;   // the XCD's tiles that run whole
+  int64_t tail_r = 0, tail_p = 1;
+  if constexpr (TSPLIT) {
+    const int64_t r = (c1 - c0) % gx;
+    if (xcd_split && G <= kSkMaxGrid && G <= PART_SLOTS && r > 0 && 4 * r <= gx) {
+      int64_t p = gx / r;
+      if (p > 8) p = 8;
+      const int64_t steps = cdiv(a.Kc, BK);
+      if (p > steps / TAIL_PIECE) p = steps / TAIL_PIECE;
+      if (p >= 2) {
+        tail_r = r;
+        tail_p = p;
+        whole = c1 - c0 - r;
+      }
+    }
+  }
+  // the workgroup's k-th item code (-1: none)
   auto item_of = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
     if (dyn) {
       const int code = uni(qring[k & 15]);
-      return code < 0 ? c1 : code;   // none left (or the counter was not zeroed)
+      return code < 0 ? -1 : code;   // none left (or the counter was not zeroed)
     }
-    if (snake) return k * G + ((k & 1) ? (G - 1 - (int64_t)blockIdx.x) : (int64_t)blockIdx.x);
-    return c0 + dj + k * gx;
+    const int64_t u = dj + k * gx;
+    if (u < whole) return c0 + u;
+    const int64_t v = u - whole;
+    return TSPLIT && v < tail_r * tail_p ? items + v : -1;
   };
-  if (item_of(0) >= c1) {
+  if (item_of(0) < 0) {
     queue_exit();
     return;
   }
   // (every field is workgroup-uniform; said so, so that items live in SGPRs)
   auto fetch = [&](int64_t w) __attribute__((always_inline)) {
-    Item it = get_item<BM, BNE, KIND, ELEM, BK, DK, RASTER>(a, tab, w, n_tiles, m_tiles_dk, nullptr, sp);
+    int64_t t = 0, j = 0;
+    if (TSPLIT && w >= items) {   // piece j of the XCD's last-round tile t
+      t = (w - items) % tail_r;
+      j = (w - items) / tail_r;
+    }
+    Item it = get_item<BM, BNE, KIND, ELEM, BK, DK, RASTER>(a, tab, TSPLIT && w >= items ? c0 + whole + t : w,
+                                                           n_tiles, m_tiles_dk, nullptr, sp);
+    if (TSPLIT && w >= items) {   // k-steps [j S / P, (j + 1) S / P) of the tile's S
+      const int s0 = (int)(j * it.nsteps / tail_p), s1 = (int)((j + 1) * it.nsteps / tail_p);
+      const int base = (int)((blockIdx.x & 7) * gx);
+      it.c_begin = (int64_t)s0 * BK;
+      it.nsteps = s1 - s0;
+      it.split = ((int)tail_p << 16) | (int)j;
+      it.sloc = ((base + (int)t) << 16) | (base + (int)(t * tail_p));
+    }
     it.g = uni(it.g);
     it.rowbase = uni64(it.rowbase);
     it.m_valid = uni(it.m_valid);
@@ -429,7 +477,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       return;
     }
     const int64_t nw = item_of(++lk);
-    if (nw < 0 || nw >= c1) {   // (negative only from counters the caller failed to zero)
+    if (nw < 0) {
       ldone = true;
       return;
     }
@@ -675,10 +723,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
           const int cw = 32 * jj + 8 * q + 4 * hi;   // column in the 64-wide staging row
           float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
           float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-          if constexpr (DK) {
+          if constexpr (PIECES) {
             if (npieces > 0) {
               v0 = v1 = v2 = v3 = 0.f;
-              for (int p = 0; p < npieces; ++p) {
+              for (int p = 0; p < (DK ? npieces : 0); ++p) {
                 const i32x4 pv = __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(slot0 + p), (int)pvo,
                                                                         ((i * 4 + j) * 4 + q) * 1024, kPolicyDevice);
                 v0 += __int_as_float(pv[0]);
@@ -711,7 +759,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int rw = qq >> 3, ch = qq & 7;
         const uint4 v = *reinterpret_cast<const uint4*>(stg + rw * SROW + ch * 8);
         const int row = wm * 128 + 32 * i + rw, col = wn * 128 + 64 * h + ch * 8;
-        const uint32_t vo = (row < it.m_valid && col < it.n_valid) ? (uint32_t)((row * a.c_ld + col) * 2) : kOOB;
+        const bool ok = row < it.m_valid && col < it.n_valid && !(TSPLIT && npieces > 0);
+        const uint32_t vo = ok ? (uint32_t)((row * a.c_ld + col) * 2) : kOOB;
         i32x4 d;
         d[0] = (int)v.x;
         d[1] = (int)v.y;
@@ -753,7 +802,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   // A piece of a split tile: store the partial, count the arrival; returns
   // true for the last piece to arrive, which then writes the tile from the
-  // partials (epilogue with npieces).  The accumulators are zero afterwards.
+  // partials (combine, then the epilogue).  The accumulators are zero
+  // afterwards.
   auto dk_arrive = [&](const Item& it) __attribute__((always_inline)) -> bool {
     int32_t* flag = reinterpret_cast<int32_t*>(tab.scratch);
     part_store(slot_rsrc(it.slot() + it.piece()), it);
@@ -772,6 +822,86 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     return last;
   };
 
+  // A split last-round tile, written by the last of its pieces to arrive
+  // (after its item loop: the accumulators are free, no transfer is in
+  // flight): every output element is the sum, in piece order, of the
+  // pieces' partials in slots slot0 .. slot0 + P - 1, scaled as the
+  // epilogue scales, rounded to bf16 and stored 4 columns at a time.  Each
+  // wave takes the 128 x 128 region its own partials hold; per round, two
+  // 32 x 32 blocks of up to four pieces are in flight (a load past the last
+  // piece is out of range and reads zeros, and adding zero to a sum that
+  // started at +0 changes no bit).
+  auto tail_out = [&](const Item& it) __attribute__((always_inline)) {
+    const int P = it.pieces(), slot0 = it.slot();
+    uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + (int64_t)it.g * a.c_gs + it.rowbase * a.c_ld + it.n0;
+    int ln = threadIdx.x & 63;   // (an opaque copy: nothing lane-derived is held across the k-loop for this)
+    asm volatile("" : "+v"(ln));
+    const int l31 = ln & 31, hi = ln >> 5;
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + 32 * i + l31;
+      const bool rok = row < it.m_valid;
+      const uint32_t pvo = rok ? (uint32_t)(ln * 16) : kOOB;
+      float rs = 1.f;
+      if constexpr (SCALED) {
+        const float v = rok ? a.sa[it.rowbase + row] : 0.f;
+        rs = v != 0.f ? 1.f / v : 0.f;
+      }
+#pragma unroll 1
+      for (int j = 0; j < 4; j += 2) {
+        float sm[2][4][4];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sm[jj][q][c] = 0.f;
+        for (int p0 = 0; p0 < P; p0 += 4) {
+          i32x4 ld[4][2][4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const __amdgpu_buffer_rsrc_t r = slot_rsrc(slot0 + p0 + u);
+            const int vo = (int)(p0 + u < P ? pvo : kOOB);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                ld[u][jj][q] = __builtin_amdgcn_raw_buffer_load_b128(r, vo, ((i * 4 + j + jj) * 4 + q) * 1024,
+                                                                     kPolicyDevice);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sm[jj][q][c] += __int_as_float(ld[u][jj][q][c]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = wn * 128 + 32 * (j + jj) + 8 * q + 4 * hi;
+            if (!rok || col >= it.n_valid) continue;   // (column counts are multiples of 8)
+            float v[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              v[c] = sm[jj][q][c];
+              if constexpr (SCALED) {
+                const float w = a.sb[(int64_t)it.g * a.Nout + it.n0 + col + c];
+                v[c] = (v[c] * (w != 0.f ? 1.f / w : 0.f)) * rs;
+              }
+            }
+            uint2 pk;
+            pk.x = pack_bf16x2_hw(v[0], v[1]);
+            pk.y = pack_bf16x2_hw(v[2], v[3]);
+            *reinterpret_cast<uint2*>(C + (int64_t)row * a.c_ld + col) = pk;
+          }
+      }
+    }
+  };
+
   // ---- main loop ----
   // prologue: the first NS k-steps fill every stage
 #pragma unroll
@@ -782,6 +912,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   int64_t cw = item_of(0);
   Item ci = fetch(cw);
   int cseq = 0;                     // items finished by the compute cursor
+  bool tail_last = false;           // the workgroup is the last piece of a split last-round tile
   Frag256<ELEM> F0, F1;
 #pragma unroll
   for (int n = 0; n < NREAD; ++n) read_one(F0, 0, 0, n);
@@ -855,18 +986,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     // the last k-step's stage holds the epilogue's staging, then its refill
     bool write = true;
     int npieces = 0;
-    if constexpr (DK) {
+    if constexpr (PIECES) {
       if (ci.pieces() > 1) {
         write = dk_arrive(ci);
         npieces = ci.pieces();
       }
     }
+    if constexpr (TSPLIT) tail_last = write && npieces > 0;
     if (write) epilogue(st_last, ci, cseq % NSCB, npieces, ci.slot());   // (leaves the accumulators zeroed)
     if (dyn) grab(ck + 7);
     lds_sync();
     load_step(st_last);
     const int64_t nw = item_of(++ck);
-    if (nw < 0 || nw >= c1) break;
+    if (nw < 0) break;
     cw = nw;
     ci = fetch(cw);
     ++cseq;
@@ -877,6 +1009,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     G256_FENCE();
   }
   wait_vm_all();   // no LDS-DMA transfer may outlive the workgroup
+  if constexpr (TSPLIT) {
+    if (tail_last) tail_out(ci);
+  }
   // every request of this workgroup precedes its exit count, so the last to
   // count has seen all requests done: the counters start at zero again
   queue_exit();

@@ -8,8 +8,9 @@ partial, group ends cut row tiles, one group is empty.  Covered: bf16 with B
 as [K, N] and as [N, K], dX, e4m3 forward and dX with row and column scales,
 the A rows taken through the token-sorted index with and without the
 SiLU*mul epilogue, the e4m3 dynamic-K dW over skewed groups whose row
-ranges start and end inside 16-byte chunks, and a captured launch replayed
-after the device group sizes change."""
+ranges start and end inside 16-byte chunks, a captured launch replayed
+after the device group sizes change, and last rounds whose tiles are cut
+along the contraction into pieces summed by the last to arrive."""
 import numpy as np
 import pytest
 import torch
@@ -188,3 +189,87 @@ def test_captured_launch_follows_device_sizes_changed_between_replays():
         _wide()
         torch.cuda.synchronize()
         assert torch.equal(y, y_e)
+
+
+def _last_round_pieces(sizes, n_cols, k_steps):
+    """(r, P) per XCD of a fixed-M launch: the last round's r tiles and the
+    pieces each is cut into (1: whole), from the kernel's rule -- the XCD's
+    n tiles over its gx = G / 8 workgroups leave r = n % gx; r <= gx / 4
+    cuts each into min(8, gx / r, k_steps / 32) pieces."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = int(sum((int(s) + 255) // 256 for s in sizes)) * ((n_cols + 255) // 256)
+    G = min(tiles, cus)
+    assert G % 8 == 0
+    gx, plan = G // 8, []
+    for x in range(8):
+        n = (x + 1) * tiles // 8 - x * tiles // 8
+        r = n % gx
+        p = min(8, gx // r, k_steps // 32) if 0 < 4 * r <= gx else 1
+        plan.append((r, p if p >= 2 else 1))
+    return plan
+
+
+LAST_SIZES = np.array([8701, 0, 9211], np.int32)   # 34 + 36 row tiles: 560 tiles of 2000 columns, 70 per XCD
+K_LAST, N_LAST = 5128, 2000                         # 160.25 bf16 k-steps; 7.8 column tiles
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_bf16_last_round_in_pieces(trans_b):
+    """560 tiles on 256 CUs: every XCD runs 2 full rounds and a last round of
+    6 tiles, each cut into 5 pieces of 32 or 33 k-steps (K = 5128: the last
+    piece ends inside a k-step; group ends cut the row tiles).  The arrival
+    counters are back at zero after the call, and a second call gives the
+    same bits (the pieces are summed in piece order)."""
+    E, M = len(LAST_SIZES), int(LAST_SIZES.sum())
+    assert set(_last_round_pieces(LAST_SIZES, N_LAST, 161)) == {(6, 5)}
+    X = wl.normal_bf16((M, K_LAST), 1.0, 46, wl.T_X)
+    W = wl.stacked_normal_bf16(E, (K_LAST, N_LAST), 0.05, 46, wl.T_W)
+    Wg = np.ascontiguousarray(np.transpose(W, (0, 2, 1))) if trans_b else W
+    x, w, gs = bf16_dev(X), bf16_dev(Wg), dev(LAST_SIZES)
+    ws = mg.workspace(E, M)
+    y = mg.gmm_fwd(x, w, gs, trans_b=trans_b, ws=ws)
+    _wide()
+    y2 = mg.gmm_fwd(x, w, gs, trans_b=trans_b, ws=ws)
+    torch.cuda.synchronize()
+    assert (ws[:1280].view(torch.int32)[1:] == 0).all()
+    assert torch.equal(y, y2)
+    Xf, Wf = oracle.bf16_to_f64(X), oracle.bf16_to_f64(W)
+    assert_close(_f64(y), oracle.gmm_fwd(Xf, Wf, LAST_SIZES), BF16_TOL, GEMM_BF16, "Y",
+                 fwd_norms(Xf, Wf, LAST_SIZES))
+
+
+def test_gathered_rows_last_round_in_pieces():
+    """The token-sorted A load on the same 560-tile launch: rows through
+    sorted_token_ids / top_k (T = 8192 tokens, top-2), a padding sentinel
+    every 40th row giving zero rows."""
+    E, M, T, k = len(LAST_SIZES), int(LAST_SIZES.sum()), 8192, 2
+    g = wl.rng(47, wl.T_X)
+    sids = g.integers(0, T * k, size=M).astype(np.int32)
+    sids[::40] = T * k
+    x = wl.normal_bf16((T, K_LAST), 1.0, 47, wl.T_X)
+    W = wl.stacked_normal_bf16(E, (K_LAST, N_LAST), 0.05, 47, wl.T_W)
+    h = mg.gmm_fwd_gather(bf16_dev(x), dev(sids), k, bf16_dev(W), dev(LAST_SIZES))
+    _wide()
+    torch.cuda.synchronize()
+    xs = oracle.gather_rows(x, k, sids)
+    Xf, Wf = oracle.bf16_to_f64(xs), oracle.bf16_to_f64(W)
+    assert_close(_f64(h), oracle.gmm_fwd(Xf, Wf, LAST_SIZES), BF16_TOL, GEMM_BF16, "h",
+                 fwd_norms(Xf, Wf, LAST_SIZES))
+
+
+def test_fp8_last_round_in_pieces():
+    """e4m3 with row and column scales on the 560-tile launch: K = 5136 is 81
+    k-steps of 64 bytes, so the 6 last-round tiles of each XCD are cut into
+    2 pieces of 40 and 41 k-steps, the scales applied once to their sum."""
+    E, M, Kq, Nq = len(LAST_SIZES), int(LAST_SIZES.sum()), 5136, N_LAST
+    assert set(_last_round_pieces(LAST_SIZES, Nq, 81)) == {(6, 2)}
+    g = wl.rng(48, wl.T_W)
+    xq, sx = _codes(g, (M, Kq)), _scales(g, M)
+    wq_c, sw_c = _codes(g, (E, Nq, Kq)), _scales(g, (E, Nq))
+    y = mg.gmm_fwd_fp8(dev(xq), dev(sx), dev(wq_c), dev(sw_c), Kq, Nq * Kq, dev(LAST_SIZES), Nq)
+    _wide()
+    torch.cuda.synchronize()
+    A = oracle.dequant_rowwise(xq, sx)
+    Wf = np.transpose(oracle.dequant_rowwise(wq_c.reshape(E * Nq, Kq), sw_c.reshape(E * Nq)).reshape(E, Nq, Kq),
+                      (0, 2, 1))
+    assert_close(_f64(y), oracle.gmm_fwd(A, Wf, LAST_SIZES), FP8_TOL, GEMM_FP8, "Y", fwd_norms(A, Wf, LAST_SIZES))
