@@ -52,8 +52,9 @@ def algorithmic_bytes(E, M, K, N):
     return {"fwd": w + M * K * 2 + M * N * 2, "dx": w + M * N * 2 + M * K * 2, "dw": w + M * K * 2 + M * N * 2}
 
 
-KERNEL_SOURCES = ["moe_grouped_gemm_device_amd/csrc/gmm.hip", "moe_grouped_gemm_device_amd/csrc/worklist.h",
-                  "moe_grouped_gemm_device_amd/csrc/common.h", "moe_grouped_gemm_device_amd/csrc/kernels.h"]
+KERNEL_SOURCES = ["moe_grouped_gemm_device_amd/csrc/gmm.hip", "moe_grouped_gemm_device_amd/csrc/gemm_dev.h",
+                  "moe_grouped_gemm_device_amd/csrc/worklist.h", "moe_grouped_gemm_device_amd/csrc/common.h",
+                  "moe_grouped_gemm_device_amd/csrc/kernels.h"]
 TRAFFIC_PROFILE = "profiles/gmm_bf16_balanced_traffic.md"
 
 
