@@ -72,10 +72,13 @@ enum {
 /* ------------------------------------------------------------------------ */
 
 /* Bytes of device workspace that a grouped-GEMM call with these E and
- * total_M needs: a 256-byte header (the sticky error word), one arrival
- * counter per workgroup of a stream-K launch (at most 256) and two fp32
- * partial output tiles (128 x 256) per workgroup, about 64 MiB in all.  The
- * work lists themselves are built in LDS by every kernel's prologue.
+ * total_M needs: a 256-byte header (the sticky error word, and the two
+ * counters of the work queue that the 256 x 256-tile dW kernel deals
+ * unequal groups' tiles from), 256 arrival counters (one per split tile or
+ * stream-K workgroup) and 64 MiB of fp32 partial output tiles (two
+ * 128 x 256 tiles per workgroup of the 8-wave kernel, one 256 x 256 tile
+ * per workgroup of the 4-wave kernel), about 64 MiB in all.  The work
+ * lists themselves are built in LDS by every kernel's prologue.
  * Depends on host values only; the pointer must be 256-byte aligned.
  * A fresh workspace must be zeroed once before its first use (a
  * zero-filled allocation, or mg_workspace_clear); the GEMM calls (the
@@ -89,8 +92,8 @@ size_t mg_workspace_bytes(int32_t E, int64_t total_M);
  * 0 = none, 1 = negative group size, 2 = sizes sum past total_M. */
 int32_t mg_workspace_error(const void* ws);
 
-/* Zeroes the workspace header (error word) and the stream-K counters
- * (enqueued on stream, by a fill kernel). */
+/* Zeroes the workspace header (error word, work-queue counters) and the
+ * arrival counters (enqueued on stream, by a fill kernel). */
 int mg_workspace_clear(void* ws, mg_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
