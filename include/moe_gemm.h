@@ -397,6 +397,20 @@ int moe_unpermute(const void* y_sorted, const int32_t* inv_pos,
 int silu_mul(const void* h, int64_t rows, int32_t inter, void* act,
              mg_stream_t stream);
 
+/* SiLU*mul then rowwise e4m3 ([FMOE] fused_moe: silu_and_mul between the
+ * two expert GEMMs; [FP8] commit message: the rowwise scale and cast as one
+ * fused kernel), for the e4m3 operand of the second expert GEMM:
+ * act = silu_mul(h) exactly as silu_mul computes it (bf16), then codes
+ * q e4m3 [rows, inter] and scales fp32 [rows] exactly as
+ * quantize_rowwise_fp8 computes them from act -- the same bits as the two
+ * calls, in one pass over h.  act (bf16 [rows, inter]) may be NULL; when
+ * given it receives act as well.  h bf16 [rows, 2*inter] contiguous,
+ * 16-byte aligned (act too), q 8-byte aligned; inter % 8 == 0;
+ * rows < 2^31. */
+int silu_mul_quantize_rowwise_fp8(const void* h, int64_t rows, int32_t inter,
+                                  void* act, uint8_t* q, float* scales,
+                                  mg_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                              */
 /* ------------------------------------------------------------------------ */

@@ -61,6 +61,7 @@ _SIGS = {
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_unpermute": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "silu_mul": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "silu_mul_quantize_rowwise_fp8": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
     "moe_route_topk": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "mg_last_error": (ctypes.c_char_p, []),
     "mg_version": (ctypes.c_char_p, []),
@@ -490,26 +491,30 @@ def moe_permute(topk_ids, E, block_m, x=None, ws=None, stream=None):
                 inv=inv[:T * k], padded_sizes=padded, x_sorted=None if xs is None else xs[:cap])
 
 
-def fused_moe_f8i4(x, w1_4, s1, w2_4, s2, topk_ids, topk_weights, block_m=16, ws=None, stream=None):
+def fused_moe_f8i4(x, w1_4, s1, w2_4, s2, topk_ids, topk_weights, block_m=16, ws=None, stream=None,
+                   keep_act=False):
     """Token-sorted MoE expert FFN with int4 expert weights and fp8
     activations, for decode-sized token counts: align -> rowwise e4m3
-    quantization of the token rows in sorted order -> F8I4 GEMM1 -> SiLU*mul -> rowwise e4m3 quantization
-    -> F8I4 GEMM2 -> top-k weighted combine.  Weights as quantize_int4_weights
-    returns them: w1_4 uint8 [E, 2I, H/2] with s1 bf16 [E, H/128, 2I] (from
-    W1 [E, H, 2I]), w2_4 uint8 [E, H, I/2] with s2 bf16 [E, I/128, H] (from
-    W2 [E, I, H]).  Every weight tile is streamed once per 32 sorted rows, so
-    this path suits small T; large T belongs on the bf16 or fp8 kernels.
-    Returns (out bf16 [T, H], dict of the intermediates)."""
+    quantization of the token rows in sorted order -> F8I4 GEMM1 -> SiLU*mul
+    and rowwise e4m3 quantization in one pass -> F8I4 GEMM2 -> top-k
+    weighted combine.  Weights as quantize_int4_weights returns them: w1_4
+    uint8 [E, 2I, H/2] with s1 bf16 [E, H/128, 2I] (from W1 [E, H, 2I]),
+    w2_4 uint8 [E, H, I/2] with s2 bf16 [E, I/128, H] (from W2 [E, I, H]).
+    Every weight tile is streamed once per 32 sorted rows, so this path
+    suits small T; large T belongs on the bf16 or fp8 kernels.  Returns
+    (out bf16 [T, H], dict of the intermediates); the bf16 activations are
+    written and returned only with keep_act."""
     T, k = topk_ids.shape
     E = w1_4.shape[0]
+    inter = w1_4.shape[1] // 2
     p = moe_permute(topk_ids, E, block_m, stream=stream)
     ids, sizes = p["sorted_token_ids"], p["padded_sizes"]
     ws = default_workspace(x.device, stream) if ws is None else ws
     # the token rows are read through the sorted order by the quantizer
     xq, sx = quantize_rowwise_fp8_gather(x, ids, k, stream=stream)
     h1 = gmm_fwd_f8i4(xq, sx, w1_4, s1, sizes, ws=ws, stream=stream)
-    act = silu_mul(h1, stream=stream)
-    aq, sa = quantize_rowwise_fp8(act, stream=stream)
+    act = torch.empty(h1.shape[0], inter, dtype=torch.bfloat16, device=x.device) if keep_act else None
+    aq, sa = silu_mul_quantize_rowwise_fp8(h1, act=act, stream=stream)
     y2 = gmm_fwd_f8i4(aq, sa, w2_4, s2, sizes, ws=ws, stream=stream)
     out = moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream)
     return out, dict(permute=p, xq=xq, sx=sx, h1=h1, act=act, aq=aq, sa=sa, y2=y2)
@@ -527,15 +532,17 @@ def quantize_fp8_expert_weights(w, stream=None):
     return quantize_colwise_per_group_fp8(w.reshape(E * K, N), sizes, stream=stream)
 
 
-def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=None, stream=None):
+def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=None, stream=None,
+                  keep_act=False):
     """Token-sorted MoE expert FFN with e4m3 expert weights and
     activations: align -> rowwise e4m3 of the token rows in sorted order ->
-    fp8 GEMM1 (row scales x per-(expert, column) weight scales) -> SiLU*mul ->
-    rowwise e4m3 of the activations -> fp8 GEMM2 -> top-k weighted combine.
-    Weights as quantize_fp8_expert_weights returns them: w1q uint8 [2I, E*H]
-    with s1 fp32 [E, 2I] (from W1 [E, H, 2I]), w2q uint8 [H, E*I] with s2
-    fp32 [E, H] (from W2 [E, I, H]).  Returns (out bf16 [T, H], dict of the
-    intermediates)."""
+    fp8 GEMM1 (row scales x per-(expert, column) weight scales) -> SiLU*mul
+    and rowwise e4m3 of the activations in one pass -> fp8 GEMM2 -> top-k
+    weighted combine.  Weights as quantize_fp8_expert_weights returns them:
+    w1q uint8 [2I, E*H] with s1 fp32 [E, 2I] (from W1 [E, H, 2I]), w2q
+    uint8 [H, E*I] with s2 fp32 [E, H] (from W2 [E, I, H]).  Returns (out
+    bf16 [T, H], dict of the intermediates); the bf16 activations are
+    written and returned only with keep_act."""
     T, k = topk_ids.shape
     E, two_i = s1.shape
     H = x.shape[1]
@@ -550,8 +557,8 @@ def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=
     # the token rows are read through the sorted order by the quantizer
     xq, sx = quantize_rowwise_fp8_gather(x, ids, k, stream=stream)
     h1 = gmm_fwd_fp8(xq, sx, w1q, s1, E * H, H, sizes, two_i, ws=ws, stream=stream)
-    act = silu_mul(h1, stream=stream)
-    aq, sa = quantize_rowwise_fp8(act, stream=stream)
+    act = torch.empty(h1.shape[0], inter, dtype=torch.bfloat16, device=x.device) if keep_act else None
+    aq, sa = silu_mul_quantize_rowwise_fp8(h1, act=act, stream=stream)
     y2 = gmm_fwd_fp8(aq, sa, w2q, s2, E * inter, inter, sizes, H, ws=ws, stream=stream)
     out = moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream)
     return out, dict(permute=p, xq=xq, sx=sx, h1=h1, act=act, aq=aq, sa=sa, y2=y2)
@@ -591,6 +598,22 @@ def silu_mul(h, out=None, stream=None):
     out = torch.empty(R, I2 // 2, dtype=torch.bfloat16, device=h.device) if out is None else out
     _call("silu_mul", _ptr(h), R, I2 // 2, _ptr(out), _stream(stream))
     return out
+
+
+def silu_mul_quantize_rowwise_fp8(h, q=None, scales=None, act=None, stream=None):
+    """silu(h[:, :I]) * h[:, I:] in bf16, then rowwise e4m3 of it, in one
+    pass: returns (codes uint8 [R, I], fp32 scales [R]), the same bits as
+    quantize_rowwise_fp8(silu_mul(h)).  act, a bf16 [R, I] buffer, also
+    receives the bf16 activations when given."""
+    _need(h, torch.bfloat16, "h", 2)
+    R, I2 = h.shape
+    q, scales = _rowwise_outputs(q, scales, R, I2 // 2, h.device)
+    if act is not None:
+        _need(act, torch.bfloat16, "act", 2)
+        if tuple(act.shape) != (R, I2 // 2) or act.device != h.device:
+            raise ValueError(f"act must be [{R}, {I2 // 2}] on h's device")
+    _call("silu_mul_quantize_rowwise_fp8", _ptr(h), R, I2 // 2, _ptr(act), _ptr(q), _ptr(scales), _stream(stream))
+    return q, scales
 
 
 def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, ws=None, stream=None):

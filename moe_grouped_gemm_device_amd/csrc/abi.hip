@@ -695,4 +695,18 @@ int silu_mul(const void* h, int64_t rows, int32_t inter, void* act, mg_stream_t 
                     "silu_mul");
 }
 
+int silu_mul_quantize_rowwise_fp8(const void* h, int64_t rows, int32_t inter, void* act, uint8_t* q, float* scales,
+                                  mg_stream_t stream) {
+  if (rows < 0 || inter < 1) return fail(MG_EINVAL, "rows >= 0 and inter >= 1 required");
+  if (inter % 8) return fail(MG_EUNSUPPORTED, "inter must be a multiple of 8");
+  if (rows >= kMaxRows) return fail(MG_EINVAL, "rows must be below 2^31");
+  if (rows == 0) return ok();
+  if (!h || !q || !scales) return fail(MG_EINVAL, "NULL tensor argument");
+  if (!aligned16(h) || (act && !aligned16(act)) || (reinterpret_cast<uintptr_t>(q) & 7))
+    return fail(MG_EUNSUPPORTED, "h and act must be 16-byte and q 8-byte aligned");
+  return hip_status(launch_silu_mul_quant(reinterpret_cast<const uint16_t*>(h), rows, inter,
+                                          reinterpret_cast<uint16_t*>(act), q, scales, S(stream)),
+                    "silu_mul_quantize_rowwise_fp8");
+}
+
 }  // extern "C"

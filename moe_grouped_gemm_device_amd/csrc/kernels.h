@@ -135,6 +135,10 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int32_t E, int32_t 
                              float* wts, hipStream_t stream);
 hipError_t launch_silu_mul(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* act,
                            hipStream_t stream);
+// act = silu(h[:, :inter]) * h[:, inter:] (bf16), then rowwise e4m3 of act:
+// codes q [rows, inter], scales [rows]; act also written when non-null
+hipError_t launch_silu_mul_quant(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* act, uint8_t* q,
+                                 float* scales, hipStream_t stream);
 
 int device_cu_count();
 

@@ -190,6 +190,89 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int32_t cols, i
 }
 
 // ---------------------------------------------------------------------------
+// SiLU*mul followed by rowwise e4m3, in one pass: the second FFN GEMM's e4m3
+// operand straight from the first GEMM's [rows, 2I] output (applied-ai issue
+// "Column-major fused MoE", fused_moe: act = silu(gate) * up; torchao commit
+// "Optimize FP8 MoE backward pass": the rowwise scale+cast as one kernel).
+// act is formed exactly as silu_mul_kernel forms it (fp32 from the bf16
+// halves, rounded to bf16), and its codes and scale exactly as the rowwise
+// quantizer forms them from those bf16 values, so the result is the same
+// bits as silu_mul followed by quantize_rowwise_fp8, without the bf16 act
+// making a round trip through HBM.  One workgroup per row; a row of up to
+// 256 * 8 * SQ_HELD values stays in registers between the amax and the
+// cast, longer rows recompute act from h for the cast.  act is written too
+// when the caller passes a buffer for it.
+// ---------------------------------------------------------------------------
+constexpr int SQ_HELD = 8;   // act chunks (8 values each) per thread held in registers
+
+// act chunk ch of row hr (gate at hr, up at hr + inter): 8 bf16 values
+__device__ inline uint4 silu_mul_chunk(const uint16_t* hr, int32_t inter, int ch) {
+  const uint4 g = *reinterpret_cast<const uint4*>(hr + ch * 8);
+  const uint4 u = *reinterpret_cast<const uint4*>(hr + inter + ch * 8);
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+  const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float g0 = bf16_to_f32(gw[i] & 0xFFFFu), g1 = bf16_to_f32(gw[i] >> 16);
+    const float u0 = bf16_to_f32(uw[i] & 0xFFFFu), u1 = bf16_to_f32(uw[i] >> 16);
+    const float a0 = g0 / (1.f + expf(-g0)) * u0;
+    const float a1 = g1 / (1.f + expf(-g1)) * u1;
+    o[i] = pack_bf16x2(a0, a1);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__global__ void __launch_bounds__(256) silu_mul_quant_kernel(const uint16_t* __restrict__ h, int32_t inter,
+                                                            uint16_t* __restrict__ act, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scales) {
+  __shared__ uint32_t wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const uint16_t* hr = h + row * (2 * (int64_t)inter);
+  uint8_t* qr = q + row * (int64_t)inter;
+  uint16_t* ar = act != nullptr ? act + row * (int64_t)inter : nullptr;
+  const int ncols = inter >> 3;
+  uint4 held[SQ_HELD];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < SQ_HELD; ++i) {
+    const int ch = tid + i * 256;
+    held[i] = make_uint4(0, 0, 0, 0);
+    if (ch < ncols) {
+      held[i] = silu_mul_chunk(hr, inter, ch);
+      m = max(m, chunk_absmax_bits(held[i]));
+      if (ar != nullptr) *reinterpret_cast<uint4*>(ar + ch * 8) = held[i];
+    }
+  }
+  for (int ch = tid + SQ_HELD * 256; ch < ncols; ch += 256) {
+    const uint4 v = silu_mul_chunk(hr, inter, ch);
+    m = max(m, chunk_absmax_bits(v));
+    if (ar != nullptr) *reinterpret_cast<uint4*>(ar + ch * 8) = v;
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float s = fp8_scale_from_amax(__uint_as_float(m));
+  if (tid == 0) scales[row] = s;
+#pragma unroll
+  for (int i = 0; i < SQ_HELD; ++i) {
+    const int ch = tid + i * 256;
+    if (ch < ncols) *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(held[i], s);
+  }
+  for (int ch = tid + SQ_HELD * 256; ch < ncols; ch += 256)
+    *reinterpret_cast<uint2*>(qr + ch * 8) = quant_chunk(silu_mul_chunk(hr, inter, ch), s);
+}
+
+hipError_t launch_silu_mul_quant(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* act, uint8_t* q,
+                                 float* scales, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(silu_mul_quant_kernel, dim3((unsigned)rows), dim3(256), 0, stream, h, inter, act, q, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // K4: per-group colwise, single or dual.  The unit of work is a tile of 64
 // columns x 256 rows of one group: the device group table cuts every group's
 // rows into 256-row chunks, so a large group spreads over many workgroups

@@ -225,7 +225,7 @@ def test_fused_ffn_f8i4_mixtral_full_size(T, mixtral_weights):
     x = wl.normal_bf16((T, H), 1.0, 0, wl.T_X)
     w1_4, s1 = mg.quantize_int4_weights(w1d)
     w2_4, s2 = mg.quantize_int4_weights(w2d)
-    out, st = mg.fused_moe_f8i4(bf16_dev(x), w1_4, s1, w2_4, s2, dev(ids), dev(w))
+    out, st = mg.fused_moe_f8i4(bf16_dev(x), w1_4, s1, w2_4, s2, dev(ids), dev(w), keep_act=True)
     torch.cuda.synchronize()
     al, n = _check_permutation(st["permute"], ids, E, 16)
     sizes = al["padded_sizes"]
@@ -274,7 +274,7 @@ def test_fused_ffn_fp8_mixtral_full_size(T, mixtral_weights):
     x = wl.normal_bf16((T, H), 1.0, 0, wl.T_X)
     w1q, s1 = mg.quantize_fp8_expert_weights(w1d)
     w2q, s2 = mg.quantize_fp8_expert_weights(w2d)
-    out, st = mg.fused_moe_fp8(bf16_dev(x), w1q, s1, w2q, s2, dev(ids), dev(w))
+    out, st = mg.fused_moe_fp8(bf16_dev(x), w1q, s1, w2q, s2, dev(ids), dev(w), keep_act=True)
     torch.cuda.synchronize()
     bm = 16 if T * k <= 64 * E else 128
     al, n = _check_permutation(st["permute"], ids, E, bm)

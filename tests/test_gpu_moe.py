@@ -247,7 +247,7 @@ def test_fused_moe_f8i4_stages_match_the_oracle(T):
     W2 = wl.stacked_normal_bf16(E, (I, H), 0.05, 3, wl.T_W2)
     w1_4, s1 = mg.quantize_int4_weights(bf16_dev(W1))
     w2_4, s2 = mg.quantize_int4_weights(bf16_dev(W2))
-    out, st = mg.fused_moe_f8i4(bf16_dev(x), w1_4, s1, w2_4, s2, dev(ids), dev(w), block_m=bm)
+    out, st = mg.fused_moe_f8i4(bf16_dev(x), w1_4, s1, w2_4, s2, dev(ids), dev(w), block_m=bm, keep_act=True)
     torch.cuda.synchronize()
     p1, q1 = oracle.quant_int4(oracle.bf16_to_f64(W1), 128)
     p2, q2 = oracle.quant_int4(oracle.bf16_to_f64(W2), 128)
@@ -293,7 +293,7 @@ def test_fused_moe_fp8_stages_match_the_oracle(T):
     W2 = wl.stacked_normal_bf16(E, (I, H), 0.05, 5, wl.T_W2)
     w1q, s1 = mg.quantize_fp8_expert_weights(bf16_dev(W1))
     w2q, s2 = mg.quantize_fp8_expert_weights(bf16_dev(W2))
-    out, st = mg.fused_moe_fp8(bf16_dev(x), w1q, s1, w2q, s2, dev(ids), dev(w))
+    out, st = mg.fused_moe_fp8(bf16_dev(x), w1q, s1, w2q, s2, dev(ids), dev(w), keep_act=True)
     torch.cuda.synchronize()
     bm = 16 if T * k <= 64 * E else 128
     full = lambda n: np.full(E, n, np.int32)

@@ -169,3 +169,34 @@ def test_rowwise_gather_bit_exact(T, k, E, bm, cols):
     q_ref, s_ref = oracle.quant_rowwise(oracle.gather_rows(x, k, sids))
     np.testing.assert_array_equal(host(q), q_ref)
     np.testing.assert_array_equal(host(s), s_ref)
+
+
+@pytest.mark.parametrize("rows,inter", [(1, 8), (7, 1408), (300, 14336), (5, 16392), (3, 40000)])
+def test_silu_mul_quantize_rowwise_one_pass(rows, inter):
+    """SiLU*mul and rowwise e4m3 in one pass: codes and scales bit-exact
+    against the oracle's rowwise quantizer applied to the library's own
+    SiLU*mul output, and the same bits as silu_mul followed by
+    quantize_rowwise_fp8, with and without the bf16 activations written
+    out.  Rows of 16392 and 40000 values are longer than the registers
+    hold (the cast recomputes act from h); one row is zero, one spans
+    large magnitudes."""
+    g = wl.rng(60 + rows, wl.T_X)
+    h = wl.normal_bf16((rows, 2 * inter), 1.0, 60 + rows, wl.T_X)
+    hf = wl.bf16_bits_to_f32(h)
+    if rows > 2:
+        h[1] = 0
+        hf[2] *= np.float32(2.0) ** g.integers(-20, 20, size=2 * inter)
+        h[2] = wl.f32_to_bf16_bits(hf[2])
+    hd = bf16_dev(h)
+    act = mg.silu_mul(hd)
+    q2, s2 = mg.quantize_rowwise_fp8(act)
+    q1, s1 = mg.silu_mul_quantize_rowwise_fp8(hd)
+    act1 = torch.empty_like(act)
+    q3, s3 = mg.silu_mul_quantize_rowwise_fp8(hd, act=act1)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_rowwise(bf16_host(act))
+    np.testing.assert_array_equal(host(s1), s_ref)
+    np.testing.assert_array_equal(host(q1), q_ref)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    assert torch.equal(q1, q3) and torch.equal(s1, s3)
+    assert torch.equal(act1, act)
