@@ -7,26 +7,31 @@
 // builder (32-row tiles) times 32-column slices of N forms the work items;
 // empty experts never appear in it.
 //
-// The work is bound by streaming the int4 weights, so the kernel reads them
-// straight into registers in the layout of v_mfma_scale_f32_32x32x64_f8f6f4
-// (lane l: output column l % 32, a run of 32 consecutive k), turns each
-// nibble into the e4m3 code of the same integer (exact: -8..7 are e4m3
-// values) with two byte permutes, and runs the fp8 MFMA per 128-long K chunk
-// into a fresh accumulator that is then scaled by that chunk's bf16 weight
-// scale (keeping the dequantization exact) and added to the running sum.
+// The work is bound by streaming the int4 weights.  Each wave moves them
+// into its own LDS buffers by LDS-DMA, whole 128-byte lines of a column (two
+// K chunks) per lane group, so every load instruction covers 8 full lines,
+// not a 32-byte piece of 32 lines; the 16-byte slots of a line are XOR-
+// swizzled by the column so that the fragment reads below hit distinct
+// banks.  A fragment read gives each lane the layout of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (lane l: output column l % 32, a run of
+// 32 consecutive k); each nibble becomes the e4m3 code of the same integer
+// (exact: -8..7 are e4m3 values) with two byte permutes, and the fp8 MFMA
+// runs per 128-long K chunk into a fresh accumulator that is then scaled by
+// that chunk's bf16 weight scale (keeping the dequantization exact) and
+// added to the running sum.
 // The waves of a workgroup (8 for contractions of 64 or more chunks, else 4)
 // split K.  When the items are too few to give every slot of the grid one
 // (one or two routed rows over a narrow N), K is also split across
 // workgroups: each piece stores its fp32 partial tile in the workspace, and
 // the last piece to arrive adds them all in piece order (the same bits
-// whatever the arrival order) and writes the output.  Each wave requests the operands of its next chunk before it
-// computes the current one, so two chunks stream per wave; the loads' offsets
-// are opaque to the compiler, which would otherwise branch around the
-// out-of-range loads and drain every load in flight.  The partial tiles are
-// summed in LDS in wave order, divided by the row scale of the activations
-// and rounded to bf16.
-#include "kernels.h"
-#include "worklist.h"
+// whatever the arrival order) and writes the output.  Each wave requests the
+// operands of its next two chunks (a line per column) before it computes the
+// current two; the activation and scale loads' offsets are opaque to the
+// compiler, which would otherwise branch around the out-of-range loads and
+// drain every load in flight.  The partial tiles are summed in LDS (the
+// weight buffers, free after the K loop) in wave order, divided by the row
+// scale of the activations and rounded to bf16.
+#include "gemm_dev.h"
 
 namespace mg {
 
@@ -76,23 +81,51 @@ __device__ inline __amdgpu_buffer_rsrc_t f_rsrc(const void* base, int64_t bytes)
 }
 
 
-// One 128-long K chunk of a wave's work: the two 64-long halves of the
-// weight fragment (int4, 16 bytes each), the chunk's bf16 weight scale, and
-// the two matching fp8 activation fragments.
+// One 128-long K chunk of a wave's work in the register path: the two
+// 64-long halves of the weight fragment (int4, 16 bytes each), the chunk's
+// bf16 weight scale, and the two matching fp8 activation fragments.
 struct F8I4Chunk {
   i32x4 w[2];
   float sc;
   i32x8 x[2];
 };
 
+constexpr int F_LINE = 32 * 128;   // a wave's weight buffer: 32 columns x one 128-byte line (two K chunks)
+
+// The register operands of one line step (two 128-long K chunks) of a
+// wave's work: each chunk's bf16 weight scale and its two fp8 activation
+// fragments (64 k each).  The weights of the step are in LDS.
+struct F8I4Step {
+  float sc[2];
+  i32x8 x[2][2];
+};
+
+// The LDS-DMA asm takes its resource in SGPRs; it is workgroup-uniform.
+__device__ inline i32x4 f_uni4(i32x4 r) {
+  i32x4 u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
+}
+
 // F_WAVES waves per workgroup, each owning a contiguous run of K chunks: 8
 // for long contractions (many chunks per wave to keep streaming), 4
-// otherwise (less reduction work per tile).
-template <int F_WAVES>
+// otherwise (less reduction work per tile).  LDSW: the weights go through
+// LDS by DMA (4 waves: at 124-149 VGPRs the 8-wave workgroup would lose half
+// its occupancy to the extra activation registers, and measured slower),
+// else each lane loads its own column's fragments into registers.
+template <int F_WAVES, bool LDSW>
 __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
-  __shared__ float red[F_WAVES][F_BM * F_BN];
+  // LDSW: two weight buffers per wave; after the K loop the same memory
+  // holds the cross-wave reduction
+  constexpr int WL_BYTES = LDSW ? F_WAVES * 2 * F_LINE : F_WAVES * F_BM * F_BN * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t wl[WL_BYTES];
+  static_assert(WL_BYTES >= F_WAVES * F_BM * F_BN * 4, "the reduction fits the weight buffers");
+  float(*red)[F_BM * F_BN] = reinterpret_cast<float(*)[F_BM * F_BN]>(wl);
   __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int K = a.Kc;
   const int N = a.Nout;
   const int nchunk = K / 128;
@@ -121,8 +154,11 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
     if (S < 1) S = 1;
   }
   const int64_t units = items * S;
-  // chunk range of a wave: piece s, wave q -> run s * F_WAVES + q
-  const int per = (nchunk + S * F_WAVES - 1) / (S * F_WAVES);
+  // chunk range of a wave: piece s, wave q -> run s * F_WAVES + q (through
+  // LDS: of an even length, so that a wave's runs start on a line)
+  int per = (nchunk + S * F_WAVES - 1) / (S * F_WAVES);
+  if (LDSW) per = (per + 1) & ~1;
+  const uint32_t wlds = lds_address(wl) + (uint32_t)(wave * 2 * F_LINE);
   const __amdgpu_buffer_rsrc_t pr = f_rsrc(a.sk_part, units * (int64_t)(F_BM * F_BN * 4));
 
   int64_t first = blockIdx.x;
@@ -145,68 +181,159 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
     const int half = lane >> 5;
     const bool col_ok = n0 + col < N;
     const bool row_ok = col < m_valid;   // A fragment row = lane % 32
-    const __amdgpu_buffer_rsrc_t wr = f_rsrc(w4 + (int64_t)g * N * (K / 2), (int64_t)N * (K / 2));
-    const __amdgpu_buffer_rsrc_t sr = f_rsrc(a.s4 + (int64_t)g * nchunk * N, (int64_t)nchunk * N * 2);
-    const uint32_t wrow = (uint32_t)((n0 + col) * (K / 2));
-    const uint32_t xrow = (uint32_t)((row0 + col) * (int64_t)K);
-    const uint32_t srow = (uint32_t)((n0 + col) * 2);
-
-    // Requests every operand of chunk j (zeros past the wave's range).  The
-    // weights keep the default cache policy although they are read once: a
-    // lane's 16 bytes are a quarter of a 64-byte run whose 128-byte line the
-    // next chunk reads too, and non-temporal loads fetched such lines from
-    // HBM twice (measured: 1.9 -> 3.0 TB/s at 16 routed rows over 128
-    // experts).
-    auto load = [&](int j, F8I4Chunk& c) {
-      const bool live = j < j1;
-      // k = 128 j + 64 s + 32 half .. +32  ->  weight bytes (128 j + 64 s + 32 half) / 2
-      uint32_t wo = (live && col_ok) ? wrow + j * 64 + half * 16 : F_OOB;
-      asm volatile("" : "+v"(wo));   // opaque: no per-lane branch around the loads
-      c.w[0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
-      c.w[1] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 32, 0);
-      uint32_t so = (live && col_ok) ? srow + (uint32_t)j * (uint32_t)N * 2u : F_OOB;
-      asm volatile("" : "+v"(so));
-      c.sc = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)so, 0, 0));
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        uint32_t xo = (live && row_ok) ? xrow + j * 128 + sh * 64 + half * 32 : F_OOB;
-        asm volatile("" : "+v"(xo));
-        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 0, 0);
-        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 16, 0);
-        c.x[sh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    };
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-    // chunk product into a fresh accumulator, scaled by the chunk's weight
-    // scale and added to the running sum
-    auto compute = [&](const F8I4Chunk& c) {
-      f32x16 part;
+    if constexpr (LDSW) {
+      const i32x4 wrw = f_uni4(make_rsrc_words(w4 + (int64_t)g * N * (K / 2), (int64_t)N * (K / 2)));
+      const __amdgpu_buffer_rsrc_t sr = f_rsrc(a.s4 + (int64_t)g * nchunk * N, (int64_t)nchunk * N * 2);
+      const uint32_t xrow = (uint32_t)((row0 + col) * (int64_t)K);
+      const uint32_t srow = (uint32_t)((n0 + col) * 2);
+      // weight transfers: instruction i covers columns 8 i .. 8 i + 7, lane l
+      // the 16-byte slot l % 8 of column 8 i + l / 8's line, which holds part
+      // (l % 8) ^ (column % 8) of the column's 128 bytes
+      uint32_t dvo[4];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part[v] = 0.f;
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const uint4 wq = make_uint4((uint32_t)c.w[sh][0], (uint32_t)c.w[sh][1], (uint32_t)c.w[sh][2],
-                                    (uint32_t)c.w[sh][3]);
-        const i32x8 bf = i4x32_to_e4m3(wq);
-        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(c.x[sh], bf, part, 0, 0, 0, 127, 0, 127);
+      for (int i = 0; i < 4; ++i) {
+        const int dc = 8 * i + (lane >> 3);
+        const int part = (lane & 7) ^ (dc & 7);
+        dvo[i] = n0 + dc < N ? (uint32_t)((n0 + dc) * (K / 2) + part * 16) : F_OOB;
       }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] += part[v] * c.sc;
-    };
+      const int L0 = j0 >> 1, L1 = (j1 + 1) >> 1;   // the wave's lines
 
-    // Two chunks in flight: chunk j + 1's operands are requested before
-    // chunk j is computed, so each wave keeps its next weight run streaming
-    // while the MFMAs of the current one run.
-    F8I4Chunk c0, c1;
-    load(j0, c0);
-    for (int j = j0; j < j1; j += 2) {
-      load(j + 1, c1);
-      compute(c0);
-      load(j + 2, c0);
-      if (j + 1 < j1) compute(c1);
+      // Requests every operand of line L into buffer b (zeros past the wave's
+      // range): 4 weight transfers, then per chunk its scale and activations
+      // (14 vector-memory operations per lane).  The LDS reads of the line
+      // that last used buffer b are complete first.
+      auto issue = [&](int L, int b, F8I4Step& st) __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const bool live = L < L1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dma16<kPolicyStream>(wrw, wlds + (uint32_t)(b * F_LINE + i * 1024),
+                               live && dvo[i] != F_OOB ? dvo[i] + (uint32_t)L * 128u : F_OOB);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int j = 2 * L + c;
+          const bool cl = live && j < j1;
+          uint32_t so = (cl && col_ok) ? srow + (uint32_t)j * (uint32_t)N * 2u : F_OOB;
+          asm volatile("" : "+v"(so));
+          st.sc[c] = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)so, 0, 0));
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh) {
+            uint32_t xo = (cl && row_ok) ? xrow + j * 128 + sh * 64 + half * 32 : F_OOB;
+            asm volatile("" : "+v"(xo));
+            const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 0, 0);
+            const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 16, 0);
+            st.x[c][sh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
+      };
+      // line L from buffer b: per chunk, the product into a fresh
+      // accumulator, scaled by the chunk's weight scale and added to the
+      // running sum; a chunk past the wave's range (the second half of its
+      // last line) is skipped
+      const uint8_t* wbuf = wl + wave * 2 * F_LINE;
+      auto compute = [&](int L, int b, const F8I4Step& st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if (2 * L + c >= j1) break;
+          f32x16 part;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) part[v] = 0.f;
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh) {
+            const int p = c * 4 + sh * 2 + half;
+            const i32x4 w = *reinterpret_cast<const i32x4*>(wbuf + b * F_LINE + col * 128 + ((p ^ (col & 7)) << 4));
+            const uint4 wq = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
+            const i32x8 bf = i4x32_to_e4m3(wq);
+            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(st.x[c][sh], bf, part, 0, 0, 0, 127, 0, 127);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[v] += part[v] * st.sc[c];
+        }
+      };
+
+      // Two lines in flight: line L + 1's operands are requested before line L
+      // is computed.  Before a line's fragments are read, only the next line's
+      // 14 operations may still be in flight (loads retire in order).
+      F8I4Step s0, s1;
+      issue(L0, 0, s0);
+      for (int L = L0; L < L1; L += 2) {
+        issue(L + 1, 1, s1);
+        asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+        compute(L, 0, s0);
+        issue(L + 2, 0, s0);
+        if (L + 1 < L1) {
+          asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+          compute(L + 1, 1, s1);
+        }
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t wr = f_rsrc(w4 + (int64_t)g * N * (K / 2), (int64_t)N * (K / 2));
+      const __amdgpu_buffer_rsrc_t sr = f_rsrc(a.s4 + (int64_t)g * nchunk * N, (int64_t)nchunk * N * 2);
+      const uint32_t wrow = (uint32_t)((n0 + col) * (K / 2));
+      const uint32_t xrow = (uint32_t)((row0 + col) * (int64_t)K);
+      const uint32_t srow = (uint32_t)((n0 + col) * 2);
+
+      // Requests every operand of chunk j (zeros past the wave's range).  The
+      // weights keep the default cache policy although they are read once: a
+      // lane's 16 bytes are a quarter of a 64-byte run whose 128-byte line the
+      // next chunk reads too, and non-temporal loads fetched such lines from
+      // HBM twice (measured: 1.9 -> 3.0 TB/s at 16 routed rows over 128
+      // experts).
+      auto load = [&](int j, F8I4Chunk& c) {
+        const bool live = j < j1;
+        // k = 128 j + 64 s + 32 half .. +32  ->  weight bytes (128 j + 64 s + 32 half) / 2
+        uint32_t wo = (live && col_ok) ? wrow + j * 64 + half * 16 : F_OOB;
+        asm volatile("" : "+v"(wo));   // opaque: no per-lane branch around the loads
+        c.w[0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
+        c.w[1] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 32, 0);
+        uint32_t so = (live && col_ok) ? srow + (uint32_t)j * (uint32_t)N * 2u : F_OOB;
+        asm volatile("" : "+v"(so));
+        c.sc = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)so, 0, 0));
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          uint32_t xo = (live && row_ok) ? xrow + j * 128 + sh * 64 + half * 32 : F_OOB;
+          asm volatile("" : "+v"(xo));
+          const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 0, 0);
+          const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 16, 0);
+          c.x[sh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      };
+      // chunk product into a fresh accumulator, scaled by the chunk's weight
+      // scale and added to the running sum
+      auto compute = [&](const F8I4Chunk& c) {
+        f32x16 part;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[v] = 0.f;
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const uint4 wq = make_uint4((uint32_t)c.w[sh][0], (uint32_t)c.w[sh][1], (uint32_t)c.w[sh][2],
+                                      (uint32_t)c.w[sh][3]);
+          const i32x8 bf = i4x32_to_e4m3(wq);
+          part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(c.x[sh], bf, part, 0, 0, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] += part[v] * c.sc;
+      };
+
+      // Two chunks in flight: chunk j + 1's operands are requested before
+      // chunk j is computed, so each wave keeps its next weight run streaming
+      // while the MFMAs of the current one run.
+      F8I4Chunk c0, c1;
+      load(j0, c0);
+      for (int j = j0; j < j1; j += 2) {
+        load(j + 1, c1);
+        compute(c0);
+        load(j + 2, c0);
+        if (j + 1 < j1) compute(c1);
+      }
     }
+    // every transfer of this wave has landed, and every wave is done with
+    // its weight buffers, before they hold the reduction
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 
     // cross-wave reduction of the K slices, in a fixed order
 #pragma unroll
@@ -282,9 +409,9 @@ hipError_t launch_f8i4(const GemmArgs& a, int64_t cap_entries, hipStream_t strea
   // routed row over 128 experts, K=5120, N=8192: 19.4 -> 26.8 us).
   const int grid = (int)(max_items < slots ? max_items : slots);
   if (wide)
-    hipLaunchKernelGGL(f8i4_kernel<8>, dim3(grid), dim3(8 * 64), (size_t)table_lds_bytes(a.E), stream, a);
+    hipLaunchKernelGGL((f8i4_kernel<8, false>), dim3(grid), dim3(8 * 64), (size_t)table_lds_bytes(a.E), stream, a);
   else
-    hipLaunchKernelGGL(f8i4_kernel<4>, dim3(grid), dim3(4 * 64), (size_t)table_lds_bytes(a.E), stream, a);
+    hipLaunchKernelGGL((f8i4_kernel<4, true>), dim3(grid), dim3(4 * 64), (size_t)table_lds_bytes(a.E), stream, a);
   return hipGetLastError();
 }
 
