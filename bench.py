@@ -507,6 +507,9 @@ def _row_cases(torch, mg):
     x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
     w1 = (torch.randn(E, H, 2 * I, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
     w2 = (torch.randn(E, I, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    # the bf16 expert GEMMs take the weights in the (E, N, K) layout of the
+    # applied-ai page's fused_moe_kernel: W1 as [E, 2I, H], W2 as [E, H, I]
+    w1n, w2n = w1.transpose(1, 2).contiguous(), w2.transpose(1, 2).contiguous()
     logits = torch.randn(T, E, generator=g, device="cuda")
     yield ("A0_route_topk", f"router: fp32 softmax + top-{k} of {T}x{E} logits (renormalized)",
            lambda: mg.route_topk(logits, k, renormalize=True), T * E * 4 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
@@ -520,33 +523,36 @@ def _row_cases(torch, mg):
     xs, psz, sids = p["x_sorted"], p["padded_sizes"], p["sorted_token_ids"]
     wsf = mg.workspace(E, xs.shape[0])
     h1 = torch.empty(xs.shape[0], 2 * I, dtype=torch.bfloat16, device="cuda")
-    yield ("A10_gemm1", f"H1 = X[sorted_ids / {k}] . W1_e (gather in the A load), {ntpp} padded rows, K={H}, "
-                        f"N={2 * I} (useful flops of {T * k} rows)",
-           lambda: mg.gmm_fwd_gather(x, sids, k, w1, psz, out=h1, ws=wsf), 2.0 * T * k * H * 2 * I, "TFLOP/s",
-           PEAK_BF16_TFLOPS, 5)
+    yield ("A10_gemm1", f"H1 = X[sorted_ids / {k}] . W1_e (gather in the A load; W1 as [E, 2I, H]), {ntpp} padded "
+                        f"rows, K={H}, N={2 * I} (useful flops of {T * k} rows)",
+           lambda: mg.gmm_fwd_gather(x, sids, k, w1n, psz, trans_b=True, out=h1, ws=wsf), 2.0 * T * k * H * 2 * I,
+           "TFLOP/s", PEAK_BF16_TFLOPS, 5)
     act = torch.empty(xs.shape[0], I, dtype=torch.bfloat16, device="cuda")
     yield ("A10_A11_gemm1_silu_fused", f"act = silu*mul(X[sorted_ids / {k}] . W1_e) in one kernel (what the fused path "
-                                       f"runs), {ntpp} padded rows, K={H}, 2I={2 * I} (useful flops of {T * k} rows)",
-           lambda: mg.gmm_fwd_silu_mul(x, w1, psz, sorted_token_ids=sids, top_k=k, out=act, ws=wsf),
+                                       f"runs; W1 as [E, 2I, H]), {ntpp} padded rows, K={H}, 2I={2 * I} (useful flops "
+                                       f"of {T * k} rows)",
+           lambda: mg.gmm_fwd_silu_mul(x, w1n, psz, sorted_token_ids=sids, top_k=k, trans_b=True, out=act, ws=wsf),
            2.0 * T * k * H * 2 * I, "TFLOP/s", PEAK_BF16_TFLOPS, 5)
     yield ("A11_silu_mul", f"silu(H1[:, :I]) * H1[:, I:], {xs.shape[0]} rows, I={I}",
            lambda: mg.silu_mul(h1, out=act), xs.shape[0] * I * 6, "GB/s", PEAK_HBM_GBS, 10)
     y2 = torch.empty(xs.shape[0], H, dtype=torch.bfloat16, device="cuda")
-    yield ("A12_gemm2", f"Y2 = act . W2_e, K={I}, N={H} (useful flops of {T * k} rows)",
-           lambda: mg.gmm_fwd(act, w2, psz, out=y2, ws=wsf), 2.0 * T * k * I * H, "TFLOP/s", PEAK_BF16_TFLOPS, 5)
+    yield ("A12_gemm2", f"Y2 = act . W2_e (W2 as [E, H, I]), K={I}, N={H} (useful flops of {T * k} rows)",
+           lambda: mg.gmm_fwd(act, w2n, psz, trans_b=True, out=y2, ws=wsf), 2.0 * T * k * I * H, "TFLOP/s",
+           PEAK_BF16_TFLOPS, 5)
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     yield ("A13_moe_unpermute", f"top-{k} weighted combine of {T * k} rows, hidden {H}",
            lambda: mg.moe_unpermute(y2, p["inv"], wts, T, k, out=out),
            T * k * H * 2 + T * H * 2 + T * k * 8, "GB/s", PEAK_HBM_GBS, 10)
-    yield ("C3_fused_ffn_T4096", "align -> gathered GEMM1 with SiLU*mul epilogue -> GEMM2 -> combine, end to end",
-           lambda: mg.fused_moe(x, w1, w2, ids, wts, block_m=bm, ws=wsf), 2.0 * T * k * H * 3 * I,
+    yield ("C3_fused_ffn_T4096", "align -> gathered GEMM1 with SiLU*mul epilogue -> GEMM2 -> combine, end to end "
+                                 "(weights in the (E, N, K) layout)",
+           lambda: mg.fused_moe(x, w1n, w2n, ids, wts, block_m=bm, ws=wsf, trans_b=True), 2.0 * T * k * H * 3 * I,
            "TFLOP/s", PEAK_BF16_TFLOPS, 3)
     for Tsmall in (1, 64):
         sub_ids, sub_w = ids[:Tsmall].contiguous(), wts[:Tsmall].contiguous()
         xsub = x[:Tsmall].contiguous()
         experts = int(torch.unique(sub_ids).numel())
         yield (f"C3_fused_ffn_T{Tsmall}", f"end to end, {experts} experts touched: weight bytes of those experts",
-               lambda: mg.fused_moe(xsub, w1, w2, sub_ids, sub_w, ws=wsf),
+               lambda: mg.fused_moe(xsub, w1n, w2n, sub_ids, sub_w, ws=wsf, trans_b=True),
                experts * (H * 2 * I + I * H) * 2, "GB/s", PEAK_HBM_GBS, 5)
     # the same FFN with e4m3 expert weights (one scale per expert and output
     # column) and e4m3 activations

@@ -187,7 +187,9 @@ int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids,
  * with A[r, :] = x[sorted_token_ids[r] / top_k, :] (zero row for ids
  * >= T*top_k) when sorted_token_ids is non-NULL, else x[r, :].
  *   x     bf16 [T, K] (gathered) or [total_M, K] row-major
- *   w1    bf16 [E, K, 2I] (gate columns 0..I-1, up columns I..2I-1)
+ *   w1    bf16 [E, K, 2I] (gate columns 0..I-1, up columns I..2I-1), or
+ *         with trans_b, [E, 2I, K] (gate rows 0..I-1, up rows I..2I-1: the
+ *         (E, N, K) weight layout of [FMOE] fused_moe_kernel)
  *   act   bf16 [total_M, I]; rows past the groups untouched
  * The same bits as gmm_fwd (or gmm_fwd_gather) into h followed by silu_mul
  * whenever neither launch splits a tile along K; where the stream-K tail
@@ -197,7 +199,8 @@ int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids,
 int gmm_fwd_silu_mul(const void* x, int64_t T, const int32_t* sorted_token_ids,
                      int32_t top_k, const void* w1, const int32_t* group_sizes,
                      int32_t E, int64_t total_M, int32_t K, int32_t I,
-                     void* act, void* ws, size_t ws_bytes, mg_stream_t stream);
+                     int32_t trans_b, void* act, void* ws, size_t ws_bytes,
+                     mg_stream_t stream);
 
 /* Backward of gmm_fwd for an upstream gradient dy [total_M, N]:
  *   dx[r, :] = dy[r, :] . W[g(r)]^T          (bf16 [total_M, K]; may be NULL)

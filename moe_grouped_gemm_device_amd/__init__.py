@@ -45,7 +45,7 @@ _SIGS = {
     "gmm_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P]),
     "gmm_fwd_gather": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
-    "gmm_fwd_silu_mul": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "gmm_fwd_silu_mul": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "gmm_fwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_bwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
@@ -247,15 +247,20 @@ def gmm_fwd_gather(x, sorted_token_ids, top_k, w, group_sizes, trans_b=False, ou
     return y
 
 
-def gmm_fwd_silu_mul(x, w1, group_sizes, sorted_token_ids=None, top_k=1, out=None, ws=None, stream=None):
+def gmm_fwd_silu_mul(x, w1, group_sizes, sorted_token_ids=None, top_k=1, trans_b=False, out=None, ws=None,
+                     stream=None):
     """act = silu(h[:, :I]) * h[:, I:] with h = A @ w1[g] rounded to bf16,
-    in one kernel (w1 [E, K, 2I]).  A is x (one row per output row) or, with
-    sorted_token_ids, x[sorted_token_ids // top_k] with zero padding rows."""
+    in one kernel (w1 [E, K, 2I], or [E, 2I, K] with trans_b).  A is x (one
+    row per output row) or, with sorted_token_ids, x[sorted_token_ids //
+    top_k] with zero padding rows."""
     _need(x, torch.bfloat16, "x", 2)
     _need(w1, torch.bfloat16, "w1", 3)
     _need(group_sizes, torch.int32, "group_sizes", 1)
     T, K = x.shape
-    E, K2, N2 = w1.shape
+    if trans_b:
+        E, N2, K2 = w1.shape
+    else:
+        E, K2, N2 = w1.shape
     if K2 != K or N2 % 2 or group_sizes.numel() != E:
         raise ValueError("shape mismatch between x, w1 and group_sizes")
     I = N2 // 2
@@ -270,7 +275,7 @@ def gmm_fwd_silu_mul(x, w1, group_sizes, sorted_token_ids=None, top_k=1, out=Non
         raise ValueError("out must be [rows, I]")
     ws = default_workspace(x.device, stream) if ws is None else ws
     _call("gmm_fwd_silu_mul", _ptr(x), T, _ptr(sorted_token_ids), int(top_k), _ptr(w1), _ptr(group_sizes), E, M,
-          K, I, _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
+          K, I, int(bool(trans_b)), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
     return y
 
 
@@ -616,10 +621,11 @@ def silu_mul_quantize_rowwise_fp8(h, q=None, scales=None, act=None, stream=None)
     return q, scales
 
 
-def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, ws=None, stream=None):
+def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, ws=None, stream=None, trans_b=False):
     """Token-sorted MoE expert FFN: align -> gmm(W1) over the token rows
     looked up through the sorted order, with SiLU*mul in its epilogue ->
-    gmm(W2) -> top-k weighted combine.  w1 [E, H, 2I], w2 [E, I, H] bf16."""
+    gmm(W2) -> top-k weighted combine.  w1 [E, H, 2I], w2 [E, I, H] bf16,
+    or with trans_b w1 [E, 2I, H], w2 [E, H, I] (the (E, N, K) layout)."""
     T, k = topk_ids.shape
     E = w1.shape[0]
     if block_m is None:
@@ -630,6 +636,6 @@ def fused_moe(x, w1, w2, topk_ids, topk_weights, block_m=None, ws=None, stream=N
     ws = default_workspace(x.device, stream) if ws is None else ws
     # GEMM1 reads the token rows through the sorted order (no sorted copy)
     # and applies SiLU-and-mul in its epilogue (no [rows, 2I] intermediate)
-    act = gmm_fwd_silu_mul(x, w1, sizes, sorted_token_ids=ids, top_k=k, ws=ws, stream=stream)
-    y2 = gmm_fwd(act, w2, sizes, ws=ws, stream=stream)
+    act = gmm_fwd_silu_mul(x, w1, sizes, sorted_token_ids=ids, top_k=k, trans_b=trans_b, ws=ws, stream=stream)
+    y2 = gmm_fwd(act, w2, sizes, trans_b=trans_b, ws=ws, stream=stream)
     return moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream), p

@@ -281,8 +281,8 @@ int gmm_fwd_gather(const void* x, int64_t T, const int32_t* sorted_token_ids, in
 }
 
 int gmm_fwd_silu_mul(const void* x, int64_t T, const int32_t* sorted_token_ids, int32_t top_k, const void* w1,
-                     const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K, int32_t I, void* act,
-                     void* ws, size_t ws_bytes, mg_stream_t stream) {
+                     const int32_t* group_sizes, int32_t E, int64_t total_M, int32_t K, int32_t I, int32_t trans_b,
+                     void* act, void* ws, size_t ws_bytes, mg_stream_t stream) {
   int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
   if (rc) return rc;
   if (K < 1 || I < 1) return fail(MG_EINVAL, "K and I must be positive");
@@ -306,7 +306,9 @@ int gmm_fwd_silu_mul(const void* x, int64_t T, const int32_t* sorted_token_ids, 
     a.gather_limit = (int32_t)(T * top_k);
   }
   a.B = w1;
-  a.b_ld = 2 * (int64_t)I;       // W1[g, k, n]: gate columns 0..I-1, up columns I..2I-1
+  // W1[g, k, n]: gate columns 0..I-1, up columns I..2I-1; with trans_b,
+  // W1[g, n, k]: gate rows 0..I-1, up rows I..2I-1
+  a.b_ld = trans_b ? (int64_t)K : 2 * (int64_t)I;
   a.b_gs = (int64_t)K * 2 * I;
   a.C = act;
   a.c_ld = I;
@@ -321,7 +323,7 @@ int gmm_fwd_silu_mul(const void* x, int64_t T, const int32_t* sorted_token_ids, 
   L.kind = FIXED_M;
   L.elem = EL_BF16;
   L.a_kc = true;
-  L.b_kc = false;
+  L.b_kc = trans_b != 0;
   L.swiglu = true;
   return hip_status(launch_gemm(L, a, S(stream)), "gmm_fwd_silu_mul");
 }

@@ -102,6 +102,18 @@ struct KcTile {
       voff[i] = row < rows_valid ? (uint32_t)(row * ld * T::ESZ + chunk_of(wave, lane, i) * 16) : kOOB;
     }
   }
+  // Paired rows: the first R / 2 rows of the tile are rows 0.. of the
+  // operand (from the tile origin), the last R / 2 are rows half_off + R / 2..
+  // (the up rows of a fused gate/up weight stored as [2I, K]); a row pair
+  // exists when its first-half row is below rows_valid.
+  __device__ inline void setup_paired(int wave, int lane, int64_t ld, int rows_valid, int half_off) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int row = row_of(wave, lane, i);
+      const int src = row + (row >= R / 2 ? half_off : 0);
+      voff[i] = row % (R / 2) < rows_valid ? (uint32_t)(src * ld * T::ESZ + chunk_of(wave, lane, i) * 16) : kOOB;
+    }
+  }
   // The same with the tile's rows looked up: row r is source row
   // ids[r] / div, or zeros when ids[r] >= limit (the source holds fewer
   // than 2^31 bytes, checked on the host).  The 8 ids of a DMA block are
@@ -244,7 +256,7 @@ __global__ void __launch_bounds__(NW * 64) gmm_kernel(GemmArgs a) {
   // epilogues that apply fp8 scales; EPI_SWIGLU pairs gate and up columns
   constexpr bool SCALED = EPI == EPI_ROW_COL || EPI == EPI_GROUP;
   constexpr bool SWIGLU = EPI == EPI_SWIGLU;
-  static_assert(!SWIGLU || (KIND == FIXED_M && ELEM == EL_BF16 && !B_KC && NW == 8 && BN == 256 && BM == 128),
+  static_assert(!SWIGLU || (KIND == FIXED_M && ELEM == EL_BF16 && NW == 8 && BN == 256 && BM == 128),
                 "the paired gate/up epilogue is built for bf16 fixed-M 128 x 256 tiles with B as [K, N]");
   constexpr int BNE = SWIGLU ? BN / 2 : BN;   // output columns per tile
   constexpr int SC_BYTES = SCALED ? (BM + BN) * 4 : 0;
@@ -1080,7 +1092,7 @@ hipError_t launch_gemm(const GemmLaunch& L, const GemmArgs& a, hipStream_t strea
     if (L.kind == FIXED_M) {
       if (!L.a_kc) return hipErrorInvalidValue;
       if (L.swiglu) {
-        if (L.b_kc) return hipErrorInvalidValue;
+        if (L.b_kc) return launch_one<128, 256, 3, true, true, FIXED_M, EL_BF16, EPI_SWIGLU, kGemmWaves>(a, stream);
         return launch_one<128, 256, 3, true, false, FIXED_M, EL_BF16, EPI_SWIGLU, kGemmWaves>(a, stream);
       }
       if (L.b_kc) return launch_one<128, 256, 3, true, true, FIXED_M, EL_BF16, EPI_NONE, kGemmWaves>(a, stream);

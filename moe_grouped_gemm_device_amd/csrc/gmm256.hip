@@ -6,8 +6,11 @@
 // Optimization for Sparse M": only non-empty groups own work), for launches
 // with enough rows per group that 256-row tiles stay mostly full:
 //   bf16 fixed-M, B as [K, N] or [N, K], optionally with the A rows taken
-//   through the token-sorted index and/or the SiLU*mul epilogue ([FMOE]);
-//   e4m3 fixed-M with per-row and per-column scales ([FP8]).
+//   through the token-sorted index and/or the SiLU*mul epilogue
+//   (applied-ai issue "Column-major fused MoE": fused_moe_kernel and
+//   silu_and_mul), the gate and up halves of B as column or row blocks;
+//   e4m3 fixed-M with per-row and per-column scales (torchao commit
+//   "Optimize FP8 MoE backward pass": the rowwise scaled operands).
 //
 // Design (CDNA4):
 //  * 256 threads = 4 waves in a 2 x 2 arrangement; a wave owns a 128 x 128
@@ -118,7 +121,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr bool PIECES = DK || TSPLIT;
   static_assert(ELEM == EL_BF16 || (B_KC && SCALED), "fp8: both operands k-contiguous, scaled");
   static_assert(!DK || (ELEM == EL_FP8 && EPI == EPI_GROUP), "dynamic-K: e4m3 with per-group scales");
-  static_assert(!SWIGLU || (ELEM == EL_BF16 && !B_KC), "paired gate/up epilogue: bf16, B as [K, N]");
+  static_assert(!SWIGLU || ELEM == EL_BF16, "paired gate/up epilogue: bf16");
   static_assert(ELEM == EL_FP8 || EPI == EPI_NONE || SWIGLU, "bf16 epilogues");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
@@ -377,7 +380,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         int c;
         const int row = kc_row(ln, q, c);
         chunks |= (uint32_t)c << (2 * (4 + q));
-        voB[q] = row < it.n_valid ? (uint32_t)row * b_row + (uint32_t)(c * 16) : kOOB;
+        if constexpr (SWIGLU) {
+          // gate rows n0.. in tile rows 0..127, up rows I + n0.. in 128..255
+          const int src = row + (row >= BNE ? a.Nout - BNE : 0);
+          voB[q] = (row & (BNE - 1)) < it.n_valid ? (uint32_t)src * b_row + (uint32_t)(c * 16) : kOOB;
+        } else {
+          voB[q] = row < it.n_valid ? (uint32_t)row * b_row + (uint32_t)(c * 16) : kOOB;
+        }
       } else {
         // 32 contraction rows of 512 bytes; instruction i covers rows 2i, 2i+1
         const int i = 4 * wave + q;
@@ -1067,7 +1076,10 @@ bool gemm256_eligible(const GemmLaunch& L, const GemmArgs& a) {
 
 hipError_t launch_gemm256(const GemmLaunch& L, const GemmArgs& a, hipStream_t stream) {
   if (L.elem == EL_BF16) {
-    if (L.swiglu) return launch_256<false, EL_BF16, EPI_SWIGLU, FIXED_M>(a, stream);
+    if (L.swiglu) {
+      if (L.b_kc) return launch_256<true, EL_BF16, EPI_SWIGLU, FIXED_M>(a, stream);
+      return launch_256<false, EL_BF16, EPI_SWIGLU, FIXED_M>(a, stream);
+    }
     if (L.b_kc) return launch_256<true, EL_BF16, EPI_NONE, FIXED_M>(a, stream);
     return launch_256<false, EL_BF16, EPI_NONE, FIXED_M>(a, stream);
   }

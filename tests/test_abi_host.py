@@ -166,14 +166,14 @@ def test_gathered_and_silu_gemms_reject_bad_arguments(lib):
     assert g(32, 2, _p(FAKE), 60, 64, need) == mg.MG_EUNSUPPORTED         # K % 8
     assert g(32, 2, _p(FAKE), 64, 64, need - 1) == mg.MG_EWORKSPACE
     assert g(1 << 20, 2, _p(FAKE), 4096, 64, need) == mg.MG_EUNSUPPORTED  # x past 2 GiB
-    # gmm_fwd_silu_mul(x, T, ids, top_k, w1, sizes, E, total_M, K, I, act, ws, ws_bytes, stream)
-    s = lambda ids, k, K, I, wsb: lib.gmm_fwd_silu_mul(_p(FAKE), 32, ids, k, _p(FAKE), _p(FAKE), 4, 64, K, I,
+    # gmm_fwd_silu_mul(x, T, ids, top_k, w1, sizes, E, total_M, K, I, trans_b, act, ws, ws_bytes, stream)
+    s = lambda ids, k, K, I, wsb: lib.gmm_fwd_silu_mul(_p(FAKE), 32, ids, k, _p(FAKE), _p(FAKE), 4, 64, K, I, 0,
                                                       _p(FAKE), ws, wsb, None)
     assert s(None, 1, 64, 36, need) == mg.MG_EUNSUPPORTED                 # I % 8
     assert s(None, 1, 0, 64, need) == mg.MG_EINVAL                        # K = 0
     assert s(_p(FAKE), 0, 64, 64, need) == mg.MG_EINVAL                   # gathered, top_k < 1
     assert s(None, 1, 64, 64, need - 1) == mg.MG_EWORKSPACE
-    assert lib.gmm_fwd_silu_mul(None, 32, None, 1, _p(FAKE), _p(FAKE), 4, 64, 64, 64, _p(FAKE), ws, need,
+    assert lib.gmm_fwd_silu_mul(None, 32, None, 1, _p(FAKE), _p(FAKE), 4, 64, 64, 64, 1, _p(FAKE), ws, need,
                                 None) == mg.MG_EINVAL                   # no x
 
 

@@ -160,7 +160,8 @@ def _check_permutation(p, ids, E, bm):
 @pytest.mark.parametrize("T", [1, 64, 4096])   # block_m 16, 16 and 128 (the benchmarked launch)
 def test_fused_ffn_mixtral_full_size(T, mixtral_weights):
     """fused_moe at the Mixtral shapes, every output element: the product
-    path equals its stages run one at a time (bitwise), and each stage --
+    path equals its stages run one at a time and the same path with the
+    weights in the (E, N, K) layout (bitwise), and each stage --
     alignment, GEMM1 over the gathered rows, SiLU*mul, GEMM2, combine -- is
     checked against the oracle fed the library's input to that stage; at
     T <= 64 also the whole output against the oracle's own chain."""
@@ -177,8 +178,14 @@ def test_fused_ffn_mixtral_full_size(T, mixtral_weights):
     act_u = mg.silu_mul(h)
     y2 = mg.gmm_fwd(act, w2d, sizes)
     out2 = mg.moe_unpermute(y2, p["inv"], wd, T, k)
+    # the same weights in the (E, N, K) layout -- the launch bench.py times
+    # -- give the same bits
+    w1t, w2t = w1d.transpose(1, 2).contiguous(), w2d.transpose(1, 2).contiguous()
+    out_t, _ = mg.fused_moe(xd, w1t, w2t, idsd, wd, trans_b=True)
     torch.cuda.synchronize()
+    del w1t, w2t
     assert torch.equal(out, out2)
+    assert torch.equal(out, out_t)
     al, n = _check_permutation(p, ids, E, bm)
     sz = al["padded_sizes"]
     hh, acth, actuh, y2h = bf16_host(h)[:n], bf16_host(act)[:n], bf16_host(act_u)[:n], bf16_host(y2)[:n]

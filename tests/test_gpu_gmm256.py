@@ -131,22 +131,25 @@ def test_fp8_dw_skewed_groups():
     assert (dwh[1] == 0).all()
 
 
-def test_gathered_rows_and_silu_mul_epilogue():
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_gathered_rows_and_silu_mul_epilogue(trans_b):
     """The token-sorted GEMM1: A rows through sorted_token_ids / top_k with
     zero rows for the padding sentinel, against the oracle on the gathered
     rows; and the same with SiLU*mul in the epilogue (gate and up columns of
     one 256-column tile), against the oracle's GEMM rounded to bf16 and
-    passed through its SiLU*mul."""
+    passed through its SiLU*mul.  With trans_b the weights are [E, 2I, H]
+    (gate rows, then up rows)."""
     T, k, E, H, I = 4096, 2, 8, 1032, 1600
     x = wl.normal_bf16((T, H), 1.0, 43, wl.T_X)
     W1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.05, 43, wl.T_W)
     ids, _ = wl.softmax_topk_routing(T, E, k, 43)
-    xd, w1d = bf16_dev(x), bf16_dev(W1)
+    xd = bf16_dev(x)
+    w1d = bf16_dev(np.ascontiguousarray(np.transpose(W1, (0, 2, 1))) if trans_b else W1)
     p = mg.moe_permute(dev(ids), E, 128)
     sids, sizes = p["sorted_token_ids"], p["padded_sizes"]
-    h = mg.gmm_fwd_gather(xd, sids, k, w1d, sizes)
+    h = mg.gmm_fwd_gather(xd, sids, k, w1d, sizes, trans_b=trans_b)
     _wide()
-    act = mg.gmm_fwd_silu_mul(xd, w1d, sizes, sorted_token_ids=sids, top_k=k)
+    act = mg.gmm_fwd_silu_mul(xd, w1d, sizes, sorted_token_ids=sids, top_k=k, trans_b=trans_b)
     _wide()
     torch.cuda.synchronize()
     sz = sizes.cpu().numpy()

@@ -114,9 +114,13 @@ def test_fused_moe_small_matches_oracle(T, bm):
     w1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.05, 0, wl.T_W1)
     w2 = wl.stacked_normal_bf16(E, (I, H), 0.05, 0, wl.T_W2)
     out, _ = mg.fused_moe(bf16_dev(x), bf16_dev(w1), bf16_dev(w2), dev(ids), dev(w), block_m=bm)
+    # the same weights in the (E, N, K) layout give the same bits
+    t = lambda a: bf16_dev(np.ascontiguousarray(np.transpose(a, (0, 2, 1))))
+    out_t, _ = mg.fused_moe(bf16_dev(x), t(w1), t(w2), dev(ids), dev(w), block_m=bm, trans_b=True)
     torch.cuda.synchronize()
     ref, _ = oracle.fused_moe(x, w1, w2, ids, w, bm)
     assert_close(oracle.bf16_to_f64(bf16_host(out)), ref, BF16_TOL, CHAIN_ELEM)
+    assert torch.equal(out, out_t)
 
 
 @pytest.mark.parametrize("T,k,E,bm,K,N,trans_b", [
@@ -156,7 +160,8 @@ def test_gmm_fwd_gather_equals_the_sorted_copy(T, k, E, bm, K, N, trans_b):
     dict(E=64, T=300, k=6, bm=32, K=200, I=392, gather=True),
     dict(E=8, T=1500, k=2, bm=128, K=512, I=1024, gather=True),
 ])
-def test_gmm_fwd_silu_mul_equals_the_unfused_steps(case):
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_gmm_fwd_silu_mul_equals_the_unfused_steps(case, trans_b):
     """The GEMM with SiLU-and-mul in its epilogue is bit-identical to the GEMM
     into h followed by the silu_mul kernel, with and without the gathered A
     rows (at these shapes every tile is whole, so both kernels sum each
@@ -164,10 +169,11 @@ def test_gmm_fwd_silu_mul_equals_the_unfused_steps(case):
     split points differ between the two and only the oracle bars hold), and
     matches the oracle's silu_mul of the oracle GEMM rounded to bf16 (both
     halves are rounded to bf16 before SiLU*mul, as the fused path stores
-    them)."""
+    them).  With trans_b the weights are [E, 2I, K]: gate rows, then up
+    rows."""
     E, K, I = case["E"], case["K"], case["I"]
     W1 = wl.stacked_normal_bf16(E, (K, 2 * I), 0.3, 11, wl.T_W1)
-    w1 = bf16_dev(W1)
+    w1 = bf16_dev(np.ascontiguousarray(np.transpose(W1, (0, 2, 1))) if trans_b else W1)
     if case["gather"]:
         T, k, bm = case["T"], case["k"], case["bm"]
         rng = np.random.default_rng(T)
@@ -175,8 +181,8 @@ def test_gmm_fwd_silu_mul_equals_the_unfused_steps(case):
         x = wl.normal_bf16((T, K), 1.0, 11, wl.T_X)
         p = mg.moe_permute(dev(ids), E, bm)
         sizes, sids = p["padded_sizes"], p["sorted_token_ids"]
-        h = mg.gmm_fwd_gather(bf16_dev(x), sids, k, w1, sizes)
-        act = mg.gmm_fwd_silu_mul(bf16_dev(x), w1, sizes, sorted_token_ids=sids, top_k=k)
+        h = mg.gmm_fwd_gather(bf16_dev(x), sids, k, w1, sizes, trans_b=trans_b)
+        act = mg.gmm_fwd_silu_mul(bf16_dev(x), w1, sizes, sorted_token_ids=sids, top_k=k, trans_b=trans_b)
         n = int(host(p["num_tokens_post_padded"])[0])
         al = oracle.moe_align(ids, E, bm)
         xa = oracle.gather_rows(x, k, al["sorted_token_ids"])[:n]
@@ -186,8 +192,8 @@ def test_gmm_fwd_silu_mul_equals_the_unfused_steps(case):
         osz = wl.random_group_sizes(E, M, 11, zero_frac=0.25)
         x = wl.normal_bf16((M, K), 1.0, 11, wl.T_X)
         sizes = dev(osz)
-        h = mg.gmm_fwd(bf16_dev(x), w1, sizes)
-        act = mg.gmm_fwd_silu_mul(bf16_dev(x), w1, sizes)
+        h = mg.gmm_fwd(bf16_dev(x), w1, sizes, trans_b=trans_b)
+        act = mg.gmm_fwd_silu_mul(bf16_dev(x), w1, sizes, trans_b=trans_b)
         n, xa = M, x
     ref_act = mg.silu_mul(h[:n].contiguous())
     torch.cuda.synchronize()
