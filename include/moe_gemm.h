@@ -89,7 +89,8 @@ enum {
 size_t mg_workspace_bytes(int32_t E, int64_t total_M);
 
 /* Reads the sticky device error word of a workspace (hipMemcpy, blocking):
- * 0 = none, 1 = negative group size, 2 = sizes sum past total_M. */
+ * 0 = none, 1 = negative group size, 2 = sizes sum past total_M.  Also
+ * reads a colwise quantizer workspace, whose first word is the same. */
 int32_t mg_workspace_error(const void* ws);
 
 /* Zeroes the workspace header (error word, work-queue counters) and the
@@ -316,15 +317,39 @@ int quantize_rowwise_fp8_gather(const void* x, int64_t T, const int32_t* sorted_
  * written column-major: qa[c * rows + r]; scales sa[g * cols_a + c].  b,
  * qb, sb are either all NULL (single tensor) or all set (both tensors share
  * the group sizes and row count).  Rows beyond the sizes' sum are not
- * written.  cols % 8 == 0; 1 <= G <= MG_MAX_EXPERTS; rows < 2^31.  Enqueues
- * four kernels (zero the scales, column amax per 256-row chunk of a group,
- * cast, amax -> scale); sa and sb hold amax bits between them, so they must
- * not be read before the call's work has completed on the stream. */
+ * written; an empty group gets the scales of amax 0.  cols % 8 == 0,
+ * cols <= 2^20; 1 <= G <= MG_MAX_EXPERTS; rows < 2^31.
+ *
+ * Two kernel launches.  Work is cut into (tensor, group, 64-column
+ * block) sets.  A group of at most 256 rows is one chunk; a longer group's
+ * chunks are its pieces of the global 256-row blocks (a group touching more
+ * than 128 blocks gives each chunk several).  The first launch holds a
+ * chunk in registers: a set of one chunk is quantized there from a single
+ * read of its input, a chunk of a larger set leaves its partial column
+ * maxima in the workspace.  The second launch reads those chunks again
+ * (most recently read first, so partly from cache), takes the set's
+ * maximum from the partials and writes their codes.
+ *
+ *   ws        device workspace of at least
+ *             quantize_colwise_workspace_bytes(G, rows, cols_a, cols_b)
+ *             bytes (cols_b = 0 for a single tensor), 256-byte aligned,
+ *             caller-owned.  Its first word is a sticky error word
+ *             (mg_workspace_error): 1 for a negative group size, 2 for
+ *             sizes that sum past rows, as for the GEMMs (meaningful when
+ *             it started at zero); the rest needs no initialising.  Calls
+ *             that share a workspace must not overlap in time (enqueue them
+ *             on one stream).
+ * Errors: MG_EINVAL for the ranges above and NULL pointers,
+ * MG_EUNSUPPORTED for misaligned inputs (16-byte) or cols above 2^20,
+ * MG_EWORKSPACE for a missing, misaligned or small workspace. */
+size_t quantize_colwise_workspace_bytes(int32_t G, int64_t rows, int32_t cols_a,
+                                        int32_t cols_b);
 int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a,
                                    const void* b, int32_t cols_b,
                                    const int32_t* group_sizes, int32_t G,
                                    int64_t rows, uint8_t* qa, float* sa,
-                                   uint8_t* qb, float* sb, mg_stream_t stream);
+                                   uint8_t* qb, float* sb, void* ws,
+                                   size_t ws_bytes, mg_stream_t stream);
 
 /* int4 weight quantizer for gmm_fwd_f8i4: w bf16 [E, K, N] -> w4 packed
  * [E][N][K/2] and sw bf16 [E][K/128][N]; per (e, n, 128-chunk j):

@@ -53,7 +53,9 @@ _SIGS = {
     "gmm_fwd_f8i4": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "quantize_rowwise_fp8": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P, _P]),
     "quantize_rowwise_fp8_gather": (ctypes.c_int, [_P, _I64, _P, _I32, _I64, _I32, _P, _P, _P]),
-    "quantize_colwise_per_group_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _I32, _I64, _P, _P, _P, _P, _P]),
+    "quantize_colwise_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32]),
+    "quantize_colwise_per_group_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _I32, _I64, _P, _P, _P, _P, _P,
+                                                      _SZ, _P]),
     "quantize_int4_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "moe_sorted_capacity": (_I64, [_I64, _I32, _I32, _I32]),
     "moe_block_capacity": (_I64, [_I64, _I32, _I32, _I32]),
@@ -404,12 +406,45 @@ def quantize_rowwise_fp8_gather(x, sorted_token_ids, top_k, q=None, scales=None,
     return q, scales
 
 
-def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None):
+def colwise_workspace_bytes(G, rows, cols_a, cols_b=0):
+    return int(lib().quantize_colwise_workspace_bytes(int(G), int(rows), int(cols_a), int(cols_b)))
+
+
+_CW_CACHE = {}
+
+
+def default_colwise_workspace(nbytes, device=None, stream=None):
+    """The colwise quantizer's workspace for a call made without ``ws``: one
+    per (device, stream), zero-filled when created (its first word is the
+    sticky error word) and replaced by a larger one when a call needs more.
+    It carries partial maxima from the quantizer's first launch to its
+    second and nothing between calls; calls on one stream never overlap, so
+    they may share it.  It cannot be created or grown during graph capture:
+    make one eager call of the largest shape first, or pass ``ws``."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    s = torch.cuda.current_stream(idx) if stream is None else stream
+    key = (idx, s.cuda_stream)
+    ws = _CW_CACHE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("no colwise workspace of this size for this stream yet and the stream is capturing: "
+                               "make one eager call of this shape on it first, or pass ws")
+        with torch.cuda.device(idx), torch.cuda.stream(s):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=torch.device("cuda", idx))
+        _CW_CACHE[key] = ws
+    return ws
+
+
+def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None, ws=None):
     """Per-group colwise quantization of a (and b).  Returns
     (qa [Ca, M] column-major codes, sa [G, Ca]) or, with b,
     (qa, sa, qb, sb).  Codes of rows past the groups are not written (a
     fresh output holds whatever its allocation held there); out=(qa, sa[,
-    qb, sb]) reuses buffers, checked for dtype, shape and device."""
+    qb, sb]) reuses buffers, checked for dtype, shape and device.  ws: a
+    uint8 device tensor of at least colwise_workspace_bytes(G, M, Ca, Cb)
+    bytes whose first word (the sticky error word) starts at zero (default:
+    the cached one of the device and stream)."""
     _need(a, torch.bfloat16, "a", 2)
     _need(group_sizes, torch.int32, "group_sizes", 1)
     M, Ca = a.shape
@@ -439,8 +474,15 @@ def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None
         else:
             qb = torch.empty(Cb, M, dtype=torch.uint8, device=a.device)
             sb = torch.empty(G, Cb, dtype=torch.float32, device=a.device)
+    need = colwise_workspace_bytes(G, M, Ca, Cb)
+    if ws is None:
+        ws = default_colwise_workspace(need, a.device, stream)
+    else:
+        _need(ws, torch.uint8, "ws", 1)
+        if ws.device != a.device:
+            raise ValueError("ws must be on the input's device")
     _call("quantize_colwise_per_group_fp8", _ptr(a), Ca, _ptr(b), Cb, _ptr(group_sizes), G, M, _ptr(qa),
-          _ptr(sa), _ptr(qb), _ptr(sb), _stream(stream))
+          _ptr(sa), _ptr(qb), _ptr(sb), _ptr(ws), ws.numel(), _stream(stream))
     return (qa, sa) if b is None else (qa, sa, qb, sb)
 
 

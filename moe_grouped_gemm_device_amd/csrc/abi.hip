@@ -592,9 +592,21 @@ int quantize_rowwise_fp8_gather(const void* x, int64_t T, const int32_t* sorted_
                     "quantize_rowwise_fp8_gather");
 }
 
+// Largest column count of a colwise operand: a 1024-row block's byte
+// offsets (row * cols * 2) stay below 2^31.
+constexpr int32_t kColwiseMaxCols = 1 << 20;
+
+size_t quantize_colwise_workspace_bytes(int32_t G, int64_t rows, int32_t cols_a, int32_t cols_b) {
+  const int32_t g = G < 1 ? 1 : (G > MG_MAX_EXPERTS ? MG_MAX_EXPERTS : G);
+  const int64_t r = rows < 0 ? 0 : (rows >= kMaxRows ? kMaxRows - 1 : rows);
+  const int32_t ca = cols_a < 1 ? 1 : (cols_a > kColwiseMaxCols ? kColwiseMaxCols : cols_a);
+  const int32_t cb = cols_b < 1 ? 0 : (cols_b > kColwiseMaxCols ? kColwiseMaxCols : cols_b);
+  return (size_t)colwise_layout(g, r, ca, cb).total;
+}
+
 int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a, const void* b, int32_t cols_b,
                                    const int32_t* group_sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
-                                   uint8_t* qb, float* sb, mg_stream_t stream) {
+                                   uint8_t* qb, float* sb, void* ws, size_t ws_bytes, mg_stream_t stream) {
   if (G < 1 || G > MG_MAX_EXPERTS) return fail(MG_EINVAL, "G=%d outside [1, %d]", G, MG_MAX_EXPERTS);
   if (rows < 0 || rows >= kMaxRows) return fail(MG_EINVAL, "rows out of range");
   if (!a || !qa || !sa || !group_sizes) return fail(MG_EINVAL, "NULL tensor argument");
@@ -602,10 +614,17 @@ int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a, const void* b,
   if (dual != (qb != nullptr) || dual != (sb != nullptr)) return fail(MG_EINVAL, "b, qb, sb must be all set or all NULL");
   if (cols_a < 1 || (dual && cols_b < 1)) return fail(MG_EINVAL, "cols must be positive");
   if (cols_a % 8 || (dual && cols_b % 8)) return fail(MG_EUNSUPPORTED, "cols must be multiples of 8");
+  if (cols_a > kColwiseMaxCols || (dual && cols_b > kColwiseMaxCols))
+    return fail(MG_EUNSUPPORTED, "cols above 2^20");
   if (!aligned16(a) || (dual && !aligned16(b))) return fail(MG_EUNSUPPORTED, "inputs must be 16-byte aligned");
+  const ColwiseLayout L = colwise_layout(G, rows, cols_a, dual ? cols_b : 0);
+  if (L.items + 65536 >= kMaxRows) return fail(MG_EUNSUPPORTED, "too many (row block, column block) pairs");
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < (size_t)L.total)
+    return fail(MG_EWORKSPACE, "colwise workspace missing, not 256-byte aligned or below %lld bytes",
+                (long long)L.total);
   return hip_status(launch_quant_colwise(reinterpret_cast<const uint16_t*>(a), cols_a,
                                          reinterpret_cast<const uint16_t*>(b), dual ? cols_b : 0, group_sizes, G,
-                                         rows, qa, sa, qb, sb, S(stream)),
+                                         rows, qa, sa, qb, sb, ws, S(stream)),
                     "quantize_colwise_per_group_fp8");
 }
 

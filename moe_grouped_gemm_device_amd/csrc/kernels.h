@@ -112,10 +112,21 @@ constexpr int kF8I4RowTile = 32;
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int32_t cols,
                                 int64_t ld, uint8_t* q, float* s, hipStream_t stream,
                                 const int32_t* src = nullptr, int32_t top_k = 1, int64_t n_pairs = 0);
+// Per-group colwise (single or dual) in two launches.  Its workspace: a
+// 256-byte header (word 0: the sticky error word) and 64 partial column
+// maxima per (chunk slot, column block) at part_off; nothing in it needs
+// initialising.
+struct ColwiseLayout {
+  int64_t slots;      // chunk slots per column block
+  int64_t part_off;   // bytes
+  int64_t total;      // bytes
+  int64_t items;      // upper bound on a launch's work items
+};
+ColwiseLayout colwise_layout(int32_t G, int64_t rows, int32_t cols_a, int32_t cols_b);
 hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_t* b,
                                 int32_t cols_b, const int32_t* sizes, int32_t G,
                                 int64_t rows, uint8_t* qa, float* sa, uint8_t* qb,
-                                float* sb, hipStream_t stream);
+                                float* sb, void* ws, hipStream_t stream);
 hipError_t launch_quant_int4(const uint16_t* w, int32_t E, int32_t K, int32_t N,
                              uint8_t* w4, uint16_t* sw, hipStream_t stream);
 

@@ -11,10 +11,10 @@
 // The format is OCP e4m3fn (largest finite 448): gfx950's fp8 convert and
 // MFMA instructions use it, where the page's MI300X runs used e4m3fnuz.
 //
-// All three kernels are HBM-bound: each element is read twice (amax pass,
-// cast pass; the second read mostly hits cache) and written once as a byte.
-#include "kernels.h"
-#include "worklist.h"
+// All of them are HBM-bound.  The rowwise kernels hold a row in registers
+// and the colwise kernel a 1024-row chunk of 64 columns, so each element is
+// read from HBM once and written once as a byte.
+#include "gemm_dev.h"
 
 namespace mg {
 
@@ -273,331 +273,472 @@ hipError_t launch_silu_mul_quant(const uint16_t* h, int64_t rows, int32_t inter,
 }
 
 // ---------------------------------------------------------------------------
-// K4: per-group colwise, single or dual.  The unit of work is a tile of 64
-// columns x 256 rows of one group: the device group table cuts every group's
-// rows into 256-row chunks, so a large group spreads over many workgroups
-// (with Zipf-skewed loads one group can hold a sixth of the rows).  Four
-// launches on the stream:
-//   1. zero the scale arrays, which hold column amax bits until step 4;
-//   2. per tile: column |x| max, folded in with an integer atomic max on the
-//      fp32 bits (non-negative floats order like their bit patterns);
-//   3. per tile, walked in reverse order so that the second read meets the
-//      most recently read rows still in cache: the scale from the finished
-//      amax, the cast, a transpose through LDS and column-major 16-byte
-//      stores (byte stores only where a run starts or ends inside a 16-byte
-//      piece shared with a neighbouring group);
-//   4. amax -> scale.
-// Codes of rows past the groups are not written.
+// K4: per-group colwise, single or dual, in two launches.
+//
+// Sets and chunks.  A set is (tensor, group, block of 64 columns).  A group
+// of at most CW_CHUNK rows is one chunk; a longer group's chunks are its
+// intersections with the global CW_CHUNK-row blocks, so that interior chunk
+// edges fall on block boundaries (16-byte aligned in the column-major
+// output when the row count is a multiple of 16) and only the group's own
+// first and last rows can share a 16-byte piece of a column with another
+// group.  A group touching more than CW_MAX_CHUNKS blocks gives each chunk
+// several consecutive blocks ("runs").  An empty group has one chunk of no
+// rows, which writes the scales of amax 0.
+//
+// Pass 1 walks every chunk.  A workgroup reads the chunk's first run (up to
+// 256 rows x 64 columns) into registers, 8 consecutive rows x 8 columns per
+// thread (waves whose rows all lie past the run skip their share), and
+// folds the column |x| maxima.  A set of one chunk is finished there and
+// then: scales from the maxima, cast, transpose through LDS, column-major
+// stores in aligned 16-byte pieces, and the bytes of pieces shared with a
+// neighbouring group one per lane -- its input is read from HBM once.  A chunk
+// of a larger set stores its 64 partial maxima in the workspace instead.
+// Pass 2 walks the chunks of the larger sets, most recently read first so
+// that the second read meets them in cache: maximum of the set's partials,
+// scales (the set's first chunk writes them), cast and stores as above.
+// Neither pass waits on another workgroup, and the workspace holds no
+// counters.
 // ---------------------------------------------------------------------------
-constexpr int QC_COLS = 64;    // columns per tile
-constexpr int QC_ROWS = 256;   // rows per tile (chunk of a group)
+constexpr int CW_COLS = 64;                    // columns per set
+constexpr int CW_RPT = 8;                      // rows per thread held in registers
+constexpr int CW_CHUNK = (256 / 8) * CW_RPT;   // rows per chunk run (256)
+constexpr int CW_UNITS = CW_CHUNK / 16;        // 16-byte units per column row of the LDS tile
+constexpr int CW_PIECES = CW_UNITS + 1;        // aligned 16-byte pieces a column's run can touch
+constexpr int CW_MAX_CHUNKS = 128;             // chunks per set at most
 
 struct ColwiseArgs {
   const uint16_t* x[2];
   int32_t cols[2];
+  int32_t ncb[2];     // 64-column blocks per tensor
   uint8_t* q[2];
-  uint32_t* s[2];    // scale arrays [G][cols], amax bits until the last launch
+  float* s[2];
   const int32_t* sizes;
   int32_t G;
   int32_t ntensors;
   int64_t rows;
+  int32_t* err;       // sticky error word (invalid group sizes)
+  uint32_t* part;     // partial maxima: 64 words per (chunk slot, column block)
+  int64_t part_t1;    // word offset of tensor 1's partials
 };
 
-// Chunks of a group are its intersections with the global 256-row blocks,
-// so interior chunk edges fall on 256-row boundaries (16-byte aligned in the
-// column-major output when the row count is a multiple of 16) and only a
-// group's own first and last rows can share a 16-byte piece with another
-// group.  Rewrites tab.tstart with these chunk counts (build_group_table must
-// have filled off/eff); called by all threads.
-__device__ inline void colwise_chunk_table(GroupTable& tab, int32_t G) {
+ColwiseLayout colwise_layout(int32_t G, int64_t rows, int32_t cols_a, int32_t cols_b) {
+  ColwiseLayout L;
+  const int64_t ncb = cdiv(cols_a, CW_COLS) + (cols_b > 0 ? cdiv(cols_b, CW_COLS) : 0);
+  // chunk slots per column block: a chunk lies in one of the row blocks,
+  // consecutive groups share at most one block, and an empty group adds one
+  L.slots = cdiv(rows, CW_CHUNK) + 2 * (int64_t)G;
+  L.part_off = 256;
+  L.total = L.part_off + 4 * L.slots * ncb * CW_COLS;
+  L.items = L.slots * ncb;
+  return L;
+}
+
+// Blocks a group touches, the blocks per chunk (1 unless the group touches
+// more than CW_MAX_CHUNKS), and the group's chunk count (1 for a group of
+// at most CW_CHUNK rows, wherever it starts).
+__device__ inline int32_t cw_blocks_of(int32_t off, int32_t eff) {
+  return (off + eff - 1) / CW_CHUNK - off / CW_CHUNK + 1;
+}
+__device__ inline int32_t cw_runs_per_chunk(int32_t nblk) { return (nblk + CW_MAX_CHUNKS - 1) / CW_MAX_CHUNKS; }
+__device__ inline int32_t cw_chunks_of(int32_t off, int32_t eff) {
+  if (eff <= CW_CHUNK) return 1;
+  const int32_t nblk = cw_blocks_of(off, eff);
+  const int32_t f = cw_runs_per_chunk(nblk);
+  return (nblk + f - 1) / f;
+}
+
+// Chunk tables, from off/eff (build_group_table): tab.tstart[g] = chunks of
+// groups before g (every group), big[g] = chunks of the groups before g
+// that have more than one; called by all threads.
+__device__ inline void cw_chunk_tables(GroupTable& tab, int32_t* big, int32_t G) {
   const int tid = threadIdx.x;
   const int per = (G + kTableThreads - 1) / kTableThreads;
   const int g0 = tid * per;
   int32_t cnt[4];
-  int64_t local = 0;
+  int64_t local = 0, local_big = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     cnt[i] = 0;
     if (i < per && g0 + i < G) {
-      const int32_t off = tab.off[g0 + i], eff = tab.eff[g0 + i];
-      if (eff > 0) cnt[i] = (int32_t)(((int64_t)off + eff - 1) / QC_ROWS - off / QC_ROWS + 1);
+      cnt[i] = cw_chunks_of(tab.off[g0 + i], tab.eff[g0 + i]);
       local += cnt[i];
+      local_big += cnt[i] > 1 ? cnt[i] : 0;
     }
   }
   const int64_t incl = block_incl_scan64(local, tab.scratch);
-  int32_t run = (int32_t)(incl - local);
+  const int64_t incl_big = block_incl_scan64(local_big, tab.scratch + 8);
+  int32_t run = (int32_t)(incl - local), run_big = (int32_t)(incl_big - local_big);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i < per && g0 + i < G) {
       tab.tstart[g0 + i] = run;
+      big[g0 + i] = run_big;
       run += cnt[i];
+      run_big += cnt[i] > 1 ? cnt[i] : 0;
     }
   }
-  if (tid == (G - 1) / per) tab.tstart[G] = (int32_t)incl;
+  if (tid == (G - 1) / per) {
+    tab.tstart[G] = (int32_t)incl;
+    big[G] = (int32_t)incl_big;
+  }
   __syncthreads();
 }
 
-// Chunk -> {group, first row, rows}.
-__device__ inline int4 colwise_chunk(const GroupTable& tab, int32_t G, int32_t chunk) {
-  int lo = 0, hi = G - 1;
-  while (lo < hi) {   // last group whose first chunk is <= chunk
-    const int mid = (lo + hi + 1) >> 1;
-    if (tab.tstart[mid] <= chunk) lo = mid; else hi = mid - 1;
-  }
-  const int64_t off = tab.off[lo], end = off + tab.eff[lo];
-  const int64_t b0 = (off / QC_ROWS + (chunk - tab.tstart[lo])) * (int64_t)QC_ROWS;
-  const int64_t r0 = b0 > off ? b0 : off;
-  const int64_t r1 = b0 + QC_ROWS < end ? b0 + QC_ROWS : end;
-  return make_int4(lo, (int)r0, (int)(r1 - r0), 0);
+// The last group g with start[g] <= key (start non-decreasing from 0): two
+// ballots of one wave, G <= 64 * 64.  Uniform across the wave.
+__device__ inline int cw_find_group(const int32_t* start, int G, int32_t key) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int S = (G + kWave - 1) / kWave;
+  const int g1 = lane * S;
+  const uint64_t b1 = __ballot(g1 < G && start[g1] <= key);
+  const int base = (63 - __builtin_clzll(b1)) * S;
+  const int g2 = base + lane;
+  const uint64_t b2 = __ballot(lane < S && g2 < G && start[g2] <= key);
+  return base + 63 - __builtin_clzll(b2);
 }
 
-// Tile index -> (tensor, chunk, block of W columns); consecutive tiles share
-// rows.
-template <int W>
-__device__ inline void colwise_tile(const ColwiseArgs& a, int64_t nch, int64_t item, int& t, int32_t& chunk,
-                                    int& cb) {
-  const int64_t cba = cdiv(a.cols[0], W);
-  t = 0;
-  if (item >= nch * cba) {
-    item -= nch * cba;
-    t = 1;
-  }
-  const int64_t cbs = cdiv(a.cols[t], W);
-  chunk = (int32_t)(item / cbs);
-  cb = (int)(item - (int64_t)chunk * cbs);
+// Element k (0..7, compile-time) of a 16-byte chunk of bf16, as fp32.
+template <int K>
+__device__ inline float bf16_elem(const uint4& v) {
+  const uint32_t w = K / 2 == 0 ? v.x : (K / 2 == 1 ? v.y : (K / 2 == 2 ? v.z : v.w));
+  return bf16_to_f32(K % 2 == 0 ? (w & 0xFFFFu) : (w >> 16));
 }
 
-template <int W>
-__device__ inline int64_t colwise_tiles(const ColwiseArgs& a, int64_t nch) {
-  int64_t n = nch * cdiv(a.cols[0], W);
-  if (a.ntensors > 1) n += nch * cdiv(a.cols[1], W);
-  return n;
-}
-
-// Workgroups that take part in a persistent loop over n equal items: with
-// r = ceil(n / grid) rounds, ceil(n / r) workgroups suffice, and every round
-// but the last keeps all of them busy.
-__device__ inline int64_t balanced_active(int64_t n) {
-  const int64_t G = gridDim.x;
-  if (n <= 0) return 0;
-  const int64_t rounds = (n + G - 1) / G;
-  return (n + rounds - 1) / rounds;
-}
-
-constexpr int QA_COLS = 256;   // columns per amax tile: a wave reads two 512-byte row runs per load
-
-__global__ void __launch_bounds__(256) colwise_zero_kernel(ColwiseArgs a) {
-  for (int t = 0; t < a.ntensors; ++t) {
-    const int64_t n = (int64_t)a.G * a.cols[t];
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) a.s[t][i] = 0u;
+// Column maxima of 8 columns over a thread's rows (fp32 bits of |x|).
+__device__ inline void cw_fold_max(uint32_t (&m)[8], const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[2 * i] = max(m[2 * i], (w[i] & 0x7FFFu) << 16);
+    m[2 * i + 1] = max(m[2 * i + 1], (w[i] >> 16 & 0x7FFFu) << 16);
   }
 }
 
-__global__ void __launch_bounds__(256) colwise_amax_kernel(ColwiseArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
-  __shared__ uint32_t red[4][QA_COLS];
-  const GroupTable tab = carve_table(table_lds, a.G);
-  GroupTable tabw = tab;
-  build_group_table(a.sizes, a.G, a.rows, QC_ROWS, false, tabw);
-  colwise_chunk_table(tabw, a.G);
-  const int64_t nch = tab.tstart[a.G];
-  const int64_t n = colwise_tiles<QA_COLS>(a, nch);
+// LDS tile of codes: column c's row r at byte c * CW_CHUNK + (((r / 16) ^
+// (c / 8 % 8)) * 16) + r % 16.  The unit index is XORed with the column's
+// 8-column group, so that the 8 lanes writing one row group's unit of 8
+// columns reach 8 different bank groups.
+__device__ inline int cw_tile_unit(int cl, int unit) { return cl * CW_CHUNK + ((unit ^ ((cl >> 3) & 7)) << 4); }
+
+// Codes of column K for a thread's 8 rows, four rows per word, as one half
+// of a 16-byte unit of the tile.
+template <int K>
+__device__ inline void cw_cast_col(uint8_t* tile, const uint4 (&v)[CW_RPT], float s, int cc, int rg) {
+  static_assert(CW_RPT == 8, "half a 16-byte unit per thread and column");
+  uint32_t d[2];
+#pragma unroll
+  for (int qd = 0; qd < 2; ++qd) {
+    const int i = 4 * qd;
+    d[qd] = e4m3x4(clamp448(bf16_elem<K>(v[i]) * s), clamp448(bf16_elem<K>(v[i + 1]) * s),
+                   clamp448(bf16_elem<K>(v[i + 2]) * s), clamp448(bf16_elem<K>(v[i + 3]) * s));
+  }
+  *reinterpret_cast<uint2*>(tile + cw_tile_unit(cc * 8 + K, rg >> 1) + (rg & 1) * 8) = make_uint2(d[0], d[1]);
+}
+
+// LDS of either pass besides the group tables: the code tile and the
+// per-column maxima, scales and piece shifts.
+struct CwShared {
+  uint8_t tile[CW_COLS * CW_CHUNK];
+  uint32_t red[4][CW_COLS];
+  float sc[CW_COLS];
+  int sh[CW_COLS];
+};
+
+// One chunk of one set.  Its run sb covers rows [max(lo, (B0 + sb) *
+// CW_CHUNK), min(end, (B0 + sb + 1) * CW_CHUNK)) for a chunk on the block
+// grid, and [lo, end) for a one-chunk group (B0 = -1).
+struct CwChunk {
+  int t, g, cb, j, nch, nsb;
+  int32_t slot0;        // chunk slot of the set's first chunk
+  int64_t B0, lo, end;  // first block (or -1), the group's first row and end
+};
+
+// Work item -> chunk.  key counts the items of tensor t: groups in order,
+// then column blocks, then chunks; start[g] counts the chunks of the groups
+// before g that the pass walks (all, or those of sets of several chunks).
+__device__ inline CwChunk cw_decode(const ColwiseArgs& a, const GroupTable& tab, const int32_t* start, int t,
+                                    int64_t key) {
+  CwChunk c;
+  const int ncb = a.ncb[t];
+  c.t = t;
+  c.g = cw_find_group(start, a.G, (int32_t)(key / ncb));
+  const int32_t c0 = start[c.g];
+  c.nch = start[c.g + 1] - c0;
+  const int64_t rem = key - (int64_t)c0 * ncb;
+  c.cb = (int)(rem / c.nch);
+  c.j = (int)(rem - (int64_t)c.cb * c.nch);
+  c.slot0 = tab.tstart[c.g];
+  const int32_t eff = tab.eff[c.g], off = tab.off[c.g];
+  c.lo = off;
+  c.end = (int64_t)off + eff;
+  c.nsb = 1;
+  c.B0 = -1;
+  if (eff > CW_CHUNK) {
+    const int32_t nblk = cw_blocks_of(off, eff);
+    const int32_t f = cw_runs_per_chunk(nblk);
+    c.B0 = (int64_t)(off / CW_CHUNK) + (int64_t)c.j * f;
+    const int64_t left = (c.end - 1) / CW_CHUNK - c.B0 + 1;
+    c.nsb = (int)(f < left ? f : left);
+  }
+  return c;
+}
+
+// The work of both passes on one chunk.  PASS 1: read run 0 and fold the
+// maxima; a chunk of a larger set stores its partial maxima and is done.
+// PASS 2: the set's maximum from the partials.  Then (a one-chunk set in
+// pass 1, every chunk in pass 2): scales, cast and stores of every run.
+template <int PASS>
+__device__ inline void cw_chunk(const ColwiseArgs& a, const CwChunk& c, CwShared& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cc = tid & 31, rg = tid >> 5;   // 8-column chunk of the tile, row group (rows rg + 8 j)
-  // balanced rounds: the fewest workgroups that take the tiles in as many
-  // rounds as the grid needs, so no round runs with most of the grid idle
-  const int64_t active = balanced_active(n);
-  if ((int64_t)blockIdx.x >= active) return;
-  for (int64_t item = blockIdx.x; item < n; item += active) {
-    int t, cb;
-    int32_t chunk;
-    colwise_tile<QA_COLS>(a, nch, item, t, chunk, cb);
-    const int4 e = colwise_chunk(tab, a.G, chunk);
-    const int cols = a.cols[t];
-    const int c = cb * QA_COLS + cc * 8;
-    const uint16_t* x = a.x[t] + (int64_t)e.y * cols + c;
-    uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < cols) {
-      // 32 rows per thread, 8 loads in flight at a time; rows past the chunk
-      // re-read its first row
+  const int cc = tid & 7, rg = tid >> 3;   // 8-column group, row group (rows 8 rg .. 8 rg + 7)
+  const int t = c.t, cb = c.cb;
+  const int ncb = a.ncb[t], cols = a.cols[t];
+  const int64_t M = a.rows;
+  const int64_t row_bytes = 2 * (int64_t)cols;
+  const uint32_t vo0 = (uint32_t)(rg * CW_RPT * row_bytes) + (uint32_t)(cc * 16);
+  constexpr int WAVE_ROWS = CW_CHUNK / 4;   // rows of wave w: [WAVE_ROWS w, WAVE_ROWS (w + 1))
+  auto run_first = [&](int sb) -> int64_t {
+    if (c.B0 < 0) return c.lo;
+    const int64_t b = (c.B0 + sb) * CW_CHUNK;
+    return b > c.lo ? b : c.lo;
+  };
+  auto run_rows = [&](int sb) -> int {
+    const int64_t s0 = run_first(sb);
+    const int64_t lim = c.B0 < 0 ? c.end : (c.B0 + sb + 1) * CW_CHUNK;
+    const int64_t e1 = lim < c.end ? lim : c.end;
+    return e1 > s0 ? (int)(e1 - s0) : 0;
+  };
+  // buffer over a run's rows from the set's first column: rows past the run
+  // and columns past the tensor's last read as zeros
+  auto run_rsrc = [&](int sb, int nr) {
+    return make_rsrc(a.x[t] + run_first(sb) * cols + cb * CW_COLS,
+                     (int64_t)nr * row_bytes - 2 * (int64_t)cb * CW_COLS);
+  };
+  // a run into v (a wave with no rows in the run reads nothing); kept in
+  // cache when pass 2 reads it again, streamed otherwise
+  uint4 v[CW_RPT];
+  auto load_run = [&](int sb, int nr, bool keep) {
+    if (WAVE_ROWS * wave >= nr) return;
+    const auto r = run_rsrc(sb, nr);
 #pragma unroll
-      for (int jb = 0; jb < QC_ROWS / 8; jb += 8) {
-        uint4 v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = rg + 8 * (jb + j);
-          v[j] = *reinterpret_cast<const uint4*>(x + (int64_t)(r < e.z ? r : 0) * cols);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            m[2 * i] = max(m[2 * i], (w[i] & 0x7FFFu) << 16);
-            m[2 * i + 1] = max(m[2 * i + 1], (w[i] >> 16 & 0x7FFFu) << 16);
-          }
-        }
-      }
+    for (int i = 0; i < CW_RPT; ++i) {
+      const int vo = (int)(vo0 + (uint32_t)(i * row_bytes));
+      const i32x4 w = keep ? __builtin_amdgcn_raw_buffer_load_b128(r, vo, 0, kPolicyCached)
+                           : __builtin_amdgcn_raw_buffer_load_b128(r, vo, 0, kPolicyStream);
+      v[i] = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
     }
-    // reduce over the 8 row groups: the two of a wave by a shuffle, then the
+  };
+  // the set's partial maxima: chunk jj's 64 words at pbase + jj * ncb * 64
+  uint32_t* pbase = a.part + (t ? a.part_t1 : 0) + ((int64_t)c.slot0 * ncb + cb) * CW_COLS;
+  const int64_t pstride = (int64_t)ncb * CW_COLS;
+  uint32_t cmax = 0;
+  int nr = run_rows(0);
+  if constexpr (PASS == 1) {
+#pragma unroll
+    for (int i = 0; i < CW_RPT; ++i) v[i] = make_uint4(0, 0, 0, 0);
+    // every run of the chunk through v (only a one-chunk set, which has one
+    // run, keeps it for the cast; a wave with no rows in a later run folds
+    // the earlier run's rows of the same set again, which leaves the maxima
+    // unchanged)
+    uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int sb = 0; sb < c.nsb; ++sb) {
+      load_run(sb, sb == 0 ? nr : run_rows(sb), c.nch > 1);
+#pragma unroll
+      for (int i = 0; i < CW_RPT; ++i) cw_fold_max(m, v[i]);
+    }
+    // column maxima over the 32 row groups: 8 per wave by shuffles, then the
     // 4 waves through LDS
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = max(m[i], (uint32_t)__shfl_xor((int)m[i], 32, kWave));
-    if (lane < 32) {
+    for (int k = 0; k < 8; ++k) {
+      m[k] = max(m[k], (uint32_t)__shfl_xor((int)m[k], 8, kWave));
+      m[k] = max(m[k], (uint32_t)__shfl_xor((int)m[k], 16, kWave));
+      m[k] = max(m[k], (uint32_t)__shfl_xor((int)m[k], 32, kWave));
+    }
+    if (lane < 8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
+      for (int k = 0; k < 8; ++k) L.red[wave][lane * 8 + k] = m[k];
     }
     __syncthreads();
-    {
-      const uint32_t v = max(max(red[0][tid], red[1][tid]), max(red[2][tid], red[3][tid]));
-      const int col = cb * QA_COLS + tid;
-      if (col < cols && v != 0u) atomicMax(a.s[t] + (int64_t)e.x * cols + col, v);
+    if (tid < CW_COLS) cmax = max(max(L.red[0][tid], L.red[1][tid]), max(L.red[2][tid], L.red[3][tid]));
+    if (c.nch > 1) {
+      if (tid < CW_COLS) pbase[c.j * pstride + tid] = cmax;
+      return;
     }
+  } else {
+    // the set's maximum over its chunks' partials: wave w folds chunks w,
+    // w + 4, ..., eight loads in flight per lane, then the 4 waves through
+    // LDS
+    uint32_t pm = 0;
+    for (int jb = wave; jb < c.nch; jb += 32) {
+      uint32_t pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = jb + 4 * u;
+        pv[u] = jj < c.nch ? pbase[jj * pstride + lane] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pm = max(pm, pv[u]);
+    }
+    L.red[wave][lane] = pm;
     __syncthreads();
+    if (tid < CW_COLS) cmax = max(max(L.red[0][tid], L.red[1][tid]), max(L.red[2][tid], L.red[3][tid]));
   }
-}
-
-__global__ void __launch_bounds__(256) colwise_cast_kernel(ColwiseArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
-  // tile[c][r]: code of row r of column c.  Rows of 276 bytes: the dword
-  // writes below (4 rows of one column per lane) hit 64 distinct banks.
-  constexpr int TROW = QC_ROWS + 20;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[QC_COLS][TROW];
-  __shared__ float sc[QC_COLS];
-  __shared__ int sh[QC_COLS];
-  const GroupTable tab = carve_table(table_lds, a.G);
-  GroupTable tabw = tab;
-  build_group_table(a.sizes, a.G, a.rows, QC_ROWS, false, tabw);
-  colwise_chunk_table(tabw, a.G);
-  const int64_t nch = tab.tstart[a.G];
-  const int64_t n = colwise_tiles<QC_COLS>(a, nch);
-  const int tid = threadIdx.x;
-  const int cc = tid & 7, rq = tid >> 3;   // 8-column chunk, row quad within 128 rows
-  const int64_t active = balanced_active(n);   // as in the amax pass
-  if ((int64_t)blockIdx.x >= active) return;
-  for (int64_t item = n - 1 - blockIdx.x; item >= 0; item -= active) {
-    int t, cb;
-    int32_t chunk;
-    colwise_tile<QC_COLS>(a, nch, item, t, chunk, cb);
-    const int4 e = colwise_chunk(tab, a.G, chunk);
-    const int cols = a.cols[t];
-    const int64_t M = a.rows;
-    if (tid < QC_COLS) {
-      const int col = cb * QC_COLS + tid;
-      float v = 0.f;
-      if (col < cols) v = fp8_scale_from_amax(__uint_as_float(a.s[t][(int64_t)e.x * cols + col]));
-      sc[tid] = v;
-      // byte offset of the column's first row within its 16-byte piece
-      sh[tid] = (int)((reinterpret_cast<uintptr_t>(a.q[t]) + (uint64_t)((int64_t)col * M + e.y)) & 15u);
+  if (tid < CW_COLS) {
+    const float s = fp8_scale_from_amax(__uint_as_float(cmax));
+    L.sc[tid] = s;
+    const int col = cb * CW_COLS + tid;
+    if (c.j == 0 && col < cols) a.s[t][(int64_t)c.g * cols + col] = s;
+  }
+  // ---- cast and store, run by run
+  for (int sb = 0; sb < c.nsb; ++sb) {
+    const int64_t s0 = run_first(sb);
+    if (PASS == 2 || sb > 0) {
+      nr = run_rows(sb);
+      load_run(sb, nr, false);
+    }
+    if (tid < CW_COLS) {
+      // byte offset of the column's first row of this run within its 16-byte
+      // piece
+      const int64_t col = cb * CW_COLS + tid;
+      L.sh[tid] = (int)((reinterpret_cast<uintptr_t>(a.q[t]) + (uint64_t)(col * M + s0)) & 15u);
+    }
+    __syncthreads();   // sc and sh visible; the tile's previous contents consumed
+    if (WAVE_ROWS * wave < nr) {
+      float sv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv[k] = L.sc[cc * 8 + k];
+      cw_cast_col<0>(L.tile, v, sv[0], cc, rg);
+      cw_cast_col<1>(L.tile, v, sv[1], cc, rg);
+      cw_cast_col<2>(L.tile, v, sv[2], cc, rg);
+      cw_cast_col<3>(L.tile, v, sv[3], cc, rg);
+      cw_cast_col<4>(L.tile, v, sv[4], cc, rg);
+      cw_cast_col<5>(L.tile, v, sv[5], cc, rg);
+      cw_cast_col<6>(L.tile, v, sv[6], cc, rg);
+      cw_cast_col<7>(L.tile, v, sv[7], cc, rg);
     }
     __syncthreads();
-    const int c = cb * QC_COLS + cc * 8;
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = sc[cc * 8 + i];
-    const uint16_t* x = a.x[t] + (int64_t)e.y * cols + c;
-    // the whole tile's loads first (rows past the chunk re-read its first row)
-    constexpr int HALVES = QC_ROWS / 128;
-    uint4 vv[HALVES][4];
-#pragma unroll
-    for (int h = 0; h < HALVES; ++h)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = 128 * h + 4 * rq + k;
-        vv[h][k] = make_uint4(0, 0, 0, 0);
-        if (c < cols) vv[h][k] = *reinterpret_cast<const uint4*>(x + (int64_t)(r < e.z ? r : 0) * cols);
-      }
-#pragma unroll
-    for (int h = 0; h < HALVES; ++h) {
-      const int r0 = 128 * h + 4 * rq;
-      // codes of 4 rows x 8 columns; column i's 4 codes form one dword
-      uint32_t col4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w[4] = {vv[h][k].x, vv[h][k].y, vv[h][k].z, vv[h][k].w};
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float f0 = clamp448(bf16_to_f32(w[i / 2] & 0xFFFFu) * sv[i]);
-          const float f1 = clamp448(bf16_to_f32(w[i / 2] >> 16) * sv[i + 1]);
-          const uint32_t codes = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0u, false);
-          col4[i] |= (codes & 0xFFu) << (8 * k);
-          col4[i + 1] |= (codes >> 8 & 0xFFu) << (8 * k);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&tile[cc * 8 + i][r0]) = col4[i];
-    }
-    __syncthreads();
-    // Column-major stores.  Column cl's rows [0, e.z) start at global byte
-    // address A = col * M + row0 (plus the base), which sits s0 bytes into a
-    // 16-byte piece; piece p covers rows [16 p - s0, 16 p - s0 + 16).  Its
-    // bytes come from the tile by a byte funnel shift of aligned dwords.
-    constexpr int PIECES = QC_ROWS / 16 + 1;
-    for (int qi = tid; qi < QC_COLS * PIECES; qi += 256) {
-      const int cl = qi / PIECES, p = qi - cl * PIECES;
-      const int col = cb * QC_COLS + cl;
+    // Column-major stores.  Column cl's rows [0, nr) start at global byte
+    // address A = col * M + s0 (plus the base), which sits sh bytes into a
+    // 16-byte piece; piece p covers rows [16 p - sh, 16 p - sh + 16).  Its
+    // bytes come from the tile by a byte funnel shift of aligned words.
+    // Pieces the run fills are stored whole here; the others (shared with a
+    // neighbouring group, or the run's only piece) byte by byte below.
+    bool edges = false;
+    for (int qi = tid; qi < CW_COLS * CW_PIECES; qi += 256) {
+      const int cl = qi / CW_PIECES, p = qi - cl * CW_PIECES;
+      const int col = cb * CW_COLS + cl;
       if (col >= cols) continue;
-      const int s0 = sh[cl];
-      const int lo = p * 16 - s0, hi = lo + 16;   // rows of this piece
-      if (hi <= 0 || lo >= e.z) continue;
-      uint8_t* dst = a.q[t] + (int64_t)col * M + e.y + lo;   // 16-byte aligned
-      if (lo >= 0 && hi <= e.z) {
-        const int d0 = lo >> 2, sb = lo & 3;   // first dword, byte shift
-        const uint32_t* trow = reinterpret_cast<const uint32_t*>(&tile[cl][0]);
-        uint32_t w[5];
+      const int lo = p * 16 - L.sh[cl], hi = lo + 16;   // rows of this piece
+      if (hi <= 0 || lo >= nr) continue;
+      if (lo < 0 || hi > nr) {
+        edges = true;
+        continue;
+      }
+      uint8_t* dst = a.q[t] + (int64_t)col * M + s0 + lo;   // 16-byte aligned
+      const int d0 = lo >> 2, bs = lo & 3;                   // first word, byte shift
+      uint32_t w[5];
 #pragma unroll
-        for (int j = 0; j < 5; ++j) w[j] = trow[d0 + j < TROW / 4 ? d0 + j : TROW / 4 - 1];
-        uint4 out;
-        out.x = __builtin_amdgcn_alignbyte(w[1], w[0], sb);
-        out.y = __builtin_amdgcn_alignbyte(w[2], w[1], sb);
-        out.z = __builtin_amdgcn_alignbyte(w[3], w[2], sb);
-        out.w = __builtin_amdgcn_alignbyte(w[4], w[3], sb);
-        *reinterpret_cast<uint4*>(dst) = out;
-      } else {
-        for (int b = 0; b < 16; ++b) {
-          const int r = lo + b;
-          if (r >= 0 && r < e.z) dst[b] = tile[cl][r];
+      for (int jw = 0; jw < 5; ++jw) {
+        const int d = d0 + jw < 4 * CW_UNITS ? d0 + jw : 4 * CW_UNITS - 1;
+        w[jw] = *reinterpret_cast<const uint32_t*>(L.tile + cw_tile_unit(cl, d >> 2) + (d & 3) * 4);
+      }
+      uint4 o;
+      o.x = __builtin_amdgcn_alignbyte(w[1], w[0], bs);
+      o.y = __builtin_amdgcn_alignbyte(w[2], w[1], bs);
+      o.z = __builtin_amdgcn_alignbyte(w[3], w[2], bs);
+      o.w = __builtin_amdgcn_alignbyte(w[4], w[3], bs);
+      *reinterpret_cast<uint4*>(dst) = o;
+    }
+    // Bytes of the pieces not stored whole, one per lane: a column's run
+    // has at most 15 such bytes before its first whole piece (or all nr if
+    // it has none) and 15 after its last.
+    if (__syncthreads_or(edges)) {
+      for (int qi = tid; qi < CW_COLS * 32; qi += 256) {
+        const int cl = qi >> 5, e = qi & 31;
+        const int col = cb * CW_COLS + cl;
+        if (col >= cols) continue;
+        const int sh = L.sh[cl];
+        const int head = sh == 0 ? 0 : (16 - sh < nr ? 16 - sh : nr);   // rows before the first whole piece
+        const int whole = (nr - head) / 16;                              // whole pieces after them
+        const int tail = nr - head - 16 * whole;                         // rows after those
+        int r;
+        if (e < 16) {
+          if (e >= head) continue;
+          r = e;
+        } else {
+          if (e - 16 >= tail) continue;
+          r = head + 16 * whole + (e - 16);
         }
+        a.q[t][(int64_t)col * M + s0 + r] = L.tile[cw_tile_unit(cl, r >> 4) + (r & 15)];
       }
     }
-    __syncthreads();
+    __syncthreads();   // the tile and sh are free again
   }
 }
 
-__global__ void __launch_bounds__(256) colwise_finalize_kernel(ColwiseArgs a) {
-  for (int t = 0; t < a.ntensors; ++t) {
-    const int64_t n = (int64_t)a.G * a.cols[t];
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-      a.s[t][i] = __float_as_uint(fp8_scale_from_amax(__uint_as_float(a.s[t][i])));
+__host__ __device__ inline int64_t cw_bytes_dyn(int G) { return table_lds_bytes(G) + 4 * (G + 1); }
+
+// Both passes: group tables, then a grid-stride walk over the pass's
+// chunks (pass 2 from the last).
+template <int PASS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 5))) colwise_kernel(ColwiseArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t table_lds[];
+  __shared__ __attribute__((aligned(16))) CwShared L;
+  const GroupTable tab = carve_table(table_lds, a.G);
+  int32_t* big = reinterpret_cast<int32_t*>(table_lds + table_lds_bytes(a.G));
+  GroupTable tabw = tab;
+  const int err = build_group_table(a.sizes, a.G, a.rows, CW_CHUNK, false, tabw);
+  if (PASS == 1 && err != 0 && blockIdx.x == 0 && threadIdx.x == 0) *a.err = err;
+  cw_chunk_tables(tabw, big, a.G);
+  const int32_t* start = PASS == 1 ? tab.tstart : big;
+  const int64_t nchk = start[a.G];
+  const int64_t n0 = nchk * a.ncb[0];
+  const int64_t n = n0 + (a.ntensors > 1 ? nchk * a.ncb[1] : 0);
+  for (int64_t k = blockIdx.x; k < n; k += gridDim.x) {
+    const int64_t it = PASS == 1 ? k : n - 1 - k;
+    const int t = it >= n0 ? 1 : 0;
+    const CwChunk c = cw_decode(a, tab, start, t, t ? it - n0 : it);
+    cw_chunk<PASS>(a, c, L);
+    __syncthreads();   // LDS free for the next chunk
   }
 }
 
 hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_t* b, int32_t cols_b,
                                 const int32_t* sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
-                                uint8_t* qb, float* sb, hipStream_t stream) {
+                                uint8_t* qb, float* sb, void* ws, hipStream_t stream) {
+  const ColwiseLayout L = colwise_layout(G, rows, cols_a, b != nullptr ? cols_b : 0);
   ColwiseArgs x;
   x.x[0] = a;
   x.cols[0] = cols_a;
+  x.ncb[0] = (int32_t)cdiv(cols_a, CW_COLS);
   x.q[0] = qa;
-  x.s[0] = reinterpret_cast<uint32_t*>(sa);
+  x.s[0] = sa;
   x.ntensors = b != nullptr ? 2 : 1;
   x.x[1] = b;
   x.cols[1] = b != nullptr ? cols_b : 0;
+  x.ncb[1] = b != nullptr ? (int32_t)cdiv(cols_b, CW_COLS) : 0;
   x.q[1] = qb;
-  x.s[1] = reinterpret_cast<uint32_t*>(sb);
+  x.s[1] = sb;
   x.sizes = sizes;
   x.G = G;
   x.rows = rows;
-  const int64_t scale_words = (int64_t)G * (cols_a + x.cols[1]);
-  const int small = (int)(cdiv(scale_words, 256) < 1024 ? cdiv(scale_words, 256) : 1024);
-  const int grid = device_cu_count() * 8;
-  const size_t dyn = (size_t)table_lds_bytes(G);
-  hipLaunchKernelGGL(colwise_zero_kernel, dim3(small), dim3(256), 0, stream, x);
-  if (rows > 0) {
-    hipLaunchKernelGGL(colwise_amax_kernel, dim3(grid), dim3(256), dyn, stream, x);
-    hipLaunchKernelGGL(colwise_cast_kernel, dim3(grid), dim3(256), dyn, stream, x);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  x.err = reinterpret_cast<int32_t*>(w);
+  x.part = reinterpret_cast<uint32_t*>(w + L.part_off);
+  x.part_t1 = L.slots * x.ncb[0] * CW_COLS;
+  const size_t dyn = (size_t)cw_bytes_dyn(G);
+  // resident workgroups per CU at this group table's size (cached per G)
+  static int occ_of[kMaxExperts + 1];
+  int occ = occ_of[G];
+  if (occ == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, colwise_kernel<1>, 256, dyn) != hipSuccess || occ < 1)
+      occ = 1;
+    occ_of[G] = occ;
   }
-  hipLaunchKernelGGL(colwise_finalize_kernel, dim3(small), dim3(256), 0, stream, x);
+  const int64_t resident = (int64_t)device_cu_count() * occ;
+  const int grid = (int)(L.items < resident ? L.items : resident);
+  hipLaunchKernelGGL(colwise_kernel<1>, dim3(grid), dim3(256), dyn, stream, x);
+  hipLaunchKernelGGL(colwise_kernel<2>, dim3(grid), dim3(256), dyn, stream, x);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ["gmm_fwd", "gmm_bwd", "quantize_rowwise_fp8", "quantize_colwise_per_group_fp8",
+                     "quantize_colwise_workspace_bytes",
                      "moe_permute", "moe_unpermute", "gmm_fwd_fp8", "gmm_bwd_fp8", "gmm_fwd_f8i4",
                      "gmm_build_worklist", "silu_mul", "quantize_int4_weights"]:
         assert required in names
@@ -123,13 +124,35 @@ def test_fp8_and_f8i4_reject_unsupported_alignment(lib):
                            None) == mg.MG_EUNSUPPORTED                   # dw needs total_M % 16
 
 
+def test_colwise_workspace_size(lib):
+    # a 256-byte header and 64 partial maxima per (chunk slot, column block),
+    # with rows / 256 + 2 G chunk slots
+    f = lib.quantize_colwise_workspace_bytes
+    ncb = 22 + 32
+    assert f(64, 98304, 1408, 2048) == 256 + 4 * (384 + 128) * ncb * 64
+    assert f(64, 98304, 1408, 0) < f(64, 98304, 1408, 2048)
+    assert f(64, 98304, 1408, 2048) < f(64, 98305, 1408, 2048) < f(65, 98305, 1408, 2048)
+    assert f(1, 0, 8, 0) == 256 + 4 * 2 * 64
+
+
 def test_quantizers_reject_bad_arguments(lib):
     assert lib.quantize_rowwise_fp8(_p(FAKE), 4, 12, 12, _p(FAKE), _p(FAKE), None) == mg.MG_EUNSUPPORTED
     assert lib.quantize_rowwise_fp8(_p(FAKE), 4, 16, 8, _p(FAKE), _p(FAKE), None) == mg.MG_EINVAL
-    assert lib.quantize_colwise_per_group_fp8(_p(FAKE), 16, _p(FAKE), 16, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE),
-                                              None, _p(FAKE), None) == mg.MG_EINVAL   # b without qb
-    assert lib.quantize_colwise_per_group_fp8(_p(FAKE), 16, None, 0, _p(FAKE), 0, 64, _p(FAKE), _p(FAKE),
-                                              None, None, None) == mg.MG_EINVAL       # G = 0
+    cw = lib.quantize_colwise_per_group_fp8
+    need = lib.quantize_colwise_workspace_bytes(4, 64, 16, 16)
+    assert cw(_p(FAKE), 16, _p(FAKE), 16, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, _p(FAKE),
+              _p(0x10000), need, None) == mg.MG_EINVAL        # b without qb
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 0, 64, _p(FAKE), _p(FAKE), None, None,
+              _p(0x10000), need, None) == mg.MG_EINVAL        # G = 0
+    assert cw(_p(FAKE), (1 << 20) + 8, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+              _p(0x10000), 1 << 40, None) == mg.MG_EUNSUPPORTED   # cols above 2^20
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+              None, need, None) == mg.MG_EWORKSPACE           # no workspace
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+              _p(0x10080), need, None) == mg.MG_EWORKSPACE    # not 256-byte aligned
+    single = lib.quantize_colwise_workspace_bytes(4, 64, 16, 0)
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+              _p(0x10000), single - 4, None) == mg.MG_EWORKSPACE   # too small
     assert lib.quantize_int4_weights(_p(FAKE), 2, 100, 16, _p(FAKE), _p(FAKE), None) == mg.MG_EUNSUPPORTED
     g = lib.quantize_rowwise_fp8_gather
     assert g(_p(FAKE), 4, _p(FAKE), 2, 8, 12, _p(FAKE), _p(FAKE), None) == mg.MG_EUNSUPPORTED   # cols % 8

@@ -272,13 +272,14 @@ def test_captured_step_replays_bitwise():
     sx = torch.empty(M, dtype=torch.float32, device="cuda")
     cq = (torch.zeros(N, M, dtype=torch.uint8, device="cuda"), torch.empty(E, N, dtype=torch.float32, device="cuda"))
     ws = mg.workspace(E, M)
+    cws = torch.zeros(mg.colwise_workspace_bytes(E, M, N), dtype=torch.uint8, device="cuda")
 
     def step():
         mg.gmm_fwd(x, w, gs, out=y, ws=ws)
         mg.gmm_bwd(dy, x, w, gs, need_dw=False, dx=dx, ws=ws)
         mg.gmm_bwd(dy, x, w, gs, need_dx=False, dw=dw, ws=ws)
         mg.quantize_rowwise_fp8(x, q=xq, scales=sx)
-        mg.quantize_colwise_per_group_fp8(dy, gs, out=cq)
+        mg.quantize_colwise_per_group_fp8(dy, gs, out=cq, ws=cws)
 
     outs = (y, dx, dw, xq, sx, cq[0], cq[1])
     step()

@@ -123,6 +123,97 @@ def test_colwise_rows_outside_groups_untouched():
     _check_colwise(x, sizes, qa, sa)
 
 
+@pytest.mark.parametrize("M,C,sizes", [
+    # groups over several 512-row blocks (the second pass), one-chunk groups
+    # that straddle a block boundary, starts and ends off the 16-byte grid,
+    # a row count that is not a multiple of 16 (every column's run sits
+    # differently in its pieces), a partial last 64-column block, empty
+    # groups and rows past the groups
+    (20001, 200, [1, 5000, 0, 9000, 3, 5990]),
+    (8200, 72, [1023, 1025, 2048, 0, 4097]),
+    (3072, 8, [3072]),
+    (5000, 64, [300, 400, 5, 511, 512, 513, 1, 2000]),
+    (2000, 72, [255, 256, 257, 1, 512, 513, 0, 100]),
+])
+def test_colwise_sets_of_several_chunks(M, C, sizes):
+    sizes = np.array(sizes, np.int32)
+    x = wl.normal_bf16((M, C), 1.0, 11, wl.T_DY)
+    qa, sa = mg.quantize_colwise_per_group_fp8(bf16_dev(x), dev(sizes))
+    torch.cuda.synchronize()
+    _check_colwise(x, sizes, qa, sa)
+
+
+def test_colwise_group_longer_than_128_blocks():
+    # 150000 rows from row 17 touch 294 blocks of 512 rows: each chunk takes
+    # three blocks (the first pass folds them all, the second reads them
+    # again for the cast)
+    M, C = 153200, 64
+    sizes = np.array([17, 150000, 3000], np.int32)
+    x = wl.normal_bf16((M, C), 1.0, 12, wl.T_X)
+    qa, sa = mg.quantize_colwise_per_group_fp8(bf16_dev(x), dev(sizes))
+    torch.cuda.synchronize()
+    _check_colwise(x, sizes, qa, sa)
+
+
+def test_colwise_repeated_calls_share_a_workspace():
+    # the workspace carries partial maxima from the first pass to the second
+    # and nothing from one call to the next: calls of different chunkings in
+    # a row, on one workspace that is never cleared, each match the oracle
+    M, C, G = 12000, 136, 4
+    ws = torch.full((mg.colwise_workspace_bytes(G, M, C, 64),), 0x5A, dtype=torch.uint8, device="cuda")
+    ws[:4].zero_()   # the sticky error word
+    a = wl.normal_bf16((M, C), 1.0, 13, wl.T_DY)
+    b = wl.normal_bf16((M, 64), 1.0, 13, wl.T_X)
+    for sizes in ([5000, 0, 6500, 400], [1, 11998, 0, 1], [3000, 3000, 3000, 3000], [512, 513, 1024, 0]):
+        sizes = np.array(sizes, np.int32)
+        qa, sa, qb, sb = mg.quantize_colwise_per_group_fp8(bf16_dev(a), dev(sizes), b=bf16_dev(b), ws=ws)
+        torch.cuda.synchronize()
+        _check_colwise(a, sizes, qa, sa)
+        _check_colwise(b, sizes, qb, sb)
+        assert mg.workspace_error(ws) == 0
+
+
+def test_colwise_rejects_a_small_workspace():
+    x = bf16_dev(wl.normal_bf16((2048, 64), 1.0, 0, wl.T_X))
+    gs = dev(np.array([2048], np.int32))
+    ws = torch.zeros(mg.colwise_workspace_bytes(1, 2048, 64) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(RuntimeError):
+        mg.quantize_colwise_per_group_fp8(x, gs, ws=ws)
+
+
+def test_colwise_graph_replay_follows_new_group_sizes():
+    """The quantizer captured in a graph reads the device group sizes at every
+    replay, so replays after the sizes change in place match fresh eager
+    calls."""
+    M, C, G = 9000, 136, 5
+    x = bf16_dev(wl.normal_bf16((M, C), 1.0, 14, wl.T_DY))
+    gs = dev(np.array([2000, 2000, 2000, 2000, 1000], np.int32))
+    ws = torch.zeros(mg.colwise_workspace_bytes(G, M, C), dtype=torch.uint8, device="cuda")
+    qa = torch.zeros(C, M, dtype=torch.uint8, device="cuda")
+    sa = torch.zeros(G, C, dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mg.quantize_colwise_per_group_fp8(x, gs, out=(qa, sa), ws=ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mg.quantize_colwise_per_group_fp8(x, gs, out=(qa, sa), ws=ws)
+    for sizes in ([2000, 2000, 2000, 2000, 1000], [0, 8999, 0, 1, 0], [1500, 1, 3000, 0, 4000],
+                  [9000, 0, 0, 0, 0]):
+        gs.copy_(dev(np.array(sizes, np.int32)))
+        qa.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        qr, sr = mg.quantize_colwise_per_group_fp8(x, gs, ws=torch.zeros_like(ws))
+        torch.cuda.synchronize()
+        covered = int(sum(sizes))
+        assert torch.equal(sa, sr)
+        assert torch.equal(qa[:, :covered], qr[:, :covered])
+    assert mg.workspace_error(ws) == 0
+
+
 def test_quantizers_reject_mismatched_output_buffers():
     x = bf16_dev(wl.normal_bf16((64, 32), 1.0, 0, wl.T_X))
     with pytest.raises(ValueError):
