@@ -199,7 +199,10 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
         const int part = (lane & 7) ^ (dc & 7);
         dvo[i] = n0 + dc < N ? (uint32_t)((n0 + dc) * (K / 2) + part * 16) : F_OOB;
       }
-      const int L0 = j0 >> 1, L1 = (j1 + 1) >> 1;   // the wave's lines
+      // the wave's lines: j0 is even whenever the range is not empty (its
+      // length per is even); an empty range -- a wave past the last chunk,
+      // whose j0 = j1 = nchunk may be odd -- has no lines
+      const int L0 = j0 >> 1, L1 = j1 > j0 ? (j1 + 1) >> 1 : L0;
 
       // Requests every operand of line L into buffer b (zeros past the wave's
       // range): 4 weight transfers, then per chunk its scale and activations

@@ -93,7 +93,11 @@ def _f8i4_case(E, total_M, K, N, seed, counts=None):
 @pytest.mark.parametrize("E,total_M,K,N,seed", [(8, 5, 256, 64, 0), (16, 100, 512, 136, 1), (128, 1, 5120, 8192, 2),
                                                 (128, 16, 5120, 8192, 3),
                                                 # 70 chunks: the 8-wave kernel, 9 chunks per wave but 7 in the last
-                                                (4, 7, 8960, 96, 4)])
+                                                (4, 7, 8960, 96, 4),
+                                                # an odd chunk count with a wave past the last chunk
+                                                # (9 chunks in runs of 4; 1 chunk in runs of 2): that
+                                                # wave has no lines and adds nothing
+                                                (4, 6, 1152, 72, 5), (6, 9, 128, 40, 6)])
 def test_f8i4_sparse_m(E, total_M, K, N, seed):
     got, ref, norms = _f8i4_case(E, total_M, K, N, seed)
     assert_close(got, ref, FP8_TOL, GEMM_FP8, "Y", norms)
