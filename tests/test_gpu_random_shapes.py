@@ -12,8 +12,8 @@ import torch
 import moe_grouped_gemm_device_amd as mg
 import oracle
 import workloads as wl
-from gpu_util import (BF16_TOL, FP8_TOL, GEMM_BF16, GEMM_FP8, assert_close, bf16_dev, bf16_host, dev, dw_norms,
-                      dx_norms, fwd_norms, gpu, group_rows, host, require_gpu, vec_norms)
+from gpu_util import (BF16_TOL, CHAIN_ELEM, FP8_TOL, GEMM_BF16, GEMM_FP8, assert_close, bf16_dev, bf16_host, dev,
+                      dw_norms, dx_norms, fwd_norms, gpu, group_rows, host, require_gpu, vec_norms)
 
 pytestmark = gpu
 
@@ -186,3 +186,28 @@ def test_f8i4_random_shapes(seed):
     assert mg.workspace_error(ws) == 0
     assert_close(oracle.bf16_to_f64(bf16_host(y)), ref, FP8_TOL, GEMM_FP8, "Y",
                  (vec_norms(Xd, 1), cn, group_rows(counts, total_M)))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fused_moe_random_shapes(seed):
+    """The token-sorted FFN end to end (align, gathered GEMM1 with the
+    SiLU*mul epilogue, GEMM2, combine) on drawn token counts, expert counts,
+    top-k, widths and block sizes, in both weight layouts."""
+    r = np.random.default_rng(3000 + seed)
+    E = int(r.integers(1, 33))
+    k = int(r.integers(1, min(E, 8) + 1))
+    T = int(r.integers(1, 300))
+    H = 16 * int(r.integers(1, 33))
+    I = 16 * int(r.integers(1, 25))
+    bm = int(r.choice([16, 32, 64, 128]))
+    ids, w = wl.softmax_topk_routing(T, E, k, seed)
+    x = wl.normal_bf16((T, H), 1.0, seed, wl.T_X)
+    w1 = wl.stacked_normal_bf16(E, (H, 2 * I), 0.05, seed, wl.T_W1)
+    w2 = wl.stacked_normal_bf16(E, (I, H), 0.05, seed, wl.T_W2)
+    out, _ = mg.fused_moe(bf16_dev(x), bf16_dev(w1), bf16_dev(w2), dev(ids), dev(w), block_m=bm)
+    t = lambda a: bf16_dev(np.ascontiguousarray(np.transpose(a, (0, 2, 1))))
+    out_t, _ = mg.fused_moe(bf16_dev(x), t(w1), t(w2), dev(ids), dev(w), block_m=bm, trans_b=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.fused_moe(x, w1, w2, ids, w, bm)
+    assert_close(oracle.bf16_to_f64(bf16_host(out)), ref, BF16_TOL, CHAIN_ELEM)
+    assert torch.equal(out, out_t)
