@@ -211,3 +211,68 @@ def test_fused_moe_random_shapes(seed):
     ref, _ = oracle.fused_moe(x, w1, w2, ids, w, bm)
     assert_close(oracle.bf16_to_f64(bf16_host(out)), ref, BF16_TOL, CHAIN_ELEM)
     assert torch.equal(out, out_t)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_wide_tiles_random_shapes(seed):
+    """Drawn shapes large enough for the 256 x 256-tile kernel (at least two
+    rounds of its tiles, contractions of 1024 or more): bf16 forward and dX
+    in either B layout, e4m3 forward, dX and dW.  Tile counts, and so the
+    size of the last round (whole, or cut along the contraction), vary with
+    the draw."""
+    r = np.random.default_rng(4000 + seed)
+    E = int(r.integers(1, 13))
+    ct = int(r.integers(5, 10))                       # column tiles of 256
+    N = 16 * int(r.integers((ct - 1) * 16 + 1, ct * 16 + 1))
+    K = 16 * int(r.integers(64, 101))                 # 1024 .. 1600
+    M = -(-520 // ct) * 256 + 16 * int(r.integers(0, 190))
+    sizes = wl.random_group_sizes(E, M, seed, zero_frac=0.2) if E > 1 else np.array([M], np.int32)
+    trans_b = bool(seed % 2)
+    # dX (output width K) takes the wide tiles only with two rounds of them
+    dx_wide = (M // 256 + min(M, E)) * (-(-K // 256)) >= 2 * 256
+    X = wl.normal_bf16((M, K), 1.0, seed, wl.T_X)
+    W = wl.stacked_normal_bf16(E, (K, N), 0.05, seed, wl.T_W)
+    dY = wl.normal_bf16((M, N), 1.0, seed, wl.T_DY)
+    Wg = np.ascontiguousarray(np.transpose(W, (0, 2, 1))) if trans_b else W
+    x, w, dy, gs = bf16_dev(X), bf16_dev(Wg), bf16_dev(dY), dev(sizes)
+    ws = mg.workspace(E, M)
+    yb, y = _guarded((M, N), torch.bfloat16, 7.0)
+    mg.gmm_fwd(x, w, gs, trans_b=trans_b, out=y, ws=ws)
+    assert mg.last_gemm_tile_m() == 256
+    dxb, dx = _guarded((M, K), torch.bfloat16, 7.0)
+    mg.gmm_bwd(dy, x, w, gs, trans_b=trans_b, need_dw=False, dx=dx, ws=ws)
+    assert mg.last_gemm_tile_m() == (256 if dx_wide else 128)
+    torch.cuda.synchronize()
+    assert _guard_intact(yb, y.numel(), 7.0) and _guard_intact(dxb, dx.numel(), 7.0)
+    f = lambda t: oracle.bf16_to_f64(bf16_host(t))
+    Xf, Wf, dYf = (oracle.bf16_to_f64(a) for a in (X, W, dY))
+    assert_close(f(y), oracle.gmm_fwd(Xf, Wf, sizes), BF16_TOL, GEMM_BF16, "Y", fwd_norms(Xf, Wf, sizes))
+    assert_close(f(dx), oracle.gmm_dx(dYf, Wf, sizes), BF16_TOL, GEMM_BF16, "dX", dx_norms(dYf, Wf, sizes))
+    # e4m3 on the same operands
+    xq, sx = oracle.quant_rowwise(X)
+    wqc, swc = oracle.quant_colwise(W.reshape(E * K, N), np.full(E, K, np.int32))
+    dyq, sdy = oracle.quant_rowwise(dY)
+    wqr, swr = oracle.quant_rowwise(W.reshape(E * K, N))
+    yb8, y8 = _guarded((M, N), torch.bfloat16, 7.0)
+    mg.gmm_fwd_fp8(dev(xq), dev(sx), dev(wqc), dev(swc), E * K, K, gs, N, out=y8, ws=ws)
+    assert mg.last_gemm_tile_m() == 256
+    dxb8, dx8 = _guarded((M, K), torch.bfloat16, 7.0)
+    mg.gmm_bwd_fp8(gs, K, N, dyq=dev(dyq), sdy=dev(sdy), wq=dev(wqr), sw=dev(swr), w_ld=N, w_expert_stride=K * N,
+                   need_dw=False, dx=dx8, ws=ws)
+    assert mg.last_gemm_tile_m() == (256 if dx_wide else 128)
+    dyc, sdyc = oracle.quant_colwise(dY, sizes)
+    xc, sxc = oracle.quant_colwise(X, sizes)
+    dwb8, dw8 = _guarded((E, K, N), torch.bfloat16, 7.0)
+    mg.gmm_bwd_fp8(gs, K, N, xc=dev(xc), sxc=dev(sxc), dyc=dev(dyc), sdyc=dev(sdyc), need_dx=False, dw=dw8, ws=ws)
+    torch.cuda.synchronize()
+    for b, t in ((yb8, y8), (dxb8, dx8), (dwb8, dw8)):
+        assert _guard_intact(b, t.numel(), 7.0)
+    assert mg.workspace_error(ws) == 0
+    A = oracle.dequant_rowwise(xq, sx)
+    Wc = oracle.dequant_colwise(wqc, swc, np.full(E, K, np.int32)).reshape(E, K, N)
+    assert_close(f(y8), oracle.gmm_fwd(A, Wc, sizes), FP8_TOL, GEMM_FP8, "Y8", fwd_norms(A, Wc, sizes))
+    Wr = oracle.dequant_rowwise(wqr, swr).reshape(E, K, N)
+    dYr = oracle.dequant_rowwise(dyq, sdy)
+    assert_close(f(dx8), oracle.gmm_dx(dYr, Wr, sizes), FP8_TOL, GEMM_FP8, "dX8", dx_norms(dYr, Wr, sizes))
+    Xc, dYc = oracle.dequant_colwise(xc, sxc, sizes), oracle.dequant_colwise(dyc, sdyc, sizes)
+    assert_close(f(dw8), oracle.gmm_dw(Xc, dYc, sizes), FP8_TOL, GEMM_FP8, "dW8", dw_norms(Xc, dYc, sizes))
