@@ -276,3 +276,48 @@ def test_wide_tiles_random_shapes(seed):
     assert_close(f(dx8), oracle.gmm_dx(dYr, Wr, sizes), FP8_TOL, GEMM_FP8, "dX8", dx_norms(dYr, Wr, sizes))
     Xc, dYc = oracle.dequant_colwise(xc, sxc, sizes), oracle.dequant_colwise(dyc, sdyc, sizes)
     assert_close(f(dw8), oracle.gmm_dw(Xc, dYc, sizes), FP8_TOL, GEMM_FP8, "dW8", dw_norms(Xc, dYc, sizes))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_f8i4_split_random_shapes(seed):
+    """Sparse M with the rows in one to three experts of up to 16: the items
+    then fill a fraction of a grid sized for one tile per possible expert,
+    so the contraction is split across workgroups (pieces summed by the
+    last to arrive); odd chunk counts and the 8-wave kernel (64 chunks or
+    more) come up among the draws."""
+    r = np.random.default_rng(5000 + seed)
+    E = int(r.integers(2, 17))
+    touched = r.choice(E, size=int(r.integers(1, 4)), replace=False)
+    total_M = int(r.integers(1, 61))
+    K = 128 * int(r.integers(1, 81))
+    N = 8 * int(r.integers(1, 65))
+    counts = np.zeros(E, np.int32)
+    for i in range(total_M):
+        counts[touched[i % len(touched)]] += 1
+    X = wl.normal_bf16((total_M, K), 1.0, seed, wl.T_X)
+    xq, sx = oracle.quant_rowwise(X)
+    Xd = oracle.dequant_rowwise(xq, sx)
+    offs = oracle.offsets(counts)
+    w4 = torch.zeros(E, N, K // 2, dtype=torch.uint8, device="cuda")
+    sw = torch.zeros(E, K // 128, N, dtype=torch.bfloat16, device="cuda")
+    ref = np.zeros((total_M, N))
+    cn = np.zeros((E, N))
+    for e in np.flatnonzero(counts):
+        We = oracle.bf16_to_f64(wl.normal_bf16((K, N), 0.02, seed, wl.T_W, int(e)))[None]
+        p, q = oracle.quant_int4(We, 128)
+        w4[e] = dev(p[0])
+        sw[e] = bf16_dev(q[0])
+        Wq = oracle.dequant_int4(p, q, 128)
+        rows = slice(offs[e], offs[e + 1])
+        ref[rows] = oracle.gmm_fwd(Xd[rows], Wq, np.array([counts[e]]))
+        cn[e] = vec_norms(Wq[0], 0)
+    yb, y = _guarded((total_M, N), torch.bfloat16, 7.0)
+    ws = mg.workspace(E, total_M)
+    mg.gmm_fwd_f8i4(dev(xq), dev(sx), w4, sw, dev(counts), out=y, ws=ws)
+    y2 = mg.gmm_fwd_f8i4(dev(xq), dev(sx), w4, sw, dev(counts), ws=ws)   # counters back at zero: same bits
+    torch.cuda.synchronize()
+    assert _guard_intact(yb, y.numel(), 7.0)
+    assert torch.equal(y, y2)
+    assert mg.workspace_error(ws) == 0
+    assert_close(oracle.bf16_to_f64(bf16_host(y)), ref, FP8_TOL, GEMM_FP8, "Y",
+                 (vec_norms(Xd, 1), cn, group_rows(counts, total_M)))
