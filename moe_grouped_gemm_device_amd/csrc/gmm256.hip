@@ -563,7 +563,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // so acc[i][j] holds the transposed 32 x 32 block: lane l has output row
   // 32 i + l % 32 of the wave's block and columns 32 j + 8 q + 4 (l / 32) + r
   // in element 4 q + r.
-  auto mfma_one = [&](const Frag256<ELEM>& f, int n) __attribute__((always_inline)) {
+  // LIVE false: the wave's 128 x 128 quadrant lies wholly outside the
+  // tile's valid rows or columns, and its MFMAs are left out (the transfers,
+  // fragment reads and barriers stay, so every wave follows one schedule).
+  auto mfma_one = [&](const Frag256<ELEM>& f, int n, auto live_c) __attribute__((always_inline)) {
+    if constexpr (!decltype(live_c)::value) return;
     const int i = n >> 2, j = n & 3;
     if constexpr (ELEM == EL_BF16)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
@@ -573,13 +577,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int RPG = NREAD / 8;
   // A sub-step inside a k-step (bf16 only): the 16 MFMAs on cur, the reads
   // of nxt (the k-step's second sub-step) interleaved, one read per 2 MFMAs.
-  auto inner_sub = [&](const Frag256<ELEM>& cur, Frag256<ELEM>& nxt, int st) __attribute__((always_inline)) {
+  auto inner_sub = [&](const Frag256<ELEM>& cur, Frag256<ELEM>& nxt, int st, auto live_c)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int r = 0; r < RPG; ++r) read_one(nxt, st, 1, t * RPG + r);
-      mfma_one(cur, 2 * t);
-      mfma_one(cur, 2 * t + 1);
+      mfma_one(cur, 2 * t, live_c);
+      mfma_one(cur, 2 * t + 1, live_c);
       G256_FENCE();
     }
   };
@@ -588,12 +593,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // with the other 14 MFMAs.  At an item's last k-step (LAST) neither: the
   // refill waits for the epilogue, which stages the output in stage j, and
   // the next k-step's fragments are read after it.
-  auto boundary_sub = [&](const Frag256<ELEM>& cur, Frag256<ELEM>& nxt, int stj, auto last_c)
+  auto boundary_sub = [&](const Frag256<ELEM>& cur, Frag256<ELEM>& nxt, int stj, auto last_c, auto live_c)
       __attribute__((always_inline)) {
     constexpr bool LAST = decltype(last_c)::value;
     const int stn = stj + 1 == NS ? 0 : stj + 1;
-    mfma_one(cur, 0);
-    mfma_one(cur, 1);
+    mfma_one(cur, 0, live_c);
+    mfma_one(cur, 1, live_c);
     G256_FENCE();
     wait_vm_sync<(NS - 2) * LPW>();
     if constexpr (!LAST) {
@@ -607,15 +612,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int r = 0; r < RPG; ++r) read_one(nxt, stn, 0, t * RPG + r);
         if (t < 7) {
-          mfma_one(cur, 2 + 2 * t);
-          mfma_one(cur, 3 + 2 * t);
+          mfma_one(cur, 2 + 2 * t, live_c);
+          mfma_one(cur, 3 + 2 * t, live_c);
         }
         G256_FENCE();
       }
     } else {
       G256_FENCE();
 #pragma unroll
-      for (int n = 2; n < 16; ++n) mfma_one(cur, n);
+      for (int n = 2; n < 16; ++n) mfma_one(cur, n, live_c);
       G256_FENCE();
     }
   };
@@ -931,13 +936,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // One k-step on cur (its first sub-step's fragments); the next k-step's
   // first fragments end up in nxt (bf16: back in cur), except after an
   // item's last k-step.
-  auto kstep = [&](Frag256<ELEM>& cur, Frag256<ELEM>& nxt, auto last_c) __attribute__((always_inline)) {
+  auto kstep = [&](Frag256<ELEM>& cur, Frag256<ELEM>& nxt, auto last_c, auto live_c) __attribute__((always_inline)) {
     const int st = stage;
     if constexpr (KSUB == 2) {
-      inner_sub(cur, nxt, st);
-      boundary_sub(nxt, cur, st, last_c);
+      inner_sub(cur, nxt, st, live_c);
+      boundary_sub(nxt, cur, st, last_c, live_c);
     } else {
-      boundary_sub(cur, nxt, st, last_c);
+      boundary_sub(cur, nxt, st, last_c, live_c);
     }
     stage = st + 1 == NS ? 0 : st + 1;
   };
@@ -969,29 +974,44 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
   };
-  for (;;) {
-    // every k-step of the item but the last refills the stage it used
+  // every k-step of the item but the last refills the stage it used
+  auto item_steps = [&](auto live_c) __attribute__((always_inline)) {
     const int nst = ci.nsteps;
     if constexpr (KSUB == 2) {
-      for (int s = 0; s + 1 < nst; ++s) kstep(F0, F1, BoolConst<false>{});
+      for (int s = 0; s + 1 < nst; ++s) kstep(F0, F1, BoolConst<false>{}, live_c);
     } else {
       // e4m3: one sub-step per k-step, fragments alternate between F0 and F1
       int s = 0;
       for (; s + 2 < nst; s += 2) {
         edge_mask(F0, s);
-        kstep(F0, F1, BoolConst<false>{});
+        kstep(F0, F1, BoolConst<false>{}, live_c);
         edge_mask(F1, s + 1);
-        kstep(F1, F0, BoolConst<false>{});
+        kstep(F1, F0, BoolConst<false>{}, live_c);
       }
       if (s + 1 < nst) {
         edge_mask(F0, s);
-        kstep(F0, F1, BoolConst<false>{});
+        kstep(F0, F1, BoolConst<false>{}, live_c);
         F0 = F1;   // once per item
       }
     }
-    const int st_last = stage;
+    const int stl = stage;   // the last k-step's stage
     edge_mask(F0, nst - 1);
-    kstep(F0, F1, BoolConst<true>{});
+    kstep(F0, F1, BoolConst<true>{}, live_c);
+    return stl;
+  };
+  for (;;) {
+    // a wave whose quadrant has no valid row or column (the bottom half of a
+    // group's last row tile, the right half of a last column tile) skips its
+    // MFMAs.  bf16 without the SiLU*mul epilogue only: there a second copy of
+    // the k-loop costs registers the epilogue needs (spills), and the e4m3
+    // kernels measured slower with it (their registers are laid out anew).
+    int st_last;
+    if constexpr (SWIGLU || ELEM != EL_BF16) {
+      st_last = item_steps(BoolConst<true>{});
+    } else {
+      const bool live = wm * 128 < ci.m_valid && wn * 128 < ci.n_valid;
+      st_last = live ? item_steps(BoolConst<true>{}) : item_steps(BoolConst<false>{});
+    }
     // the last k-step's stage holds the epilogue's staging, then its refill
     bool write = true;
     int npieces = 0;
