@@ -125,6 +125,7 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
   static_assert(WL_BYTES >= F_WAVES * F_BM * F_BN * 4, "the reduction fits the weight buffers");
   float(*red)[F_BM * F_BN] = reinterpret_cast<float(*)[F_BM * F_BN]>(wl);
   __shared__ int s_last;
+  __shared__ float s_rs[F_BM];   // the tile's activation row scales
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int K = a.Kc;
   const int N = a.Nout;
@@ -141,6 +142,7 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
   // their scales get one descriptor per expert, since all experts' int4
   // weights together may pass 2 GiB)
   const __amdgpu_buffer_rsrc_t xr = f_rsrc(a.A, a.total_rows * (int64_t)K);
+  const __amdgpu_buffer_rsrc_t sar = f_rsrc(a.sa, a.total_rows * 4);
   const uint8_t* w4 = reinterpret_cast<const uint8_t*>(a.B);
 
   // K pieces per item: more than one only while the items leave slots idle,
@@ -181,6 +183,16 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
     const int half = lane >> 5;
     const bool col_ok = n0 + col < N;
     const bool row_ok = col < m_valid;   // A fragment row = lane % 32
+    // thread r < F_BM: the activation scale of the tile's row r, requested
+    // before the K loop (older than every load the loop's waits count, so it
+    // has landed by the first of them) and put in LDS after it, for the
+    // output stores
+    float rsv;
+    {
+      uint32_t so = tid < m_valid ? (uint32_t)((row0 + tid) * 4) : F_OOB;
+      asm volatile("" : "+v"(so));
+      rsv = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sar, (int)so, 0, 0));
+    }
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
@@ -336,6 +348,7 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
     // every transfer of this wave has landed, and every wave is done with
     // its weight buffers, before they hold the reduction
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid < F_BM) s_rs[tid] = rsv;
     __syncthreads();
 
     // cross-wave reduction of the K slices, in a fixed order
@@ -352,7 +365,7 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
           float sum = red[0][idx];
 #pragma unroll
           for (int q = 1; q < F_WAVES; ++q) sum += red[q][idx];
-          const float y = sum * (1.f / a.sa[row0 + r]);
+          const float y = sum * (1.f / s_rs[r]);
           reinterpret_cast<uint16_t*>(a.C)[(row0 + r) * a.c_ld + n0 + c] = (uint16_t)f32_to_bf16_rne(y);
         }
       }
@@ -388,7 +401,7 @@ __global__ void __launch_bounds__(F_WAVES * 64) f8i4_kernel(GemmArgs a) {
                   pr, (int)(((w * S + q) * (F_BM * F_BN) + idx) * 4), 0, F_DEVICE));
               sum = q == 0 ? v : sum + v;
             }
-            const float y = sum * (1.f / a.sa[row0 + r]);
+            const float y = sum * (1.f / s_rs[r]);
             reinterpret_cast<uint16_t*>(a.C)[(row0 + r) * a.c_ld + n0 + c] = (uint16_t)f32_to_bf16_rne(y);
           }
         }
