@@ -74,19 +74,37 @@ __device__ inline int64_t block_incl_scan64(int64_t x, int64_t* s_wave) {
 // thread) an error code: 0, 1 (a negative size) or 2 (sizes sum past
 // total_M).  want_order builds the dynamic-K ordering (O(E^2/256) work)
 // instead of the fixed-M tile starts.
-// Up to 64 groups, one per lane of wave 0: no workgroup-wide scans, one
-// barrier.  The running sum of the sizes saturates at total_M + 1 (every
-// partial sum then fits 32 bits, and min(sum, total_M) and "sum > total_M"
-// are unchanged), so the results equal the general path's.
+// Up to 64 * P groups, P consecutive groups per lane of wave 0: no
+// workgroup-wide scans, one barrier.  The running sum of the sizes saturates
+// at total_M + 1 (every partial sum then fits 32 bits, and min(sum, total_M)
+// and "sum > total_M" are unchanged; a saturating sum of non-negative terms
+// does not depend on how the terms are grouped), so the results equal the
+// general path's.
+template <int P>
 __device__ inline int build_group_table_wave(const int32_t* __restrict__ sizes, int E, int64_t total_M, int bm,
                                              bool want_order, GroupTable t) {
   const int lane = threadIdx.x & (kWave - 1);
   if (threadIdx.x < kWave) {
-    const bool mine = lane < E;
-    const int32_t raw = mine ? sizes[lane] : 0;
+    const int g0 = lane * P;
     const uint32_t cap = (uint32_t)(total_M + 1);   // total_M < 2^31
-    const uint32_t v0 = raw > 0 ? ((uint32_t)raw < cap ? (uint32_t)raw : cap) : 0u;
-    uint32_t incl = v0;
+    const uint32_t tm = (uint32_t)total_M;
+    int32_t raw[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) raw[i] = g0 + i < E ? sizes[g0 + i] : 0;
+    // the lane's own groups: saturating inclusive sums
+    uint32_t pre[P];
+    uint32_t run = 0;
+    bool neg = false;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      neg = neg || raw[i] < 0;
+      const uint32_t v = raw[i] > 0 ? ((uint32_t)raw[i] < cap ? (uint32_t)raw[i] : cap) : 0u;
+      const uint64_t sum = (uint64_t)run + v;
+      run = sum < cap ? (uint32_t)sum : cap;
+      pre[i] = run;
+    }
+    // lane totals across the wave
+    uint32_t incl = run;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
       const uint32_t o = (uint32_t)__shfl_up((int)incl, d, kWave);
@@ -95,37 +113,66 @@ __device__ inline int build_group_table_wave(const int32_t* __restrict__ sizes, 
         incl = sum < cap ? (uint32_t)sum : cap;
       }
     }
-    const uint32_t excl = (uint32_t)__shfl_up((int)incl, 1, kWave);
-    const uint32_t tm = (uint32_t)total_M;
-    const uint32_t a = lane == 0 ? 0u : (excl < tm ? excl : tm);
-    const uint32_t b = incl < tm ? incl : tm;
-    const int32_t eff = mine ? (int32_t)(b - a) : 0;
-    const int32_t tiles = (int32_t)(((uint32_t)eff + (uint32_t)bm - 1u) / (uint32_t)bm);
+    const uint32_t up = (uint32_t)__shfl_up((int)incl, 1, kWave);
+    const uint32_t excl = lane == 0 ? 0u : up;
+    int32_t off[P], eff[P];
+    int32_t tiles = 0;
+    uint32_t a = excl < tm ? excl : tm;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const uint64_t sum = (uint64_t)excl + pre[i];
+      const uint32_t end = sum < cap ? (uint32_t)sum : cap;
+      const uint32_t b = end < tm ? end : tm;
+      off[i] = (int32_t)a;
+      eff[i] = (int32_t)(b - a);   // 0 past E: those groups add nothing
+      tiles += (int32_t)(((uint32_t)eff[i] + (uint32_t)bm - 1u) / (uint32_t)bm);
+      a = b;
+    }
     int32_t tincl = tiles;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
       const int32_t o = __shfl_up(tincl, d, kWave);
       if (lane >= d) tincl += o;
     }
-    if (mine) {
-      t.off[lane] = (int32_t)a;
-      t.eff[lane] = eff;
-      if (!want_order) t.tstart[lane] = tincl - tiles;
+    int32_t tr = tincl - tiles;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (g0 + i < E) {
+        t.off[g0 + i] = off[i];
+        t.eff[g0 + i] = eff[i];
+        if (!want_order) t.tstart[g0 + i] = tr;
+      }
+      tr += (int32_t)(((uint32_t)eff[i] + (uint32_t)bm - 1u) / (uint32_t)bm);
     }
-    const uint32_t total = (uint32_t)__shfl((int)incl, E - 1, kWave);
-    if (lane == E - 1) {
+    // the last lane's inclusive sums are the totals (lanes past E add 0)
+    const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1, kWave);
+    const int32_t ttotal = __shfl(tincl, kWave - 1, kWave);
+    if (lane == 0) {
       t.off[E] = (int32_t)(total < tm ? total : tm);
-      if (!want_order) t.tstart[E] = tincl;
+      if (!want_order) t.tstart[E] = ttotal;
     }
-    const bool any_neg = __ballot(mine && raw < 0) != 0;
+    const bool any_neg = __ballot(neg) != 0;
     const bool any_over = total > tm;
     if (want_order) {   // every lane of the wave takes part in the shuffles
-      int rank = 0;
-      for (int h = 0; h < E; ++h) {
-        const int32_t e = __shfl(eff, h, kWave);
-        rank += (e > eff) || (e == eff && h < lane);
+      // rank of group g: groups with a larger size, or the same size and a
+      // smaller index (a slot past E holds size 0 and a larger index than
+      // any group, so it never counts)
+      int rank[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i) rank[i] = 0;
+      const int lanes = (E + P - 1) / P;
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        for (int hl = 0; hl < lanes; ++hl) {
+          const int32_t e = __shfl(eff[j], hl, kWave);
+          const int h = hl * P + j;
+#pragma unroll
+          for (int i = 0; i < P; ++i) rank[i] += (e > eff[i]) || (e == eff[i] && h < g0 + i);
+        }
       }
-      if (mine) t.order[rank] = lane;
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        if (g0 + i < E) t.order[rank[i]] = g0 + i;
     }
     if (lane == 0) t.scratch[15] = any_neg ? 1 : any_over ? 2 : 0;
   }
@@ -135,7 +182,8 @@ __device__ inline int build_group_table_wave(const int32_t* __restrict__ sizes, 
 
 __device__ inline int build_group_table(const int32_t* __restrict__ sizes, int E, int64_t total_M, int bm,
                                         bool want_order, GroupTable t) {
-  if (E <= kWave) return build_group_table_wave(sizes, E, total_M, bm, want_order, t);
+  if (E <= kWave) return build_group_table_wave<1>(sizes, E, total_M, bm, want_order, t);
+  if (E <= 4 * kWave) return build_group_table_wave<4>(sizes, E, total_M, bm, want_order, t);
   const int tid = threadIdx.x;
   const int per = (E + kTableThreads - 1) / kTableThreads;   // groups per thread (<= 4)
   const int g0 = tid * per;

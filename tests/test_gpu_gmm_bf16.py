@@ -26,6 +26,9 @@ def _gpu():
     (4, 37, 16, 0), (8, 1024, 128, 1), (128, 1, 32, 2), (128, 16, 32, 3), (128, 128, 32, 4),
     (64, 5000, 128, 5), (1024, 20000, 16, 6), (1, 0, 128, 7), (7, 3, 1, 8), (300, 777, 64, 9),
     (65, 5000, 128, 10), (63, 999, 16, 11), (1, 77, 16, 12),
+    # four groups per lane of one wave (65..256 groups), ragged last lane
+    (129, 3000, 32, 13), (255, 70000, 128, 14), (256, 256, 1, 15), (256, 0, 32, 16), (257, 4000, 64, 17),
+    (200, 9, 16, 18),
 ])
 def test_builder_fixed_m_bit_exact(E, total, bm, seed):
     sizes = wl.random_group_sizes(E, total, seed, zero_frac=0.5)
@@ -38,7 +41,8 @@ def test_builder_fixed_m_bit_exact(E, total, bm, seed):
 
 
 @pytest.mark.parametrize("E,total,seed", [(8, 1024, 0), (64, 98304, 1), (1024, 3000, 2), (3, 0, 3), (128, 1, 4),
-                                          (65, 4000, 5), (1, 9, 6)])
+                                          (65, 4000, 5), (1, 9, 6), (129, 5000, 7), (256, 100000, 8),
+                                          (255, 300, 9), (257, 6000, 10), (200, 0, 11)])
 def test_builder_dynamic_k_bit_exact(E, total, seed):
     sizes = wl.random_group_sizes(E, total, seed, zero_frac=0.3)
     sizes[: E // 3] = sizes[0]   # ties
@@ -71,7 +75,7 @@ def test_builder_flags_bad_sizes_without_writing_out_of_bounds():
     assert mg.workspace_error(ws) == 0
 
 
-@pytest.mark.parametrize("E", [64, 65])   # one-wave table build, and the workgroup-wide one
+@pytest.mark.parametrize("E", [64, 65, 256, 257])   # one group per lane, four per lane, workgroup-wide
 def test_builder_flags_survive_int32_running_sums(E):
     M, K, N = 64, 64, 64
     big = 2**31 - 1
