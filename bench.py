@@ -456,17 +456,19 @@ def _row_cases(torch, mg):
     sx = torch.empty(M, dtype=torch.float32, device="cuda")
     yield ("A5_quantize_rowwise_fp8", f"X [{M},{H}] bf16 -> e4m3 + row scales",
            lambda: mg.quantize_rowwise_fp8(X, q=xq, scales=sx), M * H * 3 + M * 4, "GB/s", PEAK_HBM_GBS, 10)
-    cq = (torch.zeros(I, M, dtype=torch.uint8, device="cuda"), torch.empty(E, I, dtype=torch.float32, device="cuda"),
-          torch.zeros(H, M, dtype=torch.uint8, device="cuda"), torch.empty(E, H, dtype=torch.float32, device="cuda"))
+    ldc = mg.colwise_ld(M)   # code rows of the column-major operands, padded as the library pads them
+    cq = (torch.zeros(I, ldc, dtype=torch.uint8, device="cuda")[:, :M],
+          torch.empty(E, I, dtype=torch.float32, device="cuda"),
+          torch.zeros(H, ldc, dtype=torch.uint8, device="cuda")[:, :M],
+          torch.empty(E, H, dtype=torch.float32, device="cuda"))
     yield ("A6_quantize_colwise_dual", f"dY [{M},{I}] and X [{M},{H}], {E} Zipf groups -> column-major e4m3",
            lambda: mg.quantize_colwise_per_group_fp8(dY, sizes, b=X, out=cq),
            M * (I + H) * 3 + E * (I + H) * 4, "GB/s", PEAK_HBM_GBS, 10)
     dyc, sdyc, xc, sxc = cq
-    wq_c, sw_c = mg.quantize_colwise_per_group_fp8(W.reshape(E * H, I),
-                                                   torch.full((E,), H, dtype=torch.int32, device="cuda"))
+    wq_c, sw_c = mg.quantize_fp8_expert_weights(W)
     y = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
     yield ("A7_fp8_gmm_fwd", f"Y [{M},{I}] = Xq . Wq_g, K={H}",
-           lambda: mg.gmm_fwd_fp8(xq, sx, wq_c, sw_c, E * H, H, sizes, I, out=y, ws=ws),
+           lambda: mg.gmm_fwd_fp8(xq, sx, wq_c, sw_c, None, H, sizes, I, out=y, ws=ws),
            2.0 * M * H * I, "TFLOP/s", PEAK_FP8_TFLOPS, 10)
     dyq = torch.empty(M, I, dtype=torch.uint8, device="cuda")
     sdy = torch.empty(M, dtype=torch.float32, device="cuda")

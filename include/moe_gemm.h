@@ -72,9 +72,10 @@ enum {
 /* ------------------------------------------------------------------------ */
 
 /* Bytes of device workspace that a grouped-GEMM call with these E and
- * total_M needs: a 256-byte header (the sticky error word, and the two
+ * total_M needs: a 256-byte header (the sticky error word, and the
  * counters of the work queue that the 256 x 256-tile dW kernel deals
- * unequal groups' tiles from), 256 arrival counters (one per split tile or
+ * unequal groups' tiles from: one shared, one per XCD, one of finished
+ * workgroups), 256 arrival counters (one per split tile or
  * stream-K workgroup) and 64 MiB of fp32 partial output tiles (two
  * 128 x 256 tiles per workgroup of the 8-wave kernel, one 256 x 256 tile
  * per workgroup of the 4-wave kernel), about 64 MiB in all.  The work
@@ -251,13 +252,19 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w,
  *       [E][K] (the rowwise quantizer on W viewed [E*K, N] gives ld = N,
  *       expert_stride = K*N);
  *   dw[g,k,n] = sum_{r in g} (xc[k,r]/sxc[g,k]) * (dyc[n,r]/sdyc[g,n])
- *       xc e4m3 column-major [K][total_M] with sxc [E][K], dyc column-major
- *       [N][total_M] with sdyc [E][N] (the dual per-group colwise quantizer);
- *       dw bf16 [E, K, N]; empty groups give zero.
+ *       xc e4m3 column-major, xc[k,r] at xc + k*ldc + r, with sxc [E][K];
+ *       dyc column-major, dyc[n,r] at dyc + n*ldc + r, with sdyc [E][N]
+ *       (the dual per-group colwise quantizer); dw bf16 [E, K, N]; empty
+ *       groups give zero.  Bytes of a row past total_M are never used.
+ *   ldc the row stride of xc and dyc in bytes: a multiple of 16, at least
+ *       total_M (ignored without dw).  A stride that is a multiple of a
+ *       large power of two (98304 = 3 * 2^15 bytes, say) puts the 256 rows
+ *       a tile reads on the same few HBM channels: an odd multiple of 256
+ *       avoids that.
  * total_M must be a multiple of 16 when dw is requested. */
 int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w,
                 const uint8_t* xc, const float* sxc, const uint8_t* dyc,
-                const float* sdyc, const int32_t* group_sizes, int32_t E,
+                const float* sdyc, int64_t ldc, const int32_t* group_sizes, int32_t E,
                 int64_t total_M, int32_t K, int32_t N, void* dx, void* dw,
                 void* ws, size_t ws_bytes, mg_stream_t stream);
 
@@ -314,11 +321,14 @@ int quantize_rowwise_fp8_gather(const void* x, int64_t T, const int32_t* sorted_
 
 /* Per-group colwise, single or dual: for each group g and column c of a
  * (and of b, if non-NULL), one scale over the group's rows.  Codes are
- * written column-major: qa[c * rows + r]; scales sa[g * cols_a + c].  b,
+ * written column-major: qa[c * ld + r]; scales sa[g * cols_a + c].  b,
  * qb, sb are either all NULL (single tensor) or all set (both tensors share
  * the group sizes and row count).  Rows beyond the sizes' sum are not
- * written; an empty group gets the scales of amax 0.  cols % 8 == 0,
- * cols <= 2^20; 1 <= G <= MG_MAX_EXPERTS; rows < 2^31.
+ * written, nor are the bytes r in [rows, ld) of a code row; an empty group
+ * gets the scales of amax 0.  cols % 8 == 0, cols <= 2^20;
+ * 1 <= G <= MG_MAX_EXPERTS; rows < 2^31; rows <= ld < 2^32 (ld, the code
+ * rows' stride in bytes, shared by qa and qb: see gmm_bwd_fp8's ldc for
+ * the choice that keeps the fp8 dW off a few HBM channels).
  *
  * Two kernel launches.  Work is cut into (tensor, group, 64-column
  * block) sets.  A group of at most 256 rows is one chunk; a longer group's
@@ -347,8 +357,8 @@ size_t quantize_colwise_workspace_bytes(int32_t G, int64_t rows, int32_t cols_a,
 int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a,
                                    const void* b, int32_t cols_b,
                                    const int32_t* group_sizes, int32_t G,
-                                   int64_t rows, uint8_t* qa, float* sa,
-                                   uint8_t* qb, float* sb, void* ws,
+                                   int64_t rows, int64_t ld, uint8_t* qa,
+                                   float* sa, uint8_t* qb, float* sb, void* ws,
                                    size_t ws_bytes, mg_stream_t stream);
 
 /* int4 weight quantizer for gmm_fwd_f8i4: w bf16 [E, K, N] -> w4 packed

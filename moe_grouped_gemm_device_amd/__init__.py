@@ -48,14 +48,14 @@ _SIGS = {
     "gmm_fwd_silu_mul": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gmm_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "gmm_fwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
-    "gmm_bwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32,
-                                   _P, _P, _P, _SZ, _P]),
+    "gmm_bwd_fp8": (ctypes.c_int, [_P, _P, ctypes.POINTER(FP8Weight), _P, _P, _P, _P, _I64, _P, _I32, _I64, _I32,
+                                   _I32, _P, _P, _P, _SZ, _P]),
     "gmm_fwd_f8i4": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "quantize_rowwise_fp8": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P, _P]),
     "quantize_rowwise_fp8_gather": (ctypes.c_int, [_P, _I64, _P, _I32, _I64, _I32, _P, _P, _P]),
     "quantize_colwise_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32]),
-    "quantize_colwise_per_group_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _I32, _I64, _P, _P, _P, _P, _P,
-                                                      _SZ, _P]),
+    "quantize_colwise_per_group_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _I32, _I64, _I64, _P, _P, _P, _P,
+                                                      _P, _SZ, _P]),
     "quantize_int4_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "moe_sorted_capacity": (_I64, [_I64, _I32, _I32, _I32]),
     "moe_block_capacity": (_I64, [_I64, _I32, _I32, _I32]),
@@ -306,11 +306,22 @@ def gmm_bwd(dy, x, w, group_sizes, trans_b=False, need_dx=True, need_dw=True, dx
 # --------------------------------------------------------------------------
 
 def _fp8w(codes, scales, ld, expert_stride):
+    """The weight descriptor; ld (the bytes between output columns' code
+    runs) defaults to the codes tensor's row stride, and an explicit ld must
+    equal it (a colwise-quantized weight is a view of padded rows)."""
+    if codes.dim() < 2 or codes.stride(-1) != 1:
+        raise ValueError("fp8 weight codes need at least 2 dimensions and a unit last stride")
+    row = codes.stride(-2)
+    if ld is None:
+        ld = row
+    elif int(ld) != row:
+        raise ValueError(f"w_ld={ld} differs from the codes' row stride {row}")
     return FP8Weight(codes.data_ptr(), scales.data_ptr(), int(ld), int(expert_stride))
 
 
 def gmm_fwd_fp8(xq, sx, wq, sw, w_ld, w_expert_stride, group_sizes, N, out=None, ws=None, stream=None):
-    """y[r,n] = sum_k (xq[r,k]/sx[r]) (Wq(g,k,n)/sw[g,n]); Wq(e,k,n) at e*w_expert_stride + n*w_ld + k."""
+    """y[r,n] = sum_k (xq[r,k]/sx[r]) (Wq(g,k,n)/sw[g,n]); Wq(e,k,n) at e*w_expert_stride + n*w_ld + k.
+    w_ld None: the row stride of wq."""
     _need(xq, torch.uint8, "xq", 2)
     _need(sx, torch.float32, "sx", 1)
     _need(group_sizes, torch.int32, "group_sizes", 1)
@@ -324,7 +335,7 @@ def gmm_fwd_fp8(xq, sx, wq, sw, w_ld, w_expert_stride, group_sizes, N, out=None,
     return y
 
 
-def gmm_bwd_fp8(group_sizes, K, N, dyq=None, sdy=None, wq=None, sw=None, w_ld=0, w_expert_stride=0,
+def gmm_bwd_fp8(group_sizes, K, N, dyq=None, sdy=None, wq=None, sw=None, w_ld=None, w_expert_stride=0,
                 xc=None, sxc=None, dyc=None, sdyc=None, need_dx=True, need_dw=True, dx=None, dw=None,
                 ws=None, stream=None):
     """fp8 backward; see gmm_bwd_fp8 in include/moe_gemm.h for operand layouts."""
@@ -332,6 +343,14 @@ def gmm_bwd_fp8(group_sizes, K, N, dyq=None, sdy=None, wq=None, sw=None, w_ld=0,
     E = group_sizes.numel()
     dev = group_sizes.device
     M = dyq.shape[0] if dyq is not None else xc.shape[1]
+    ldc = 0
+    if need_dw:
+        for t, name in ((xc, "xc"), (dyc, "dyc")):
+            if t is None or t.dtype != torch.uint8 or t.dim() != 2 or t.device.type != "cuda" or t.stride(1) != 1:
+                raise ValueError(f"{name} must be a 2-D uint8 device tensor with unit column stride")
+        ldc = xc.stride(0)
+        if dyc.stride(0) != ldc or xc.shape[1] != M or dyc.shape[1] != M:
+            raise ValueError("xc and dyc must be [K, M] and [N, M] views with one row stride")
     if need_dx and dx is None:
         dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
     if need_dw and dw is None:
@@ -339,7 +358,7 @@ def gmm_bwd_fp8(group_sizes, K, N, dyq=None, sdy=None, wq=None, sw=None, w_ld=0,
     ws = default_workspace(dev, stream) if ws is None else ws
     wd = _fp8w(wq, sw, w_ld, w_expert_stride) if need_dx else None
     _call("gmm_bwd_fp8", _ptr(dyq), _ptr(sdy), ctypes.byref(wd) if wd is not None else None, _ptr(xc),
-          _ptr(sxc), _ptr(dyc), _ptr(sdyc), _ptr(group_sizes), E, M, int(K), int(N),
+          _ptr(sxc), _ptr(dyc), _ptr(sdyc), ldc, _ptr(group_sizes), E, M, int(K), int(N),
           _ptr(dx if need_dx else None), _ptr(dw if need_dw else None), _ptr(ws), ws.numel(), _stream(stream))
     return (dx if need_dx else None), (dw if need_dw else None)
 
@@ -436,12 +455,24 @@ def default_colwise_workspace(nbytes, device=None, stream=None):
     return ws
 
 
+def colwise_ld(M):
+    """Row stride (bytes) the colwise quantizer's fresh outputs get for M
+    rows: M rounded up to an odd multiple of 256.  The fp8 dW reads 256 such
+    rows per tile at once; with a stride that is a multiple of a large power
+    of two (98304 rows = 3 * 2^15, say) they share a few HBM channels."""
+    ld = (int(M) + 255) // 256 * 256
+    return ld + 256 if (ld // 256) % 2 == 0 else ld
+
+
 def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None, ws=None):
     """Per-group colwise quantization of a (and b).  Returns
     (qa [Ca, M] column-major codes, sa [G, Ca]) or, with b,
-    (qa, sa, qb, sb).  Codes of rows past the groups are not written (a
-    fresh output holds whatever its allocation held there); out=(qa, sa[,
-    qb, sb]) reuses buffers, checked for dtype, shape and device.  ws: a
+    (qa, sa, qb, sb).  Fresh code tensors are [C, M] views of [C,
+    colwise_ld(M)] buffers.  Codes of rows past the groups, and the bytes
+    past M of a code row, are not written (a fresh output holds whatever
+    its allocation held there); out=(qa, sa[, qb, sb]) reuses buffers,
+    checked for dtype, shape and device (code tensors: unit column stride,
+    row stride at least M, the same for qa and qb).  ws: a
     uint8 device tensor of at least colwise_workspace_bytes(G, M, Ca, Cb)
     bytes whose first word (the sticky error word) starts at zero (default:
     the cached one of the device and stream)."""
@@ -450,16 +481,21 @@ def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None
     M, Ca = a.shape
     G = group_sizes.numel()
     def check(q, sc, C, name):
-        _need(q, torch.uint8, "q" + name, 2)
+        if q.device.type != "cuda" or q.dtype != torch.uint8 or q.dim() != 2:
+            raise ValueError(f"q{name} must be a 2-D uint8 device tensor")
+        if q.stride(1) != 1 or q.stride(0) < M:
+            raise ValueError(f"q{name} needs a unit column stride and a row stride of at least {M}")
         _need(sc, torch.float32, "s" + name, 2)
         if tuple(q.shape) != (C, M) or tuple(sc.shape) != (G, C) or q.device != a.device or sc.device != a.device:
             raise ValueError(f"q{name} must be [{C}, {M}] and s{name} [{G}, {C}] on the input's device")
 
+    ld = colwise_ld(M)
     if out is not None:
         qa, sa = out[0], out[1]
         check(qa, sa, Ca, "a")
+        ld = qa.stride(0)
     else:
-        qa = torch.empty(Ca, M, dtype=torch.uint8, device=a.device)
+        qa = torch.empty(Ca, ld, dtype=torch.uint8, device=a.device)[:, :M]
         sa = torch.empty(G, Ca, dtype=torch.float32, device=a.device)
     qb = sb = None
     Cb = 0
@@ -471,8 +507,10 @@ def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None
         if out is not None:
             qb, sb = out[2], out[3]
             check(qb, sb, Cb, "b")
+            if qb.stride(0) != ld:
+                raise ValueError("qa and qb must have the same row stride")
         else:
-            qb = torch.empty(Cb, M, dtype=torch.uint8, device=a.device)
+            qb = torch.empty(Cb, ld, dtype=torch.uint8, device=a.device)[:, :M]
             sb = torch.empty(G, Cb, dtype=torch.float32, device=a.device)
     need = colwise_workspace_bytes(G, M, Ca, Cb)
     if ws is None:
@@ -481,7 +519,7 @@ def quantize_colwise_per_group_fp8(a, group_sizes, b=None, stream=None, out=None
         _need(ws, torch.uint8, "ws", 1)
         if ws.device != a.device:
             raise ValueError("ws must be on the input's device")
-    _call("quantize_colwise_per_group_fp8", _ptr(a), Ca, _ptr(b), Cb, _ptr(group_sizes), G, M, _ptr(qa),
+    _call("quantize_colwise_per_group_fp8", _ptr(a), Ca, _ptr(b), Cb, _ptr(group_sizes), G, M, ld, _ptr(qa),
           _ptr(sa), _ptr(qb), _ptr(sb), _ptr(ws), ws.numel(), _stream(stream))
     return (qa, sa) if b is None else (qa, sa, qb, sb)
 
@@ -571,12 +609,16 @@ def quantize_fp8_expert_weights(w, stream=None):
     """Expert weights w bf16 [E, K, N] -> (wq uint8 [N, E*K], sw fp32 [E, N]):
     column-major e4m3 codes with one power-of-two scale per (expert, output
     column) over its K weights.  This is the per-group colwise quantizer on w
-    viewed as [E*K, N] with E groups of K rows; gmm_fwd_fp8 takes the result
-    with w_ld = E*K and w_expert_stride = K."""
+    viewed as [E*K, N] with E groups of K rows, into contiguous codes (the
+    forward reads weight rows E*K bytes apart faster than the padded rows
+    the quantizer gives activations); gmm_fwd_fp8 takes them with w_ld =
+    E*K (or None) and w_expert_stride = K."""
     _need(w, torch.bfloat16, "w", 3)
     E, K, N = w.shape
     sizes = torch.full((E,), K, dtype=torch.int32, device=w.device)
-    return quantize_colwise_per_group_fp8(w.reshape(E * K, N), sizes, stream=stream)
+    out = (torch.empty(N, E * K, dtype=torch.uint8, device=w.device),
+           torch.empty(E, N, dtype=torch.float32, device=w.device))
+    return quantize_colwise_per_group_fp8(w.reshape(E * K, N), sizes, stream=stream, out=out)
 
 
 def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=None, stream=None,
@@ -603,10 +645,10 @@ def fused_moe_fp8(x, w1q, s1, w2q, s2, topk_ids, topk_weights, block_m=None, ws=
     ws = default_workspace(x.device, stream) if ws is None else ws
     # the token rows are read through the sorted order by the quantizer
     xq, sx = quantize_rowwise_fp8_gather(x, ids, k, stream=stream)
-    h1 = gmm_fwd_fp8(xq, sx, w1q, s1, E * H, H, sizes, two_i, ws=ws, stream=stream)
+    h1 = gmm_fwd_fp8(xq, sx, w1q, s1, None, H, sizes, two_i, ws=ws, stream=stream)
     act = torch.empty(h1.shape[0], inter, dtype=torch.bfloat16, device=x.device) if keep_act else None
     aq, sa = silu_mul_quantize_rowwise_fp8(h1, act=act, stream=stream)
-    y2 = gmm_fwd_fp8(aq, sa, w2q, s2, E * inter, inter, sizes, H, ws=ws, stream=stream)
+    y2 = gmm_fwd_fp8(aq, sa, w2q, s2, None, inter, sizes, H, ws=ws, stream=stream)
     out = moe_unpermute(y2, p["inv"], topk_weights, T, k, stream=stream)
     return out, dict(permute=p, xq=xq, sx=sx, h1=h1, act=act, aq=aq, sa=sa, y2=y2)
 

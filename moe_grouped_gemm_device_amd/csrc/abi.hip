@@ -455,8 +455,8 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w, cons
 }
 
 int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, const uint8_t* xc,
-                const float* sxc, const uint8_t* dyc, const float* sdyc, const int32_t* group_sizes, int32_t E,
-                int64_t total_M, int32_t K, int32_t N, void* dx, void* dw, void* ws, size_t ws_bytes,
+                const float* sxc, const uint8_t* dyc, const float* sdyc, int64_t ldc, const int32_t* group_sizes,
+                int32_t E, int64_t total_M, int32_t K, int32_t N, void* dx, void* dw, void* ws, size_t ws_bytes,
                 mg_stream_t stream) {
   int rc = check_common(group_sizes, E, total_M, ws, ws_bytes);
   if (rc) return rc;
@@ -473,6 +473,8 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
   if (dw) {
     if (!sxc || !sdyc || (total_M > 0 && (!xc || !dyc))) return fail(MG_EINVAL, "NULL dw operand");
     if (total_M % 16) return fail(MG_EUNSUPPORTED, "dw needs total_M % 16 == 0");
+    if (ldc < total_M || ldc % 16) return fail(MG_EINVAL, "ldc must be a multiple of 16 and at least total_M");
+    if ((rc = check_extents(ldc, K, N, 1))) return rc;
     if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "dw needs K and N multiples of 8");
     if (!aligned16(xc) || !aligned16(dyc) || !aligned16(dw)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
   }
@@ -508,9 +510,9 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
   } else if (dw) {
     GemmArgs a = blank_args();
     a.A = xc;
-    a.a_ld = total_M;
+    a.a_ld = ldc;
     a.B = dyc;
-    a.b_ld = total_M;
+    a.b_ld = ldc;
     a.b_gs = 0;
     a.C = dw;
     a.c_ld = N;
@@ -605,10 +607,12 @@ size_t quantize_colwise_workspace_bytes(int32_t G, int64_t rows, int32_t cols_a,
 }
 
 int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a, const void* b, int32_t cols_b,
-                                   const int32_t* group_sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
-                                   uint8_t* qb, float* sb, void* ws, size_t ws_bytes, mg_stream_t stream) {
+                                   const int32_t* group_sizes, int32_t G, int64_t rows, int64_t ld, uint8_t* qa,
+                                   float* sa, uint8_t* qb, float* sb, void* ws, size_t ws_bytes,
+                                   mg_stream_t stream) {
   if (G < 1 || G > MG_MAX_EXPERTS) return fail(MG_EINVAL, "G=%d outside [1, %d]", G, MG_MAX_EXPERTS);
   if (rows < 0 || rows >= kMaxRows) return fail(MG_EINVAL, "rows out of range");
+  if (ld < rows || ld >= 2 * kMaxRows) return fail(MG_EINVAL, "ld=%lld below rows or out of range", (long long)ld);
   if (!a || !qa || !sa || !group_sizes) return fail(MG_EINVAL, "NULL tensor argument");
   const bool dual = b != nullptr;
   if (dual != (qb != nullptr) || dual != (sb != nullptr)) return fail(MG_EINVAL, "b, qb, sb must be all set or all NULL");
@@ -624,7 +628,7 @@ int quantize_colwise_per_group_fp8(const void* a, int32_t cols_a, const void* b,
                 (long long)L.total);
   return hip_status(launch_quant_colwise(reinterpret_cast<const uint16_t*>(a), cols_a,
                                          reinterpret_cast<const uint16_t*>(b), dual ? cols_b : 0, group_sizes, G,
-                                         rows, qa, sa, qb, sb, ws, S(stream)),
+                                         rows, ld, qa, sa, qb, sb, ws, S(stream)),
                     "quantize_colwise_per_group_fp8");
 }
 

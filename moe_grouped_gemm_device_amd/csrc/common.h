@@ -19,10 +19,11 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
 
 // Workspace layout (bytes).  The header holds the sticky error word and
-// the two counters of a work-queue launch.
+// the counters of a work-queue launch.
 constexpr int64_t kWsHeader = 256;
 constexpr int kWsErrorWord = 0;   // int32 index into the header
-constexpr int kWsQueueWord = 1;   // work-queue counters at words 1 and 9: items handed out, workgroups finished
+constexpr int kWsQueueWord = 1;   // work-queue counters: words 1 (items handed out), 9 (workgroups finished)
+                                  // and 17-24 (items handed out of each XCD's run)
 constexpr int kMinTileM = 16;     // smallest row tile any kernel uses
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

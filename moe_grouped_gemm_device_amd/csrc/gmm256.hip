@@ -69,6 +69,8 @@ constexpr int64_t PART = 256LL * 256 * 4;   // one fp32 partial tile (split dyna
 constexpr int PART_SLOTS = (int)(2 * kSkMaxGrid * kSkPartBytes / PART);   // partial slots in the workspace
 constexpr int64_t MIN_PIECE = 8;            // shortest piece of a split dynamic-K contraction (k-steps)
 constexpr int64_t TAIL_PIECE = 32;          // shortest piece of a split fixed-M last-round tile (k-steps)
+constexpr int64_t DK_CAP_DIV = 1;           // dynamic-K split: pieces of at most a workgroup's share / this
+constexpr int64_t HEAD_PCT = 60;            // unequal dynamic-K items: percent of the work dealt by XCD
 
 // chunk swizzle of a contraction-contiguous tile: line L holds rows 2L, 2L+1
 __device__ inline int kc_swz(int L) { return (L ^ (L >> 1)) & 3; }
@@ -154,13 +156,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // counter per split tile (kSkMaxGrid), one partial slot per piece
   // (PART_SLOTS).  Every workgroup computes the same plan from the table.
   __shared__ DkSplit sp;
+  auto steps_of = [&](int g) -> int64_t {   // k-steps of group g's contraction (dynamic-K)
+    const int32_t off = tab.off[g], eff = tab.eff[g];
+    if (eff <= 0) return 1;
+    const int64_t start = (int64_t)off & ~(int64_t)15;
+    return cdiv((int64_t)off + eff - start, BK);
+  };
   if constexpr (DK) {
-    auto steps_of = [&](int g) -> int64_t {   // k-steps of group g's contraction
-      const int32_t off = tab.off[g], eff = tab.eff[g];
-      if (eff <= 0) return 1;
-      const int64_t start = (int64_t)off & ~(int64_t)15;
-      return cdiv((int64_t)off + eff - start, BK);
-    };
     int64_t mine = 0;
     for (int g = tid; g < a.E; g += 256) mine += steps_of(g);
     const int64_t all = block_incl_scan64(mine, tab.scratch);   // the last thread's value is the total
@@ -168,7 +170,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     __syncthreads();
     if (tid == 0) {
       const int per = m_tiles_dk * n_tiles;
-      int64_t cap = cdiv(tab.scratch[15] * per, G);
+      int64_t cap = cdiv(tab.scratch[15] * per, (int64_t)G * DK_CAP_DIV);
       if (cap < MIN_PIECE) cap = MIN_PIECE;
       int ns = 0, slots = 0;
       sp.items_before[0] = 0;
@@ -219,12 +221,63 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Zipf-skewed groups of a DeepSeek-MoE layer share, it still beats a
   // static longest-first deal.)
   const bool dyn = DK && !equal_items;
+  // With a grid of whole XCD rounds, the queue has two levels.  The first
+  // HEAD_PCT percent of the work (the longest items) is cut into 8 runs of
+  // equal work, one per XCD, each handed out by that XCD's own counter.
+  // The tiles of one group share their operand slabs, and a run keeps them
+  // in one L2: measured on the Zipf-skewed groups of a DeepSeek-MoE layer
+  // share, a single queue spread every group over all 8 L2s and fetched
+  // 8 times the operand bytes.  The rest, the short items, comes from one
+  // counter shared by all, which evens out the finish.
+  const bool xq = HEAD_PCT > 0 && dyn && (G & 7) == 0;
+  __shared__ int32_t seg[9];   // XCD x's run: items [seg[x], seg[x + 1]); seg[8]: the first shared item
+  if (xq) {
+    const int per_t = m_tiles_dk * n_tiles;
+    const int ns = sp.groups;
+    const int pp = (a.E + 255) / 256;   // group-order positions per thread (<= 4)
+    const int q0 = tid * pp;
+    int64_t wl = 0;   // work (k-steps x tiles) of this thread's positions
+    for (int i = 0; i < pp; ++i)
+      if (q0 + i < a.E) wl += steps_of(tab.order[q0 + i]) * per_t;
+    const int64_t incl = block_incl_scan64(wl, tab.scratch);
+    const int64_t head = tab.scratch[15] * per_t * HEAD_PCT / 100;   // of all the work
+    int64_t before = incl - wl;
+    for (int i = 0; i < pp; ++i) {
+      const int q = q0 + i;
+      if (q >= a.E) break;
+      const int64_t wq_ = steps_of(tab.order[q]) * per_t;
+      const int64_t n = q < ns ? (int64_t)sp.pieces[q] * per_t : per_t;   // its items, of equal work
+      const int64_t ib = q < ns ? sp.items_before[q] : sp.items_before[ns] + (int64_t)(q - ns) * per_t;
+      for (int x = 1; x <= 8; ++x) {   // the item where work head * x / 8 falls
+        const int64_t t = head * x / 8;
+        if (t >= before && t < before + wq_) seg[x] = (int32_t)(ib + (t - before) * n / wq_);
+      }
+      before += wq_;
+    }
+    if (tid == 0) seg[0] = 0;
+    __syncthreads();
+  }
   __shared__ int32_t qring[16];   // the workgroup's n-th item at [n % 16] (-1: none)
+  bool own_left = true;           // (thread 0) the XCD's run may hold more items
   auto grab = [&](int64_t n) __attribute__((always_inline)) {
     if (tid == 0) {
       int code = -1;
-      if (n == 0) code = (int)blockIdx.x;
-      else {
+      if (xq) {
+        const int x = blockIdx.x & 7;
+        if (own_left) {
+          const int l = n == 0 ? (int)(blockIdx.x >> 3)
+                               : (G >> 3) + __hip_atomic_fetch_add(a.wq + 16 + x, 1, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT);
+          if (l >= 0 && l < seg[x + 1] - seg[x]) code = seg[x] + l;
+          else own_left = false;
+        }
+        if (code < 0) {
+          const int l = __hip_atomic_fetch_add(a.wq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (l >= 0 && l < items - seg[8]) code = seg[8] + l;
+        }
+      } else if (n == 0) {
+        code = (int)blockIdx.x;
+      } else {
         const int l = G + __hip_atomic_fetch_add(a.wq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (l >= 0 && l < items) code = l;
       }
@@ -238,6 +291,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (done == G - 1) {
         __hip_atomic_store(a.wq, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.wq + 8, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int x = 0; x < 8; ++x) __hip_atomic_store(a.wq + 16 + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   };

@@ -125,7 +125,7 @@ struct ColwiseLayout {
 ColwiseLayout colwise_layout(int32_t G, int64_t rows, int32_t cols_a, int32_t cols_b);
 hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_t* b,
                                 int32_t cols_b, const int32_t* sizes, int32_t G,
-                                int64_t rows, uint8_t* qa, float* sa, uint8_t* qb,
+                                int64_t rows, int64_t ld, uint8_t* qa, float* sa, uint8_t* qb,
                                 float* sb, void* ws, hipStream_t stream);
 hipError_t launch_quant_int4(const uint16_t* w, int32_t E, int32_t K, int32_t N,
                              uint8_t* w4, uint16_t* sw, hipStream_t stream);

@@ -316,6 +316,7 @@ struct ColwiseArgs {
   int32_t G;
   int32_t ntensors;
   int64_t rows;
+  int64_t ld;         // bytes from one code row (input column) to the next, >= rows
   int32_t* err;       // sticky error word (invalid group sizes)
   uint32_t* part;     // partial maxima: 64 words per (chunk slot, column block)
   int64_t part_t1;    // word offset of tensor 1's partials
@@ -493,7 +494,7 @@ __device__ inline void cw_chunk(const ColwiseArgs& a, const CwChunk& c, CwShared
   const int cc = tid & 7, rg = tid >> 3;   // 8-column group, row group (rows 8 rg .. 8 rg + 7)
   const int t = c.t, cb = c.cb;
   const int ncb = a.ncb[t], cols = a.cols[t];
-  const int64_t M = a.rows;
+  const int64_t LD = a.ld;
   const int64_t row_bytes = 2 * (int64_t)cols;
   const uint32_t vo0 = (uint32_t)(rg * CW_RPT * row_bytes) + (uint32_t)(cc * 16);
   constexpr int WAVE_ROWS = CW_CHUNK / 4;   // rows of wave w: [WAVE_ROWS w, WAVE_ROWS (w + 1))
@@ -600,7 +601,7 @@ __device__ inline void cw_chunk(const ColwiseArgs& a, const CwChunk& c, CwShared
       // byte offset of the column's first row of this run within its 16-byte
       // piece
       const int64_t col = cb * CW_COLS + tid;
-      L.sh[tid] = (int)((reinterpret_cast<uintptr_t>(a.q[t]) + (uint64_t)(col * M + s0)) & 15u);
+      L.sh[tid] = (int)((reinterpret_cast<uintptr_t>(a.q[t]) + (uint64_t)(col * LD + s0)) & 15u);
     }
     __syncthreads();   // sc and sh visible; the tile's previous contents consumed
     if (WAVE_ROWS * wave < nr) {
@@ -618,7 +619,7 @@ __device__ inline void cw_chunk(const ColwiseArgs& a, const CwChunk& c, CwShared
     }
     __syncthreads();
     // Column-major stores.  Column cl's rows [0, nr) start at global byte
-    // address A = col * M + s0 (plus the base), which sits sh bytes into a
+    // address A = col * LD + s0 (plus the base), which sits sh bytes into a
     // 16-byte piece; piece p covers rows [16 p - sh, 16 p - sh + 16).  Its
     // bytes come from the tile by a byte funnel shift of aligned words.
     // Pieces the run fills are stored whole here; the others (shared with a
@@ -634,7 +635,7 @@ __device__ inline void cw_chunk(const ColwiseArgs& a, const CwChunk& c, CwShared
         edges = true;
         continue;
       }
-      uint8_t* dst = a.q[t] + (int64_t)col * M + s0 + lo;   // 16-byte aligned
+      uint8_t* dst = a.q[t] + (int64_t)col * LD + s0 + lo;   // 16-byte aligned
       const int d0 = lo >> 2, bs = lo & 3;                   // first word, byte shift
       uint32_t w[5];
 #pragma unroll
@@ -669,7 +670,7 @@ __device__ inline void cw_chunk(const ColwiseArgs& a, const CwChunk& c, CwShared
           if (e - 16 >= tail) continue;
           r = head + 16 * whole + (e - 16);
         }
-        a.q[t][(int64_t)col * M + s0 + r] = L.tile[cw_tile_unit(cl, r >> 4) + (r & 15)];
+        a.q[t][(int64_t)col * LD + s0 + r] = L.tile[cw_tile_unit(cl, r >> 4) + (r & 15)];
       }
     }
     __syncthreads();   // the tile and sh are free again
@@ -704,7 +705,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 5))
 }
 
 hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_t* b, int32_t cols_b,
-                                const int32_t* sizes, int32_t G, int64_t rows, uint8_t* qa, float* sa,
+                                const int32_t* sizes, int32_t G, int64_t rows, int64_t ld, uint8_t* qa, float* sa,
                                 uint8_t* qb, float* sb, void* ws, hipStream_t stream) {
   const ColwiseLayout L = colwise_layout(G, rows, cols_a, b != nullptr ? cols_b : 0);
   ColwiseArgs x;
@@ -722,6 +723,7 @@ hipError_t launch_quant_colwise(const uint16_t* a, int32_t cols_a, const uint16_
   x.sizes = sizes;
   x.G = G;
   x.rows = rows;
+  x.ld = ld;
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   x.err = reinterpret_cast<int32_t*>(w);
   x.part = reinterpret_cast<uint32_t*>(w + L.part_off);

@@ -119,9 +119,18 @@ def test_fp8_and_f8i4_reject_unsupported_alignment(lib):
                             _p(0x10000), need, None) == mg.MG_EUNSUPPORTED  # K % 128
     assert lib.gmm_fwd_f8i4(_p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 4, 64, 65536, 65536, _p(FAKE),
                             _p(0x10000), need, None) == mg.MG_EUNSUPPORTED  # one expert's weights past 2 GiB
-    assert lib.gmm_bwd_fp8(None, None, None, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 4, 40, 64, 64,
+    assert lib.gmm_bwd_fp8(None, None, None, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 48, _p(FAKE), 4, 40, 64, 64,
                            None, _p(FAKE), _p(0x10000), lib.mg_workspace_bytes(4, 40),
                            None) == mg.MG_EUNSUPPORTED                   # dw needs total_M % 16
+
+
+def test_fp8_dw_rejects_bad_row_stride(lib):
+    need = lib.mg_workspace_bytes(4, 64)
+    dw = lambda ldc: lib.gmm_bwd_fp8(None, None, None, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), ldc, _p(FAKE), 4, 64,
+                                     64, 64, None, _p(FAKE), _p(0x10000), need, None)
+    assert dw(48) == mg.MG_EINVAL         # below total_M
+    assert dw(72) == mg.MG_EINVAL         # not a multiple of 16
+    assert dw(1 << 30) == mg.MG_EUNSUPPORTED   # K rows of that stride past 2 GiB
 
 
 def test_colwise_workspace_size(lib):
@@ -140,18 +149,20 @@ def test_quantizers_reject_bad_arguments(lib):
     assert lib.quantize_rowwise_fp8(_p(FAKE), 4, 16, 8, _p(FAKE), _p(FAKE), None) == mg.MG_EINVAL
     cw = lib.quantize_colwise_per_group_fp8
     need = lib.quantize_colwise_workspace_bytes(4, 64, 16, 16)
-    assert cw(_p(FAKE), 16, _p(FAKE), 16, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, _p(FAKE),
+    assert cw(_p(FAKE), 16, _p(FAKE), 16, _p(FAKE), 4, 64, 64, _p(FAKE), _p(FAKE), None, _p(FAKE),
               _p(0x10000), need, None) == mg.MG_EINVAL        # b without qb
-    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 0, 64, _p(FAKE), _p(FAKE), None, None,
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 0, 64, 64, _p(FAKE), _p(FAKE), None, None,
               _p(0x10000), need, None) == mg.MG_EINVAL        # G = 0
-    assert cw(_p(FAKE), (1 << 20) + 8, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+    assert cw(_p(FAKE), (1 << 20) + 8, None, 0, _p(FAKE), 4, 64, 64, _p(FAKE), _p(FAKE), None, None,
               _p(0x10000), 1 << 40, None) == mg.MG_EUNSUPPORTED   # cols above 2^20
-    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, 64, _p(FAKE), _p(FAKE), None, None,
               None, need, None) == mg.MG_EWORKSPACE           # no workspace
-    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, 64, _p(FAKE), _p(FAKE), None, None,
               _p(0x10080), need, None) == mg.MG_EWORKSPACE    # not 256-byte aligned
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, 63, _p(FAKE), _p(FAKE), None, None,
+              _p(0x10000), need, None) == mg.MG_EINVAL        # code rows closer than the row count
     single = lib.quantize_colwise_workspace_bytes(4, 64, 16, 0)
-    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, _p(FAKE), _p(FAKE), None, None,
+    assert cw(_p(FAKE), 16, None, 0, _p(FAKE), 4, 64, 64, _p(FAKE), _p(FAKE), None, None,
               _p(0x10000), single - 4, None) == mg.MG_EWORKSPACE   # too small
     assert lib.quantize_int4_weights(_p(FAKE), 2, 100, 16, _p(FAKE), _p(FAKE), None) == mg.MG_EUNSUPPORTED
     g = lib.quantize_rowwise_fp8_gather

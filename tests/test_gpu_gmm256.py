@@ -129,6 +129,19 @@ def test_fp8_dw_skewed_groups():
     Xc, dYc = oracle.dequant_colwise(xc, sxc, sizes), oracle.dequant_colwise(dyc, sdyc, sizes)
     assert_close(dwh, oracle.gmm_dw(Xc, dYc, sizes), FP8_TOL, GEMM_FP8, "dW", dw_norms(Xc, dYc, sizes))
     assert (dwh[1] == 0).all()
+    # the same codes in rows of a padded stride (the library's own, and a
+    # 16-byte multiple off every power of two) whose pad bytes are NaN
+    # codes: the pads are never used, so the bits do not change
+    for ld in (mg.colwise_ld(M), M + 48):
+        xp = torch.full((Kq, ld), 0x7F, dtype=torch.uint8, device="cuda")
+        dp = torch.full((Nq, ld), 0x7F, dtype=torch.uint8, device="cuda")
+        xp[:, :M].copy_(dev(xc))
+        dp[:, :M].copy_(dev(dyc))
+        _, dw3 = mg.gmm_bwd_fp8(dev(sizes), Kq, Nq, xc=xp[:, :M], sxc=dev(sxc), dyc=dp[:, :M], sdyc=dev(sdyc),
+                                need_dx=False, ws=ws)
+        _wide()
+        torch.cuda.synchronize()
+        assert torch.equal(dw3, dw), ld
 
 
 @pytest.mark.parametrize("trans_b", [False, True])

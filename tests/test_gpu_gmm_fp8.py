@@ -63,6 +63,30 @@ def test_fp8_backward(E, M, K, N, seed):
     assert_close(dwh, oracle.gmm_dw(Xc, dYc, sizes), FP8_TOL, GEMM_FP8, "dW", dw_norms(Xc, dYc, sizes))
     for g in np.flatnonzero(sizes == 0):
         assert (dwh[g] == 0).all()
+    # xc and dyc in rows of a padded stride whose pad bytes are NaN codes:
+    # same bits (the dW reads nothing past total_M in a row)
+    ld = M + 48
+    xp = torch.full((K, ld), 0x7F, dtype=torch.uint8, device="cuda")
+    dp = torch.full((N, ld), 0x7F, dtype=torch.uint8, device="cuda")
+    xp[:, :M].copy_(dev(xc))
+    dp[:, :M].copy_(dev(dyc))
+    _, dw2 = mg.gmm_bwd_fp8(dev(sizes), K, N, xc=xp[:, :M], sxc=dev(sxc), dyc=dp[:, :M], sdyc=dev(sdyc),
+                            need_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dw2, dw)
+
+
+def test_fp8_weight_row_stride_must_match_the_codes():
+    wq = torch.zeros(64, 256, dtype=torch.uint8, device="cuda")[:, :128]
+    sw = torch.ones(1, 64, dtype=torch.float32, device="cuda")
+    xq = torch.zeros(16, 128, dtype=torch.uint8, device="cuda")
+    sx = torch.ones(16, dtype=torch.float32, device="cuda")
+    gs = torch.tensor([16], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        mg.gmm_fwd_fp8(xq, sx, wq, sw, 128, 128, gs, 64)   # the view's rows are 256 bytes apart
+    y = mg.gmm_fwd_fp8(xq, sx, wq, sw, None, 128, gs, 64)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
 
 
 def _f8i4_case(E, total_M, K, N, seed, counts=None):

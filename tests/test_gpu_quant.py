@@ -111,6 +111,31 @@ def test_colwise_dual_equals_two_singles_and_oracle():
     _check_colwise(b, sizes, qb, sb)
 
 
+@pytest.mark.parametrize("pad", [37, None])   # an odd stride, and the library's own (colwise_ld)
+def test_colwise_padded_code_rows(pad):
+    """Code rows ld bytes apart: the codes equal those of contiguous rows,
+    and the bytes past M of every row keep what they held."""
+    M, G = 3000, 6
+    sizes = wl.random_group_sizes(G, M, 11, zero_frac=0.2)
+    a = wl.normal_bf16((M, 136), 1.0, 11, wl.T_DY)
+    b = wl.normal_bf16((M, 264), 1.0, 11, wl.T_X)
+    gs = dev(sizes)
+    ld = M + pad if pad is not None else mg.colwise_ld(M)
+    qa = torch.full((136, ld), 0xA5, dtype=torch.uint8, device="cuda")
+    qb = torch.full((264, ld), 0xA5, dtype=torch.uint8, device="cuda")
+    out = (qa[:, :M], torch.empty(G, 136, dtype=torch.float32, device="cuda"),
+           qb[:, :M], torch.empty(G, 264, dtype=torch.float32, device="cuda"))
+    mg.quantize_colwise_per_group_fp8(bf16_dev(a), gs, b=bf16_dev(b), out=out)
+    ref = (torch.empty(136, M, dtype=torch.uint8, device="cuda"), torch.empty(G, 136, dtype=torch.float32, device="cuda"),
+           torch.empty(264, M, dtype=torch.uint8, device="cuda"), torch.empty(G, 264, dtype=torch.float32, device="cuda"))
+    mg.quantize_colwise_per_group_fp8(bf16_dev(a), gs, b=bf16_dev(b), out=ref)
+    torch.cuda.synchronize()
+    for u, v in zip(out, ref):
+        assert torch.equal(u, v)
+    assert (qa[:, M:] == 0xA5).all() and (qb[:, M:] == 0xA5).all()
+    _check_colwise(a, sizes, out[0], out[1])
+
+
 def test_colwise_rows_outside_groups_untouched():
     M, C = 300, 64
     sizes = np.array([50, 0, 70], np.int32)       # covers 120 rows
