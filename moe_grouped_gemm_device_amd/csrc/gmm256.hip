@@ -41,8 +41,8 @@
 //    the transfer that would refill that stage is issued after the
 //    epilogue and a barrier.
 //  * Each XCD owns a contiguous eighth of the tiles and its workgroups take
-//    them round-robin; tiles come in raster blocks of up to 4 row tiles, so
-//    the 32 tiles an XCD runs at once cover about 4 row tiles x 8 column
+//    them round-robin; tiles come in raster blocks of up to 5 row tiles, so
+//    the 32 tiles an XCD runs at once cover about 5 row tiles x 6 column
 //    tiles and share their operand slices in its L2.  When the XCD's last
 //    round would leave most of its workgroups idle (at most a quarter of
 //    them busy), each of that round's tiles is cut along the contraction
@@ -60,7 +60,7 @@ constexpr int NS = 4;                 // LDS stages
 constexpr int OPB = 256 * RB;         // bytes of one operand per stage (16 KB)
 constexpr int STAGE = 2 * OPB;        // 32 KB
 constexpr int LPW = 8;                // 16-byte transfers per lane per k-step (4 A + 4 B)
-constexpr uint32_t RASTER = 4;        // row tiles per raster block
+constexpr uint32_t RASTER = 5;        // row tiles per raster block
 constexpr int NSCB = NS + 1;          // fp8 scale buffers, used round-robin by item
 constexpr int SROW = 64 + 8;          // epilogue staging row (bf16 elements)
 static_assert(NW * 32 * SROW * 2 <= STAGE, "epilogue staging fits a stage");
