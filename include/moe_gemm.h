@@ -257,7 +257,7 @@ int gmm_fwd_fp8(const uint8_t* xq, const float* sx, const mg_fp8_weight* w,
  *       (the dual per-group colwise quantizer); dw bf16 [E, K, N]; empty
  *       groups give zero.  Bytes of a row past total_M are never used.
  *   ldc the row stride of xc and dyc in bytes: a multiple of 16, at least
- *       total_M (ignored without dw).  A stride that is a multiple of a
+ *       total_M (ignored without dw or without rows).  A stride that is a multiple of a
  *       large power of two (98304 = 3 * 2^15 bytes, say) puts the 256 rows
  *       a tile reads on the same few HBM channels: an odd multiple of 256
  *       avoids that.

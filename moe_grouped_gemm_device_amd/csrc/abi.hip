@@ -473,8 +473,9 @@ int gmm_bwd_fp8(const uint8_t* dyq, const float* sdy, const mg_fp8_weight* w, co
   if (dw) {
     if (!sxc || !sdyc || (total_M > 0 && (!xc || !dyc))) return fail(MG_EINVAL, "NULL dw operand");
     if (total_M % 16) return fail(MG_EUNSUPPORTED, "dw needs total_M % 16 == 0");
-    if (ldc < total_M || ldc % 16) return fail(MG_EINVAL, "ldc must be a multiple of 16 and at least total_M");
-    if ((rc = check_extents(ldc, K, N, 1))) return rc;
+    if (total_M > 0 && (ldc < total_M || ldc % 16))
+      return fail(MG_EINVAL, "ldc must be a multiple of 16 and at least total_M");
+    if (total_M > 0 && (rc = check_extents(ldc, K, N, 1))) return rc;
     if (K % 8 || N % 8) return fail(MG_EUNSUPPORTED, "dw needs K and N multiples of 8");
     if (!aligned16(xc) || !aligned16(dyc) || !aligned16(dw)) return fail(MG_EUNSUPPORTED, "tensors must be 16-byte aligned");
   }

@@ -76,6 +76,21 @@ def test_fp8_backward(E, M, K, N, seed):
     assert torch.equal(dw2, dw)
 
 
+def test_fp8_dw_without_rows_is_zero():
+    """No rows: every group is empty and dW is zero, whatever the empty
+    operands' strides."""
+    E, K, N = 3, 64, 48
+    gs = torch.zeros(E, dtype=torch.int32, device="cuda")
+    xc = torch.empty(K, 0, dtype=torch.uint8, device="cuda")
+    dyc = torch.empty(N, 0, dtype=torch.uint8, device="cuda")
+    sc = torch.ones(E, K, dtype=torch.float32, device="cuda")
+    sd = torch.ones(E, N, dtype=torch.float32, device="cuda")
+    dw = torch.full((E, K, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    mg.gmm_bwd_fp8(gs, K, N, xc=xc, sxc=sc, dyc=dyc, sdyc=sd, need_dx=False, dw=dw)
+    torch.cuda.synchronize()
+    assert (dw == 0).all()
+
+
 def test_fp8_weight_row_stride_must_match_the_codes():
     wq = torch.zeros(64, 256, dtype=torch.uint8, device="cuda")[:, :128]
     sw = torch.ones(1, 64, dtype=torch.float32, device="cuda")
