@@ -16,7 +16,11 @@ sample of the same workload, and the sparse-M latency of the F8I4 grouped
 GEMM (one routed token over 128 experts, K=5120, N=8192) next to the same
 call with a single expert.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 200] [--no-cpu]
+(The GPU's clocks settle only after some tens of milliseconds of sustained
+work: with 5 warmup steps, 1.5 ms, the timed steps of the balanced step ran
+at 487-497 TFLOP/s, with 200 at 645-653 on the same box; the defaults
+measure the steady state.)
 """
 import argparse
 import json
@@ -692,8 +696,8 @@ def cpu_baseline(host):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse-M latency measurement")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other configurations")
