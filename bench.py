@@ -412,11 +412,20 @@ def sparse_m_latency(torch, mg, reps=50):
     return res
 
 
-def _timeit(torch, fn, reps=10):
-    """Average microseconds of fn over reps back-to-back launches (HIP events)."""
-    fn()
-    torch.cuda.synchronize()
+def _timeit(torch, fn, reps=10, settle_ms=30.0):
+    """Average microseconds of fn over reps back-to-back launches (HIP events),
+    after untimed launches covering about settle_ms of GPU time (at most
+    200): the clocks settle only after some tens of milliseconds of
+    sustained work, and each row starts after its inputs were made."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    e1.synchronize()
+    one_ms = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(min(200, int(settle_ms / one_ms))):
+        fn()
+    torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
         fn()
