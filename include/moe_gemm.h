@@ -235,8 +235,9 @@ typedef struct mg_fp8_weight {
 /* Forward: Y[r, n] = sum_k (xq[r,k] / sx[r]) * (Wq(g,k,n) / sw[g,n]).
  *   xq  e4m3 [total_M, K] row-major, sx fp32 [total_M] (rowwise quantizer)
  *   w   codes of W(e,k,n) at e*expert_stride + n*ld + k, scales [E][N]
- *       (e.g. the colwise quantizer on W viewed [E*K, N] with E equal groups
- *       gives ld = E*K, expert_stride = K)
+ *       (e.g. the colwise quantizer on W viewed [E*K, N] with E equal groups,
+ *       its code rows ld bytes apart, gives that ld and expert_stride = K;
+ *       unpadded rows, ld = E*K, read fastest here)
  *   y   bf16 [total_M, N]
  * K must be a multiple of 16 and N a multiple of 8; ld and expert_stride
  * multiples of 16. */
